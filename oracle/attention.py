@@ -1,0 +1,130 @@
+"""Read path: one decode step of grouped-query attention and its risk meter.
+
+TEST INFRASTRUCTURE ONLY: nothing on the product path imports this module.
+
+For one (layer, request, KV head) slice with S cached tokens in logical order
+(shared prefix first, then the request's suffix; cartridge page, "One kernel
+spans cartridge and live KV": both regions form one sequence under one
+softmax), and each of the G query heads q_h sharing that KV head:
+
+    l_t  = sm_scale * <q_h, k_t>        exact keys
+    l~_t = sm_scale * <q_h, k^_t>       reconstructed (stored) keys
+    p = softmax(l),  p~ = softmax(l~)
+    out_h = sum_t p~_t v^_t
+    TV_h  = 1/2 sum_t |p_t - p~_t|                        (WitCert, Sec. 3)
+    c_t   = sm_scale * sum_b ||q_{h,b}|| w_{t,b}           (WitCert, Thm. 2)
+    log A = logsumexp(l~ + c) - logsumexp(l~)   (A = E_p~[e^c], Thm. 1, evaluated
+                                                 in the log domain, Sec. 3)
+    bound_raw = 1/2 (A^2 - 1) = 1/2 expm1(2 log A); +inf when it exceeds the
+                largest float32 (Sec. 6.2.4: overflow to +inf is sound)
+    meter = min(1, bound_raw)                              (Sec. 3 / Sec. 4.3)
+
+Everything is evaluated in float64; nothing is split or reordered beyond what
+the definitions state.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .quant import band_coords
+
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def logsumexp(x: np.ndarray, axis: int = -1) -> np.ndarray:
+    m = np.max(x, axis=axis, keepdims=True)
+    return (m + np.log(np.sum(np.exp(x - m), axis=axis, keepdims=True))).squeeze(axis)
+
+
+def softmax(x: np.ndarray, axis: int = -1) -> np.ndarray:
+    m = np.max(x, axis=axis, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def band_norms(q: np.ndarray, n_bands: int = 16) -> np.ndarray:
+    """||q_b|| for each band b (q shape (..., d))."""
+    q = np.asarray(q, np.float64)
+    coords = band_coords(q.shape[-1], n_bands)
+    return np.sqrt(np.sum(q[..., coords] ** 2, axis=-1))
+
+
+def total_variation(p: np.ndarray, p_tilde: np.ndarray) -> np.ndarray:
+    return 0.5 * np.sum(np.abs(p - p_tilde), axis=-1)
+
+
+def bound_from_log_a(log_a) -> np.ndarray:
+    """Theorem 1's 1/2 (A^2 - 1) from log A, +inf past the float32 range."""
+    log_a = np.asarray(log_a, np.float64)
+    with np.errstate(over="ignore"):
+        b = 0.5 * np.expm1(2.0 * log_a)
+    return np.where(b > FLT_MAX, np.inf, b)
+
+
+def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float):
+    """One (layer, request, KV head) cell.
+
+    q: (G, d) query heads sharing this KV head (float32 values).
+    k_exact, k_hat, v_hat: (S, d) exact keys, reconstructed keys and values.
+    w16: (S, B) stored witness (float16) or None when the stored keys are the
+         exact keys (then c = 0).
+    Returns a dict of float64 arrays: out (G, d), out_exact (G, d), tv, log_a,
+    bound_raw, meter (G,), plus the per-token logits and bounds for checks.
+    """
+    q = np.asarray(q, np.float64)
+    ke = np.asarray(k_exact, np.float64)
+    kh = np.asarray(k_hat, np.float64)
+    vh = np.asarray(v_hat, np.float64)
+    sm = float(sm_scale)
+    l_exact = sm * (q @ ke.T)                 # (G, S)
+    l_tilde = sm * (q @ kh.T)
+    p = softmax(l_exact)
+    pt = softmax(l_tilde)
+    out = pt @ vh
+    out_exact = p @ vh
+    tv = total_variation(p, pt)
+    if w16 is None:
+        c = np.zeros_like(l_tilde)
+    else:
+        qn = band_norms(q, np.asarray(w16).shape[1])          # (G, B)
+        c = sm * (qn @ np.asarray(w16, np.float64).T)         # (G, S)
+    log_a = logsumexp(l_tilde + c) - logsumexp(l_tilde)
+    bound_raw = bound_from_log_a(log_a)
+    meter = np.minimum(1.0, bound_raw)
+    return dict(out=out, out_exact=out_exact, tv=tv, log_a=log_a,
+                bound_raw=bound_raw, meter=meter, l_exact=l_exact,
+                l_tilde=l_tilde, c=c, p=p, p_tilde=pt)
+
+
+def kv_head_view(per_qhead: np.ndarray, group: int) -> np.ndarray:
+    """Any-of-G view: the maximum over the G query heads of each KV head."""
+    a = np.asarray(per_qhead)
+    return a.reshape(a.shape[:-1] + (a.shape[-1] // group, group)).max(axis=-1)
+
+
+def merge_partials(parts):
+    """Merge per-split (m, z, acc) online-softmax states (flash decoding).
+
+    parts: list of (m, z, acc) with acc = sum_t e^{l_t - m} v_t.  The merged
+    state equals the unsplit one exactly (up to rounding); used only to check
+    that splitting the sequence does not change the definition.
+    """
+    m = max(pm for pm, _, _ in parts)
+    z = sum(pz * math.exp(pm - m) for pm, pz, _ in parts)
+    acc = sum(pa * math.exp(pm - m) for pm, _, pa in parts)
+    return m, z, acc
+
+
+def flawed_dispersion_certificate(p_tilde, c) -> float:
+    """The unsound Eq. (1) of WitCert Sec. 3 (kept only to pin our reading).
+
+    1/2 e^{2 c_max} (E_p~[|c - c_bar|] + c_bar (e^{c_max} - 1)), c_bar = E_p~[c].
+    """
+    p_tilde = np.asarray(p_tilde, np.float64)
+    c = np.asarray(c, np.float64)
+    cbar = float(np.sum(p_tilde * c))
+    cmax = float(np.max(c))
+    return 0.5 * math.exp(2 * cmax) * (float(np.sum(p_tilde * np.abs(c - cbar)))
+                                        + cbar * (math.exp(cmax) - 1.0))

@@ -1,0 +1,121 @@
+"""Write path of the quantized cache: encoders, dequantizers and the witness.
+
+TEST INFRASTRUCTURE ONLY: nothing on the product path imports this module.
+
+Every function takes one (region, KV head) slice: x has shape (T, d) and holds
+the exact cache values (bf16 or fp32 inputs, carried as float64, exact).
+
+FP8 per-token (cartridge page, byte table and "What fake quantization does"):
+    amax = max_c |x_c|;  s = fp32(amax / 448)  (s = 1 when amax = 0)
+    y_c  = fp32(x_c / s) clamped to [-448, 448];  code = E4M3(y_c)
+    x^_c = E4M3value(code) * s                       (exact in float64)
+  The scale is stored as fp32 and the same stored scale encodes and decodes
+  (WitCert, Sec. 6.2.1: quantize with the stored scale).
+
+INT8 with subtractive dither, per (256-token block, channel) scales
+(WitCert, Sec. 4.2 "Subtractive dither" and Sec. 6.1.1 "BLK = 256"):
+    s32 = fp32(amax_blk,c / 126.5);  s = fp16(s32) rounded to nearest even
+    y = fp32(x / s);  z = fp32(y + xi);  code = rint(z) (ties to even), |code| <= 127
+    x^ = s * (code - xi)                              (exact in float64)
+  with xi the Philox dither of oracle.philox.  s = 0 gives code 0 and x^ = 0.
+
+Witness (WitCert, Sec. 4.1, Eq. (2)): r = x^ - x;  w_b = ||r_b|| over the 8
+coordinates of band b, stored as fp16 rounded toward +infinity.  Bands follow
+the rotate-half RoPE pairing (coordinate j pairs with j + d/2); band b holds
+pairs 4b..4b+3, i.e. coordinates {4b..4b+3} and {d/2+4b..d/2+4b+3} for d=128,
+B=16.  The sum of squares is taken in float64 in that coordinate order, one
+rounded operation per square and per addition, then a correctly rounded sqrt.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import E4M3_MAX, e4m3_decode, e4m3_encode, fp16_round_up
+
+INT8_Q = 127
+INT8_DIV = 126.5          # Q - 1/2
+BLOCK = 256
+N_BANDS = 16
+
+
+def band_coords(d: int = 128, n_bands: int = N_BANDS) -> np.ndarray:
+    """(n_bands, 2 * pairs_per_band) coordinate indices, in summation order."""
+    half = d // 2
+    ppb = half // n_bands
+    rows = []
+    for b in range(n_bands):
+        first = [b * ppb + i for i in range(ppb)]
+        rows.append(first + [half + j for j in first])
+    return np.array(rows, dtype=np.int64)
+
+
+def fp8_token_quantize(x: np.ndarray):
+    """x (T, d) exact values -> (codes uint8 (T, d), scale float32 (T,))."""
+    x = np.asarray(x, dtype=np.float64)
+    x32 = x.astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), x):
+        raise ValueError("fp8_token_quantize: inputs must be float32-exact")
+    amax = np.max(np.abs(x32), axis=1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    y = (x32 / s[:, None]).astype(np.float32)
+    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(y), s
+
+
+def fp8_token_dequant(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return e4m3_decode(codes) * np.asarray(scale, np.float64)[:, None]
+
+
+def int8_dither_quantize(x: np.ndarray, xi: np.ndarray, block: int = BLOCK):
+    """x (T, d) exact values, xi (T, d) float32 dither.
+
+    Returns (codes int8 (T, d), scale float16 (ceil(T/block), d), clipped count).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    x32 = x.astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), x):
+        raise ValueError("int8_dither_quantize: inputs must be float32-exact")
+    xi = np.asarray(xi, dtype=np.float32)
+    T, d = x.shape
+    nb = (T + block - 1) // block
+    codes = np.zeros((T, d), np.int8)
+    scales = np.zeros((nb, d), np.float16)
+    clipped = 0
+    for j in range(nb):
+        sl = slice(j * block, min(T, (j + 1) * block))
+        amax = np.max(np.abs(x32[sl]), axis=0)
+        s32 = (amax / np.float32(INT8_DIV)).astype(np.float32)
+        s16 = s32.astype(np.float16)             # round to nearest even
+        scales[j] = s16
+        s = s16.astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            y = (x32[sl] / s[None, :]).astype(np.float32)
+            z = (y + xi[sl]).astype(np.float32)
+        c = np.rint(z)
+        c = np.where(s[None, :] == 0, 0.0, c)
+        clipped += int(np.sum(np.abs(c) > INT8_Q))
+        codes[sl] = np.clip(c, -INT8_Q, INT8_Q).astype(np.int8)
+    return codes, scales, clipped
+
+
+def int8_dither_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
+                        block: int = BLOCK) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.float64)
+    T = codes.shape[0]
+    s = np.asarray(scales, np.float64)[np.arange(T) // block]
+    out = s * (codes - np.asarray(xi, np.float32).astype(np.float64))
+    return np.where(s == 0, 0.0, out)
+
+
+def witness(x_hat: np.ndarray, x: np.ndarray, n_bands: int = N_BANDS):
+    """Per-band residual norms: (w float64 (T, B), w16 float16 (T, B) rounded up)."""
+    r = np.asarray(x_hat, np.float64) - np.asarray(x, np.float64)
+    coords = band_coords(r.shape[1], n_bands)
+    w = np.empty((r.shape[0], n_bands), np.float64)
+    for b in range(n_bands):
+        acc = r[:, coords[b, 0]] * r[:, coords[b, 0]]
+        for c in coords[b, 1:]:
+            acc = acc + r[:, c] * r[:, c]
+        w[:, b] = np.sqrt(acc)
+    return w, fp16_round_up(w)
