@@ -1,0 +1,248 @@
+"""Decode-step benchmark of the quantized-KV GQA attention with the fused meter.
+
+Workload (one GPU): 36 layers x 8 KV heads x head_dim 128, 32 query heads,
+batch 64, 12,628 tokens per request; K8/V8 FP8 E4M3 with per-token scales, the
+bf16 exact cache for the TV, 16-band fp16 witness.  One step = for every layer,
+write the newest token of every request (kvq_quantize: codes, scales,
+witness) and run kvq_decode_attn over the whole context with TV, log A, bound
+and meter emitted per (request, query head).  All 36 layers' caches stay
+resident in HBM; inputs are seeded synthetic tensors.
+
+Prints one JSON line (see the design doc for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, budget_s: float):
+    """Time the oracle (as it stands) on (layer, request) slices of the same
+    workload.  Per slice and KV head the oracle's cache state (codes, scales,
+    witness) is prepared untimed; the timed part is the step itself: write the
+    newest token (quantize + witness) and decode over the whole context with TV
+    and bound, in float64.  Slices run in a process pool, one single-threaded
+    oracle per worker, until about budget_s of wall time is used."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    n_workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    done, busy = 0, 0.0
+    with cf.ProcessPoolExecutor(max_workers=n_workers, mp_context=ctx,
+                                initializer=_pool_init) as ex:
+        list(ex.map(_oracle_warm, range(n_workers)))           # imports, not timed
+        t0 = time.perf_counter()
+        layer_req = [(l, b) for l in range(cfg.layers) for b in range(cfg.batch)]
+        i = 0
+        while time.perf_counter() - t0 < budget_s and i < len(layer_req):
+            batch = layer_req[i:i + n_workers]
+            i += len(batch)
+            busy += sum(ex.map(_oracle_slice, batch))
+            done += len(batch)
+    kv_tokens = done * cfg.suffix.length                         # one token of one layer, all KV heads
+    return dict(value=kv_tokens * n_workers / busy, unit="KV tokens/s", cores=n_workers,
+                kind="oracle",
+                sample=f"{done} (layer, request) slices x {cfg.h_kv} KV heads x {cfg.suffix.length} "
+                       f"tokens: newest-token write + decode with TV and bound in fp64; "
+                       f"{busy:.1f} s of oracle time over {n_workers} single-threaded workers")
+
+
+def _pool_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+    sys.path.insert(0, ROOT)
+
+
+def _oracle_warm(_):
+    import oracle  # noqa: F401
+    import workloads  # noqa: F401
+    return 0
+
+
+def _oracle_slice(lb):
+    import numpy as np
+    import torch
+    torch.set_num_threads(1)
+    from oracle.pipeline import RegionSpec, decode_cell, encode_region
+    from workloads import CONFIGS, gen_layer
+    cfg = CONFIGS[3]
+    layer, b = lb
+    inp = gen_layer(cfg, layer, "cpu", requests=[b])           # input synthesis, not timed
+    q = inp["q"][0].double().numpy()
+    k = inp["suffix_k"][0].double().numpy()
+    v = inp["suffix_v"][0].double().numpy()
+    G = cfg.group
+    sm = float(np.float32(128 ** -0.5))
+    spec = RegionSpec("fp8", "fp8", layer=layer, stream=b)
+    encs = [encode_region(k[h], v[h], spec, h) for h in range(cfg.h_kv)]   # cache state, not timed
+    t = time.perf_counter()
+    for kvh in range(cfg.h_kv):
+        encode_region(k[kvh, -1:], v[kvh, -1:], spec, kvh)                 # newest token
+        decode_cell(q[kvh * G:(kvh + 1) * G], [(k[kvh], encs[kvh], spec)], sm)
+    return time.perf_counter() - t
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design doc describes how the step would shard)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from quantized_kv_cache_gqa_amd import kvq
+    from workloads import CONFIGS, gen_layer
+    from oracle.accounting import token_head_bytes  # byte accounting only
+
+    cfg = CONFIGS[3]
+    L = args.layers or cfg.layers
+    B, HQ, HKV, S, D = cfg.batch, cfg.h_q, cfg.h_kv, cfg.suffix.length, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = kvq.load()
+    sm_scale = float(np.float32(1.0 / math.sqrt(128.0)))
+    log(f"setup: {L} layers x batch {B} x {S} tokens, generating and writing the caches")
+    t0 = time.time()
+    layers = []
+    for layer in range(L):
+        inp = gen_layer(cfg, layer, dev)
+        st = kvq.alloc_stored(B, HKV, S, "fp8", "fp8", True, dev)
+        kvq.quantize_into(st, inp["suffix_k"], inp["suffix_v"], layer=layer)   # prefill write
+        view = kvq.RegionView(st, S, k_exact=inp["suffix_k"], layer=layer)
+        layers.append(dict(q=inp["q"], k=inp["suffix_k"], v=inp["suffix_v"], st=st, view=view))
+        del inp
+        if layer % 6 == 5:
+            log(f"  layer {layer + 1}/{L} ready ({time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    log(f"setup done in {time.time() - t0:.0f} s; HBM in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+    mbuf = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev)
+            for k in ("tv", "bound_raw", "meter", "log_a")}
+    meter = kvq.MeterOut(**{k: v.data_ptr() for k, v in mbuf.items()})
+    # prebuilt C arguments per layer
+    qargs, aargs = [], []
+    for layer, Ld in enumerate(layers):
+        st = Ld["st"]
+        qargs.append(kvq.QuantArgs(
+            k_format=1, v_format=1, in_format=0, k_in=Ld["k"].data_ptr(), v_in=Ld["v"].data_ptr(),
+            n_seq=B, num_kv_heads=HKV, head_dim=D, capacity=S, tok_begin=S - 1, tok_end=S,
+            k_out=st.k.data_ptr(), v_out=st.v.data_ptr(), k_scale_out=st.k_scale.data_ptr(),
+            v_scale_out=st.v_scale.data_ptr(), witness_out=st.witness.data_ptr(), layer=layer))
+        aargs.append(kvq.AttnArgs(batch=B, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D,
+                                  sm_scale=sm_scale, split_tokens=0, q=Ld["q"].data_ptr(),
+                                  prefix=kvq.Region(), suffix=Ld["view"].to_c(), out=out.data_ptr()))
+    ws_bytes = lib.kvq_workspace_bytes(ctypes.byref(aargs[0]), ctypes.byref(meter))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    assert lib.kvq_workspace_init(ws.data_ptr(), ws_bytes, sp) == 0
+
+    def step(ev=None):
+        for layer in range(L):
+            rc = lib.kvq_quantize(ctypes.byref(qargs[layer]), sp)
+            if rc:
+                raise RuntimeError(f"kvq_quantize status {rc}")
+            if ev is not None:
+                ev[layer][0].record(stream)
+            rc = lib.kvq_decode_attn(ctypes.byref(aargs[layer]), ctypes.byref(meter), ws.data_ptr(),
+                                     ws_bytes, sp)
+            if ev is not None:
+                ev[layer][1].record(stream)
+            if rc:
+                raise RuntimeError(f"kvq_decode_attn status {rc}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: whole steps, no events inside
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall_ms / args.steps:.3f} ms/step)")
+
+    # per-launch duration of the decode kernel, events on the launch stream
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        step([list(p) for p in evs[s]])
+    torch.cuda.synchronize()
+    dec_ms = [a.elapsed_time(b) for row in evs for a, b in row]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+
+    per_th = token_head_bytes("fp8", "fp8", exact_k=True, witness=True)      # 552 B
+    io_bytes = B * HQ * D * 4 * 2 + 4 * B * HQ * 4                              # q, out, meter
+    bytes_launch = B * HKV * S * per_th + io_bytes
+    achieved = bytes_launch / (dec_avg_ms * 1e-3) / 1e9
+    kv_tok_s = B * S * L / (ms_step * 1e-3)
+    step_bytes = L * (bytes_launch + B * HKV * (256 * 2 + 2 * (128 + 4) + 32))  # + appends
+    res = {
+        "metric": "decode-attn KV tokens/s + HBM GB/s (% peak), Qwen3-8B shape, b=64, 12.6k ctx",
+        "value": kv_tok_s,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"qwen3-8b-shape decode step: {L} layers x batch {B} x {S} tokens, "
+                               f"{HQ} q / {HKV} KV heads, d=128, K8/V8 FP8 E4M3 per-token scales, "
+                               f"bf16 exact keys for TV, 16-band fp16 witness bound",
+                   "global_batch": B, "seq_len": S, "layers": L,
+                   "step_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "decode_kernel<4, FP8, FP8> (one launch per layer)",
+                     "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_launch},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on host cores")
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

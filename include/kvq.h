@@ -1,0 +1,209 @@
+/*
+ * kvq.h - C ABI of the quantized-KV grouped-query decode attention library
+ * with its fused quantization-risk meter (gfx950 / MI355X).
+ *
+ * The method comes from two public pages:
+ *  - "WitCert: Sound Runtime Risk Observability and Gating for KV-Cache
+ *    Quantization" (arXiv 2607.28699v1): the total-variation target (Sec. 3),
+ *    Theorem 1 (e-form bound), the band-norm witness and Theorem 2 (Sec. 4.1),
+ *    the subtractively dithered INT8 quantizer (Sec. 4.2, 6.2.1), the split-KV
+ *    merge of the meter (Sec. 6.2.2) and its numerics (Sec. 3, 4.3, 6.2.4).
+ *  - "Compress the shared cartridge. Keep the keys." (knlp.io): BF16/FP8 key
+ *    and value layouts, the shared cartridge read with each request's live
+ *    suffix in one online softmax ("One kernel spans cartridge and live KV").
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers on the current HIP device unless
+ *    stated; the caller owns every buffer.  The library never allocates,
+ *    frees, copies to or from the host, or synchronizes; work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the null stream) in call order.
+ *  - Argument checks run on the host before anything is enqueued and return a
+ *    status; nothing aborts or throws across the ABI.  A launch failure
+ *    reported by the runtime returns KVQ_ERR_LAUNCH.
+ *  - Unsupported combinations are rejected with a status, never degraded.
+ *  - head_dim is 128; the witness has 16 bands (2 bytes each, 32 B per token
+ *    and head); INT8 scales cover blocks of 256 tokens.
+ *  - Tensor element layouts are row-major with the listed shapes; every base
+ *    pointer must be 16-byte aligned.
+ *  - Results are bitwise reproducible for a given shape: the split of the
+ *    sequence and every reduction order depend only on the shapes.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_HEAD_DIM 128
+#define KVQ_N_BANDS 16
+#define KVQ_INT8_BLOCK 256
+#define KVQ_MAX_GROUP 8
+
+typedef void *kvq_stream; /* hipStream_t */
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  KVQ_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  KVQ_ERR_FORMAT = 3,      /* unknown format code, or a format not allowed here */
+  KVQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  KVQ_ERR_UNSUPPORTED = 5, /* a valid combination this library does not implement */
+  KVQ_ERR_WORKSPACE = 6,   /* workspace missing or smaller than kvq_workspace_bytes() */
+  KVQ_ERR_LAUNCH = 7       /* the HIP runtime reported an error at launch */
+} kvq_status;
+
+/* Storage formats.  Scale layouts follow the format:
+ *  KVQ_FMT_BF16         values stored as bf16, no scale.
+ *  KVQ_FMT_FP8_E4M3     OCP E4M3FN codes (1 byte) with one fp32 scale per (token, KV
+ *                       head): s = amax/448, code = nearest-even E4M3(x/s) (cartridge
+ *                       page, "What fake quantization does"; WitCert Sec. 6.2.1 for
+ *                       encoding with the stored scale).
+ *  KVQ_FMT_INT8_DITHER  int8 codes with subtractive dither and one fp16 scale per
+ *                       (256-token block, KV head, channel): s = fp16(amax/126.5),
+ *                       code = rint(x/s + xi), x^ = s (code - xi), xi regenerated from
+ *                       Philox4x32-10 (WitCert Sec. 4.2, 6.1.1, 6.2.1).
+ *  KVQ_FMT_FP32         exact keys / write-path input only. */
+typedef enum kvq_format {
+  KVQ_FMT_BF16 = 0,
+  KVQ_FMT_FP8_E4M3 = 1,
+  KVQ_FMT_INT8_DITHER = 2,
+  KVQ_FMT_FP32 = 3
+} kvq_format;
+
+/* One KV region: the shared prefix ("cartridge", no batch dimension) or the
+ * per-request suffix.  Shapes, with L = length, Hk = num_kv_heads, D = 128:
+ *   dense prefix   codes [Hk, L, D]        fp8 scale [Hk, L]     int8 scale [Hk, ceil(L/256), D]
+ *                  witness [Hk, L, 16]     exact keys [Hk, L, D]
+ *   dense suffix   the same with a leading [batch] (L = capacity per request)
+ *   paged suffix   codes [n_pages, Hk, P, D], fp8 scale [n_pages, Hk, P], witness
+ *                  [n_pages, Hk, P, 16], exact keys [n_pages, Hk, P, D]; token i of
+ *                  request b sits in page page_table[b * max_pages + i / P], row i % P.
+ *                  Paged INT8 is rejected (its 256-token blocks would span pages).
+ * Semantics:
+ *   witness NULL  -> the stored keys are claimed exact for the meter (c_t = 0).
+ *   k_exact NULL  -> the stored keys are claimed exact for the TV (l_t = l~_t).
+ * Logical token order is prefix tokens 0..P-1, then suffix tokens 0..n_b-1; the
+ * dither stream of a token uses its index inside its own region. */
+typedef struct kvq_region {
+  int32_t k_format;         /* KVQ_FMT_BF16 | KVQ_FMT_FP8_E4M3 | KVQ_FMT_INT8_DITHER */
+  int32_t v_format;         /* same set */
+  const void *k;            /* stored key codes */
+  const void *v;            /* stored value codes (may be NULL for kvq_meter) */
+  const void *k_scale;      /* float (FP8) or fp16 bits (INT8); NULL for BF16 */
+  const void *v_scale;
+  const uint16_t *witness;  /* fp16 bits, or NULL */
+  const void *k_exact;      /* exact keys for the TV, or NULL */
+  int32_t k_exact_format;   /* KVQ_FMT_BF16 or KVQ_FMT_FP32 */
+  int32_t length;           /* prefix: tokens (0 = no prefix); suffix: capacity per request */
+  const int32_t *lengths;   /* suffix: device int32 [batch] tokens per request (<= length),
+                               NULL = every request has `length` tokens; prefix: NULL */
+  const int32_t *page_table;/* suffix only: device int32 [batch, max_pages], NULL = dense */
+  int32_t page_size;        /* paged: 8 or 16 */
+  int32_t max_pages;        /* paged: row length of page_table; capacity = max_pages * page_size */
+  uint64_t seed;            /* INT8 dither: Philox key */
+  int32_t layer;            /* INT8 dither: layer index, < 32768 */
+  int32_t stream_id;        /* INT8 dither: prefix stream id; suffix: request b uses stream_id + b */
+  const int32_t *stream_ids;/* suffix: optional device int32 [batch] stream ids (overrides) */
+} kvq_region;
+
+/* Decode-step attention over prefix ++ suffix for every (request, query head).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).  sm_scale is the
+ * logit scale (1/sqrt(128) for the workloads here). */
+typedef struct kvq_attn_args {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;     /* num_q_heads / num_kv_heads must be 1, 2, 4 or 8 */
+  int32_t head_dim;         /* must be 128 */
+  float sm_scale;
+  int32_t split_tokens;     /* tokens per work chunk; 0 = library choice; else a multiple of 64 */
+  const float *q;           /* device fp32 [batch, num_q_heads, 128], post-RoPE */
+  kvq_region prefix;        /* prefix.length == 0: no shared prefix */
+  kvq_region suffix;
+  float *out;               /* device fp32 [batch, num_q_heads, 128] = sum_t p~_t v^_t */
+} kvq_attn_args;
+
+/* Per-(request, query head) meter outputs, device fp32 [batch, num_q_heads] each;
+ * any may be NULL.  (WitCert Sec. 3, Thm. 1, Thm. 2, Sec. 4.3, 6.2.4)
+ *   tv        = 1/2 sum_t |p_t - p~_t|, p from exact keys, p~ from stored keys
+ *   log_a     = log E_p~[e^{c_t}],  c_t = sm_scale * sum_b ||q_b|| w_{t,b}
+ *   bound_raw = 1/2 (A^2 - 1), +inf when beyond the float range
+ *   meter     = min(1, bound_raw) */
+typedef struct kvq_meter_out {
+  float *tv;
+  float *bound_raw;
+  float *meter;
+  float *log_a;
+} kvq_meter_out;
+
+/* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store
+ * codes, scales and (optionally) the witness of the keys (WitCert Sec. 4.1,
+ * Eq. (2): w_{t,b} = ||k^_t - k_t|| over band b, stored as fp16 rounded up).
+ * Inputs are dense [n_seq, num_kv_heads, capacity, 128] in in_format (BF16 or
+ * FP32); outputs use the dense region layouts above (a prefix is n_seq = 1).
+ * For INT8 a call covers whole 256-token blocks: tok_begin must be a multiple of
+ * 256 and the last block ends at tok_end.  A target format equal to the input
+ * format copies the values.  The witness is computed in float64 and rounded
+ * up to fp16, so it bounds the true residual norm. */
+typedef struct kvq_quant_args {
+  int32_t k_format;         /* target formats */
+  int32_t v_format;
+  int32_t in_format;        /* KVQ_FMT_BF16 or KVQ_FMT_FP32 */
+  const void *k_in;         /* exact keys */
+  const void *v_in;         /* exact values (NULL: values not written) */
+  int32_t n_seq;
+  int32_t num_kv_heads;
+  int32_t head_dim;         /* must be 128 */
+  int32_t capacity;
+  int32_t tok_begin;
+  int32_t tok_end;
+  void *k_out;
+  void *v_out;
+  void *k_scale_out;        /* float [n_seq, Hk, capacity] or fp16 [n_seq, Hk, ceil(capacity/256), 128] */
+  void *v_scale_out;
+  uint16_t *witness_out;    /* fp16 bits [n_seq, Hk, capacity, 16], or NULL */
+  uint64_t seed;            /* INT8 dither parameters, as in kvq_region */
+  int32_t layer;
+  int32_t stream_id;
+  const int32_t *stream_ids;
+} kvq_quant_args;
+
+/* Library ABI version (KVQ_ABI_VERSION of the build). */
+int kvq_abi_version(void);
+
+/* Static English name of a status code. */
+const char *kvq_status_string(kvq_status status);
+
+/* Write path (see kvq_quant_args). */
+kvq_status kvq_quantize(const kvq_quant_args *args, kvq_stream stream);
+
+/* Bytes of device workspace kvq_decode_attn / kvq_meter need for these
+ * arguments (host-only, no device access).  Returns 0 on invalid arguments. */
+size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter);
+
+/* Prepare a workspace for first use: clears the arrival counters at its start.
+ * A workspace stays ready after every successful kvq_decode_attn / kvq_meter
+ * call (the last work-group of each (request, KV head) resets its counter).
+ * Calls that share a workspace must not overlap in time. */
+kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, kvq_stream stream);
+
+/* Decode attention with the fused meter (WitCert Sec. 6 meter loop, read path;
+ * cartridge page, one online softmax over cartridge and suffix).  meter may be
+ * NULL (attention only).  args->out must be non-NULL. */
+kvq_status kvq_decode_attn(const kvq_attn_args *args, const kvq_meter_out *meter,
+                           void *workspace, size_t workspace_bytes, kvq_stream stream);
+
+/* Meter only ("observatory" role, WitCert Fig. 2): the same pass without the
+ * values and the output; args->out and the regions' v pointers are ignored. */
+kvq_status kvq_meter(const kvq_attn_args *args, const kvq_meter_out *meter,
+                     void *workspace, size_t workspace_bytes, kvq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,269 @@
+// C ABI of the library: host-side argument checks, work planning, workspace
+// layout and kernel launches.  Nothing here touches device memory directly.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using namespace kvq;
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool is_store_fmt(int f) {
+  return f == KVQ_FMT_BF16 || f == KVQ_FMT_FP8_E4M3 || f == KVQ_FMT_INT8_DITHER;
+}
+
+struct Plan {
+  int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
+  int prefix_len = 0, suffix_cap = 0;
+  bool tv = false, meter = false, wit_any = false;
+  size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
+};
+
+kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int batch, int h_kv) {
+  if (r.length < 0) return KVQ_ERR_SHAPE;
+  if (r.length == 0) return KVQ_OK;                          // region absent
+  if (r.length > (1 << 28)) return KVQ_ERR_SHAPE;
+  if (!is_store_fmt(r.k_format)) return KVQ_ERR_FORMAT;
+  if (need_v && !is_store_fmt(r.v_format)) return KVQ_ERR_FORMAT;
+  if (!r.k || (need_v && !r.v)) return KVQ_ERR_NULL;
+  if (r.k_format != KVQ_FMT_BF16 && !r.k_scale) return KVQ_ERR_NULL;
+  if (need_v && r.v_format != KVQ_FMT_BF16 && !r.v_scale) return KVQ_ERR_NULL;
+  if (r.k_exact && r.k_exact_format != KVQ_FMT_BF16 && r.k_exact_format != KVQ_FMT_FP32)
+    return KVQ_ERR_FORMAT;
+  const void *ptrs[] = {r.k, need_v ? r.v : nullptr, r.k_scale, need_v ? r.v_scale : nullptr,
+                        r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
+  const bool int8 = r.k_format == KVQ_FMT_INT8_DITHER || (need_v && r.v_format == KVQ_FMT_INT8_DITHER);
+  if (int8 && (r.layer < 0 || r.layer >= (1 << 15) || h_kv > (1 << 16))) return KVQ_ERR_SHAPE;
+  if (is_prefix) {
+    if (r.lengths || r.page_table || r.stream_ids) return KVQ_ERR_UNSUPPORTED;
+  } else if (r.page_table) {
+    if (int8) return KVQ_ERR_UNSUPPORTED;                    // 256-token blocks would span pages
+    if (r.page_size != 8 && r.page_size != 16) return KVQ_ERR_UNSUPPORTED;
+    if (r.max_pages <= 0 || (int64_t)r.max_pages * r.page_size != r.length) return KVQ_ERR_SHAPE;
+  }
+  (void)batch;
+  return KVQ_OK;
+}
+
+kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_only, Plan &p) {
+  if (!a) return KVQ_ERR_NULL;
+  if (a->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
+  if (a->batch <= 0 || a->num_kv_heads <= 0 || a->num_q_heads <= 0) return KVQ_ERR_SHAPE;
+  if (a->batch > (1 << 20) || a->num_q_heads > 4096) return KVQ_ERR_SHAPE;
+  if (a->num_q_heads % a->num_kv_heads) return KVQ_ERR_SHAPE;
+  p.group = a->num_q_heads / a->num_kv_heads;
+  if (p.group != 1 && p.group != 2 && p.group != 4 && p.group != 8) return KVQ_ERR_UNSUPPORTED;
+  if (!a->q) return KVQ_ERR_NULL;
+  if (!aligned16(a->q)) return KVQ_ERR_ALIGN;
+  if (!meter_only) {
+    if (!a->out) return KVQ_ERR_NULL;
+    if (!aligned16(a->out)) return KVQ_ERR_ALIGN;
+  }
+  if (!(a->sm_scale > 0.0f) || a->sm_scale > 1e6f) return KVQ_ERR_SHAPE;
+  kvq_status s = check_region(a->prefix, true, !meter_only, a->batch, a->num_kv_heads);
+  if (s != KVQ_OK) return s;
+  s = check_region(a->suffix, false, !meter_only, a->batch, a->num_kv_heads);
+  if (s != KVQ_OK) return s;
+  p.prefix_len = a->prefix.length;
+  p.suffix_cap = a->suffix.length;
+  if (p.prefix_len + (int64_t)p.suffix_cap <= 0) return KVQ_ERR_SHAPE;
+  if (a->split_tokens < 0 || (a->split_tokens % 64) != 0) return KVQ_ERR_SHAPE;
+
+  if ((int64_t)a->batch * a->num_kv_heads > (1 << 18)) return KVQ_ERR_SHAPE;  // counters fit 1 MiB
+  const int groups = a->batch * a->num_kv_heads;
+  const int smax = p.prefix_len + p.suffix_cap;
+  int chunk = a->split_tokens;
+  if (chunk == 0) {
+    chunk = 1024;                       // keep >= ~2048 work-groups in flight when possible
+    while (chunk > 256 && (int64_t)groups * ((smax + chunk - 1) / chunk) < 2048) chunk >>= 1;
+  }
+  p.chunk = chunk;
+  p.pre_chunks = (p.prefix_len + chunk - 1) / chunk;
+  p.suf_chunks = (p.suffix_cap + chunk - 1) / chunk;
+  p.total_chunks = p.pre_chunks + p.suf_chunks;
+
+  const bool any_exact = (p.prefix_len > 0 && a->prefix.k_exact) || (p.suffix_cap > 0 && a->suffix.k_exact);
+  p.wit_any = (p.prefix_len > 0 && a->prefix.witness) || (p.suffix_cap > 0 && a->suffix.witness);
+  if (m) {
+    const void *mp[] = {m->tv, m->bound_raw, m->meter, m->log_a};
+    for (const void *x : mp)
+      if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
+    p.tv = m->tv && any_exact;
+    p.meter = (m->bound_raw || m->meter || m->log_a) && p.wit_any;
+  }
+  p.off_counters = 0;
+  p.off_partials = round_up((size_t)groups * sizeof(uint32_t), kAlign);
+  p.off_spill = p.off_partials +
+                round_up((size_t)groups * p.total_chunks * p.group * PART_STRIDE * sizeof(float), kAlign);
+  p.bytes = p.off_spill;
+  if (p.tv) p.bytes += round_up((size_t)groups * (size_t)smax * p.group * 2 * sizeof(float), kAlign);
+  return KVQ_OK;
+}
+
+RegionDev region_dev(const kvq_region &r, bool is_prefix) {
+  RegionDev d;
+  memset(&d, 0, sizeof(d));
+  d.k = r.k; d.v = r.v; d.k_scale = r.k_scale; d.v_scale = r.v_scale;
+  d.witness = r.witness;
+  d.k_exact = r.k_exact;
+  d.exact_fmt = r.k_exact ? (r.k_exact_format == KVQ_FMT_FP32 ? EX_F32 : EX_BF16) : EX_NONE;
+  d.length = r.length;
+  d.lengths = is_prefix ? nullptr : r.lengths;
+  d.page_table = is_prefix ? nullptr : r.page_table;
+  d.page_size = r.page_size > 0 ? r.page_size : 1;
+  d.max_pages = r.max_pages;
+  d.paged = (!is_prefix && r.page_table) ? 1 : 0;
+  d.is_prefix = is_prefix ? 1 : 0;
+  d.seed_lo = (uint32_t)r.seed;
+  d.seed_hi = (uint32_t)(r.seed >> 32);
+  d.layer = r.layer;
+  d.stream_id = r.stream_id;
+  d.stream_ids = is_prefix ? nullptr : r.stream_ids;
+  return d;
+}
+
+kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
+                      hipStream_t stream, bool meter_only) {
+  Plan p;
+  kvq_status s = make_plan(a, m, meter_only, p);
+  if (s != KVQ_OK) return s;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
+
+  DecodeLaunch d;
+  memset(&d, 0, sizeof(d));
+  d.batch = a->batch;
+  d.h_q = a->num_q_heads;
+  d.h_kv = a->num_kv_heads;
+  d.group = p.group;
+  d.sm_scale = a->sm_scale;
+  d.q = a->q;
+  d.out = meter_only ? nullptr : a->out;
+  d.chunk = p.chunk;
+  d.total_chunks = p.total_chunks;
+  d.prefix_len = p.prefix_len;
+  d.suffix_cap = p.suffix_cap;
+  d.suffix_lengths = p.suffix_cap > 0 ? a->suffix.lengths : nullptr;
+  d.has_tv = p.tv;
+  d.has_meter = p.meter;
+  d.has_out = meter_only ? 0 : 1;
+  d.has_wit_any = p.wit_any;
+  if (m) {
+    d.tv = m->tv; d.bound_raw = m->bound_raw; d.meter = m->meter; d.log_a = m->log_a;
+  }
+  char *w = static_cast<char *>(ws);
+  d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);
+  d.partials = reinterpret_cast<float *>(w + p.off_partials);
+  d.spill = p.tv ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+
+  hipError_t e = hipSuccess;
+  if (p.pre_chunks > 0) {
+    d.region = region_dev(a->prefix, true);
+    d.k_format = a->prefix.k_format;
+    d.v_format = meter_only ? VF_NONE : a->prefix.v_format;
+    d.n_chunks = p.pre_chunks;
+    d.chunk_base = 0;
+    e = launch_decode(d, stream);
+    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  }
+  if (p.suf_chunks > 0) {
+    d.region = region_dev(a->suffix, false);
+    d.k_format = a->suffix.k_format;
+    d.v_format = meter_only ? VF_NONE : a->suffix.v_format;
+    d.n_chunks = p.suf_chunks;
+    d.chunk_base = p.pre_chunks;
+    e = launch_decode(d, stream);
+    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char *kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "size out of range or inconsistent";
+    case KVQ_ERR_FORMAT: return "unknown or disallowed format";
+    case KVQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
+  if (!a) return KVQ_ERR_NULL;
+  if (a->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
+  if (a->in_format != KVQ_FMT_BF16 && a->in_format != KVQ_FMT_FP32) return KVQ_ERR_FORMAT;
+  if (!is_store_fmt(a->k_format)) return KVQ_ERR_FORMAT;
+  if (a->v_in && !is_store_fmt(a->v_format)) return KVQ_ERR_FORMAT;
+  if (a->n_seq <= 0 || a->num_kv_heads <= 0 || a->capacity <= 0) return KVQ_ERR_SHAPE;
+  if (a->capacity > (1 << 28) || (int64_t)a->n_seq * a->num_kv_heads > (1 << 24)) return KVQ_ERR_SHAPE;
+  if (a->tok_begin < 0 || a->tok_end > a->capacity || a->tok_begin >= a->tok_end) return KVQ_ERR_SHAPE;
+  if (!a->k_in || !a->k_out) return KVQ_ERR_NULL;
+  if (a->v_in && !a->v_out) return KVQ_ERR_NULL;
+  if (a->k_format != KVQ_FMT_BF16 && !a->k_scale_out) return KVQ_ERR_NULL;
+  if (a->v_in && a->v_format != KVQ_FMT_BF16 && !a->v_scale_out) return KVQ_ERR_NULL;
+  const void *ptrs[] = {a->k_in, a->v_in, a->k_out, a->v_out, a->k_scale_out, a->v_scale_out,
+                        a->witness_out, a->stream_ids};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
+  const bool int8 = a->k_format == KVQ_FMT_INT8_DITHER || (a->v_in && a->v_format == KVQ_FMT_INT8_DITHER);
+  if (int8) {
+    if (a->tok_begin % KVQ_INT8_BLOCK) return KVQ_ERR_UNSUPPORTED;
+    if (a->layer < 0 || a->layer >= (1 << 15) || a->num_kv_heads > (1 << 16)) return KVQ_ERR_SHAPE;
+  }
+  QuantLaunch q;
+  q.k_format = a->k_format; q.v_format = a->v_format; q.in_format = a->in_format;
+  q.k_in = a->k_in; q.v_in = a->v_in;
+  q.n_seq = a->n_seq; q.h_kv = a->num_kv_heads; q.capacity = a->capacity;
+  q.tok_begin = a->tok_begin; q.tok_end = a->tok_end;
+  q.k_out = a->k_out; q.v_out = a->v_out; q.k_scale_out = a->k_scale_out; q.v_scale_out = a->v_scale_out;
+  q.witness_out = a->witness_out;
+  q.seed = a->seed; q.layer = a->layer; q.stream_id = a->stream_id; q.stream_ids = a->stream_ids;
+  return launch_quantize(q, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+size_t kvq_workspace_bytes(const kvq_attn_args *a, const kvq_meter_out *m) {
+  Plan p;
+  if (make_plan(a, m, true, p) != KVQ_OK) return 0;   // size does not depend on out/v
+  return p.bytes;
+}
+
+kvq_status kvq_workspace_init(void *ws, size_t bytes, kvq_stream stream) {
+  if (!ws) return KVQ_ERR_NULL;
+  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
+  // the counters sit at the start; clearing the first partial offset's worth is
+  // enough, but clearing up to 1 MiB covers every plan with <= 256K groups
+  size_t n = bytes < ((size_t)1 << 20) ? bytes : ((size_t)1 << 20);
+  return launch_fill_zero(ws, n & ~(size_t)3, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+kvq_status kvq_decode_attn(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
+                           kvq_stream stream) {
+  return run_decode(a, m, ws, ws_bytes, (hipStream_t)stream, false);
+}
+
+kvq_status kvq_meter(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
+                     kvq_stream stream) {
+  return run_decode(a, m, ws, ws_bytes, (hipStream_t)stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// --------------------------------------------------------------- write path
+
+struct QuantLaunch {
+  int k_format, v_format, in_format;
+  const void *k_in, *v_in;
+  int n_seq, h_kv, capacity, tok_begin, tok_end;
+  void *k_out, *v_out, *k_scale_out, *v_scale_out;
+  uint16_t *witness_out;
+  uint64_t seed;
+  int layer, stream_id;
+  const int32_t *stream_ids;
+};
+
+hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
+
+// --------------------------------------------------------------- read path
+
+// Exact-key format codes seen by the kernels.
+enum ExactFmt : int { EX_NONE = 0, EX_BF16 = 1, EX_F32 = 2 };
+// Value format code used by the meter-only path.
+constexpr int VF_NONE = 4;
+
+struct RegionDev {
+  const void *k, *v, *k_scale, *v_scale;
+  const uint16_t *witness;
+  const void *k_exact;
+  int exact_fmt;          // ExactFmt
+  int length;             // prefix length, or suffix capacity
+  const int32_t *lengths; // suffix per-request lengths (nullable)
+  const int32_t *page_table;
+  int page_size, max_pages, paged, is_prefix;
+  uint32_t seed_lo, seed_hi;
+  int layer, stream_id;
+  const int32_t *stream_ids;
+};
+
+struct DecodeLaunch {
+  int batch, h_q, h_kv, group;
+  float sm_scale;
+  const float *q;
+  float *out;
+  RegionDev region;
+  int k_format, v_format;       // of this region (v_format = VF_NONE for the meter)
+  int chunk;                    // tokens per chunk
+  int n_chunks;                 // chunks of this region per (request, KV head)
+  int chunk_base;               // index of this region's first chunk in the group
+  int total_chunks;             // prefix + suffix chunks per (request, KV head)
+  int prefix_len;               // tokens before the suffix in the logical order
+  int suffix_cap;               // suffix capacity (spill rows per group = prefix_len + suffix_cap)
+  const int32_t *suffix_lengths;// for the finalize (nullable: all = suffix_cap)
+  int has_tv, has_meter, has_out, has_wit_any;
+  float *tv, *bound_raw, *meter, *log_a;
+  uint32_t *counters;
+  float *partials;
+  float *spill;
+};
+
+constexpr int PART_STRIDE = 136;  // m~, z~, m', z', m_e, z_e, 2 pad, acc[128]
+
+hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
+
+}  // namespace kvq

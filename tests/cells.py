@@ -1,0 +1,221 @@
+"""Shared test plumbing: run one layer of a workload through the HIP library and
+the same cells through the oracle, then compare.
+
+The two sides share only the seeded inputs from ``workloads``: the GPU side
+quantizes and attends with libkvq.so, the oracle re-derives every code, scale,
+witness and result from the exact inputs on the CPU.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+import torch
+
+from oracle.pipeline import RegionSpec, decode_cell, encode_region
+from workloads import Config, gen_layer
+
+SM_SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+PREFIX_STREAM = 1_000_000
+
+
+def dither_seed(cfg: Config) -> int:
+    return (cfg.seed * 0x9E3779B97F4A7C15) % (1 << 64)
+
+
+def _spec(cfg: Config, region, layer: int, stream: int) -> RegionSpec:
+    return RegionSpec(k_fmt=region.k_fmt, v_fmt=region.v_fmt, seed=dither_seed(cfg), layer=layer,
+                      stream=stream, witness=region.witness, exact_k=region.exact_k)
+
+
+class GpuCase:
+    """One layer of a workload quantized and stored by the HIP write path."""
+
+    def __init__(self, cfg: Config, layer: int = 0, device="cuda", page_seed: int = 0,
+                 fp32_exact: bool = False):
+        from quantized_kv_cache_gqa_amd import kvq
+        self.kvq = kvq
+        self.cfg, self.layer, self.device = cfg, layer, device
+        self.fp32_exact = fp32_exact
+        self.inp = gen_layer(cfg, layer, device, want_fp32_keys=fp32_exact)
+        G, hkv = cfg.group, cfg.h_kv
+        seed = dither_seed(cfg)
+        self.prefix_view = None
+        self.prefix_store = None
+        if cfg.prefix is not None and cfg.prefix.length > 0:
+            pr = cfg.prefix
+            P = pr.length
+            kin = (self.inp["prefix_k32"] if fp32_exact else self.inp["prefix_k"])[None].contiguous()
+            vin = self.inp["prefix_v"][None].contiguous()
+            if fp32_exact:
+                vin = vin.float()
+            st = kvq.alloc_stored(1, hkv, P, pr.k_fmt, pr.v_fmt, pr.witness or fp32_exact, device)
+            kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=PREFIX_STREAM)
+            exact = kin[0] if (pr.exact_k or fp32_exact) else None
+            self.prefix_store = st
+            self.prefix_view = kvq.RegionView(st, P, k_exact=exact, seed=seed, layer=layer,
+                                              stream_id=PREFIX_STREAM,
+                                              use_witness=pr.witness or fp32_exact)
+        sf = cfg.suffix
+        cap = sf.length
+        kin = self.inp["suffix_k32"] if fp32_exact else self.inp["suffix_k"]
+        vin = self.inp["suffix_v"].float() if fp32_exact else self.inp["suffix_v"]
+        st = kvq.alloc_stored(cfg.batch, hkv, cap, sf.k_fmt, sf.v_fmt, sf.witness or fp32_exact, device)
+        kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=0)
+        self.suffix_store = st
+        exact = kin if (sf.exact_k or fp32_exact) else None
+        lens = self.inp["suffix_lens"]
+        if sf.paged:
+            self.suffix_view = self._paged_view(st, exact, lens, page_seed)
+        else:
+            self.suffix_view = kvq.RegionView(st, cap, k_exact=exact, lengths=lens, seed=seed,
+                                              layer=layer, stream_id=0,
+                                              use_witness=sf.witness or fp32_exact)
+
+    def _paged_view(self, st, exact, lens, page_seed):
+        """Scatter the dense suffix into shuffled pages [n_pages, h_kv, page, ...]."""
+        kvq = self.kvq
+        cfg = self.cfg
+        ps = cfg.suffix.page_size
+        cap = cfg.suffix.length
+        if cap % ps:
+            raise ValueError("paged suffix capacity must be a multiple of the page size")
+        mp = cap // ps
+        n_pages = cfg.batch * mp
+        perm = torch.from_numpy(np.random.default_rng(page_seed).permutation(n_pages).astype(np.int32))
+        table = perm.view(cfg.batch, mp).to(self.device)
+
+        def scatter(t):
+            if t is None:
+                return None
+            b, h, c = t.shape[:3]
+            rest = t.shape[3:]
+            src = t.view(b, h, mp, ps, *rest).permute(0, 2, 1, 3, *range(4, 4 + len(rest)))
+            src = src.reshape(b * mp, h, ps, *rest)
+            out = torch.empty_like(src)
+            out[table.view(-1).long()] = src
+            return out.contiguous()
+
+        paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
+                           scatter(st.v_scale), scatter(st.witness))
+        self.page_table = table
+        return kvq.RegionView(paged, cap, k_exact=scatter(exact), lengths=lens, page_table=table,
+                              page_size=ps, use_witness=st.witness is not None)
+
+    def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
+            workspace=None):
+        out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
+                                      self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
+                                      meter=meter, meter_only=meter_only, workspace=workspace)
+        torch.cuda.synchronize()
+        return out, m
+
+
+def oracle_cell(case: GpuCase, b: int, kvh: int):
+    """The oracle's view of cell (b, kvh): encoded regions and the decode result."""
+    cfg, inp, layer = case.cfg, case.inp, case.layer
+    G = cfg.group
+    q = inp["q"][b, kvh * G:(kvh + 1) * G].double().cpu().numpy()
+    regions = []
+    encs = {}
+    if case.prefix_view is not None:
+        key = "prefix_k32" if case.fp32_exact else "prefix_k"
+        k = inp[key][kvh].double().cpu().numpy()
+        v = inp["prefix_v"][kvh].double().cpu().numpy()
+        spec = _spec(cfg, cfg.prefix, layer, PREFIX_STREAM)
+        if case.fp32_exact:
+            spec.witness = True
+            spec.exact_k = True
+        enc = encode_region(k, v, spec, kvh)
+        regions.append((k, enc, spec))
+        encs["prefix"] = enc
+    n = int(inp["suffix_lens"][b])
+    key = "suffix_k32" if case.fp32_exact else "suffix_k"
+    k = inp[key][b, kvh, :n].double().cpu().numpy()
+    v = inp["suffix_v"][b, kvh, :n].double().cpu().numpy()
+    spec = _spec(cfg, cfg.suffix, layer, b)
+    if case.fp32_exact:
+        spec.witness = True
+        spec.exact_k = True
+    enc = encode_region(k, v, spec, kvh)
+    regions.append((k, enc, spec))
+    encs["suffix"] = enc
+    return encs, decode_cell(q, regions, SM_SCALE)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def check_stored(case: GpuCase, b: int, kvh: int, encs) -> None:
+    """Codes, scales and witness bit-exact against the oracle's encoders."""
+    n = int(case.inp["suffix_lens"][b])
+    pairs = [("suffix", case.suffix_store, (b, kvh), n)]
+    if case.prefix_store is not None:
+        pairs.append(("prefix", case.prefix_store, (0, kvh), case.cfg.prefix.length))
+    for name, st, (bb, hh), nn in pairs:
+        enc = encs[name]
+        np.testing.assert_array_equal(_bits(st.k[bb, hh, :nn]), np.asarray(enc.k_codes).view(_bits(st.k[bb, hh, :1]).dtype),
+                                      err_msg=f"{name} key codes")
+        np.testing.assert_array_equal(_bits(st.v[bb, hh, :nn]), np.asarray(enc.v_codes).view(_bits(st.v[bb, hh, :1]).dtype),
+                                      err_msg=f"{name} value codes")
+        for sc, ref, what in ((st.k_scale, enc.k_scale, "key"), (st.v_scale, enc.v_scale, "value")):
+            if ref is None:
+                continue
+            if ref.dtype == np.float32:
+                np.testing.assert_array_equal(_bits(sc[bb, hh, :nn]), ref.view(np.uint32),
+                                              err_msg=f"{name} {what} scales")
+            else:
+                nb = ref.shape[0]
+                np.testing.assert_array_equal(_bits(sc[bb, hh, :nb]), ref.view(np.uint16),
+                                              err_msg=f"{name} {what} scales")
+        if enc.w16 is not None and st.witness is not None:
+            np.testing.assert_array_equal(_bits(st.witness[bb, hh, :nn]), enc.w16.view(np.uint16),
+                                          err_msg=f"{name} witness")
+        assert enc.clipped == 0
+
+
+TOL_OUT = 2e-3
+TOL_METER = 1e-5
+
+
+def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kvh: int, ref,
+                  check_out: bool = True) -> Dict[str, float]:
+    """Attention output within 2e-3 relative; TV, bound and meter within 1e-5."""
+    G = case.cfg.group
+    worst = dict(out_rel=0.0, tv=0.0, bound=0.0, meter=0.0)
+    for h in range(G):
+        qh = kvh * G + h
+        if check_out:
+            og = out[b, qh].double().cpu().numpy()
+            orf = ref["out"][h]
+            rel = np.linalg.norm(og - orf) / max(np.linalg.norm(orf), 1e-30)
+            assert rel <= TOL_OUT, (b, qh, rel)
+            assert np.max(np.abs(og - orf)) <= TOL_OUT * np.max(np.abs(orf)) + 1e-30, (b, qh)
+            worst["out_rel"] = max(worst["out_rel"], rel)
+        if "tv" in meter:
+            tv = float(meter["tv"][b, qh])
+            assert abs(tv - ref["tv"][h]) <= TOL_METER, (b, qh, tv, ref["tv"][h])
+            worst["tv"] = max(worst["tv"], abs(tv - ref["tv"][h]))
+        if "bound_raw" in meter:
+            bg = float(meter["bound_raw"][b, qh])
+            br = float(ref["bound_raw"][h])
+            if math.isinf(br) or math.isinf(bg):
+                edge = 0.5 * math.log(2 * float(np.finfo(np.float32).max) + 1)
+                assert math.isinf(br) == math.isinf(bg) or abs(float(ref["log_a"][h]) - edge) < 1e-3
+            else:
+                err = abs(bg - br) / max(1.0, br)
+                assert err <= TOL_METER, (b, qh, bg, br)
+                worst["bound"] = max(worst["bound"], err)
+            mg = float(meter["meter"][b, qh])
+            assert abs(mg - float(ref["meter"][h])) <= TOL_METER
+            worst["meter"] = max(worst["meter"], abs(mg - float(ref["meter"][h])))
+    return worst

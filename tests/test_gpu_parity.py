@@ -1,0 +1,181 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Bars: stored codes, scales and witness bit-exact; attention output within 2e-3
+relative; TV, bound and meter within 1e-5 (relative above 1 for the bound).
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from cells import GpuCase, SM_SCALE, check_results, check_stored, oracle_cell
+from oracle.numerics import e4m3_table
+from workloads import CONFIGS, small_variant
+
+pytestmark = pytest.mark.gpu
+
+
+def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False):
+    cfg = case.cfg
+    out, m = case.run(split_tokens=split_tokens, meter_only=meter_only)
+    cells = cells or [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
+    worst = {}
+    for b, kvh in cells:
+        encs, ref = oracle_cell(case, b, kvh)
+        check_stored(case, b, kvh, encs)
+        w = check_results(case, out, m, b, kvh, ref, check_out=check_out and not meter_only)
+        for k, v in w.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    print(f"[{cfg.name}] cells={len(cells)} worst={worst}", flush=True)
+    return out, m, worst
+
+
+def test_fp8_hardware_decode_matches_e4m3_table(gpu_lib):
+    """One stored token with scale 1 and p~ = 1: the output is the decoded value
+    row itself, so every E4M3 code's hardware decode is compared exactly."""
+    kvq = gpu_lib
+    dev = "cuda"
+    st = kvq.alloc_stored(2, 1, 1, "bf16", "fp8", False, dev)
+    codes = torch.arange(256, dtype=torch.int32)
+    codes[codes == 0x7F] = 0
+    codes[codes == 0xFF] = 0
+    st.v.copy_(codes.to(torch.uint8).view(2, 1, 1, 128).to(dev))
+    st.v_scale.fill_(1.0)
+    view = kvq.RegionView(st, 1)
+    q = torch.zeros((2, 1, 128), dtype=torch.float32, device=dev)
+    out, _ = kvq.decode_attn(q, 1, None, view, sm_scale=SM_SCALE, meter=False)
+    torch.cuda.synchronize()
+    ref = e4m3_table()
+    ref[[0x7F, 0xFF]] = 0.0
+    np.testing.assert_array_equal(out.cpu().numpy().reshape(-1), ref.astype(np.float32))
+
+
+def test_write_path_edge_values_bit_exact(gpu_lib):
+    """Zero rows, tiny and huge magnitudes, E4M3 midpoints: codes, scales and
+    witness against the oracle encoders."""
+    from oracle.pipeline import RegionSpec, encode_region
+    kvq = gpu_lib
+    rng = np.random.default_rng(11)
+    T = 300
+    x = rng.standard_normal((1, 1, T, 128)).astype(np.float32)
+    x[0, 0, 0] = 0.0                                  # all-zero token
+    x[0, 0, 1] = -0.0
+    x[0, 0, 2] *= 1e-30                               # tiny magnitudes
+    x[0, 0, 3] *= 1e30
+    x[0, 0, 4, :] = np.float32(2.0 ** -12)            # below half the smallest subnormal step
+    mids = (e4m3_table()[1:0x7E] + e4m3_table()[2:0x7F]) / 2
+    x[0, 0, 5, :] = 0
+    x[0, 0, 5, :len(mids[:127])] = mids[:127] / 448.0 * 448.0
+    x[0, 0, 5, 127] = 448.0                           # absmax makes s = 1: y = x exactly
+    x[0, 0, 6:40] *= 8                                # outliers
+    for kf, vf in (("fp8", "fp8"), ("int8", "int8"), ("bf16", "fp8")):
+        xf = x.copy()
+        if kf == "int8":
+            xf[0, 0, 3] = x[0, 0, 3] * 1e-26          # keep the fp16 block scale finite
+        xb = torch.from_numpy(xf).to(torch.bfloat16)  # bf16 exact inputs
+        for src in ("bf16", "fp32"):
+            kin = (xb if src == "bf16" else torch.from_numpy(xf)).cuda()
+            st = kvq.alloc_stored(1, 1, T, kf, vf, True, "cuda")
+            kvq.quantize_into(st, kin, kin, seed=12345, layer=3, stream_id=7)
+            torch.cuda.synchronize()
+            kx = kin[0, 0].double().cpu().numpy()
+            spec = RegionSpec(kf, vf, seed=12345, layer=3, stream=7)
+            enc = encode_region(kx, kx, spec, 0)
+            got_k = st.k[0, 0].cpu()
+            if kf == "bf16":
+                np.testing.assert_array_equal(got_k.view(torch.int16).numpy().view(np.uint16),
+                                              enc.k_codes, err_msg=f"{kf}/{src}")
+            else:
+                np.testing.assert_array_equal(got_k.numpy(), enc.k_codes, err_msg=f"{kf}/{src}")
+            np.testing.assert_array_equal(st.v[0, 0].cpu().numpy(), enc.v_codes, err_msg=f"v {kf}/{src}")
+            if kf == "fp8":
+                np.testing.assert_array_equal(st.k_scale[0, 0].cpu().numpy().view(np.uint32),
+                                              enc.k_scale.view(np.uint32))
+            elif kf == "int8":
+                np.testing.assert_array_equal(st.k_scale[0, 0].cpu().numpy().view(np.uint16),
+                                              enc.k_scale.view(np.uint16))
+            np.testing.assert_array_equal(st.witness[0, 0].cpu().numpy().view(np.uint16),
+                                          enc.w16.view(np.uint16), err_msg=f"witness {kf}/{src}")
+            assert enc.clipped == 0
+
+
+SMALL = {
+    "cfg1": lambda: CONFIGS[1],
+    "cfg2": lambda: small_variant(CONFIGS[2], batch=3, h_kv=2, lens=(1024, 1000, 17)),
+    "cfg3": lambda: small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1234)),
+    "cfg4": lambda: small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=1000, lens=(1000, 513)),
+    "cfg5": lambda: small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=5000, lens=(5000, 4097)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_config_parity_all_cells(gpu_lib, name):
+    cfg = SMALL[name]()
+    case = GpuCase(cfg, layer=5 if cfg.layers > 5 else 0, page_seed=3)
+    out, m, worst = _all_cells(case, split_tokens=cfg.split_tokens)
+    if cfg.suffix.k_fmt == "bf16" and not cfg.suffix.exact_k:
+        # stored keys are the exact keys: TV and bound are exactly zero
+        assert torch.all(m["tv"] == 0) and torch.all(m["bound_raw"] == 0)
+
+
+def test_cfg1_fp32_exact_cache_meter_nonzero(gpu_lib):
+    """BF16 storage of fp32 keys as the quantizer: nonzero TV and witness bound."""
+    case = GpuCase(CONFIGS[1], fp32_exact=True)
+    out, m, worst = _all_cells(case)
+    assert float(m["tv"].max()) > 0 and float(m["bound_raw"].min()) > 0
+    assert torch.all(m["tv"] <= m["bound_raw"])
+
+
+@pytest.mark.parametrize("split", [64, 256, 1024])
+def test_split_size_does_not_change_results(gpu_lib, split):
+    cfg = small_variant(CONFIGS[3], batch=2, h_kv=1, suffix_len=2500, lens=(2500, 70))
+    case = GpuCase(cfg)
+    _all_cells(case, split_tokens=split)
+
+
+def test_group_sizes_and_tiny_lengths(gpu_lib):
+    for hq, lens in ((8, (1, 2)), (16, (63, 65)), (64, (129, 1))):
+        cfg = dataclasses.replace(small_variant(CONFIGS[3], batch=2, h_kv=8, suffix_len=130, lens=lens),
+                                  h_q=hq)
+        case = GpuCase(cfg)
+        _all_cells(case, cells=[(0, 0), (1, 7), (1, 3)])
+
+
+def test_prefix_only_request_and_empty_suffix(gpu_lib):
+    cfg = small_variant(CONFIGS[2], batch=2, h_kv=1, lens=(0, 16))
+    case = GpuCase(cfg, page_seed=9)
+    _all_cells(case)
+
+
+def test_meter_only_matches_decode(gpu_lib):
+    cfg = small_variant(CONFIGS[5], batch=1, h_kv=2, suffix_len=3000)
+    case = GpuCase(cfg)
+    _, m1 = case.run(split_tokens=1024)
+    _, m2 = case.run(split_tokens=1024, meter_only=True)
+    for k in ("tv", "bound_raw", "meter", "log_a"):
+        assert torch.equal(m1[k], m2[k]), k
+    _all_cells(case, meter_only=True, split_tokens=1024)
+
+
+def test_bitwise_deterministic_across_calls(gpu_lib):
+    cfg = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=700)
+    case = GpuCase(cfg)
+    o1, m1 = case.run()
+    o2, m2 = case.run()
+    assert torch.equal(o1, o2)
+    for k in m1:
+        assert torch.equal(m1[k], m2[k])
+
+
+def test_bound_dominates_tv_every_cell(gpu_lib):
+    """Theorem 1 + 2 on the GPU's own numbers (per cell, never in aggregate)."""
+    for idx in (3, 4, 5):
+        cfg = small_variant(CONFIGS[idx], batch=2, h_kv=8, suffix_len=777)
+        case = GpuCase(cfg)
+        _, m = case.run()
+        tv, bound = m["tv"], m["bound_raw"]
+        assert torch.all(tv >= 0) and torch.all(tv <= 1)
+        assert torch.all(tv <= bound + 1e-6), (idx, float((tv - bound).max()))
+        assert torch.all(m["meter"] == torch.clamp(bound, max=1.0))

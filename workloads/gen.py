@@ -18,6 +18,7 @@ theta^(-2j/d); angles are formed in float64 on the host.
 """
 from __future__ import annotations
 
+import functools
 from typing import Dict, Optional
 
 import numpy as np
@@ -35,6 +36,12 @@ def _seed(cfg: Config, layer: int, tensor: int, part: int) -> int:
 def outlier_channels(cfg: Config) -> np.ndarray:
     n = 8 if cfg.key_dist == "student_t3_8ch" else 4
     return np.sort(np.random.default_rng(cfg.seed).choice(cfg.head_dim, n, replace=False))
+
+
+@functools.lru_cache(maxsize=64)
+def _rope_tables_cached(pos0: int, n: int, d: int, theta: float, device: str):
+    cos, sin = _rope_tables(np.arange(pos0, pos0 + n), d, theta)
+    return torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device)
 
 
 def _rope_tables(positions: np.ndarray, d: int, theta: float):
@@ -69,8 +76,8 @@ def _keys(cfg: Config, n_tok: int, pos0: int, seed: int, device, h_kv: int) -> t
     else:
         raise ValueError(cfg.key_dist)
     if cfg.rope and n_tok > 0:
-        cos, sin = _rope_tables(np.arange(pos0, pos0 + n_tok), d, cfg.theta)
-        k = _apply_rope(k, torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device))
+        cos, sin = _rope_tables_cached(pos0, n_tok, d, cfg.theta, str(device))
+        k = _apply_rope(k, cos, sin)
     return k
 
 
