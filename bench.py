@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="replay the step as a HIP graph")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -179,6 +180,15 @@ def main():
             if rc:
                 raise RuntimeError(f"kvq_decode_attn status {rc}")
 
+    if args.copy_calibrate:
+        n = args.copy_calibrate // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibrate} bytes done")
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -29,7 +29,7 @@ struct Plan {
 kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int batch, int h_kv) {
   if (r.length < 0) return KVQ_ERR_SHAPE;
   if (r.length == 0) return KVQ_OK;                          // region absent
-  if (r.length > (1 << 28)) return KVQ_ERR_SHAPE;
+  if (r.length > (1 << 24)) return KVQ_ERR_SHAPE;           // < 2^24 tokens per request
   if (!is_store_fmt(r.k_format)) return KVQ_ERR_FORMAT;
   if (need_v && !is_store_fmt(r.v_format)) return KVQ_ERR_FORMAT;
   if (!r.k || (need_v && !r.v)) return KVQ_ERR_NULL;
@@ -83,8 +83,13 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   const int smax = p.prefix_len + p.suffix_cap;
   int chunk = a->split_tokens;
   if (chunk == 0) {
-    chunk = 1024;                       // keep >= ~2048 work-groups in flight when possible
-    while (chunk > 256 && (int64_t)groups * ((smax + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    // about two resident work-groups per CU (256 CUs): as many chunks per group
+    // as fill 512 work-groups, each a multiple of 64 tokens
+    const int64_t target = 512;
+    const int64_t per_group = groups >= target ? 1 : (target + groups - 1) / groups;
+    int64_t c = (smax + per_group - 1) / per_group;
+    c = (c + 63) / 64 * 64;
+    chunk = (int)(c < 64 ? 64 : c);
   }
   p.chunk = chunk;
   p.pre_chunks = (p.prefix_len + chunk - 1) / chunk;
@@ -215,7 +220,7 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   if (!is_store_fmt(a->k_format)) return KVQ_ERR_FORMAT;
   if (a->v_in && !is_store_fmt(a->v_format)) return KVQ_ERR_FORMAT;
   if (a->n_seq <= 0 || a->num_kv_heads <= 0 || a->capacity <= 0) return KVQ_ERR_SHAPE;
-  if (a->capacity > (1 << 28) || (int64_t)a->n_seq * a->num_kv_heads > (1 << 24)) return KVQ_ERR_SHAPE;
+  if (a->capacity > (1 << 24) || (int64_t)a->n_seq * a->num_kv_heads > (1 << 24)) return KVQ_ERR_SHAPE;
   if (a->tok_begin < 0 || a->tok_end > a->capacity || a->tok_begin >= a->tok_end) return KVQ_ERR_SHAPE;
   if (!a->k_in || !a->k_out) return KVQ_ERR_NULL;
   if (a->v_in && !a->v_out) return KVQ_ERR_NULL;

@@ -69,6 +69,9 @@ struct DecodeLaunch {
 constexpr int PART_STRIDE = 136;  // m~, z~, m', z', m_e, z_e, 2 pad, acc[128]
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+// Matrix-core kernel for GQA group 4 with FP8/BF16 keys and values.
+bool mfma_path_supports(const DecodeLaunch &d);
+hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 
 }  // namespace kvq

@@ -93,7 +93,7 @@ def test_workspace_plan_of_the_batch64_step(lib):
     a = _args()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
-    groups, chunks, G = 64 * 8, 13, 4
+    groups, chunks, G = 64 * 8, 1, 4        # 512 groups fill the GPU: one chunk each
     counters = 2048
     partials = groups * chunks * G * 136 * 4
     spill = groups * 12628 * G * 8

@@ -110,8 +110,18 @@ SMALL = {
 }
 
 
+@pytest.fixture(params=["auto", "generic"])
+def kernel(request, monkeypatch):
+    """Run a test with the library's kernel choice and with the vector-ALU kernel."""
+    if request.param == "generic":
+        monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
+    else:
+        monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_config_parity_all_cells(gpu_lib, name):
+def test_small_config_parity_all_cells(gpu_lib, kernel, name):
     cfg = SMALL[name]()
     case = GpuCase(cfg, layer=5 if cfg.layers > 5 else 0, page_seed=3)
     out, m, worst = _all_cells(case, split_tokens=cfg.split_tokens)
@@ -129,7 +139,7 @@ def test_cfg1_fp32_exact_cache_meter_nonzero(gpu_lib):
 
 
 @pytest.mark.parametrize("split", [64, 256, 1024])
-def test_split_size_does_not_change_results(gpu_lib, split):
+def test_split_size_does_not_change_results(gpu_lib, kernel, split):
     cfg = small_variant(CONFIGS[3], batch=2, h_kv=1, suffix_len=2500, lens=(2500, 70))
     case = GpuCase(cfg)
     _all_cells(case, split_tokens=split)
@@ -143,13 +153,13 @@ def test_group_sizes_and_tiny_lengths(gpu_lib):
         _all_cells(case, cells=[(0, 0), (1, 7), (1, 3)])
 
 
-def test_prefix_only_request_and_empty_suffix(gpu_lib):
+def test_prefix_only_request_and_empty_suffix(gpu_lib, kernel):
     cfg = small_variant(CONFIGS[2], batch=2, h_kv=1, lens=(0, 16))
     case = GpuCase(cfg, page_seed=9)
     _all_cells(case)
 
 
-def test_meter_only_matches_decode(gpu_lib):
+def test_meter_only_matches_decode(gpu_lib, kernel):
     cfg = small_variant(CONFIGS[5], batch=1, h_kv=2, suffix_len=3000)
     case = GpuCase(cfg)
     _, m1 = case.run(split_tokens=1024)
@@ -159,8 +169,9 @@ def test_meter_only_matches_decode(gpu_lib):
     _all_cells(case, meter_only=True, split_tokens=1024)
 
 
-def test_bitwise_deterministic_across_calls(gpu_lib):
-    cfg = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=700)
+@pytest.mark.parametrize("idx", [3, 4])
+def test_bitwise_deterministic_across_calls(gpu_lib, idx):
+    cfg = small_variant(CONFIGS[idx], batch=2, h_kv=2, suffix_len=700)
     case = GpuCase(cfg)
     o1, m1 = case.run()
     o2, m2 = case.run()
