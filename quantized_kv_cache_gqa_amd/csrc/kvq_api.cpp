@@ -110,7 +110,9 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   p.off_spill = p.off_partials +
                 round_up((size_t)groups * p.total_chunks * p.group * PART_STRIDE * sizeof(float), kAlign);
   p.bytes = p.off_spill;
-  if (p.tv) p.bytes += round_up((size_t)groups * (size_t)smax * p.group * 2 * sizeof(float), kAlign);
+  // spill: each region padded to whole 16-token tiles
+  const size_t spill_rows = round_up((size_t)p.prefix_len, 16) + round_up((size_t)p.suffix_cap, 16);
+  if (p.tv) p.bytes += round_up((size_t)groups * spill_rows * p.group * 2 * sizeof(float), kAlign);
   return KVQ_OK;
 }
 

@@ -106,8 +106,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
                                                  : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
   const uint32_t ktag = dither_tag(0, R.layer, kvh), vtag = dither_tag(1, R.layer, kvh);
   const int nblk_cap = (R.length + BLK - 1) / BLK;
-  float *spill_g = d.spill + ((size_t)grp * (d.prefix_len + d.suffix_cap) +
-                              (R.is_prefix ? 0 : d.prefix_len)) * (2 * G);
+  float *spill_g = do_tv ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
 
   for (int base = c0 + wv * 8; base < c1; base += 8 * WAVES) {
     const int t = base + slot;
@@ -176,12 +175,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
 
     // ---- spill (l~, l) for the TV pass
     if (do_tv && valid && j == 0) {
-      float *sp = spill_g + (size_t)t * (2 * G);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sp[2 * h] = lq[h];
-        sp[2 * h + 1] = le[h];
-      }
+      for (int h = 0; h < G; ++h)
+        *reinterpret_cast<float2 *>(spill_g + 2 * spill_entry<G>(t, h)) = make_float2(lq[h], le[h]);
     }
 
     // ---- online accumulators

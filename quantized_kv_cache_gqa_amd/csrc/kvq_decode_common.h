@@ -17,6 +17,30 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LAZY = 8.0f;  // log2 headroom before a running maximum moves
 constexpr int WAVES = 4;
 
+// Spill layout of the (l~, l) pairs of one (request, KV head): per region,
+// tiles of 16 tokens; inside a tile, 4 groups of 4 tokens; inside a group the
+// entries are head-major, token-minor.  Entry index of (region token t, head h):
+//   16 G (t / 16) + 4 G ((t % 16) / 4) + 4 h + t % 4.
+// A wavefront of the matrix-core kernel writes its tile's 64 entries in lane
+// order.  Each region's part is padded to whole tiles.
+__device__ __forceinline__ int round16(int n) { return (n + 15) & ~15; }
+
+__device__ __forceinline__ void tvp_add(float &acc, float lt, float le, float Mt, float iZt,
+                                        float Me, float iZe) {
+  acc += fabsf(fast_exp2(le - Me) * iZe - fast_exp2(lt - Mt) * iZt);
+}
+
+template <int G>
+__device__ __forceinline__ size_t spill_entry(int t, int h) {
+  return (size_t)(16 * G) * (t >> 4) + 4 * G * ((t & 15) >> 2) + 4 * h + (t & 3);
+}
+
+template <int G>
+__device__ __forceinline__ float *spill_region(const DecodeLaunch &d, int grp, bool is_prefix) {
+  const size_t rows = (size_t)round16(d.prefix_len) + round16(d.suffix_cap);
+  return d.spill + ((size_t)grp * rows + (is_prefix ? 0 : round16(d.prefix_len))) * (2 * G);
+}
+
 __device__ __forceinline__ float merge_factor(float m, float mnew) {
   return m == NEG_INF ? 0.0f : fast_exp2(m - mnew);
 }
@@ -123,7 +147,6 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
 
   // ================= finalize: this work-group arrived last for (b, kvh)
   __shared__ float fin_s[G][6];   // M~, 1/Z~, M_e, 1/Z_e (log2 units)
-  __shared__ float tv_s[WAVES][G];
   const float *pg = single ? &merged_s[0][0] : d.partials + (size_t)grp * total_chunks * G * PART_STRIDE;
   const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
   const int S = d.prefix_len + suf_len;
@@ -168,31 +191,46 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
   }
   __syncthreads();
   if (d.tv) {
-    float tvp[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) tvp[h] = 0.0f;
+    // Thread tid reads entries 2 tid + 512 k (a float4: two entries of one
+    // head); 512 is a multiple of 4G, so the head of its entries never changes.
+    __shared__ float tvpart_s[256];
+    const int hmine = ((2 * tid) % (4 * G)) / 4;
+    float acc_tv = 0.0f;
     if (do_tv) {
-      const float *sp = d.spill + (size_t)grp * (d.prefix_len + d.suffix_cap) * (2 * G);
-      for (int t = tid; t < S; t += 256) {
-        const float *r = sp + (size_t)t * (2 * G);
+      const float Mt = fin_s[hmine][0], iZt = fin_s[hmine][1];
+      const float Me = fin_s[hmine][2], iZe = fin_s[hmine][3];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pt = fast_exp2(r[2 * h] - fin_s[h][0]) * fin_s[h][1];
-          const float pe = fast_exp2(r[2 * h + 1] - fin_s[h][2]) * fin_s[h][3];
-          tvp[h] += fabsf(pe - pt);
+      for (int region = 0; region < 2; ++region) {
+        const int n = region == 0 ? d.prefix_len : suf_len;
+        if (n == 0) continue;
+        const float *sp = spill_region<G>(d, grp, region == 0);
+        const int n_entries = round16(n) * G;
+        for (int e0 = 2 * tid; e0 < n_entries; e0 += 4 * 512) {
+          float4 x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = min(e0 + 512 * u, n_entries - 2);
+            x[u] = *reinterpret_cast<const float4 *>(sp + 2 * (size_t)e);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = e0 + 512 * u;
+            if (e >= n_entries) break;
+            // entries e and e + 1: tokens of the same head
+            const int tile = e / (16 * G), r = e % (16 * G);
+            const int t = 16 * tile + 4 * (r / (4 * G)) + (r & 3);
+            if (t < n) tvp_add(acc_tv, x[u].x, x[u].y, Mt, iZt, Me, iZe);
+            if (t + 1 < n) tvp_add(acc_tv, x[u].z, x[u].w, Mt, iZt, Me, iZe);
+          }
         }
       }
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float s = wave_sum(tvp[h]);
-      if (lane == 0) tv_s[wv][h] = s;
-    }
+    tvpart_s[tid] = acc_tv;
     __syncthreads();
     if (tid < G) {
       float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) s += tv_s[w][tid];
+      for (int t = 0; t < 256; ++t)                   // fixed order: bitwise reproducible
+        if (((2 * t) % (4 * G)) / 4 == tid) s += tvpart_s[t];
       d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * s;
     }
   }

@@ -99,7 +99,11 @@ struct TileRegs {
   float ks, vs;    // scales of this lane's compact (token, head) slot
 };
 
-template <int KF, int VF, bool PAGED>
+// FULL: TV and meter requested and this region holds exact bf16 keys and a
+// witness (the common quantized case).  Then every load of a tile is issued
+// unconditionally, which lets the compiler keep the next tile's loads in
+// flight across the current tile's math (no load sits under a runtime branch).
+template <int KF, int VF, bool PAGED, bool FULL>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch d) {
   constexpr int G = 4;
   const RegionDev &R = d.region;
@@ -118,10 +122,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   const int c0 = chunk_idx * d.chunk;
   const int c1 = min(c0 + d.chunk, len);
 
-  const bool do_tv = d.has_tv != 0;
-  const bool do_meter = d.has_meter != 0;
-  const bool has_exact = R.exact_fmt == EX_BF16;
-  const bool has_wit = R.witness != nullptr;
+  const bool do_tv = FULL || d.has_tv != 0;
+  const bool do_meter = FULL || d.has_meter != 0;
+  const bool has_exact = FULL || R.exact_fmt == EX_BF16;
+  const bool has_wit = FULL || R.witness != nullptr;
   const float qs = d.sm_scale * LOG2E;
 
   // ---- B operands of the logit contractions, column j16 = 4 hh + pp
@@ -182,8 +186,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   const float *ksb = (const float *)R.k_scale + row0;
   const uint8_t *vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
   const float *vsb = (const float *)R.v_scale + row0;
-  float *spill_g = d.spill + ((size_t)grp * (d.prefix_len + d.suffix_cap) +
-                              (R.is_prefix ? 0 : d.prefix_len)) * (2 * G);
+  float *spill_g = do_tv ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
 
   auto load_tile = [&](TileRegs &T, int t0) {
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
@@ -265,8 +268,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
       lq = NEG_INF;
       le = NEG_INF;
     }
+    // spill entry of (tk, hh) is 64 (t0 / 16) + lane: one contiguous 512-byte store
     if (do_tv && valid)
-      *reinterpret_cast<float2 *>(spill_g + (size_t)tk * (2 * G) + 2 * hh) = make_float2(lq, le);
+      *reinterpret_cast<float2 *>(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane)) = make_float2(lq, le);
 
     // ---- attention softmax (maximum uniform per head)
     if (__any(lq > mq + LAZY)) {
@@ -361,17 +365,19 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
     }
   };
 
-  // two register sets, no copies: loads of one tile overlap the other's math
+  // two register sets, no copies: the loads of one tile overlap the other's
+  // math.  The next tile is always loaded (rows clamp to the last valid
+  // token, so past the end this re-reads a valid row and the data is unused).
   TileRegs ta, tb;
   constexpr int STEP = 16 * WAVES;
   int t0 = c0 + 16 * wv;
   if (t0 < c1) load_tile(ta, t0);
   while (t0 < c1) {
-    if (t0 + STEP < c1) load_tile(tb, t0 + STEP);
+    load_tile(tb, t0 + STEP);
     process(ta, t0);
     t0 += STEP;
     if (t0 >= c1) break;
-    if (t0 + STEP < c1) load_tile(ta, t0 + STEP);
+    load_tile(ta, t0 + STEP);
     process(tb, t0);
     t0 += STEP;
   }
@@ -434,14 +440,23 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   chunk_epilogue<G>(d, part_s, grp, chunk_idx, b, kvh);
 }
 
+template <int KF, int VF, bool PAGED>
+static void launch_p(const DecodeLaunch &d, hipStream_t stream, dim3 grid) {
+  const bool full = d.has_tv && d.has_meter && d.region.exact_fmt == EX_BF16 && d.region.witness;
+  if (full)
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, true>), grid, dim3(256), 0, stream, d);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, false>), grid, dim3(256), 0, stream, d);
+}
+
 template <int KF, int VF>
 static hipError_t launch_m(const DecodeLaunch &d, hipStream_t stream) {
   const long work = (long)d.batch * d.h_kv * d.n_chunks;
-  const long grid = (work + 7) / 8 * 8;
+  const dim3 grid((unsigned)((work + 7) / 8 * 8));
   if (d.region.paged)
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, true>), dim3((unsigned)grid), dim3(256), 0, stream, d);
+    launch_p<KF, VF, true>(d, stream, grid);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, false>), dim3((unsigned)grid), dim3(256), 0, stream, d);
+    launch_p<KF, VF, false>(d, stream, grid);
   return hipGetLastError();
 }
 

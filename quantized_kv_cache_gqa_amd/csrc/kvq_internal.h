@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 
 namespace kvq {
 

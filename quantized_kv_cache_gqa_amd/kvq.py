@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkvq.so")
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
 FMT = {"bf16": 0, "fp8": 1, "int8": 2, "fp32": 3}
 HEAD_DIM = 128

@@ -96,7 +96,7 @@ def test_workspace_plan_of_the_batch64_step(lib):
     groups, chunks, G = 64 * 8, 1, 4        # 512 groups fill the GPU: one chunk each
     counters = 2048
     partials = groups * chunks * G * 136 * 4
-    spill = groups * 12628 * G * 8
+    spill = groups * 12640 * G * 8                # 12628 tokens padded to 16-token tiles
     assert n == counters + partials + spill
     # without TV: no spill
     m2 = kvq.MeterOut(tv=None, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
