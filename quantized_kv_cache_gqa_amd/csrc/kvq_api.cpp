@@ -3,7 +3,14 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <time.h>
+#include <unistd.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "kvq_internal.h"
 
@@ -23,8 +30,85 @@ struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
   int prefix_len = 0, suffix_cap = 0;
   bool tv = false, meter = false, wit_any = false;
+  int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
 };
+
+// Tags of a team launch: epoch + 1 .. epoch + rounds, never 0 (the value of
+// cleared workspace) and never reused by another launch of this process
+// (the first epoch depends on the process and the clock, so a workspace left
+// by another process is unlikely to hold a matching tag).
+uint32_t next_epoch(uint32_t rounds) {
+  static std::atomic<uint32_t> next{(uint32_t)(time(nullptr) * 2654435761u) ^ ((uint32_t)getpid() << 16)};
+  for (;;) {
+    const uint32_t e = next.fetch_add(rounds + 1u);
+    if ((uint64_t)e + rounds < ((uint64_t)1 << 32)) return e;   // e + 1 .. e + rounds do not wrap to 0
+  }
+}
+
+bool env_is(const char *name, char c) {
+  const char *v = getenv(name);
+  return v && v[0] == c;
+}
+
+// Team plan for a one-region launch with the TV on the matrix-core path:
+// T members per (request, KV head), chunks of <= TEAM_MAX_CHUNK tokens (a
+// multiple of 64), persistent teams over the groups.  Picks the T with the
+// least work per member over all rounds (a round's fixed cost is counted as
+// 256 tokens).  Returns false when no team launch applies.
+bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
+  if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
+  if (!p.tv || a->split_tokens != 0 || p.group != 4) return false;
+  if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
+  const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
+  if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
+  const int vf = meter_only ? VF_NONE : r.v_format;
+  if (!meter_only && vf != KVQ_FMT_BF16 && vf != KVQ_FMT_FP8_E4M3) return false;
+  if (!r.k_exact || r.k_exact_format != KVQ_FMT_BF16) return false;
+  const bool full = p.tv && p.meter && r.witness;
+  // one plan for the decode and the meter call on the same arguments (so
+  // kvq_workspace_bytes fits both): the smaller capacity of the two kernels
+  const bool paged = p.prefix_len == 0 && r.page_table;
+  const int vf_dec = (r.v_format == KVQ_FMT_BF16 || r.v_format == KVQ_FMT_FP8_E4M3) ? r.v_format : VF_NONE;
+  const int cap = std::min(team_capacity(r.k_format, VF_NONE, paged, full),
+                           team_capacity(r.k_format, vf_dec, paged, full));
+  (void)vf;
+  if (cap <= 0) return false;
+  const int64_t len = r.length;
+  const int64_t tmin = (len + TEAM_MAX_CHUNK - 1) / TEAM_MAX_CHUNK;
+  const int64_t tmax = std::min<int64_t>(std::min<int64_t>(cap, TEAM_MAX), (len + 63) / 64);
+  int64_t best_cost = -1;
+  for (int64_t T = tmin; T <= tmax; ++T) {
+    const int64_t n_teams = std::min<int64_t>(cap / T, groups);
+    if (n_teams <= 0) break;
+    const int64_t rounds = (groups + n_teams - 1) / n_teams;
+    const int64_t chunk = ((len + T - 1) / T + 63) / 64 * 64;
+    const int64_t cost = rounds * (chunk + 256);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      p.team = (int)T;
+      p.n_teams = (int)n_teams;
+      p.chunk = (int)chunk;
+    }
+  }
+  if (p.team <= 0) return false;
+  // the grid is padded to whole XCD slices (8) and must stay resident
+  while (p.n_teams > 1 && (int64_t)round_up((size_t)p.n_teams * p.team, 8) > cap) --p.n_teams;
+  p.grid = (int)round_up((size_t)p.n_teams * p.team, 8);
+  if (p.grid > cap) {
+    p.team = 0;
+    return false;
+  }
+  p.pre_chunks = p.prefix_len > 0 ? p.team : 0;
+  p.suf_chunks = p.suffix_cap > 0 ? p.team : 0;
+  p.total_chunks = p.team;
+  p.rounds = (groups + p.n_teams - 1) / p.n_teams;
+  p.off_counters = 0;
+  p.off_partials = 0;
+  p.off_spill = round_up((size_t)p.n_teams * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
+  p.bytes = p.off_spill;
+  return true;
+}
 
 kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int batch, int h_kv) {
   if (r.length < 0) return KVQ_ERR_SHAPE;
@@ -105,6 +189,7 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     p.tv = m->tv && any_exact;
     p.meter = (m->bound_raw || m->meter || m->log_a) && p.wit_any;
   }
+  if (plan_team(a, meter_only, groups, p)) return KVQ_OK;
   p.off_counters = 0;
   p.off_partials = round_up((size_t)groups * sizeof(uint32_t), kAlign);
   p.off_spill = p.off_partials +
@@ -171,9 +256,22 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
   char *w = static_cast<char *>(ws);
   d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);
   d.partials = reinterpret_cast<float *>(w + p.off_partials);
-  d.spill = p.tv ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+  d.spill = (p.tv && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
 
   hipError_t e = hipSuccess;
+  if (p.team) {
+    const bool pre = p.prefix_len > 0;
+    d.region = region_dev(pre ? a->prefix : a->suffix, pre);
+    d.k_format = pre ? a->prefix.k_format : a->suffix.k_format;
+    d.v_format = meter_only ? VF_NONE : (pre ? a->prefix.v_format : a->suffix.v_format);
+    d.n_chunks = p.team;
+    d.chunk_base = 0;
+    d.team = p.team;
+    d.n_teams = p.n_teams;
+    d.epoch = next_epoch((uint32_t)p.rounds);
+    e = launch_decode_team(d, p.grid, stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+  }
   if (p.pre_chunks > 0) {
     d.region = region_dev(a->prefix, true);
     d.k_format = a->prefix.k_format;

@@ -99,28 +99,25 @@ struct TileRegs {
   float ks, vs;    // scales of this lane's compact (token, head) slot
 };
 
+// One (request, KV head) chunk [c0, c1) of one region, run by the whole
+// work-group (4 wavefronts, tiles of 16 tokens dealt round-robin): leaves each
+// wavefront's softmax states and output accumulator in part_s[wv].  The
+// (l~, l) pairs go to the spill: SPILL_LDS = the chunk's own LDS buffer
+// (entry 64 ((t0 - c0) / 16) + lane), else the group's workspace rows.
+//
 // FULL: TV and meter requested and this region holds exact bf16 keys and a
 // witness (the common quantized case).  Then every load of a tile is issued
 // unconditionally, which lets the compiler keep the next tile's loads in
 // flight across the current tile's math (no load sits under a runtime branch).
-template <int KF, int VF, bool PAGED, bool FULL>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch d) {
+template <int KF, int VF, bool PAGED, bool FULL, bool SPILL_LDS>
+__device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh, int grp, int c0,
+                                           int c1, float2 *spill_s, float (*w_s)[64],
+                                           float (*part_s)[4][PART_STRIDE]) {
   constexpr int G = 4;
   const RegionDev &R = d.region;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, j16 = lane & 15, hh = j16 >> 2, pp = lane & 3;
-
-  const unsigned per_xcd = gridDim.x >> 3;
-  const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
-  const unsigned n_work = (unsigned)d.batch * d.h_kv * d.n_chunks;
-  if (L >= n_work) return;
-  const int chunk_idx = (int)(L % (unsigned)d.n_chunks);
-  const int grp = (int)(L / (unsigned)d.n_chunks);
-  const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
-  const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
-  const int c0 = chunk_idx * d.chunk;
-  const int c1 = min(c0 + d.chunk, len);
 
   const bool do_tv = FULL || d.has_tv != 0;
   const bool do_meter = FULL || d.has_meter != 0;
@@ -186,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   const float *ksb = (const float *)R.k_scale + row0;
   const uint8_t *vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
   const float *vsb = (const float *)R.v_scale + row0;
-  float *spill_g = do_tv ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
+  float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
 
   auto load_tile = [&](TileRegs &T, int t0) {
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
@@ -237,7 +234,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   for (int h = 0; h < NACC; ++h)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
-  __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
 
   auto process = [&](const TileRegs &T, int t0) {
     // ---- logit contractions on the matrix cores
@@ -269,8 +265,12 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
       le = NEG_INF;
     }
     // spill entry of (tk, hh) is 64 (t0 / 16) + lane: one contiguous 512-byte store
-    if (do_tv && valid)
-      *reinterpret_cast<float2 *>(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane)) = make_float2(lq, le);
+    if constexpr (SPILL_LDS) {
+      if (do_tv) spill_s[64 * ((t0 - c0) >> 4) + lane] = make_float2(lq, le);
+    } else {
+      if (do_tv && valid)
+        *reinterpret_cast<float2 *>(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane)) = make_float2(lq, le);
+    }
 
     // ---- attention softmax (maximum uniform per head)
     if (__any(lq > mq + LAZY)) {
@@ -409,7 +409,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
         for (int i = 0; i < 16; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
   }
 
-  __shared__ float part_s[WAVES][G][PART_STRIDE];
   if (lane < 16 && pp == 0) {                      // lane 4h holds head h
     part_s[wv][hh][0] = mq; part_s[wv][hh][1] = zq;
     part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
@@ -437,7 +436,289 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
         for (int r = 0; r < 4; ++r) part_s[wv][r][8 + 8 * lane + n] = 0.0f;
     }
   }
-  chunk_epilogue<G>(d, part_s, grp, chunk_idx, b, kvh);
+}
+
+template <int KF, int VF, bool PAGED, bool FULL>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch d) {
+  const unsigned per_xcd = gridDim.x >> 3;
+  const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+  const unsigned n_work = (unsigned)d.batch * d.h_kv * d.n_chunks;
+  if (L >= n_work) return;
+  const int chunk_idx = (int)(L % (unsigned)d.n_chunks);
+  const int grp = (int)(L / (unsigned)d.n_chunks);
+  const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
+  const RegionDev &R = d.region;
+  const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
+  const int c0 = chunk_idx * d.chunk;
+  const int c1 = min(c0 + d.chunk, len);
+  __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
+  __shared__ float part_s[WAVES][4][PART_STRIDE];
+  mfma_chunk<KF, VF, PAGED, FULL, false>(d, b, kvh, grp, c0, c1, nullptr, w_s, part_s);
+  chunk_epilogue<4>(d, part_s, grp, chunk_idx, b, kvh);
+}
+
+// ----------------------------------------------------------------- teams
+// A team of T work-groups shares each (request, KV head): member m takes
+// tokens [m chunk, (m + 1) chunk) and keeps that chunk's (l~, l) pairs in its
+// own LDS, so the TV needs no spill traffic to HBM.  Teams are persistent:
+// team t handles groups t, t + n_teams, ... in rounds.
+//
+// Exchange: each member publishes, per round, its merged softmax states and
+// output accumulator into its slot, every word as (tag, value) in one 64-bit
+// store; the tag names the launch and round, so a reader polls each word
+// until its tag is the expected one.  No store has to be waited for and no
+// counter is needed.  Every member derives the exact normalizers of the
+// group from all members' states; member h % T writes head h's output, log A,
+// bound and meter.  The chunk's TV shares are published in the same slot and
+// summed (member order) by member h % T one round later, or at the end of the
+// last round.  Slots alternate between two buffers by round parity: a member
+// writes round r + 2 only after it has read every member's round r + 1
+// states, which each member publishes after it has finished with round r.
+// All reductions run in a fixed order (bitwise reproducible).  The launch is
+// cooperative (all members resident); a bounded wait leaves NaN in the
+// group's results instead of hanging.
+constexpr unsigned TEAM_SPIN_LIMIT = 1u << 18;
+constexpr int SLOT_WORDS = 544;    // 24 states (6 per head), 4 TV shares, 4 pad, 512 accumulator words
+constexpr int SLOT_TV = 24, SLOT_ACC = 32;
+
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tagged(uint64_t *p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reads N tagged words (all loads in flight together), then re-polls any
+// whose tag is not yet `tag`.  Returns false if a word never arrived.
+template <int N>
+__device__ __forceinline__ bool read_tagged(const uint64_t *const (&p)[N], uint32_t tag, float (&v)[N]) {
+  uint64_t w[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) w[i] = ld_tagged(p[i]);
+  bool ok = true;
+  unsigned spins = 0;                 // one budget for the whole batch
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    while (ok && (uint32_t)(w[i] >> 32) != tag) {
+      __builtin_amdgcn_s_sleep(2);
+      w[i] = ld_tagged(p[i]);
+      if (++spins >= TEAM_SPIN_LIMIT) ok = false;   // budget spent: no further waits
+    }
+    v[i] = __uint_as_float((uint32_t)w[i]);
+  }
+  return ok;
+}
+
+// (M, Z) merge of two online-softmax states; symmetric in its arguments
+__device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2) {
+  const float mx = fmaxf(m, m2);
+  z = z * merge_factor(m, mx) + z2 * merge_factor(m2, mx);
+  m = mx;
+}
+
+// Sum of the members' TV shares of head h (lanes c < T hold member c's share),
+// butterfly over the wavefront: the same bits in every lane.
+__device__ __forceinline__ float wave_sum_fixed(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*part_s)[4][PART_STRIDE],
+                              const float2 *spill_s, int team, int member, int round,
+                              bool last_round, int b, int kvh, int c0, int c1) {
+  constexpr int G = 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int T = d.team;
+  const bool do_tv = d.has_tv != 0;
+  const bool do_meter = d.has_meter != 0;
+  const uint32_t tag = d.epoch + (uint32_t)round + 1u;
+  uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(team * 2 + (round & 1)) * T * SLOT_WORDS;
+  uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
+  __shared__ float mq_s[G][64];
+  __shared__ float fin_s[G][4];
+  __shared__ float tvw_s[WAVES][G];
+  __shared__ int bad_s;
+  const float qnan = __builtin_nanf("");
+
+  // 1. publish this member's merged states and accumulator
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
+    const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
+    if (k == 6 || k == 7) continue;
+    const int mk = (k >= 8) ? 0 : (k & ~1);
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
+    float r;
+    if (k < 6 && (k & 1) == 0) {
+      r = M;
+    } else {
+      r = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) r += part_s[w][h][k] * merge_factor(part_s[w][h][mk], M);
+    }
+    st_tagged(mine + (k < 6 ? 6 * h + k : SLOT_ACC + 128 * h + (k - 8)), tag, r);
+  }
+
+  // 2. the group's normalizers: wavefront h reads head h of every member
+  //    (lane c = member c), then a butterfly merge gives every lane the same
+  const int h = wv;
+  bool ok = true;
+  float Mq = NEG_INF, Zq = 0.0f, Mm = NEG_INF, Zm = 0.0f, Me = NEG_INF, Ze = 0.0f;
+  if (lane < T) {
+    const uint64_t *s = slots + (size_t)lane * SLOT_WORDS + 6 * h;
+    const uint64_t *const p[6] = {s, s + 1, s + 2, s + 3, s + 4, s + 5};
+    float v[6];
+    ok = read_tagged<6>(p, tag, v);
+    Mq = v[0]; Zq = v[1]; Mm = v[2]; Zm = v[3]; Me = v[4]; Ze = v[5];
+  }
+  mq_s[h][lane] = Mq;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float a0 = __shfl_xor(Mq, off), a1 = __shfl_xor(Zq, off);
+    const float b0 = __shfl_xor(Mm, off), b1 = __shfl_xor(Zm, off);
+    const float e0 = __shfl_xor(Me, off), e1 = __shfl_xor(Ze, off);
+    mz_merge(Mq, Zq, a0, a1);
+    mz_merge(Mm, Zm, b0, b1);
+    mz_merge(Me, Ze, e0, e1);
+  }
+  if (lane == 0) {
+    fin_s[h][0] = Mq;
+    fin_s[h][1] = Zq > 0.0f ? 1.0f / Zq : 0.0f;
+    fin_s[h][2] = Me;
+    fin_s[h][3] = Ze > 0.0f ? 1.0f / Ze : 0.0f;
+  }
+  __syncthreads();
+
+  // 3. member h % T: head h's output (member order), log A, bound, meter, and
+  //    the previous round's TV
+  const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
+  if (member == h % T) {
+    if (d.has_out) {
+      float o0 = 0.0f, o1 = 0.0f;
+      for (int c0m = 0; c0m < T; c0m += 4) {
+        const uint64_t *p[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = min(c0m + i, T - 1);
+          const uint64_t *s = slots + (size_t)c * SLOT_WORDS + SLOT_ACC + 128 * h;
+          p[2 * i] = s + lane;
+          p[2 * i + 1] = s + 64 + lane;
+        }
+        float v[8];
+        ok = read_tagged<8>(p, tag, v) && ok;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (c0m + i >= T) break;
+          const float fq = merge_factor(mq_s[h][c0m + i], Mq);
+          o0 += v[2 * i] * fq;
+          o1 += v[2 * i + 1] * fq;
+        }
+      }
+      const float inv = Zq > 0.0f ? 1.0f / Zq : 0.0f;
+      d.out[qh * D + lane] = ok ? o0 * inv : qnan;
+      d.out[qh * D + 64 + lane] = ok ? o1 * inv : qnan;
+    }
+    if (lane == 0) {
+      double log_a = 0.0;
+      if (do_meter && Zq > 0.0f && Zm > 0.0f)
+        log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
+      const double bound = 0.5 * expm1(2.0 * log_a);
+      const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
+      if (d.log_a) d.log_a[qh] = ok ? (float)log_a : qnan;
+      if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
+      if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
+    }
+    if (do_tv && d.tv && round > 0) {
+      // shares of round - 1 sit in the other parity's slots
+      const uint64_t *prev = reinterpret_cast<const uint64_t *>(d.partials) +
+                             (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS;
+      float sh = 0.0f;
+      bool okp = true;
+      if (lane < T) {
+        const uint64_t *const p[1] = {prev + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
+        float v[1];
+        okp = read_tagged<1>(p, tag - 1u, v);
+        sh = v[0];
+      }
+      sh = wave_sum_fixed(sh);
+      okp = __all(okp);
+      const int pg = team + (round - 1) * d.n_teams;
+      const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
+      if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * G + h] = okp ? 0.5f * sh : qnan;
+    }
+  }
+  if (!ok) bad_s = 1;
+
+  // 4. this chunk's TV share: thread tid reads entries tid + 256 k, all of
+  //    head (tid % 16) / 4; butterfly over the lanes of a head, then waves
+  //    in order
+  float acc_tv = 0.0f;
+  if (do_tv && c1 > c0) {
+    const int hm = (lane & 15) >> 2;
+    const float Mt = fin_s[hm][0], iZt = fin_s[hm][1];
+    const float Mx = fin_s[hm][2], iZe = fin_s[hm][3];
+    const int n_entries = round16(c1 - c0) * G;
+    for (int e = tid; e < n_entries; e += 256) {
+      const float2 x = spill_s[e];
+      const int t = c0 + 16 * (e >> 6) + 4 * ((e & 63) >> 4) + (e & 3);
+      if (t < c1) tvp_add(acc_tv, x.x, x.y, Mt, iZt, Mx, iZe);
+    }
+  }
+  acc_tv += __shfl_xor(acc_tv, 1);
+  acc_tv += __shfl_xor(acc_tv, 2);
+  acc_tv += __shfl_xor(acc_tv, 16);
+  acc_tv += __shfl_xor(acc_tv, 32);
+  if (lane < 16 && (lane & 3) == 0) tvw_s[wv][lane >> 2] = acc_tv;
+  __syncthreads();
+  if (tid < G) {
+    const float share = ((tvw_s[0][tid] + tvw_s[1][tid]) + tvw_s[2][tid]) + tvw_s[3][tid];
+    st_tagged(mine + SLOT_TV + tid, tag, share);
+  }
+
+  // 5. last round: member h % T also sums this round's shares
+  if (last_round && do_tv && d.tv && member == h % T) {
+    float sh = 0.0f;
+    bool okp = true;
+    if (lane < T) {
+      const uint64_t *const p[1] = {slots + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
+      float v[1];
+      okp = read_tagged<1>(p, tag, v);
+      sh = v[0];
+    }
+    sh = wave_sum_fixed(sh);
+    okp = __all(okp) && bad_s == 0;
+    if (lane == 0) d.tv[qh] = okp ? 0.5f * sh : qnan;
+  }
+  __syncthreads();                  // LDS buffers are reused by the next round
+}
+
+template <int KF, int VF, bool PAGED, bool FULL>
+__global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLaunch d) {
+  extern __shared__ __attribute__((aligned(16))) float2 spill_s[];   // d.chunk * 4 entries
+  __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
+  __shared__ float part_s[WAVES][4][PART_STRIDE];
+  const int T = d.team;
+  const unsigned per_xcd = gridDim.x >> 3;
+  const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
+  const int team = (int)(L / (unsigned)T), member = (int)(L % (unsigned)T);
+  if (team >= d.n_teams) return;                     // grid padding: member of no team
+  const int groups = d.batch * d.h_kv;
+  const RegionDev &R = d.region;
+  for (int round = 0;; ++round) {
+    const int grp = team + round * d.n_teams;
+    if (grp >= groups) break;
+    const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
+    const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
+    const int c0 = member * d.chunk;
+    const int c1 = min(c0 + d.chunk, len);
+    mfma_chunk<KF, VF, PAGED, FULL, true>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
+    team_epilogue(d, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh, c0, c1);
+  }
 }
 
 template <int KF, int VF, bool PAGED>
@@ -458,6 +739,57 @@ static hipError_t launch_m(const DecodeLaunch &d, hipStream_t stream) {
   else
     launch_p<KF, VF, false>(d, stream, grid);
   return hipGetLastError();
+}
+
+template <int KF, int VF, bool PAGED, bool FULL>
+static const void *team_fn() {
+  return reinterpret_cast<const void *>(&decode_mfma_team_kernel<KF, VF, PAGED, FULL>);
+}
+
+template <int KF, int VF>
+static const void *team_fn_kv(bool paged, bool full) {
+  if (paged) return full ? team_fn<KF, VF, true, true>() : team_fn<KF, VF, true, false>();
+  return full ? team_fn<KF, VF, false, true>() : team_fn<KF, VF, false, false>();
+}
+
+static const void *team_kernel(int k_format, int v_format, bool paged, bool full) {
+  if (k_format == KVQ_FMT_FP8_E4M3) {
+    if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_FP8_E4M3>(paged, full);
+    if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16>(paged, full);
+    return team_fn_kv<KVQ_FMT_FP8_E4M3, VF_NONE>(paged, full);
+  }
+  if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_FP8_E4M3>(paged, full);
+  if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_BF16>(paged, full);
+  return team_fn_kv<KVQ_FMT_BF16, VF_NONE>(paged, full);
+}
+
+int team_capacity(int k_format, int v_format, bool paged, bool full) {
+  // resident work-groups of the team kernel with the largest LDS chunk;
+  // cached per device and kernel instance, 0 when the device cannot tell
+  static int cache[16][2][3][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  const int ki = k_format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
+  const int vi = v_format == KVQ_FMT_FP8_E4M3 ? 1 : (v_format == KVQ_FMT_BF16 ? 2 : 0);
+  int &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0];
+  if (c > 0) return c;
+  int coop = 0, cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, team_kernel(k_format, v_format, paged, full),
+                                                   256, (size_t)TEAM_MAX_CHUNK * 4 * sizeof(float2)) != hipSuccess)
+    return 0;
+  c = per_cu * cus;
+  return c;
+}
+
+hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream) {
+  const bool full = d.has_tv && d.has_meter && d.region.exact_fmt == EX_BF16 && d.region.witness;
+  const void *fn = team_kernel(d.k_format, d.v_format, d.region.paged != 0, full);
+  DecodeLaunch arg = d;
+  void *args[] = {&arg};
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(256), args,
+                                    (unsigned)((size_t)d.chunk * 4 * sizeof(float2)), stream);
 }
 
 bool mfma_path_supports(const DecodeLaunch &d) {

@@ -64,6 +64,9 @@ struct DecodeLaunch {
   uint32_t *counters;
   float *partials;
   float *spill;
+  int team;                     // > 0: team launch, work-groups per (request, KV head)
+  int n_teams;                  // teams in the grid
+  uint32_t epoch;               // team launch: tag of round r is epoch + r + 1
 };
 
 constexpr int PART_STRIDE = 136;  // m~, z~, m', z', m_e, z_e, 2 pad, acc[128]
@@ -73,5 +76,16 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 bool mfma_path_supports(const DecodeLaunch &d);
 hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
+
+// Team launch (matrix-core path, one region, TV requested): chunk <=
+// TEAM_MAX_CHUNK tokens per member, each kept in LDS; at most TEAM_MAX
+// members; TEAM_SLOT_BYTES of workspace per member and round parity.
+constexpr int TEAM_MAX_CHUNK = 2048;
+constexpr int TEAM_MAX = 64;
+constexpr size_t TEAM_SLOT_BYTES = 544 * 8;
+// Resident work-groups of the team kernel on the current device (0: no team
+// launch possible).
+int team_capacity(int k_format, int v_format, bool paged, bool full);
+hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream);
 
 }  // namespace kvq
