@@ -25,8 +25,9 @@
  *    and head); INT8 scales cover blocks of 256 tokens.
  *  - Tensor element layouts are row-major with the listed shapes; every base
  *    pointer must be 16-byte aligned.
- *  - Results are bitwise reproducible for a given shape: the split of the
- *    sequence and every reduction order depend only on the shapes.
+ *  - Results are bitwise reproducible for a given shape on a given device:
+ *    the split of the sequence and every reduction order depend only on the
+ *    shapes and on how many work-groups the device keeps resident.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -38,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -182,13 +183,38 @@ const char *kvq_status_string(kvq_status status);
 kvq_status kvq_quantize(const kvq_quant_args *args, kvq_stream stream);
 
 /* Bytes of device workspace kvq_decode_attn / kvq_meter need for these
- * arguments (host-only, no device access).  Returns 0 on invalid arguments. */
+ * arguments.  Host-only: reads the current device's properties, never its
+ * memory.  The decode and the meter call on the same arguments need the same
+ * size.  Returns 0 on invalid arguments. */
 size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter);
+
+/* How kvq_decode_attn (meter_only = 0) or kvq_meter (meter_only != 0) will
+ * run for these arguments on the current device (host-only, as above).
+ *  - team > 0: one cooperative launch; `team` work-groups share each
+ *    (request, KV head), each keeping its chunk's logit pairs in LDS for the
+ *    TV (WitCert Sec. 3 target), `n_teams` teams take the (request, KV head)
+ *    pairs in `rounds` rounds.  Chosen when the TV is requested for a single
+ *    region with GQA group 4, FP8/BF16 keys and values and bf16 exact keys,
+ *    and split_tokens is 0.
+ *  - team == 0: one launch per region over `chunks` chunks of each (request,
+ *    KV head); the TV's logit pairs go through the workspace. */
+typedef struct kvq_plan_info {
+  int32_t team;             /* work-groups per (request, KV head); 0: no team launch */
+  int32_t n_teams;
+  int32_t rounds;
+  int32_t grid;             /* work-groups of the team launch */
+  int32_t chunk;            /* tokens per chunk */
+  int32_t chunks;           /* chunks per (request, KV head), both regions */
+  uint64_t workspace_bytes;
+} kvq_plan_info;
+kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter, int meter_only,
+                           kvq_plan_info *info);
 
 /* Prepare a workspace for first use: clears the arrival counters at its start.
  * A workspace stays ready after every successful kvq_decode_attn / kvq_meter
- * call (the last work-group of each (request, KV head) resets its counter).
- * Calls that share a workspace must not overlap in time. */
+ * call (the last work-group of each (request, KV head) resets its counter;
+ * team launches tag their words with a per-launch epoch instead).  Calls that
+ * share a workspace must not overlap in time. */
 kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, kvq_stream stream);
 
 /* Decode attention with the fused meter (WitCert Sec. 6 meter loop, read path;

@@ -352,6 +352,22 @@ size_t kvq_workspace_bytes(const kvq_attn_args *a, const kvq_meter_out *m) {
   return p.bytes;
 }
 
+kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int meter_only,
+                           kvq_plan_info *info) {
+  if (!info) return KVQ_ERR_NULL;
+  Plan p;
+  const kvq_status s = make_plan(a, m, meter_only != 0, p);
+  if (s != KVQ_OK) return s;
+  info->team = p.team;
+  info->n_teams = p.n_teams;
+  info->rounds = p.rounds;
+  info->grid = p.grid;
+  info->chunk = p.chunk;
+  info->chunks = p.total_chunks;
+  info->workspace_bytes = p.bytes;
+  return KVQ_OK;
+}
+
 kvq_status kvq_workspace_init(void *ws, size_t bytes, kvq_stream stream) {
   if (!ws) return KVQ_ERR_NULL;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;

@@ -67,7 +67,13 @@ class QuantArgs(ctypes.Structure):
 _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
-           "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
+           "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
+ABI_VERSION = 2
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("team", c_int32), ("n_teams", c_int32), ("rounds", c_int32), ("grid", c_int32),
+                ("chunk", c_int32), ("chunks", c_int32), ("workspace_bytes", ctypes.c_uint64)]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -79,12 +85,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"libkvq.so not built at {path}; run quantized_kv_cache_gqa_amd.build")
     lib = ctypes.CDLL(path)
     lib.kvq_abi_version.restype = ctypes.c_int
+    if lib.kvq_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path}: ABI version {lib.kvq_abi_version()}, this binding is {ABI_VERSION}")
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_quantize.restype = ctypes.c_int
     lib.kvq_quantize.argtypes = [ctypes.POINTER(QuantArgs), c_void_p]
     lib.kvq_workspace_bytes.restype = ctypes.c_size_t
     lib.kvq_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut)]
+    lib.kvq_decode_plan.restype = ctypes.c_int
+    lib.kvq_decode_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut), ctypes.c_int,
+                                    ctypes.POINTER(PlanInfo)]
     lib.kvq_workspace_init.restype = ctypes.c_int
     lib.kvq_workspace_init.argtypes = [c_void_p, ctypes.c_size_t, c_void_p]
     for name in ("kvq_decode_attn", "kvq_meter"):
@@ -230,6 +241,21 @@ class Workspace:
             _check(load().kvq_workspace_init(self.buf.data_ptr(), self.buf.numel(), _stream(stream)),
                    "kvq_workspace_init")
         return self.buf
+
+
+def plan(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
+         suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
+         meter: bool = True, meter_only: bool = False) -> dict:
+    """kvq_decode_plan for the arguments decode_attn would pass (host only;
+    the output and meter pointers only need to be non-NULL and aligned)."""
+    dummy = _ptr(q) if meter else None
+    m = MeterOut(**({k: dummy for k in ("tv", "bound_raw", "meter", "log_a")} if meter else {}))
+    args = _attn_args(q, prefix, suffix, None if meter_only else q, sm_scale, split_tokens,
+                      num_kv_heads, need_v=not meter_only)
+    info = PlanInfo()
+    _check(load().kvq_decode_plan(ctypes.byref(args), ctypes.byref(m), int(meter_only), ctypes.byref(info)),
+           "kvq_decode_plan")
+    return {name: int(getattr(info, name)) for name, _ in PlanInfo._fields_}
 
 
 def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],

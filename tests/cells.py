@@ -112,6 +112,11 @@ class GpuCase:
         return out, m
 
 
+def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False) -> dict:
+    return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
+                         sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only)
+
+
 def oracle_cell(case: GpuCase, b: int, kvh: int):
     """The oracle's view of cell (b, kvh): encoded regions and the decode result."""
     cfg, inp, layer = case.cfg, case.inp, case.layer

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == 1
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 2
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -53,7 +53,8 @@ def test_ctypes_structs_match_the_c_layout(tmp_path):
     if gcc is None:
         pytest.skip("gcc not available")
     structs = {"kvq_region": kvq.Region, "kvq_attn_args": kvq.AttnArgs,
-               "kvq_meter_out": kvq.MeterOut, "kvq_quant_args": kvq.QuantArgs}
+               "kvq_meter_out": kvq.MeterOut, "kvq_quant_args": kvq.QuantArgs,
+               "kvq_plan_info": kvq.PlanInfo}
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){"]
     for cname, cls in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -89,7 +90,16 @@ def _args(batch=64, hq=32, hkv=8, prefix=0, suffix=12628, split=0, **kw):
                         suffix=_region(suffix, **kw), out=FAKE)
 
 
-def test_workspace_plan_of_the_batch64_step(lib):
+def _plan(lib, a, m, meter_only=0):
+    info = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), meter_only, ctypes.byref(info)) == 0
+    return info
+
+
+def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
+    """The per-chunk plan (team launches off, as on a host without a device):
+    one chunk per (request, KV head), partials and the TV's spill rows."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
     a = _args()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
@@ -98,9 +108,24 @@ def test_workspace_plan_of_the_batch64_step(lib):
     partials = groups * chunks * G * 136 * 4
     spill = groups * 12640 * G * 8                # 12628 tokens padded to 16-token tiles
     assert n == counters + partials + spill
+    info = _plan(lib, a, m)
+    assert (info.team, info.chunk, info.chunks, info.workspace_bytes) == (0, 12672, 1, n)
     # without TV: no spill
     m2 = kvq.MeterOut(tv=None, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     assert lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m2)) == counters + partials
+
+
+def test_plan_query_matches_workspace_bytes(lib):
+    """kvq_decode_plan reports the size kvq_workspace_bytes returns, for the
+    decode and the meter call alike; without a device there is no team plan."""
+    a = _args()
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
+    d, mo = _plan(lib, a, m, 0), _plan(lib, a, m, 1)
+    assert d.workspace_bytes == mo.workspace_bytes == n
+    if not torch.cuda.is_available():
+        assert d.team == 0
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, None) == 1
 
 
 @pytest.mark.parametrize("mutate,status", [

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from cells import GpuCase, SM_SCALE, check_results, check_stored, oracle_cell
+from cells import GpuCase, SM_SCALE, check_results, check_stored, oracle_cell, plan
 from oracle.numerics import e4m3_table
 from workloads import CONFIGS, small_variant
 
@@ -110,13 +110,16 @@ SMALL = {
 }
 
 
-@pytest.fixture(params=["auto", "generic"])
+@pytest.fixture(params=["auto", "generic", "noteam"])
 def kernel(request, monkeypatch):
-    """Run a test with the library's kernel choice and with the vector-ALU kernel."""
+    """Run a test with the library's kernel choice, with the vector-ALU kernel,
+    and with team launches off (TV spill in the workspace)."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     if request.param == "generic":
         monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
-    else:
-        monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    elif request.param == "noteam":
+        monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
     return request.param
 
 
@@ -190,3 +193,61 @@ def test_bound_dominates_tv_every_cell(gpu_lib):
         assert torch.all(tv >= 0) and torch.all(tv <= 1)
         assert torch.all(tv <= bound + 1e-6), (idx, float((tv - bound).max()))
         assert torch.all(m["meter"] == torch.clamp(bound, max=1.0))
+
+
+def _team_plan(case, monkeypatch):
+    """The plan the library reports with team launches allowed, checked against
+    what a team launch must satisfy, and the spill plan it replaces."""
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    p = plan(case)
+    cfg = case.cfg
+    groups = cfg.batch * cfg.h_kv
+    assert p["team"] > 0, p
+    assert p["chunk"] % 64 == 0 and p["chunk"] * p["team"] >= cfg.suffix.length, p
+    assert p["chunk"] <= 2048 and p["team"] <= 64, p
+    assert p["n_teams"] * p["rounds"] >= groups > p["n_teams"] * (p["rounds"] - 1), p
+    assert p["grid"] % 8 == 0 and p["grid"] >= p["team"] * p["n_teams"], p
+    assert plan(case, meter_only=True) == p          # one workspace fits both calls
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    assert plan(case)["team"] == 0
+    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    return p
+
+
+def test_team_many_members_and_empty_chunks(gpu_lib, monkeypatch):
+    """Four groups, requests of 5000 and 1500 tokens in a 5000-token region:
+    tens of members of 64+ tokens each, those past the short request's end
+    with empty chunks; parity on every cell and agreement with the
+    spill-to-workspace path."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    cfg = small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=5000, lens=(5000, 1500))
+    case = GpuCase(cfg)
+    p = _team_plan(case, monkeypatch)
+    assert p["team"] >= 16 and p["chunk"] * (p["team"] - 1) >= 1500, p   # members with no tokens
+    out_t, m_t, _ = _all_cells(case)
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    out_s, m_s = case.run()
+    # the two paths round the fp16 P.V weights against different running
+    # maxima: compare per head as the oracle bar does (norm-relative)
+    rel = (out_t - out_s).double().norm(dim=-1) / out_s.double().norm(dim=-1).clamp_min(1e-30)
+    assert float(rel.max()) <= 2e-3, float(rel.max())
+    for k in ("tv", "bound_raw", "meter", "log_a"):
+        assert torch.allclose(m_t[k], m_s[k], rtol=1e-5, atol=1e-6), k
+
+
+def test_team_several_rounds_sampled_cells(gpu_lib, monkeypatch):
+    """640 groups of ragged 3000-token requests: more groups than resident
+    teams, so every team runs several rounds (tags of successive rounds, slot
+    parity reuse); sampled cells against the oracle, bitwise repeatable."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    lens = tuple(3000 - 37 * i for i in range(80))
+    cfg = small_variant(CONFIGS[3], batch=80, h_kv=8, suffix_len=3000, lens=lens)
+    case = GpuCase(cfg)
+    p = _team_plan(case, monkeypatch)
+    assert p["rounds"] >= 3, p
+    cells = [(0, 0), (1, 7), (33, 4), (64, 2), (79, 7), (79, 0)]
+    o1, m1, _ = _all_cells(case, cells=cells)
+    o2, m2 = case.run()
+    assert torch.equal(o1, o2)
+    for k in m1:
+        assert torch.equal(m1[k], m2[k]), k
