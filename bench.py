@@ -24,6 +24,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_fp8_b64_s12628_hbm_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the ABI header (sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_gqa_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".h", ".cpp")))
+    for path in files + [os.path.join(ROOT, "include", "kvq.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the summary is missing or was taken on other kernel sources."""
+    try:
+        fields = dict(line.split(":", 1) for line in open(TRAFFIC_PROFILE)
+                      if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256", "").strip() != kernel_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -162,6 +190,12 @@ def main():
         aargs.append(kvq.AttnArgs(batch=B, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D,
                                   sm_scale=sm_scale, split_tokens=0, q=Ld["q"].data_ptr(),
                                   prefix=kvq.Region(), suffix=Ld["view"].to_c(), out=out.data_ptr()))
+    info = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(aargs[0]), ctypes.byref(meter), 0, ctypes.byref(info)) == 0
+    kernel_name = (f"decode_mfma_team_kernel<FP8, FP8, dense, full> (team {info.team}, "
+                   f"{info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk})"
+                   if info.team else f"decode_mfma_kernel<FP8, FP8, dense, full> ({info.chunks} chunk(s))")
+    log(f"plan: {kernel_name}")
     ws_bytes = lib.kvq_workspace_bytes(ctypes.byref(aargs[0]), ctypes.byref(meter))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     assert lib.kvq_workspace_init(ws.data_ptr(), ws_bytes, sp) == 0
@@ -243,8 +277,8 @@ def main():
                    "global_batch": B, "seq_len": S, "layers": L,
                    "step_gbs_algorithmic": step_bytes / (ms_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "decode_kernel<4, FP8, FP8> (one launch per layer)",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(),
+                     "kernel": kernel_name + ", one launch per layer",
                      "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_launch},
         "cpu_baseline": None,
     }
