@@ -194,8 +194,9 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    (request, KV head), each keeping its chunk's logit pairs in LDS for the
  *    TV (WitCert Sec. 3 target), `n_teams` teams take the (request, KV head)
  *    pairs in `rounds` rounds.  Chosen when the TV is requested for a single
- *    region with GQA group 4, FP8/BF16 keys and values and bf16 exact keys,
- *    and split_tokens is 0.
+ *    region of at most 131,072 tokens with GQA group 4, FP8/BF16 keys and
+ *    values and bf16 exact keys, split_tokens is 0, and the device supports
+ *    cooperative launches.
  *  - team == 0: one launch per region over `chunks` chunks of each (request,
  *    KV head); the TV's logit pairs go through the workspace. */
 typedef struct kvq_plan_info {
