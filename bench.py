@@ -28,13 +28,12 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_fp8_b64_s12628_hbm_traf
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the ABI header (sorted by name)."""
+    """sha256 over the device sources (.hip and their headers, sorted by name)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "quantized_kv_cache_gqa_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
-                   if f.endswith((".hip", ".h", ".cpp")))
-    for path in files + [os.path.join(ROOT, "include", "kvq.h")]:
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for path in files:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
