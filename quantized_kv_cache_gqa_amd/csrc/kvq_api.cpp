@@ -52,8 +52,8 @@ bool env_is(const char *name, char c) {
 }
 
 // Team plan for a one-region launch with the TV on the matrix-core path:
-// T members per (request, KV head), chunks of <= TEAM_MAX_CHUNK tokens (a
-// multiple of 64), persistent teams over the groups.  Picks the T with the
+// T members per (request, KV head), chunks of <= TEAM_MAX_CHUNK tokens (whole
+// 16-token tiles), persistent teams over the groups.  Picks the T with the
 // least work per member over all rounds (a round's fixed cost is counted as
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
@@ -82,7 +82,7 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
     const int64_t n_teams = std::min<int64_t>(cap / T, groups);
     if (n_teams <= 0) break;
     const int64_t rounds = (groups + n_teams - 1) / n_teams;
-    const int64_t chunk = ((len + T - 1) / T + 63) / 64 * 64;
+    const int64_t chunk = ((len + T - 1) / T + 15) / 16 * 16;      // whole tiles
     const int64_t cost = rounds * (chunk + 256);
     if (best_cost < 0 || cost < best_cost) {
       best_cost = cost;

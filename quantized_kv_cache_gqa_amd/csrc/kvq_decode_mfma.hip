@@ -99,6 +99,98 @@ struct TileRegs {
   float ks, vs;    // scales of this lane's compact (token, head) slot
 };
 
+// Addressing of one (request, KV head) region range ending at c1, and the
+// loads of one 16-token tile.  Dense regions: one uniform base per tensor and
+// 32-bit per-lane row offsets (a request holds < 2^24 tokens); paged suffix:
+// per-token page lookup with 64-bit rows.  Rows are clamped to the last valid
+// token, so a tile past the end re-reads a valid row (its data is unused).
+template <int KF, int VF, bool PAGED>
+struct TileSrc {
+  using RowT = typename std::conditional<PAGED, size_t, uint32_t>::type;
+  const uint8_t *kb, *keb, *vbb;
+  const uint16_t *wb;
+  const float *ksb, *vsb;
+  const int32_t *ptab;
+  int pshift, page_size, h_kv, kvh, last;
+
+  __device__ __forceinline__ TileSrc(const DecodeLaunch &d, int b, int kvh_, int c1) {
+    const RegionDev &R = d.region;
+    const size_t sh = R.is_prefix ? (size_t)kvh_ : (size_t)b * d.h_kv + kvh_;
+    const size_t row0 = PAGED ? 0 : sh * (size_t)R.length;
+    ptab = PAGED ? R.page_table + (size_t)b * R.max_pages : nullptr;
+    pshift = R.page_size == 16 ? 4 : 3;      // page sizes 8 or 16
+    page_size = R.page_size;
+    h_kv = d.h_kv;
+    kvh = kvh_;
+    last = c1 - 1;
+    kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
+    keb = (const uint8_t *)R.k_exact + row0 * (2 * D);
+    wb = R.witness + row0 * NB;
+    ksb = (const float *)R.k_scale + row0;
+    vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
+    vsb = (const float *)R.v_scale + row0;
+  }
+
+  __device__ __forceinline__ RowT row_of(int t) const {   // row index relative to row0
+    t = min(t, last);
+    if constexpr (PAGED) {
+      const size_t pg = (size_t)ptab[t >> pshift];
+      return (pg * h_kv + kvh) * page_size + (t & (page_size - 1));
+    } else {
+      return (RowT)t;
+    }
+  }
+
+  __device__ __forceinline__ void load(TileRegs &T, int t0, bool exact, bool wit) const {
+    load_keys(T, t0, exact);
+    load_rest(T, t0, wit);
+  }
+
+  // stored and exact keys with the key scale (what the logits need first)
+  __device__ __forceinline__ void load_keys(TileRegs &T, int t0, bool exact) const {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
+    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
+    if constexpr (KF == KVQ_FMT_FP8_E4M3) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * D + 32 * g);
+      T.k[0] = p[0];
+      T.k[1] = p[1];
+      T.ks = ksb[rk];
+    } else {
+      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.k[i] = p[i];
+      T.ks = 1.0f;
+    }
+    if (exact) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(keb + ra * (2 * D) + 64 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.ke[i] = p[i];
+    }
+  }
+
+  // witness, values and the value scale
+  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit) const {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
+    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
+    if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
+    if constexpr (VF == KVQ_FMT_FP8_E4M3) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + row_of(t0 + 4 * g + e) * D + 8 * j16);
+      T.vs = vsb[rk];
+    } else if constexpr (VF == KVQ_FMT_BF16) {
+      const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
+      const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
+      const uint4 *p1 = reinterpret_cast<const uint4 *>(vbb + r1 * (2 * D) + 32 * (lane & 7));
+      T.vb[0] = p0[0]; T.vb[1] = p0[1];
+      T.vb[2] = p1[0]; T.vb[3] = p1[1];
+      T.vs = 1.0f;
+    }
+  }
+};
+
 // One (request, KV head) chunk [c0, c1) of one region, run by the whole
 // work-group (4 wavefronts, tiles of 16 tokens dealt round-robin): leaves each
 // wavefront's softmax states and output accumulator in part_s[wv].  The
@@ -158,66 +250,9 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
   }
 
-  // ---- region addressing.  Dense regions: one uniform base per tensor and
-  // 32-bit per-lane row offsets (rows are clamped to the last valid token).
-  // Paged suffix: per-token page lookup.
-  const size_t sh = R.is_prefix ? (size_t)kvh : (size_t)b * d.h_kv + kvh;
-  const size_t row0 = PAGED ? 0 : sh * (size_t)R.length;
-  const int32_t *ptab = PAGED ? R.page_table + (size_t)b * R.max_pages : nullptr;
-  const int pshift = R.page_size == 16 ? 4 : 3;      // page sizes 8 or 16
-  const int last = c1 - 1;
-  // dense rows fit 32 bits (a request holds < 2^24 tokens); paged rows use 64
-  using RowT = typename std::conditional<PAGED, size_t, uint32_t>::type;
-  auto row_of = [&](int t) -> RowT {                 // row index relative to row0
-    t = min(t, last);
-    if constexpr (PAGED) {
-      const size_t pg = (size_t)ptab[t >> pshift];
-      return (pg * d.h_kv + kvh) * R.page_size + (t & (R.page_size - 1));
-    } else {
-      return (RowT)t;
-    }
-  };
-  const uint8_t *kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
-  const uint8_t *keb = (const uint8_t *)R.k_exact + row0 * (2 * D);
-  const uint16_t *wb = R.witness + row0 * NB;
-  const float *ksb = (const float *)R.k_scale + row0;
-  const uint8_t *vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
-  const float *vsb = (const float *)R.v_scale + row0;
+  const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
   float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
-
-  auto load_tile = [&](TileRegs &T, int t0) {
-    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
-    if constexpr (KF == KVQ_FMT_FP8_E4M3) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * D + 32 * g);
-      T.k[0] = p[0];
-      T.k[1] = p[1];
-      T.ks = ksb[rk];
-    } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.k[i] = p[i];
-      T.ks = 1.0f;
-    }
-    if (do_tv && has_exact) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(keb + ra * (2 * D) + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.ke[i] = p[i];
-    }
-    if (do_meter && has_wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
-    if constexpr (VF == KVQ_FMT_FP8_E4M3) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + row_of(t0 + 4 * g + e) * D + 8 * j16);
-      T.vs = vsb[rk];
-    } else if constexpr (VF == KVQ_FMT_BF16) {
-      const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
-      const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
-      const uint4 *p1 = reinterpret_cast<const uint4 *>(vbb + r1 * (2 * D) + 32 * (lane & 7));
-      T.vb[0] = p0[0]; T.vb[1] = p0[1];
-      T.vb[2] = p1[0]; T.vb[3] = p1[1];
-      T.vs = 1.0f;
-    }
-  };
+  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit); };
 
   // per-lane accumulator states (lane = one (token slot, head) pair)
   float mq = NEG_INF, zq = 0.0f;     // attention softmax, maximum uniform per head
@@ -566,7 +601,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
 
   // 2. the group's normalizers: wavefront h reads head h of every member
   //    (lane c = member c), then a butterfly merge gives every lane the same
-  const int h = wv;
+  const int h = __builtin_amdgcn_readfirstlane(wv);   // uniform: scalar slot bases
   bool ok = true;
   float Mq = NEG_INF, Zq = 0.0f, Mm = NEG_INF, Zm = 0.0f, Me = NEG_INF, Ze = 0.0f;
   if (lane < T) {
@@ -594,63 +629,65 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   }
   __syncthreads();
 
-  // 3. member h % T: head h's output (member order), log A, bound, meter, and
-  //    the previous round's TV
+  // 3. duties, spread so that no member is always the last one out:
+  //    - output: 8 units of 64 dims (head u / 2, half u % 2); unit u is
+  //      taken by member u % T, wavefront (u / T) % 4, summing the members'
+  //      accumulators in member order;
+  //    - log A, bound, meter of head h: member h % T (no loads);
+  //    - the previous round's TV of head h: member (h + 4) % T, wavefront h.
   const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
-  if (member == h % T) {
-    if (d.has_out) {
-      float o0 = 0.0f, o1 = 0.0f;
-      for (int c0m = 0; c0m < T; c0m += 4) {
+  if (d.has_out) {
+    for (int u = 0; u < 8; ++u) {
+      if (u % T != member || (u / T) % 4 != h) continue;
+      const int hu = u >> 1, dim = 64 * (u & 1) + lane;
+      const float Mu = fin_s[hu][0];
+      const float iZu = fin_s[hu][1];
+      float o = 0.0f;
+      bool oku = true;
+      for (int cb = 0; cb < T; cb += 8) {
         const uint64_t *p[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = min(c0m + i, T - 1);
-          const uint64_t *s = slots + (size_t)c * SLOT_WORDS + SLOT_ACC + 128 * h;
-          p[2 * i] = s + lane;
-          p[2 * i + 1] = s + 64 + lane;
-        }
+        for (int i = 0; i < 8; ++i)
+          p[i] = slots + (size_t)min(cb + i, T - 1) * SLOT_WORDS + SLOT_ACC + 128 * hu + dim;
         float v[8];
-        ok = read_tagged<8>(p, tag, v) && ok;
+        oku = read_tagged<8>(p, tag, v) && oku;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (c0m + i >= T) break;
-          const float fq = merge_factor(mq_s[h][c0m + i], Mq);
-          o0 += v[2 * i] * fq;
-          o1 += v[2 * i + 1] * fq;
-        }
+        for (int i = 0; i < 8; ++i)
+          if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
       }
-      const float inv = Zq > 0.0f ? 1.0f / Zq : 0.0f;
-      d.out[qh * D + lane] = ok ? o0 * inv : qnan;
-      d.out[qh * D + 64 + lane] = ok ? o1 * inv : qnan;
+      const size_t qu = (size_t)b * d.h_q + (size_t)kvh * G + hu;
+      d.out[qu * D + dim] = oku ? o * iZu : qnan;
+      ok = ok && oku;
     }
-    if (lane == 0) {
-      double log_a = 0.0;
-      if (do_meter && Zq > 0.0f && Zm > 0.0f)
-        log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
-      const double bound = 0.5 * expm1(2.0 * log_a);
-      const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
-      if (d.log_a) d.log_a[qh] = ok ? (float)log_a : qnan;
-      if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
-      if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
+  }
+  if (member == h % T && lane == 0) {
+    double log_a = 0.0;
+    if (do_meter && Zq > 0.0f && Zm > 0.0f)
+      log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
+    const double bound = 0.5 * expm1(2.0 * log_a);
+    const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
+    if (d.log_a) d.log_a[qh] = ok ? (float)log_a : qnan;
+    if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
+    if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
+  }
+  const bool tv_duty = do_tv && d.tv && member == (h + 4) % T;
+  if (tv_duty && round > 0) {
+    // shares of round - 1 sit in the other parity's slots
+    const uint64_t *prev = reinterpret_cast<const uint64_t *>(d.partials) +
+                           (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS;
+    float sh = 0.0f;
+    bool okp = true;
+    if (lane < T) {
+      const uint64_t *const p[1] = {prev + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
+      float v[1];
+      okp = read_tagged<1>(p, tag - 1u, v);
+      sh = v[0];
     }
-    if (do_tv && d.tv && round > 0) {
-      // shares of round - 1 sit in the other parity's slots
-      const uint64_t *prev = reinterpret_cast<const uint64_t *>(d.partials) +
-                             (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS;
-      float sh = 0.0f;
-      bool okp = true;
-      if (lane < T) {
-        const uint64_t *const p[1] = {prev + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
-        float v[1];
-        okp = read_tagged<1>(p, tag - 1u, v);
-        sh = v[0];
-      }
-      sh = wave_sum_fixed(sh);
-      okp = __all(okp);
-      const int pg = team + (round - 1) * d.n_teams;
-      const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
-      if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * G + h] = okp ? 0.5f * sh : qnan;
-    }
+    sh = wave_sum_fixed(sh);
+    okp = __all(okp);
+    const int pg = team + (round - 1) * d.n_teams;
+    const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
+    if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * G + h] = okp ? 0.5f * sh : qnan;
   }
   if (!ok) bad_s = 1;
 
@@ -680,8 +717,8 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     st_tagged(mine + SLOT_TV + tid, tag, share);
   }
 
-  // 5. last round: member h % T also sums this round's shares
-  if (last_round && do_tv && d.tv && member == h % T) {
+  // 5. last round: member (h + 4) % T also sums this round's shares
+  if (last_round && tv_duty) {
     float sh = 0.0f;
     bool okp = true;
     if (lane < T) {
@@ -716,6 +753,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
     const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
     const int c0 = member * d.chunk;
     const int c1 = min(c0 + d.chunk, len);
+    // (the next round's first tile is not loaded ahead: its loads would sit
+    // ahead of the exchange's polls in the in-order load counter)
     mfma_chunk<KF, VF, PAGED, FULL, true>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
     team_epilogue(d, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh, c0, c1);
   }

@@ -203,7 +203,7 @@ def _team_plan(case, monkeypatch):
     cfg = case.cfg
     groups = cfg.batch * cfg.h_kv
     assert p["team"] > 0, p
-    assert p["chunk"] % 64 == 0 and p["chunk"] * p["team"] >= cfg.suffix.length, p
+    assert p["chunk"] % 16 == 0 and p["chunk"] * p["team"] >= cfg.suffix.length, p
     assert p["chunk"] <= 2048 and p["team"] <= 64, p
     assert p["n_teams"] * p["rounds"] >= groups > p["n_teams"] * (p["rounds"] - 1), p
     assert p["grid"] % 8 == 0 and p["grid"] >= p["team"] * p["n_teams"], p
