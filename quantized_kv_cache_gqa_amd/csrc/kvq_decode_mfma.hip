@@ -552,11 +552,11 @@ __device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2)
   m = mx;
 }
 
-// Sum of the members' TV shares of head h (lanes c < T hold member c's share),
-// butterfly over the wavefront: the same bits in every lane.
-__device__ __forceinline__ float wave_sum_fixed(float x) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+// Sum of the members' TV shares of head h (lanes c < n hold member c's
+// share, the others 0): butterfly over the lowest ceil(log2 n) lane bits, so
+// lane 0 holds the sum in a fixed order.
+__device__ __forceinline__ float wave_sum_fixed(float x, int n) {
+  for (int off = 1; off < n; off <<= 1) x += __shfl_xor(x, off);
   return x;
 }
 
@@ -600,7 +600,8 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   }
 
   // 2. the group's normalizers: wavefront h reads head h of every member
-  //    (lane c = member c), then a butterfly merge gives every lane the same
+  //    (lane c = member c), then a butterfly merge over the lowest
+  //    ceil(log2 T) lane bits leaves the group's states in lane 0
   const int h = __builtin_amdgcn_readfirstlane(wv);   // uniform: scalar slot bases
   bool ok = true;
   float Mq = NEG_INF, Zq = 0.0f, Mm = NEG_INF, Zm = 0.0f, Me = NEG_INF, Ze = 0.0f;
@@ -612,8 +613,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     Mq = v[0]; Zq = v[1]; Mm = v[2]; Zm = v[3]; Me = v[4]; Ze = v[5];
   }
   mq_s[h][lane] = Mq;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
+  for (int off = 1; off < T; off <<= 1) {           // lanes >= T hold empty states
     const float a0 = __shfl_xor(Mq, off), a1 = __shfl_xor(Zq, off);
     const float b0 = __shfl_xor(Mm, off), b1 = __shfl_xor(Zm, off);
     const float e0 = __shfl_xor(Me, off), e1 = __shfl_xor(Ze, off);
@@ -683,7 +683,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
       okp = read_tagged<1>(p, tag - 1u, v);
       sh = v[0];
     }
-    sh = wave_sum_fixed(sh);
+    sh = wave_sum_fixed(sh, T);
     okp = __all(okp);
     const int pg = team + (round - 1) * d.n_teams;
     const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
@@ -727,7 +727,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
       okp = read_tagged<1>(p, tag, v);
       sh = v[0];
     }
-    sh = wave_sum_fixed(sh);
+    sh = wave_sum_fixed(sh, T);
     okp = __all(okp) && bad_s == 0;
     if (lane == 0) d.tv[qh] = okp ? 0.5f * sh : qnan;
   }
