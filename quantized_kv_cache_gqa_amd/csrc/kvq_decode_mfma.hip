@@ -691,26 +691,38 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   }
   if (!ok) bad_s = 1;
 
-  // 4. this chunk's TV share: thread tid reads entries tid + 256 k, all of
-  //    head (tid % 16) / 4; butterfly over the lanes of a head, then waves
-  //    in order
+  // 4. this chunk's TV share: thread tid reads entry pairs (2p, 2p + 1), p =
+  //    tid + 256 k, as one float4 (both of head (tid % 8) / 2), into four
+  //    independent partial sums; then a butterfly over the lanes of a head
+  //    (bits 0, 3, 4, 5) and the wavefronts in order
   float acc_tv = 0.0f;
   if (do_tv && c1 > c0) {
-    const int hm = (lane & 15) >> 2;
+    const int hm = (lane & 6) >> 1;
     const float Mt = fin_s[hm][0], iZt = fin_s[hm][1];
     const float Mx = fin_s[hm][2], iZe = fin_s[hm][3];
-    const int n_entries = round16(c1 - c0) * G;
-    for (int e = tid; e < n_entries; e += 256) {
-      const float2 x = spill_s[e];
-      const int t = c0 + 16 * (e >> 6) + 4 * ((e & 63) >> 4) + (e & 3);
-      if (t < c1) tvp_add(acc_tv, x.x, x.y, Mt, iZt, Mx, iZe);
+    const int n_pairs = round16(c1 - c0) * G / 2;
+    const float4 *sp4 = reinterpret_cast<const float4 *>(spill_s);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = tid; p0 < n_pairs; p0 += 4 * 256) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + 256 * u;
+        if (p < n_pairs) {
+          const float4 x = sp4[p];
+          const int e = 2 * p;
+          const int t = c0 + 16 * (e >> 6) + 4 * ((e & 63) >> 4) + (e & 3);
+          if (t < c1) tvp_add(a[u], x.x, x.y, Mt, iZt, Mx, iZe);
+          if (t + 1 < c1) tvp_add(a[u], x.z, x.w, Mt, iZt, Mx, iZe);
+        }
+      }
     }
+    acc_tv = (a[0] + a[1]) + (a[2] + a[3]);
   }
   acc_tv += __shfl_xor(acc_tv, 1);
-  acc_tv += __shfl_xor(acc_tv, 2);
+  acc_tv += __shfl_xor(acc_tv, 8);
   acc_tv += __shfl_xor(acc_tv, 16);
   acc_tv += __shfl_xor(acc_tv, 32);
-  if (lane < 16 && (lane & 3) == 0) tvw_s[wv][lane >> 2] = acc_tv;
+  if (lane < 8 && (lane & 1) == 0) tvw_s[wv][lane >> 1] = acc_tv;   // lanes 0, 2, 4, 6: heads 0..3
   __syncthreads();
   if (tid < G) {
     const float share = ((tvw_s[0][tid] + tvw_s[1][tid]) + tvw_s[2][tid]) + tvw_s[3][tid];
