@@ -53,9 +53,29 @@ def measured_traffic():
     return float(fields["traffic_bytes_per_launch"])
 
 
+def token_head_bytes(k_fmt, v_fmt, exact_k, witness, with_v=True):
+    """Algorithmic bytes the read path moves per cached token of one KV head:
+    key and value codes, their scales (FP8: fp32 per token; INT8: fp16 per
+    256-token block and channel, amortized), the witness (16 fp16 bands) and
+    the bf16 exact key the exact TV needs."""
+    code = {"bf16": 256, "fp8": 128, "int8": 128}
+    scale = {"bf16": 0, "fp8": 4, "int8": 1}
+    n = code[k_fmt] + scale[k_fmt]
+    if with_v:
+        n += code[v_fmt] + scale[v_fmt]
+    if witness:
+        n += 32
+    if exact_k:
+        n += 256
+    return n
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="3: the decode step (default); 1, 2, 4, 5: time one layer's decode launch of "
+                         "that workload against its roofline (a measurement aid, not the bench line)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
@@ -137,17 +157,109 @@ def _oracle_slice(lb):
     return time.perf_counter() - t
 
 
+def measure_workload(idx: int, reps: int, warmup: int):
+    """One layer of workload `idx`: stage its caches through kvq_quantize, then
+    time kvq_decode_attn (with TV, log A, bound and meter where the workload
+    has exact keys and a witness) with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    from quantized_kv_cache_gqa_amd import kvq
+    from workloads import CONFIGS, gen_layer
+    cfg = CONFIGS[idx]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = kvq.load()
+    layer = 0
+    inp = gen_layer(cfg, layer, dev)
+    seed = 0x5EED0000 + idx
+    B, HQ, HKV = cfg.batch, cfg.h_q, cfg.h_kv
+    prefix = None
+    bytes_launch = 0
+    if cfg.prefix is not None and cfg.prefix.length > 0:
+        pr = cfg.prefix
+        st = kvq.alloc_stored(1, HKV, pr.length, pr.k_fmt, pr.v_fmt, pr.witness, dev)
+        kvq.quantize_into(st, inp["prefix_k"][None].contiguous(), inp["prefix_v"][None].contiguous(),
+                          seed=seed, layer=layer, stream_id=1_000_000)
+        prefix = kvq.RegionView(st, pr.length, k_exact=inp["prefix_k"] if pr.exact_k else None, seed=seed,
+                                layer=layer, stream_id=1_000_000, use_witness=pr.witness)
+        # the shared prefix counts once per launch (every request reads the same rows)
+        bytes_launch += HKV * pr.length * token_head_bytes(pr.k_fmt, pr.v_fmt, pr.exact_k, pr.witness)
+    sf = cfg.suffix
+    st = kvq.alloc_stored(B, HKV, sf.length, sf.k_fmt, sf.v_fmt, sf.witness, dev)
+    kvq.quantize_into(st, inp["suffix_k"], inp["suffix_v"], seed=seed, layer=layer, stream_id=0)
+    lens = inp["suffix_lens"]
+    exact = inp["suffix_k"] if sf.exact_k else None
+    if sf.paged:
+        ps, mp = sf.page_size, sf.length // sf.page_size
+        perm = torch.from_numpy(np.random.default_rng(7).permutation(B * mp).astype(np.int32)).to(dev)
+        table = perm.view(B, mp)
+
+        def scatter(t):
+            if t is None:
+                return None
+            rest = t.shape[3:]
+            src = t.view(B, HKV, mp, ps, *rest).permute(0, 2, 1, 3, *range(4, 4 + len(rest)))
+            src = src.reshape(B * mp, HKV, ps, *rest)
+            o = torch.empty_like(src)
+            o[table.view(-1).long()] = src
+            return o.contiguous()
+
+        paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
+                           scatter(st.v_scale), scatter(st.witness))
+        suffix = kvq.RegionView(paged, sf.length, k_exact=scatter(exact), lengths=lens, page_table=table,
+                                page_size=ps, use_witness=sf.witness)
+    else:
+        suffix = kvq.RegionView(st, sf.length, k_exact=exact, lengths=lens, seed=seed, layer=layer,
+                                stream_id=0, use_witness=sf.witness)
+    n_tok = int(lens.sum()) if lens is not None else B * sf.length
+    bytes_launch += HKV * n_tok * token_head_bytes(sf.k_fmt, sf.v_fmt, sf.exact_k, sf.witness)
+    bytes_launch += B * HQ * 128 * 4 * 2 + 4 * B * HQ * 4                     # q, out, meter
+    sm = float(np.float32(1.0 / math.sqrt(128.0)))
+    out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
+    mbuf = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev) for k in ("tv", "bound_raw", "meter", "log_a")}
+    meter = kvq.MeterOut(**{k: v.data_ptr() for k, v in mbuf.items()})
+    a = kvq._attn_args(inp["q"], prefix, suffix, out, sm, 0, HKV)
+    info = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter), 0, ctypes.byref(info)) == 0
+    ws = torch.empty(max(info.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    assert lib.kvq_workspace_init(ws.data_ptr(), ws.numel(), sp) == 0
+    for _ in range(warmup):
+        assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(meter), ws.data_ptr(), ws.numel(), sp) == 0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(meter), ws.data_ptr(), ws.numel(), sp) == 0
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    med = ms[len(ms) // 2]
+    achieved = bytes_launch / (med * 1e-3) / 1e9
+    plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
+            if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
+    print(json.dumps({
+        "workload": f"config {idx}: {cfg.description}",
+        "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
+        "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS},
+        "plan": plan}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design doc describes how the step would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != 3:
+        measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1))
+        return
     import numpy as np
     import torch
     from quantized_kv_cache_gqa_amd import kvq
     from workloads import CONFIGS, gen_layer
-    from oracle.accounting import token_head_bytes  # byte accounting only
 
     cfg = CONFIGS[3]
     L = args.layers or cfg.layers
@@ -252,6 +364,7 @@ def main():
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
 
     per_th = token_head_bytes("fp8", "fp8", exact_k=True, witness=True)      # 552 B
+    assert per_th == 552
     io_bytes = B * HQ * D * 4 * 2 + 4 * B * HQ * 4                              # q, out, meter
     bytes_launch = B * HKV * S * per_th + io_bytes
     achieved = bytes_launch / (dec_avg_ms * 1e-3) / 1e9

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     if (do_tv && valid && j == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        *reinterpret_cast<float2 *>(spill_g + 2 * spill_entry<G>(t, h)) = make_float2(lq[h], le[h]);
+        st_pair(spill_g + 2 * spill_entry<G>(t, h), lq[h], le[h], d.total_chunks > 1);
     }
 
     // ---- online accumulators

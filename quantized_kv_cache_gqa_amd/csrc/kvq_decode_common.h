@@ -1,7 +1,7 @@
 // Pieces shared by the decode kernels: dequantization of one row segment, the
 // online-softmax merge factor, and the chunk epilogue (cross-wavefront merge,
 // partial write, arrival counter, and the finalize run by the last work-group of
-// each (request, KV head)).
+// each (request, KV head)), with the agent-scope accessors they exchange through.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +39,37 @@ template <int G>
 __device__ __forceinline__ float *spill_region(const DecodeLaunch &d, int grp, bool is_prefix) {
   const size_t rows = (size_t)round16(d.prefix_len) + round16(d.suffix_cap);
   return d.spill + ((size_t)grp * rows + (is_prefix ? 0 : round16(d.prefix_len))) * (2 * G);
+}
+
+// Words that other work-groups read (partials, and the spill when a group
+// has several chunks) go through agent-scope stores and loads, each coherent
+// at device scope by itself, so no fence has to write back or invalidate a
+// whole cache; a writer waits for its own stores (vmcnt 0) before it counts
+// itself in.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// one (l~, l) spill pair; `dev`: read by another work-group
+__device__ __forceinline__ void st_pair(float *p, float a, float b, bool dev) {
+  if (dev) {
+    const uint64_t w = ((uint64_t)__float_as_uint(b) << 32) | __float_as_uint(a);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+  }
+}
+__device__ __forceinline__ float2 ld_pair_dev(const float *p) {
+  const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+}
+__device__ __forceinline__ void wait_own_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 __device__ __forceinline__ float merge_factor(float m, float mnew) {
@@ -126,7 +157,10 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) r += part_s[w][h][k] * merge_factor(part_s[w][h][mk], M);
     }
-    part_g[idx] = r;
+    if (single)
+      part_g[idx] = r;
+    else
+      st_dev(&part_g[idx], r);
   }
   if (single) {
     // spill rows and merged_s were written by this work-group only
@@ -134,16 +168,17 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   } else {
-    __threadfence();
+    wait_own_stores();              // this thread's partial and spill words are out
     __syncthreads();
     if (tid == 0) {
-      const unsigned old = atomicAdd(d.counters + grp, 1u);
+      const unsigned old = __hip_atomic_fetch_add(d.counters + grp, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
       last_s = (old == (unsigned)(total_chunks - 1));
     }
     __syncthreads();
     if (!last_s) return;
-    __threadfence();
   }
+  auto rd = [&](const float *p) { return single ? *p : ld_dev(p); };
 
   // ================= finalize: this work-group arrived last for (b, kvh)
   __shared__ float fin_s[G][6];   // M~, 1/Z~, M_e, 1/Z_e (log2 units)
@@ -154,19 +189,19 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
     float Mq = NEG_INF, Mm = NEG_INF, Me = NEG_INF;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
-      Mq = fmaxf(Mq, pc[0]);
-      Mm = fmaxf(Mm, pc[2]);
-      Me = fmaxf(Me, pc[4]);
+      Mq = fmaxf(Mq, rd(pc + 0));
+      Mm = fmaxf(Mm, rd(pc + 2));
+      Me = fmaxf(Me, rd(pc + 4));
     }
     float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
-      const float fq = merge_factor(pc[0], Mq);
-      Zq += pc[1] * fq;
-      Zm += pc[3] * merge_factor(pc[2], Mm);
-      Ze += pc[5] * merge_factor(pc[4], Me);
-      o0 += pc[8 + lane] * fq;
-      o1 += pc[8 + 64 + lane] * fq;
+      const float fq = merge_factor(rd(pc + 0), Mq);
+      Zq += rd(pc + 1) * fq;
+      Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
+      Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
+      o0 += rd(pc + 8 + lane) * fq;
+      o1 += rd(pc + 8 + 64 + lane) * fq;
     }
     const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
     if (d.has_out) {
@@ -210,7 +245,12 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int e = min(e0 + 512 * u, n_entries - 2);
-            x[u] = *reinterpret_cast<const float4 *>(sp + 2 * (size_t)e);
+            if (single) {
+              x[u] = *reinterpret_cast<const float4 *>(sp + 2 * (size_t)e);
+            } else {
+              const float2 a = ld_pair_dev(sp + 2 * (size_t)e), c = ld_pair_dev(sp + 2 * (size_t)e + 2);
+              x[u] = make_float4(a.x, a.y, c.x, c.y);
+            }
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -234,7 +274,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * s;
     }
   }
-  if (tid == 0 && !single) d.counters[grp] = 0u;   // ready for the next call
+  if (tid == 0 && !single)                          // ready for the next call
+    __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace kvq

@@ -304,7 +304,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       if (do_tv) spill_s[64 * ((t0 - c0) >> 4) + lane] = make_float2(lq, le);
     } else {
       if (do_tv && valid)
-        *reinterpret_cast<float2 *>(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane)) = make_float2(lq, le);
+        st_pair(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane), lq, le, d.total_chunks > 1);
     }
 
     // ---- attention softmax (maximum uniform per head)
