@@ -573,6 +573,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(team * 2 + (round & 1)) * T * SLOT_WORDS;
   uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
   __shared__ float mq_s[G][64];
+  __shared__ float unit_s[WAVES][64];
   __shared__ float fin_s[G][4];
   __shared__ float tvw_s[WAVES][G];
   __shared__ int bad_s;
@@ -631,20 +632,23 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
 
   // 3. duties, spread so that no member is always the last one out:
   //    - output: 8 units of 64 dims (head u / 2, half u % 2); unit u is
-  //      taken by member u % T, wavefront (u / T) % 4, summing the members'
-  //      accumulators in member order;
+  //      taken by member u % T, wavefront (u / T) % 4 (T < 8) or by member u
+  //      (T >= 8, see below), summing the members' accumulators in order;
   //    - log A, bound, meter of head h: member h % T (no loads);
   //    - the previous round's TV of head h: member (h + 4) % T, wavefront h.
   const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
+  // T >= 8: unit u = member, its batches of 8 members dealt to the 4
+  // wavefronts in turn, partial sums added in wavefront order through LDS
+  const bool split = T >= 8;
   if (d.has_out) {
     for (int u = 0; u < 8; ++u) {
-      if (u % T != member || (u / T) % 4 != h) continue;
+      if (split ? u != member : (u % T != member || (u / T) % 4 != h)) continue;
       const int hu = u >> 1, dim = 64 * (u & 1) + lane;
       const float Mu = fin_s[hu][0];
       const float iZu = fin_s[hu][1];
       float o = 0.0f;
       bool oku = true;
-      for (int cb = 0; cb < T; cb += 8) {
+      for (int cb = split ? 8 * h : 0; cb < T; cb += split ? 32 : 8) {
         const uint64_t *p[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -656,8 +660,22 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
           if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
       }
       const size_t qu = (size_t)b * d.h_q + (size_t)kvh * G + hu;
-      d.out[qu * D + dim] = oku ? o * iZu : qnan;
-      ok = ok && oku;
+      if (split) {
+        unit_s[h][lane] = o;
+        if (!oku) bad_s = 1;
+      } else {
+        d.out[qu * D + dim] = oku ? o * iZu : qnan;
+        ok = ok && oku;
+      }
+    }
+    if (split && member < 8) {                     // uniform over the work-group
+      __syncthreads();
+      if (h == 0) {
+        const int hu = member >> 1, dim = 64 * (member & 1) + lane;
+        const float o = ((unit_s[0][lane] + unit_s[1][lane]) + unit_s[2][lane]) + unit_s[3][lane];
+        const size_t qu = (size_t)b * d.h_q + (size_t)kvh * G + hu;
+        d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
+      }
     }
   }
   if (member == h % T && lane == 0) {
