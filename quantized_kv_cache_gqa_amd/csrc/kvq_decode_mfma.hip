@@ -90,6 +90,29 @@ __device__ __forceinline__ void transpose4x4(const uint32_t t[4], uint32_t out[4
   out[3] = __builtin_amdgcn_perm(b23, a23, 0x07060302u);
 }
 
+// Two signed INT8 codes -> two bf16 (exact: |code| <= 127), packed.
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int byte0) {
+  const float a = (float)(int)(int8_t)(w >> (8 * byte0));
+  const float b = (float)(int)(int8_t)(w >> (8 * byte0 + 8));
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// The dither of 8 channels (two generator calls), split into two exact-sum
+// bf16 pieces of -xi: -xi = hi + lo + r with |r| <= 2^-18 |xi|.
+__device__ __forceinline__ void neg_dither8_bf16(uint32_t token, uint32_t g0, uint32_t tag, uint32_t stream,
+                                                 uint32_t k0, uint32_t k1, bf16x8_t &hi, bf16x8_t &lo) {
+  float xi[8];
+  dither4(token, g0, tag, stream, k0, k1, xi);
+  dither4(token, g0 + 1, tag, stream, k0, k1, xi + 4);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = -xi[e];
+    const float h = bf16_round(x);
+    hi[e] = (__bf16)h;
+    lo[e] = (__bf16)(x - h);
+  }
+}
+
 struct TileRegs {
   uint4 k[4];      // FP8: k[0..1] = 32 codes; BF16: k[0..3] = 32 values
   uint4 ke[4];     // exact keys (bf16), 32 values
@@ -123,11 +146,11 @@ struct TileSrc {
     h_kv = d.h_kv;
     kvh = kvh_;
     last = c1 - 1;
-    kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
+    kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_BF16 ? 2 * D : D);
     keb = (const uint8_t *)R.k_exact + row0 * (2 * D);
     wb = R.witness + row0 * NB;
     ksb = (const float *)R.k_scale + row0;
-    vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_FP8_E4M3 ? D : 2 * D);
+    vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_BF16 ? 2 * D : D);
     vsb = (const float *)R.v_scale + row0;
   }
 
@@ -151,11 +174,11 @@ struct TileSrc {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
-    if constexpr (KF == KVQ_FMT_FP8_E4M3) {
+    if constexpr (KF == KVQ_FMT_FP8_E4M3 || KF == KVQ_FMT_INT8_DITHER) {
       const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * D + 32 * g);
       T.k[0] = p[0];
       T.k[1] = p[1];
-      T.ks = ksb[rk];
+      T.ks = KF == KVQ_FMT_FP8_E4M3 ? ksb[rk] : 1.0f;   // INT8: block scales ride on q
     } else {
       const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
 #pragma unroll
@@ -175,11 +198,11 @@ struct TileSrc {
     const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
     if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
-    if constexpr (VF == KVQ_FMT_FP8_E4M3) {
+    if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + row_of(t0 + 4 * g + e) * D + 8 * j16);
-      T.vs = vsb[rk];
+      T.vs = VF == KVQ_FMT_FP8_E4M3 ? vsb[rk] : 1.0f;
     } else if constexpr (VF == KVQ_FMT_BF16) {
       const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
       const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
@@ -250,6 +273,51 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
   }
 
+  // INT8 (subtractive dither): x^ = s_c (code - xi) with s_c per 256-token
+  // block and channel.  The logits take the block's scales on the query side:
+  // bqs = exact three-way bf16 split of q_c s_c (log2 units), against the
+  // codes and the two pieces of -xi.  Values are dequantized to fp16.
+  constexpr bool I8K = KF == KVQ_FMT_INT8_DITHER;
+  constexpr bool I8V = VF == KVQ_FMT_INT8_DITHER;
+  bf16x8_t bqs[4];
+  float sv8[8];                                    // value scales of dims 8 j16 + n
+  uint32_t i8_stream = 0, i8_ktag = 0, i8_vtag = 0;
+  size_t i8_scale_row0 = 0;
+  if constexpr (I8K || I8V) {
+    const size_t sh = R.is_prefix ? (size_t)kvh : (size_t)b * d.h_kv + kvh;
+    i8_scale_row0 = sh * (size_t)((R.length + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK);
+    i8_stream = (uint32_t)(R.is_prefix ? R.stream_id : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
+    i8_ktag = dither_tag(0, R.layer, kvh);
+    i8_vtag = dither_tag(1, R.layer, kvh);
+  }
+  auto set_block = [&](int blk) {
+    const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
+    if constexpr (I8K) {
+      const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
+      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+#pragma unroll
+      for (int s8 = 0; s8 < 4; ++s8) {
+        const uint4 sc = *reinterpret_cast<const uint4 *>(ks + 32 * g + 8 * s8);
+        const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = qp[32 * g + 8 * s8 + e] * qs * fp16_bits_to_f32((sw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          const float hi = bf16_round(x);
+          const float mid = bf16_round(x - hi);
+          const float lo = bf16_round(x - hi - mid);
+          const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
+          bqs[s8][e] = (__bf16)piece;
+        }
+      }
+    }
+    if constexpr (I8V) {
+      const uint4 sc = *reinterpret_cast<const uint4 *>((const uint16_t *)R.v_scale + srow + 8 * j16);
+      const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+      for (int n = 0; n < 8; ++n) sv8[n] = fp16_bits_to_f32((sw[n >> 1] >> (16 * (n & 1))) & 0xffffu);
+    }
+  };
+
   const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
   float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
   auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit); };
@@ -279,6 +347,21 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2 * s], w[2 * s + 1]), bq[s], dq, 0, 0, 0);
+    } else if constexpr (I8K) {
+      // row j16 = token t0 + j16, slice s = channels 32 g + 8 s .. + 7
+      const uint32_t w[8] = {T.k[0].x, T.k[0].y, T.k[0].z, T.k[0].w,
+                             T.k[1].x, T.k[1].y, T.k[1].z, T.k[1].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 cw = {i8x2_to_bf16x2(w[2 * s], 0), i8x2_to_bf16x2(w[2 * s], 2),
+                          i8x2_to_bf16x2(w[2 * s + 1], 0), i8x2_to_bf16x2(w[2 * s + 1], 2)};
+        bf16x8_t xh, xl;
+        neg_dither8_bf16((uint32_t)(t0 + j16), (uint32_t)(8 * g + 2 * s), i8_ktag, i8_stream, R.seed_lo,
+                         R.seed_hi, xh, xl);
+        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], dq, 0, 0, 0);
+        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], dq, 0, 0, 0);
+        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bqs[s], dq, 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s) dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[s]), bq[s], dq, 0, 0, 0);
@@ -320,7 +403,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       float fh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
-      if constexpr (VF == KVQ_FMT_FP8_E4M3) {
+      if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
@@ -374,6 +457,34 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
+    } else if constexpr (I8V) {
+      // as FP8, with weights p and values s_c (code - xi) in fp16
+      w_s[wv][16 * hh + 4 * g + pp] = p;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const float4 wa = *reinterpret_cast<const float4 *>(&w_s[wv][16 * (j16 & 3) + 4 * g]);
+      const bool arow = j16 < 4;
+      const f16x4_t aw = {(_Float16)(arow ? wa.x : 0.0f), (_Float16)(arow ? wa.y : 0.0f),
+                          (_Float16)(arow ? wa.z : 0.0f), (_Float16)(arow ? wa.w : 0.0f)};
+      f16x4_t vb[8];                               // vb[n][e]: token t0 + 4 g + e, dim 8 j16 + n
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float xi[8];
+        const uint32_t tok = (uint32_t)(t0 + 4 * g + e);
+        dither4(tok, (uint32_t)(2 * j16), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi);
+        dither4(tok, (uint32_t)(2 * j16 + 1), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi + 4);
+        const uint32_t cw[2] = {T.v8[e].x, T.v8[e].y};
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const float code = (float)(int)(int8_t)(cw[n >> 2] >> (8 * (n & 3)));
+          vb[n][e] = (_Float16)(sv8[n] * (code - xi[n]));
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) ov[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(aw, vb[n], ov[n], 0, 0, 0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     } else if constexpr (VF == KVQ_FMT_BF16) {
       w_s[wv][4 * (4 * g + pp) + hh] = p;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -404,17 +515,38 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // math.  The next tile is always loaded (rows clamp to the last valid
   // token, so past the end this re-reads a valid row and the data is unused).
   TileRegs ta, tb;
-  constexpr int STEP = 16 * WAVES;
-  int t0 = c0 + 16 * wv;
-  if (t0 < c1) load_tile(ta, t0);
-  while (t0 < c1) {
-    load_tile(tb, t0 + STEP);
-    process(ta, t0);
-    t0 += STEP;
-    if (t0 >= c1) break;
-    load_tile(ta, t0 + STEP);
-    process(tb, t0);
-    t0 += STEP;
+  if constexpr (I8K || I8V) {
+    // INT8: wavefront wv takes whole 256-token blocks wv, wv + 4, ... of the
+    // chunk, so the block operands change once per 16 tiles
+    const int blk0 = c0 / KVQ_INT8_BLOCK;
+    for (int blk = blk0 + wv; blk * KVQ_INT8_BLOCK < c1; blk += WAVES) {
+      const int tb0 = max(blk * KVQ_INT8_BLOCK, c0), tb1 = min((blk + 1) * KVQ_INT8_BLOCK, c1);
+      set_block(blk);
+      int t0 = tb0;
+      load_tile(ta, t0);
+      while (t0 < tb1) {
+        load_tile(tb, t0 + 16);
+        process(ta, t0);
+        t0 += 16;
+        if (t0 >= tb1) break;
+        load_tile(ta, t0 + 16);
+        process(tb, t0);
+        t0 += 16;
+      }
+    }
+  } else {
+    constexpr int STEP = 16 * WAVES;
+    int t0 = c0 + 16 * wv;
+    if (t0 < c1) load_tile(ta, t0);
+    while (t0 < c1) {
+      load_tile(tb, t0 + STEP);
+      process(ta, t0);
+      t0 += STEP;
+      if (t0 >= c1) break;
+      load_tile(ta, t0 + STEP);
+      process(tb, t0);
+      t0 += STEP;
+    }
   }
 
   // ---- wavefront merge: lanes of one head differ in bits 0, 1, 4, 5
@@ -449,7 +581,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
     part_s[wv][hh][4] = me; part_s[wv][hh][5] = ze;
   }
-  if constexpr (VF == KVQ_FMT_FP8_E4M3) {
+  if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
     if (lane < 16) {
 #pragma unroll
       for (int n = 0; n < 8; ++n)
@@ -803,10 +935,14 @@ template <int KF, int VF>
 static hipError_t launch_m(const DecodeLaunch &d, hipStream_t stream) {
   const long work = (long)d.batch * d.h_kv * d.n_chunks;
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
-  if (d.region.paged)
-    launch_p<KF, VF, true>(d, stream, grid);
-  else
-    launch_p<KF, VF, false>(d, stream, grid);
+  if constexpr (KF == KVQ_FMT_INT8_DITHER) {
+    launch_p<KF, VF, false>(d, stream, grid);       // INT8 regions are dense
+  } else {
+    if (d.region.paged)
+      launch_p<KF, VF, true>(d, stream, grid);
+    else
+      launch_p<KF, VF, false>(d, stream, grid);
+  }
   return hipGetLastError();
 }
 
@@ -862,12 +998,19 @@ hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t strea
 }
 
 bool mfma_path_supports(const DecodeLaunch &d) {
-  return d.group == 4 && (d.k_format == KVQ_FMT_FP8_E4M3 || d.k_format == KVQ_FMT_BF16) &&
-         (d.v_format == KVQ_FMT_FP8_E4M3 || d.v_format == KVQ_FMT_BF16 || d.v_format == VF_NONE) &&
-         d.region.exact_fmt != EX_F32;
+  if (d.group != 4 || d.region.exact_fmt == EX_F32) return false;
+  if (d.k_format == KVQ_FMT_INT8_DITHER)           // dense INT8 keys and INT8 (or no) values
+    return !d.region.paged && (d.v_format == KVQ_FMT_INT8_DITHER || d.v_format == VF_NONE);
+  return (d.k_format == KVQ_FMT_FP8_E4M3 || d.k_format == KVQ_FMT_BF16) &&
+         (d.v_format == KVQ_FMT_FP8_E4M3 || d.v_format == KVQ_FMT_BF16 || d.v_format == VF_NONE);
 }
 
 hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t s) {
+  if (d.k_format == KVQ_FMT_INT8_DITHER) {
+    if (d.v_format == KVQ_FMT_INT8_DITHER)
+      return launch_m<KVQ_FMT_INT8_DITHER, KVQ_FMT_INT8_DITHER>(d, s);
+    return launch_m<KVQ_FMT_INT8_DITHER, VF_NONE>(d, s);
+  }
   if (d.k_format == KVQ_FMT_FP8_E4M3) {
     if (d.v_format == KVQ_FMT_FP8_E4M3) return launch_m<KVQ_FMT_FP8_E4M3, KVQ_FMT_FP8_E4M3>(d, s);
     if (d.v_format == KVQ_FMT_BF16) return launch_m<KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16>(d, s);
