@@ -46,6 +46,15 @@ uint32_t next_epoch(uint32_t rounds) {
   }
 }
 
+// decimal value of an environment variable in [lo, 2^32), else dflt
+unsigned env_uint(const char *name, unsigned dflt, unsigned long lo) {
+  const char *v = getenv(name);
+  if (!v || !*v) return dflt;
+  char *end = nullptr;
+  const unsigned long x = strtoul(v, &end, 10);
+  return (end && *end == 0 && x >= lo && x <= 0xffffffffUL) ? (unsigned)x : dflt;
+}
+
 bool env_is(const char *name, char c) {
   const char *v = getenv(name);
   return v && v[0] == c;
@@ -269,6 +278,12 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     d.team = p.team;
     d.n_teams = p.n_teams;
     d.epoch = next_epoch((uint32_t)p.rounds);
+    // Bounded waits of the team exchange.  Two test hooks, read from the
+    // environment: KVQ_TEAM_SPIN_LIMIT (polls per batch of words, default
+    // 2^18) and KVQ_TEAM_SILENT_MEMBER (that member of every team never
+    // publishes, so the others' waits run out and the results turn to NaN).
+    d.spin_limit = env_uint("KVQ_TEAM_SPIN_LIMIT", 1u << 18, 1);
+    d.silent_member = (int)env_uint("KVQ_TEAM_SILENT_MEMBER", 0xffffffffu, 0);
     e = launch_decode_team(d, p.grid, stream);
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
   }

@@ -644,7 +644,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
 // All reductions run in a fixed order (bitwise reproducible).  The launch is
 // cooperative (all members resident); a bounded wait leaves NaN in the
 // group's results instead of hanging.
-constexpr unsigned TEAM_SPIN_LIMIT = 1u << 18;
 constexpr int SLOT_WORDS = 544;    // 24 states (6 per head), 4 TV shares, 4 pad, 512 accumulator words
 constexpr int SLOT_TV = 24, SLOT_ACC = 32;
 
@@ -659,7 +658,8 @@ __device__ __forceinline__ void st_tagged(uint64_t *p, uint32_t tag, float v) {
 // Reads N tagged words (all loads in flight together), then re-polls any
 // whose tag is not yet `tag`.  Returns false if a word never arrived.
 template <int N>
-__device__ __forceinline__ bool read_tagged(const uint64_t *const (&p)[N], uint32_t tag, float (&v)[N]) {
+__device__ __forceinline__ bool read_tagged(const uint64_t *const (&p)[N], uint32_t tag, float (&v)[N],
+                                            unsigned limit) {
   uint64_t w[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) w[i] = ld_tagged(p[i]);
@@ -670,7 +670,7 @@ __device__ __forceinline__ bool read_tagged(const uint64_t *const (&p)[N], uint3
     while (ok && (uint32_t)(w[i] >> 32) != tag) {
       __builtin_amdgcn_s_sleep(2);
       w[i] = ld_tagged(p[i]);
-      if (++spins >= TEAM_SPIN_LIMIT) ok = false;   // budget spent: no further waits
+      if (++spins >= limit) ok = false;            // budget spent: no further waits
     }
     v[i] = __uint_as_float((uint32_t)w[i]);
   }
@@ -729,7 +729,8 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) r += part_s[w][h][k] * merge_factor(part_s[w][h][mk], M);
     }
-    st_tagged(mine + (k < 6 ? 6 * h + k : SLOT_ACC + 128 * h + (k - 8)), tag, r);
+    if (member != d.silent_member)                 // (a test hook silences one member)
+      st_tagged(mine + (k < 6 ? 6 * h + k : SLOT_ACC + 128 * h + (k - 8)), tag, r);
   }
 
   // 2. the group's normalizers: wavefront h reads head h of every member
@@ -742,8 +743,16 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     const uint64_t *s = slots + (size_t)lane * SLOT_WORDS + 6 * h;
     const uint64_t *const p[6] = {s, s + 1, s + 2, s + 3, s + 4, s + 5};
     float v[6];
-    ok = read_tagged<6>(p, tag, v);
+    ok = read_tagged<6>(p, tag, v, d.spin_limit);
     Mq = v[0]; Zq = v[1]; Mm = v[2]; Zm = v[3]; Me = v[4]; Ze = v[5];
+  }
+  // one member's words missing makes the whole group's states unknown: NaN
+  // then flows into every result of the group (never a stale value)
+  ok = __all(ok);
+  if (!ok) {
+    const float qnan_s = __builtin_nanf("");
+    Mq = Zq = Mm = Zm = Me = Ze = qnan_s;
+    if (lane == 0) bad_s = 1;
   }
   mq_s[h][lane] = Mq;
   for (int off = 1; off < T; off <<= 1) {           // lanes >= T hold empty states
@@ -786,7 +795,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
         for (int i = 0; i < 8; ++i)
           p[i] = slots + (size_t)min(cb + i, T - 1) * SLOT_WORDS + SLOT_ACC + 128 * hu + dim;
         float v[8];
-        oku = read_tagged<8>(p, tag, v) && oku;
+        oku = read_tagged<8>(p, tag, v, d.spin_limit) && oku;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
@@ -830,7 +839,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (lane < T) {
       const uint64_t *const p[1] = {prev + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
       float v[1];
-      okp = read_tagged<1>(p, tag - 1u, v);
+      okp = read_tagged<1>(p, tag - 1u, v, d.spin_limit);
       sh = v[0];
     }
     sh = wave_sum_fixed(sh, T);
@@ -876,7 +885,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   __syncthreads();
   if (tid < G) {
     const float share = ((tvw_s[0][tid] + tvw_s[1][tid]) + tvw_s[2][tid]) + tvw_s[3][tid];
-    st_tagged(mine + SLOT_TV + tid, tag, share);
+    if (member != d.silent_member) st_tagged(mine + SLOT_TV + tid, tag, share);
   }
 
   // 5. last round: member (h + 4) % T also sums this round's shares
@@ -886,7 +895,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (lane < T) {
       const uint64_t *const p[1] = {slots + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
       float v[1];
-      okp = read_tagged<1>(p, tag, v);
+      okp = read_tagged<1>(p, tag, v, d.spin_limit);
       sh = v[0];
     }
     sh = wave_sum_fixed(sh, T);

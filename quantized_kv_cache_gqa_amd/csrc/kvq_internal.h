@@ -67,6 +67,8 @@ struct DecodeLaunch {
   int team;                     // > 0: team launch, work-groups per (request, KV head)
   int n_teams;                  // teams in the grid
   uint32_t epoch;               // team launch: tag of round r is epoch + r + 1
+  unsigned spin_limit;          // team launch: polls per batch of words before giving up
+  int silent_member;            // team launch: member that never publishes (test hook; -1: none)
 };
 
 constexpr int PART_STRIDE = 136;  // m~, z~, m', z', m_e, z_e, 2 pad, acc[128]

@@ -5,6 +5,7 @@ relative; TV, bound and meter within 1e-5 (relative above 1 for the bound).
 """
 import dataclasses
 import math
+import time
 
 import numpy as np
 import pytest
@@ -251,3 +252,26 @@ def test_team_several_rounds_sampled_cells(gpu_lib, monkeypatch):
     assert torch.equal(o1, o2)
     for k in m1:
         assert torch.equal(m1[k], m2[k]), k
+
+
+def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
+    """Fault injected from the host: one member of every team never publishes
+    and the wait budget is small.  The launch still ends promptly, every
+    result of the affected groups is NaN (never a stale or partial value),
+    and the next call without the hooks is correct again."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    cfg = small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    case = GpuCase(cfg)
+    p = _team_plan(case, monkeypatch)
+    assert p["team"] >= 2, p
+    monkeypatch.setenv("KVQ_TEAM_SPIN_LIMIT", "64")
+    monkeypatch.setenv("KVQ_TEAM_SILENT_MEMBER", "1")
+    t0 = time.time()
+    out, m = case.run()
+    assert time.time() - t0 < 30
+    assert torch.isnan(out).all()
+    for k in ("tv", "bound_raw", "meter", "log_a"):
+        assert torch.isnan(m[k]).all(), k
+    monkeypatch.delenv("KVQ_TEAM_SPIN_LIMIT")
+    monkeypatch.delenv("KVQ_TEAM_SILENT_MEMBER")
+    _all_cells(case)
