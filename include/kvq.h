@@ -183,22 +183,30 @@ const char *kvq_status_string(kvq_status status);
 kvq_status kvq_quantize(const kvq_quant_args *args, kvq_stream stream);
 
 /* Bytes of device workspace kvq_decode_attn / kvq_meter need for these
- * arguments.  Host-only: reads the current device's properties, never its
- * memory.  The decode and the meter call on the same arguments need the same
- * size.  Returns 0 on invalid arguments. */
+ * arguments, with or without stream capture.  Host-only: reads the current
+ * device's properties, never its memory.  The decode and the meter call on
+ * the same arguments need the same size.  Returns 0 on invalid arguments. */
 size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter);
 
 /* How kvq_decode_attn (meter_only = 0) or kvq_meter (meter_only != 0) will
- * run for these arguments on the current device (host-only, as above).
- *  - team > 0: one cooperative launch; `team` work-groups share each
+ * run for these arguments on the current device, on a stream that is not
+ * being captured (host-only, as above).
+ *  - team > 0: one launch of at most as many work-groups as the device holds
+ *    at once; `team` work-groups share each
  *    (request, KV head), each keeping its chunk's logit pairs in LDS for the
  *    TV (WitCert Sec. 3 target), `n_teams` teams take the (request, KV head)
  *    pairs in `rounds` rounds.  Chosen when the TV is requested for a single
  *    region of at most 131,072 tokens with GQA group 4, FP8/BF16 keys and
- *    values and bf16 exact keys, split_tokens is 0, and the device supports
- *    cooperative launches.
+ *    values and bf16 exact keys, and split_tokens is 0.  Members wait only
+ *    for members of their own team, with a bounded wait: a wait that runs
+ *    out (another kernel holding the device for longer) leaves NaN in that
+ *    (request, KV head)'s results, never a hang.
  *  - team == 0: one launch per region over `chunks` chunks of each (request,
- *    KV head); the TV's logit pairs go through the workspace. */
+ *    KV head); the TV's logit pairs go through the workspace.  Calls on a
+ *    stream under graph capture always run this way (a team launch's tags
+ *    are chosen per call on the host, which a replay would repeat).
+ * workspace_bytes is what this plan needs; kvq_workspace_bytes may return
+ * more (it also covers the capture case). */
 typedef struct kvq_plan_info {
   int32_t team;             /* work-groups per (request, KV head); 0: no team launch */
   int32_t n_teams;
@@ -211,11 +219,15 @@ typedef struct kvq_plan_info {
 kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter, int meter_only,
                            kvq_plan_info *info);
 
-/* Prepare a workspace for first use: clears the arrival counters at its start.
- * A workspace stays ready after every successful kvq_decode_attn / kvq_meter
- * call (the last work-group of each (request, KV head) resets its counter;
- * team launches tag their words with a per-launch epoch instead).  Calls that
- * share a workspace must not overlap in time. */
+/* Prepare a workspace for first use: clears all of it (one fill kernel on
+ * `stream`).  A workspace stays ready after every successful kvq_decode_attn /
+ * kvq_meter call: the per-chunk plan's arrival counters (in the first MiB)
+ * are reset by the last work-group of each (request, KV head), and team
+ * launches tag their exchange words with a per-call epoch instead of
+ * clearing them.  Calls of other shapes may share the workspace; clearing it
+ * again when the shape changes also removes the small chance (2^-32 per
+ * word) that a word left by another plan carries the tag a team launch
+ * waits for.  Calls that share a workspace must not overlap in time. */
 kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, kvq_stream stream);
 
 /* Decode attention with the fused meter (WitCert Sec. 6 meter loop, read path;

@@ -19,6 +19,11 @@ namespace {
 using namespace kvq;
 
 constexpr size_t kAlign = 256;
+// The per-chunk plan's arrival counters (one per (request, KV head), at most
+// 2^18) sit in the workspace's first MiB, which must read zero at rest; the
+// team plan's slots start after it, so neither plan's words land on the
+// other's counters when calls of different shapes share a workspace.
+constexpr size_t kCounterBytes = (size_t)1 << 20;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -113,8 +118,8 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   p.total_chunks = p.team;
   p.rounds = (groups + p.n_teams - 1) / p.n_teams;
   p.off_counters = 0;
-  p.off_partials = 0;
-  p.off_spill = round_up((size_t)p.n_teams * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
+  p.off_partials = kCounterBytes;
+  p.off_spill = p.off_partials + round_up((size_t)p.n_teams * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
   p.bytes = p.off_spill;
   return true;
 }
@@ -147,7 +152,9 @@ kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int ba
   return KVQ_OK;
 }
 
-kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_only, Plan &p) {
+// allow_team = false: the per-chunk plan even where a team launch applies
+kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_only, Plan &p,
+                     bool allow_team = true) {
   if (!a) return KVQ_ERR_NULL;
   if (a->head_dim != KVQ_HEAD_DIM) return KVQ_ERR_UNSUPPORTED;
   if (a->batch <= 0 || a->num_kv_heads <= 0 || a->num_q_heads <= 0) return KVQ_ERR_SHAPE;
@@ -198,7 +205,7 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     p.tv = m->tv && any_exact;
     p.meter = (m->bound_raw || m->meter || m->log_a) && p.wit_any;
   }
-  if (plan_team(a, meter_only, groups, p)) return KVQ_OK;
+  if (allow_team && plan_team(a, meter_only, groups, p)) return KVQ_OK;
   p.off_counters = 0;
   p.off_partials = round_up((size_t)groups * sizeof(uint32_t), kAlign);
   p.off_spill = p.off_partials +
@@ -232,10 +239,18 @@ RegionDev region_dev(const kvq_region &r, bool is_prefix) {
   return d;
 }
 
+// A stream being captured into a graph gets the per-chunk plan: a team
+// launch's tags are chosen on the host per call, and a replayed graph would
+// repeat them.  A failed query counts as capturing.
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+}
+
 kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
                       hipStream_t stream, bool meter_only) {
   Plan p;
-  kvq_status s = make_plan(a, m, meter_only, p);
+  kvq_status s = make_plan(a, m, meter_only, p, !stream_capturing(stream));
   if (s != KVQ_OK) return s;
   if (!ws) return KVQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;
@@ -362,8 +377,11 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
 }
 
 size_t kvq_workspace_bytes(const kvq_attn_args *a, const kvq_meter_out *m) {
-  Plan p;
-  if (make_plan(a, m, true, p) != KVQ_OK) return 0;   // size does not depend on out/v
+  // the size does not depend on out/v; it covers the per-chunk plan too,
+  // which a call under stream capture uses
+  Plan p, q;
+  if (make_plan(a, m, true, p) != KVQ_OK) return 0;
+  if (p.team && make_plan(a, m, true, q, false) == KVQ_OK) return std::max(p.bytes, q.bytes);
   return p.bytes;
 }
 
@@ -386,10 +404,8 @@ kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int m
 kvq_status kvq_workspace_init(void *ws, size_t bytes, kvq_stream stream) {
   if (!ws) return KVQ_ERR_NULL;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;
-  // the counters sit at the start; clearing the first partial offset's worth is
-  // enough, but clearing up to 1 MiB covers every plan with <= 256K groups
-  size_t n = bytes < ((size_t)1 << 20) ? bytes : ((size_t)1 << 20);
-  return launch_fill_zero(ws, n & ~(size_t)3, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+  // the whole workspace: the counters, and tagged team words of earlier calls
+  return launch_fill_zero(ws, bytes & ~(size_t)3, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
 kvq_status kvq_decode_attn(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,

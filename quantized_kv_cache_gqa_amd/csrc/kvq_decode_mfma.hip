@@ -641,9 +641,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
 // last round.  Slots alternate between two buffers by round parity: a member
 // writes round r + 2 only after it has read every member's round r + 1
 // states, which each member publishes after it has finished with round r.
-// All reductions run in a fixed order (bitwise reproducible).  The launch is
-// cooperative (all members resident); a bounded wait leaves NaN in the
-// group's results instead of hanging.
+// All reductions run in a fixed order (bitwise reproducible).  The grid fits
+// the device at once, so all members are resident; a bounded wait leaves NaN
+// in the group's results instead of hanging.
 constexpr int SLOT_WORDS = 544;    // 24 states (6 per head), 4 TV shares, 4 pad, 512 accumulator words
 constexpr int SLOT_TV = 24, SLOT_ACC = 32;
 
@@ -987,8 +987,7 @@ int team_capacity(int k_format, int v_format, bool paged, bool full) {
   const int vi = v_format == KVQ_FMT_FP8_E4M3 ? 1 : (v_format == KVQ_FMT_BF16 ? 2 : 0);
   int &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0];
   if (c > 0) return c;
-  int coop = 0, cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
+  int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, team_kernel(k_format, v_format, paged, full),
                                                    256, (size_t)TEAM_MAX_CHUNK * 4 * sizeof(float2)) != hipSuccess)
@@ -1002,8 +1001,12 @@ hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t strea
   const void *fn = team_kernel(d.k_format, d.v_format, d.region.paged != 0, full);
   DecodeLaunch arg = d;
   void *args[] = {&arg};
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(256), args,
-                                    (unsigned)((size_t)d.chunk * 4 * sizeof(float2)), stream);
+  // A plain launch: members wait only for members of their own team, and a
+  // team's members are consecutive in dispatch order within an XCD's share of
+  // the grid, so they become resident together (the grid fits the device at
+  // once); a wait that runs out of budget gives NaN, never a hang.
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args,
+                         (size_t)d.chunk * 4 * sizeof(float2), stream);
 }
 
 bool mfma_path_supports(const DecodeLaunch &d) {

@@ -115,14 +115,22 @@ def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
     assert lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m2)) == counters + partials
 
 
-def test_plan_query_matches_workspace_bytes(lib):
-    """kvq_decode_plan reports the size kvq_workspace_bytes returns, for the
-    decode and the meter call alike; without a device there is no team plan."""
+def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
+    """kvq_decode_plan reports one size for the decode and the meter call;
+    kvq_workspace_bytes covers it and the per-chunk plan (taken under graph
+    capture); without a device there is no team plan and the sizes agree."""
     a = _args()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
     d, mo = _plan(lib, a, m, 0), _plan(lib, a, m, 1)
-    assert d.workspace_bytes == mo.workspace_bytes == n
+    assert d.workspace_bytes == mo.workspace_bytes <= n
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    assert _plan(lib, a, m, 0).workspace_bytes <= n
+    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    if d.team:
+        assert d.workspace_bytes >= (1 << 20)          # slots after the counters' MiB
+    else:
+        assert d.workspace_bytes == n
     if not torch.cuda.is_available():
         assert d.team == 0
     assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, None) == 1

@@ -275,3 +275,46 @@ def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
     monkeypatch.delenv("KVQ_TEAM_SPIN_LIMIT")
     monkeypatch.delenv("KVQ_TEAM_SILENT_MEMBER")
     _all_cells(case)
+
+
+def test_graph_capture_takes_the_per_chunk_plan(gpu_lib, monkeypatch):
+    """A call captured into a graph runs the per-chunk plan (a team launch's
+    tags are chosen per call on the host, and a replay would repeat them).
+    Every replay equals the eager per-chunk result bit for bit, with eager
+    team calls on the same workspace between the replays, which in turn keep
+    equal to the first eager team call."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    from quantized_kv_cache_gqa_amd import kvq
+    cfg = small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    case = GpuCase(cfg)
+    _team_plan(case, monkeypatch)
+    ws = kvq.Workspace(torch.device("cuda"))
+
+    def call(out=None, meter_bufs=None):
+        return kvq.decode_attn(case.inp["q"], cfg.h_kv, case.prefix_view, case.suffix_view,
+                               sm_scale=SM_SCALE, workspace=ws, out=out, meter_bufs=meter_bufs)
+
+    o_team, m_team = call()
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    o_chunk, m_chunk = case.run()
+    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    torch.cuda.synchronize()
+    og = torch.empty_like(o_chunk)
+    mg = {k: torch.empty_like(v) for k, v in m_chunk.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out=og, meter_bufs=mg)
+    for _ in range(3):
+        og.fill_(float("nan"))
+        for v in mg.values():
+            v.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(og, o_chunk)
+        for k in m_chunk:
+            assert torch.equal(mg[k], m_chunk[k]), k
+        o2, m2 = call()
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o_team)
+        for k in m_team:
+            assert torch.equal(m2[k], m_team[k]), k
