@@ -236,12 +236,22 @@ def measure_workload(idx: int, reps: int, warmup: int):
     ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     med = ms[len(ms) // 2]
     achieved = bytes_launch / (med * 1e-3) / 1e9
+    # the same launch with the meter off (no TV, no bound: attention only; an
+    # INT8 cache still regenerates every dither), to show what the meter costs
+    off_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in off_evs:
+        e0.record(stream)
+        assert lib.kvq_decode_attn(ctypes.byref(a), None, ws.data_ptr(), ws.numel(), sp) == 0
+        e1.record(stream)
+    torch.cuda.synchronize()
+    off_ms = sorted(e0.elapsed_time(e1) for e0, e1 in off_evs)[reps // 2]
     plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
             if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
     print(json.dumps({
         "workload": f"config {idx}: {cfg.description}",
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
+        "meter_off_launch_ms": off_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS},
         "plan": plan}), flush=True)

@@ -655,6 +655,25 @@ __device__ __forceinline__ void st_tagged(uint64_t *p, uint32_t tag, float v) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Words w[i] loaded earlier from addr(i): re-polls any whose tag is not yet
+// `tag` and returns the values.  Returns false if a word never arrived.
+template <int N, class Addr>
+__device__ __forceinline__ bool settle_tagged(Addr addr, uint32_t tag, uint64_t (&w)[N], float (&v)[N],
+                                              unsigned limit) {
+  bool ok = true;
+  unsigned spins = 0;                 // one budget for the whole batch
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    while (ok && (uint32_t)(w[i] >> 32) != tag) {
+      __builtin_amdgcn_s_sleep(2);
+      w[i] = ld_tagged(addr(i));
+      if (++spins >= limit) ok = false;            // budget spent: no further waits
+    }
+    v[i] = __uint_as_float((uint32_t)w[i]);
+  }
+  return ok;
+}
+
 // Reads N tagged words (all loads in flight together), then re-polls any
 // whose tag is not yet `tag`.  Returns false if a word never arrived.
 template <int N>
@@ -663,18 +682,7 @@ __device__ __forceinline__ bool read_tagged(const uint64_t *const (&p)[N], uint3
   uint64_t w[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) w[i] = ld_tagged(p[i]);
-  bool ok = true;
-  unsigned spins = 0;                 // one budget for the whole batch
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    while (ok && (uint32_t)(w[i] >> 32) != tag) {
-      __builtin_amdgcn_s_sleep(2);
-      w[i] = ld_tagged(p[i]);
-      if (++spins >= limit) ok = false;            // budget spent: no further waits
-    }
-    v[i] = __uint_as_float((uint32_t)w[i]);
-  }
-  return ok;
+  return settle_tagged<N>([&](int i) { return p[i]; }, tag, w, v, limit);
 }
 
 // (M, Z) merge of two online-softmax states; symmetric in its arguments
@@ -777,25 +785,90 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   //      (T >= 8, see below), summing the members' accumulators in order;
   //    - log A, bound, meter of head h: member h % T (no loads);
   //    - the previous round's TV of head h: member (h + 4) % T, wavefront h.
+  //    The first batch of accumulator words of this wavefront and the
+  //    previous round's TV shares are requested first; the TV pass (4.)
+  //    runs while they travel.
   const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
   // T >= 8: unit u = member, its batches of 8 members dealt to the 4
   // wavefronts in turn, partial sums added in wavefront order through LDS
   const bool split = T >= 8;
+  const int cb0 = split ? 8 * h : 0;                // this wavefront's first batch
+  int pre_u = -1;                                   // unit of the pre-issued batch
+  uint64_t pre_w[8];
+  if (d.has_out) {
+    for (int u = 0; u < 8; ++u) {
+      if (split ? u != member : (u % T != member || (u / T) % 4 != h)) continue;
+      if (cb0 < T) pre_u = u;
+      break;
+    }
+    if (pre_u >= 0) {
+      const uint64_t *ub = slots + SLOT_ACC + 128 * (pre_u >> 1) + 64 * (pre_u & 1) + lane;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pre_w[i] = ld_tagged(ub + (size_t)min(cb0 + i, T - 1) * SLOT_WORDS);
+    }
+  }
+  const bool tv_duty = do_tv && d.tv && member == (h + 4) % T;
+  // shares of round - 1 sit in the other parity's slots
+  const uint64_t *prev_tv = reinterpret_cast<const uint64_t *>(d.partials) +
+                            (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS +
+                            (size_t)min(lane, T - 1) * SLOT_WORDS + SLOT_TV + h;
+  uint64_t pre_tv[1] = {0};
+  if (tv_duty && round > 0 && lane < T) pre_tv[0] = ld_tagged(prev_tv);
+
+  // 4. this chunk's TV share: thread tid reads entry pairs (2p, 2p + 1), p =
+  //    tid + 256 k, as one float4 (both of head (tid % 8) / 2), into four
+  //    independent partial sums; then a butterfly over the lanes of a head
+  //    (bits 0, 3, 4, 5) and the wavefronts in order (published below)
+  float acc_tv = 0.0f;
+  if (do_tv && c1 > c0) {
+    const int hm = (lane & 6) >> 1;
+    const float Mt = fin_s[hm][0], iZt = fin_s[hm][1];
+    const float Mx = fin_s[hm][2], iZe = fin_s[hm][3];
+    const int n_pairs = round16(c1 - c0) * G / 2;
+    const float4 *sp4 = reinterpret_cast<const float4 *>(spill_s);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = tid; p0 < n_pairs; p0 += 4 * 256) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + 256 * u;
+        if (p < n_pairs) {
+          const float4 x = sp4[p];
+          const int e = 2 * p;
+          const int t = c0 + 16 * (e >> 6) + 4 * ((e & 63) >> 4) + (e & 3);
+          if (t < c1) tvp_add(a[u], x.x, x.y, Mt, iZt, Mx, iZe);
+          if (t + 1 < c1) tvp_add(a[u], x.z, x.w, Mt, iZt, Mx, iZe);
+        }
+      }
+    }
+    acc_tv = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+  acc_tv += __shfl_xor(acc_tv, 1);
+  acc_tv += __shfl_xor(acc_tv, 8);
+  acc_tv += __shfl_xor(acc_tv, 16);
+  acc_tv += __shfl_xor(acc_tv, 32);
+  if (lane < 8 && (lane & 1) == 0) tvw_s[wv][lane >> 1] = acc_tv;   // lanes 0, 2, 4, 6: heads 0..3
+
+  // 3 (continued): the output units
   if (d.has_out) {
     for (int u = 0; u < 8; ++u) {
       if (split ? u != member : (u % T != member || (u / T) % 4 != h)) continue;
       const int hu = u >> 1, dim = 64 * (u & 1) + lane;
       const float Mu = fin_s[hu][0];
       const float iZu = fin_s[hu][1];
+      const uint64_t *ub = slots + SLOT_ACC + 128 * hu + dim;
       float o = 0.0f;
       bool oku = true;
-      for (int cb = split ? 8 * h : 0; cb < T; cb += split ? 32 : 8) {
-        const uint64_t *p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          p[i] = slots + (size_t)min(cb + i, T - 1) * SLOT_WORDS + SLOT_ACC + 128 * hu + dim;
+      for (int cb = cb0; cb < T; cb += split ? 32 : 8) {
         float v[8];
-        oku = read_tagged<8>(p, tag, v, d.spin_limit) && oku;
+        if (u == pre_u && cb == cb0) {
+          oku = settle_tagged<8>([&](int i) { return ub + (size_t)min(cb + i, T - 1) * SLOT_WORDS; },
+                                 tag, pre_w, v, d.spin_limit) && oku;
+        } else {
+          const uint64_t *p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = ub + (size_t)min(cb + i, T - 1) * SLOT_WORDS;
+          oku = read_tagged<8>(p, tag, v, d.spin_limit) && oku;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
@@ -829,17 +902,12 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
     if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
   }
-  const bool tv_duty = do_tv && d.tv && member == (h + 4) % T;
   if (tv_duty && round > 0) {
-    // shares of round - 1 sit in the other parity's slots
-    const uint64_t *prev = reinterpret_cast<const uint64_t *>(d.partials) +
-                           (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS;
     float sh = 0.0f;
     bool okp = true;
     if (lane < T) {
-      const uint64_t *const p[1] = {prev + (size_t)lane * SLOT_WORDS + SLOT_TV + h};
       float v[1];
-      okp = read_tagged<1>(p, tag - 1u, v, d.spin_limit);
+      okp = settle_tagged<1>([&](int) { return prev_tv; }, tag - 1u, pre_tv, v, d.spin_limit);
       sh = v[0];
     }
     sh = wave_sum_fixed(sh, T);
@@ -849,39 +917,6 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * G + h] = okp ? 0.5f * sh : qnan;
   }
   if (!ok) bad_s = 1;
-
-  // 4. this chunk's TV share: thread tid reads entry pairs (2p, 2p + 1), p =
-  //    tid + 256 k, as one float4 (both of head (tid % 8) / 2), into four
-  //    independent partial sums; then a butterfly over the lanes of a head
-  //    (bits 0, 3, 4, 5) and the wavefronts in order
-  float acc_tv = 0.0f;
-  if (do_tv && c1 > c0) {
-    const int hm = (lane & 6) >> 1;
-    const float Mt = fin_s[hm][0], iZt = fin_s[hm][1];
-    const float Mx = fin_s[hm][2], iZe = fin_s[hm][3];
-    const int n_pairs = round16(c1 - c0) * G / 2;
-    const float4 *sp4 = reinterpret_cast<const float4 *>(spill_s);
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p0 = tid; p0 < n_pairs; p0 += 4 * 256) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int p = p0 + 256 * u;
-        if (p < n_pairs) {
-          const float4 x = sp4[p];
-          const int e = 2 * p;
-          const int t = c0 + 16 * (e >> 6) + 4 * ((e & 63) >> 4) + (e & 3);
-          if (t < c1) tvp_add(a[u], x.x, x.y, Mt, iZt, Mx, iZe);
-          if (t + 1 < c1) tvp_add(a[u], x.z, x.w, Mt, iZt, Mx, iZe);
-        }
-      }
-    }
-    acc_tv = (a[0] + a[1]) + (a[2] + a[3]);
-  }
-  acc_tv += __shfl_xor(acc_tv, 1);
-  acc_tv += __shfl_xor(acc_tv, 8);
-  acc_tv += __shfl_xor(acc_tv, 16);
-  acc_tv += __shfl_xor(acc_tv, 32);
-  if (lane < 8 && (lane & 1) == 0) tvw_s[wv][lane >> 1] = acc_tv;   // lanes 0, 2, 4, 6: heads 0..3
   __syncthreads();
   if (tid < G) {
     const float share = ((tvw_s[0][tid] + tvw_s[1][tid]) + tvw_s[2][tid]) + tvw_s[3][tid];
