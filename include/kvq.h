@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -201,8 +201,11 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    for members of their own team, with a bounded wait: a wait that runs
  *    out (another kernel holding the device for longer) leaves NaN in that
  *    (request, KV head)'s results, never a hang.
- *  - team == 0: one launch per region over `chunks` chunks of each (request,
- *    KV head); the TV's logit pairs go through the workspace.  Calls on a
+ *  - team == 0: `chunks` chunks of each (request, KV head) over both regions,
+ *    one work-group each, in one launch (cartridge page: one kernel spans the
+ *    shared cartridge and the live suffix) when both regions have keys of one
+ *    format and, with FP8 keys, values of one format; else one launch per
+ *    region.  The TV's logit pairs go through the workspace.  Calls on a
  *    stream under graph capture always run this way (a team launch's tags
  *    are chosen per call on the host, which a replay would repeat).
  * workspace_bytes is what this plan needs; kvq_workspace_bytes may return
@@ -214,6 +217,9 @@ typedef struct kvq_plan_info {
   int32_t grid;             /* work-groups of the team launch */
   int32_t chunk;            /* tokens per chunk */
   int32_t chunks;           /* chunks per (request, KV head), both regions */
+  int32_t launches;         /* kernel launches of the call: 1, or 2 when the
+                               two regions' formats need separate kernels */
+  int32_t reserved;         /* 0 */
   uint64_t workspace_bytes;
 } kvq_plan_info;
 kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter, int meter_only,

@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_decode_two.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

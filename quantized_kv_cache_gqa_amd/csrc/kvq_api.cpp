@@ -247,16 +247,11 @@ bool stream_capturing(hipStream_t stream) {
   return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
 }
 
-kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
-                      hipStream_t stream, bool meter_only) {
-  Plan p;
-  kvq_status s = make_plan(a, m, meter_only, p, !stream_capturing(stream));
-  if (s != KVQ_OK) return s;
-  if (!ws) return KVQ_ERR_WORKSPACE;
-  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
-  if (ws_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
-
-  DecodeLaunch d;
+// The per-chunk plan's launch arguments: the fields every launch shares, and
+// one copy per region (dp: prefix, ds: suffix).  ws may be NULL (planning
+// only: the workspace pointers are then NULL).
+void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &p, bool meter_only,
+                    void *ws, DecodeLaunch &d, DecodeLaunch &dp, DecodeLaunch &ds) {
   memset(&d, 0, sizeof(d));
   d.batch = a->batch;
   d.h_q = a->num_q_heads;
@@ -277,11 +272,49 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
   if (m) {
     d.tv = m->tv; d.bound_raw = m->bound_raw; d.meter = m->meter; d.log_a = m->log_a;
   }
-  char *w = static_cast<char *>(ws);
-  d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);
-  d.partials = reinterpret_cast<float *>(w + p.off_partials);
-  d.spill = (p.tv && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+  if (ws) {
+    char *w = static_cast<char *>(ws);
+    d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);
+    d.partials = reinterpret_cast<float *>(w + p.off_partials);
+    d.spill = (p.tv && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+  }
+  dp = d;
+  ds = d;
+  if (p.pre_chunks > 0) {
+    dp.region = region_dev(a->prefix, true);
+    dp.k_format = a->prefix.k_format;
+    dp.v_format = meter_only ? VF_NONE : a->prefix.v_format;
+    dp.n_chunks = p.pre_chunks;
+    dp.chunk_base = 0;
+  }
+  if (p.suf_chunks > 0) {
+    ds.region = region_dev(a->suffix, false);
+    ds.k_format = a->suffix.k_format;
+    ds.v_format = meter_only ? VF_NONE : a->suffix.v_format;
+    ds.n_chunks = p.suf_chunks;
+    ds.chunk_base = p.pre_chunks;
+  }
+}
 
+// Launches the per-chunk plan makes: one for both regions where the kernels
+// allow it (the cartridge page's one kernel over cartridge and live suffix),
+// else one per region.
+int chunk_launch_count(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch &ds) {
+  if (p.pre_chunks > 0 && p.suf_chunks > 0) return two_region_supported(dp, ds) ? 1 : 2;
+  return 1;
+}
+
+kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
+                      hipStream_t stream, bool meter_only) {
+  Plan p;
+  kvq_status s = make_plan(a, m, meter_only, p, !stream_capturing(stream));
+  if (s != KVQ_OK) return s;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
+
+  DecodeLaunch d, dp, ds;
+  chunk_launches(a, m, p, meter_only, ws, d, dp, ds);
   hipError_t e = hipSuccess;
   if (p.team) {
     const bool pre = p.prefix_len > 0;
@@ -302,22 +335,16 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     e = launch_decode_team(d, p.grid, stream);
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
   }
+  if (chunk_launch_count(p, dp, ds) == 1 && p.pre_chunks > 0 && p.suf_chunks > 0) {
+    e = launch_decode_two(dp, ds, stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+  }
   if (p.pre_chunks > 0) {
-    d.region = region_dev(a->prefix, true);
-    d.k_format = a->prefix.k_format;
-    d.v_format = meter_only ? VF_NONE : a->prefix.v_format;
-    d.n_chunks = p.pre_chunks;
-    d.chunk_base = 0;
-    e = launch_decode(d, stream);
+    e = launch_decode(dp, stream);
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
   }
   if (p.suf_chunks > 0) {
-    d.region = region_dev(a->suffix, false);
-    d.k_format = a->suffix.k_format;
-    d.v_format = meter_only ? VF_NONE : a->suffix.v_format;
-    d.n_chunks = p.suf_chunks;
-    d.chunk_base = p.pre_chunks;
-    e = launch_decode(d, stream);
+    e = launch_decode(ds, stream);
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
   }
   return KVQ_OK;
@@ -398,6 +425,14 @@ kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int m
   info->chunk = p.chunk;
   info->chunks = p.total_chunks;
   info->workspace_bytes = p.bytes;
+  if (p.team) {
+    info->launches = 1;
+  } else {
+    DecodeLaunch d, dp, ds;
+    chunk_launches(a, m, p, meter_only != 0, nullptr, d, dp, ds);
+    info->launches = chunk_launch_count(p, dp, ds);
+  }
+  info->reserved = 0;
   return KVQ_OK;
 }
 

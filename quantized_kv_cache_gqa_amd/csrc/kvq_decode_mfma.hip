@@ -1,609 +1,11 @@
-// Read path, matrix-core variant for GQA group 4: the per-token contractions
-// of the step run on MFMA, the softmax bookkeeping on the vector ALUs.
-//
-// Tiles of 16 tokens per wavefront step.
-//
-// Logits (v_mfma_f32_16x16x32_bf16): the tile's keys are the A operand (row i =
-// token i; lane l holds row l%16 and 8 consecutive k), the query is the B
-// operand with 16 columns j = 4h + p: head h in {0..3}, piece p of an exact
-// three-way bf16 split of the fp32 query (p = 3 is zero).  Summing the pieces
-// (two quad DPP adds) gives fp32-accurate logits for the four heads.  The
-// contraction over the 128 dims is permuted per lane group (lane group g reads
-// dims 32g..32g+31 as one contiguous row segment) and q is permuted the same
-// way.  Stored (FP8 -> bf16, exact) and exact (bf16) keys use the same B.
-// Witness dot (v_mfma_f32_16x16x16_f16): fp16 witness as A, a two-piece fp16
-// split of the scaled band norms as B, same column layout.
-//
-// After the piece sum lane 16g + 4h + p owns (token 4g + p, head h): its
-// stored-key logit, exact logit and c.  One exp per lane and accumulator
-// covers the tile.  The attention maximum is uniform per head (all tokens of a
-// head share the output accumulator) and moves only when a logit exceeds it by
-// more than 8 (log2 units).
-//
-// Output (FP8 values, v_mfma_f32_16x16x16_f16): A = the tile's weights
-// p~ * s_v in fp16 (row = head, k = token), B = the values in fp16 (exact for
-// E4M3).  Column j of N-tile n stands for dim 8j + n, so lane l loads bytes
-// 8j..8j+7 of four token rows (a contiguous 512-byte span per load across the
-// wavefront) and a byte transpose in registers (v_perm) forms, for each n, the
-// four tokens' bytes of dim 8j + n.  The 8 N-tiles accumulate the whole output
-// of the four heads (lanes 0..15 hold it).  BF16 values use vector-ALU FMAs.
+// Read path, matrix-core kernels for GQA group 4 (the tile loop and its
+// operand layouts are described in kvq_decode_mfma.h): the per-chunk kernel of
+// one region, and the persistent team kernel of the single-region TV case.
 #include <hip/hip_runtime.h>
 
-#include <type_traits>
-
-#include "kvq_decode_common.h"
+#include "kvq_decode_mfma.h"
 
 namespace kvq {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf16_round(float x) {
-  return __uint_as_float(f32_to_bf16_bits(x) << 16);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-
-// 8 E4M3 codes (two dwords) -> 8 bf16, exact.
-__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-  const bf16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
-}
-
-// 4 E4M3 codes (one dword) -> 4 fp16, exact.
-__device__ __forceinline__ f16x4_t fp8x4_to_f16(uint32_t w) {
-  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-  return f16x4_t{a[0], a[1], b[0], b[1]};
-}
-
-// Sum of the 4 lanes of a quad (every lane gets the same bits), then lane p
-// keeps register p: the value of (token 4g + p, head h).
-__device__ __forceinline__ float collapse(f32x4_t x, int p) {
-  float r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float t = x[i] + dpp<DPP_QUAD_XOR1>(x[i]);
-    r[i] = t + dpp<DPP_QUAD_XOR2>(t);
-  }
-  const float a01 = (p & 1) ? r[1] : r[0];
-  const float a23 = (p & 1) ? r[3] : r[2];
-  return (p & 2) ? a23 : a01;
-}
-
-// Byte transpose: t[e] = dword of token e (4 dims); out[n] = byte n of the four
-// tokens, token e in byte e.
-__device__ __forceinline__ void transpose4x4(const uint32_t t[4], uint32_t out[4]) {
-  const uint32_t a01 = __builtin_amdgcn_perm(t[1], t[0], 0x05010400u);  // t0b0 t1b0 t0b1 t1b1
-  const uint32_t a23 = __builtin_amdgcn_perm(t[1], t[0], 0x07030602u);  // t0b2 t1b2 t0b3 t1b3
-  const uint32_t b01 = __builtin_amdgcn_perm(t[3], t[2], 0x05010400u);
-  const uint32_t b23 = __builtin_amdgcn_perm(t[3], t[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(b01, a01, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(b01, a01, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(b23, a23, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(b23, a23, 0x07060302u);
-}
-
-// Two signed INT8 codes -> two bf16 (exact: |code| <= 127), packed.
-__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int byte0) {
-  const float a = (float)(int)(int8_t)(w >> (8 * byte0));
-  const float b = (float)(int)(int8_t)(w >> (8 * byte0 + 8));
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
-// The dither of 8 channels (two generator calls), split into two exact-sum
-// bf16 pieces of -xi: -xi = hi + lo + r with |r| <= 2^-18 |xi|.
-__device__ __forceinline__ void neg_dither8_bf16(uint32_t token, uint32_t g0, uint32_t tag, uint32_t stream,
-                                                 uint32_t k0, uint32_t k1, bf16x8_t &hi, bf16x8_t &lo) {
-  float xi[8];
-  dither4(token, g0, tag, stream, k0, k1, xi);
-  dither4(token, g0 + 1, tag, stream, k0, k1, xi + 4);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = -xi[e];
-    const float h = bf16_round(x);
-    hi[e] = (__bf16)h;
-    lo[e] = (__bf16)(x - h);
-  }
-}
-
-struct TileRegs {
-  uint4 k[4];      // FP8: k[0..1] = 32 codes; BF16: k[0..3] = 32 values
-  uint4 ke[4];     // exact keys (bf16), 32 values
-  uint2 wit;       // 4 witness bands (fp16)
-  uint2 v8[4];     // FP8 values: 8 dims of 4 tokens (MFMA B layout)
-  uint4 vb[4];     // BF16 values: 16 dims of 2 tokens (vector-ALU layout)
-  float ks, vs;    // scales of this lane's compact (token, head) slot
-};
-
-// Addressing of one (request, KV head) region range ending at c1, and the
-// loads of one 16-token tile.  Dense regions: one uniform base per tensor and
-// 32-bit per-lane row offsets (a request holds < 2^24 tokens); paged suffix:
-// per-token page lookup with 64-bit rows.  Rows are clamped to the last valid
-// token, so a tile past the end re-reads a valid row (its data is unused).
-template <int KF, int VF, bool PAGED>
-struct TileSrc {
-  using RowT = typename std::conditional<PAGED, size_t, uint32_t>::type;
-  const uint8_t *kb, *keb, *vbb;
-  const uint16_t *wb;
-  const float *ksb, *vsb;
-  const int32_t *ptab;
-  int pshift, page_size, h_kv, kvh, last;
-
-  __device__ __forceinline__ TileSrc(const DecodeLaunch &d, int b, int kvh_, int c1) {
-    const RegionDev &R = d.region;
-    const size_t sh = R.is_prefix ? (size_t)kvh_ : (size_t)b * d.h_kv + kvh_;
-    const size_t row0 = PAGED ? 0 : sh * (size_t)R.length;
-    ptab = PAGED ? R.page_table + (size_t)b * R.max_pages : nullptr;
-    pshift = R.page_size == 16 ? 4 : 3;      // page sizes 8 or 16
-    page_size = R.page_size;
-    h_kv = d.h_kv;
-    kvh = kvh_;
-    last = c1 - 1;
-    kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_BF16 ? 2 * D : D);
-    keb = (const uint8_t *)R.k_exact + row0 * (2 * D);
-    wb = R.witness + row0 * NB;
-    ksb = (const float *)R.k_scale + row0;
-    vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_BF16 ? 2 * D : D);
-    vsb = (const float *)R.v_scale + row0;
-  }
-
-  __device__ __forceinline__ RowT row_of(int t) const {   // row index relative to row0
-    t = min(t, last);
-    if constexpr (PAGED) {
-      const size_t pg = (size_t)ptab[t >> pshift];
-      return (pg * h_kv + kvh) * page_size + (t & (page_size - 1));
-    } else {
-      return (RowT)t;
-    }
-  }
-
-  __device__ __forceinline__ void load(TileRegs &T, int t0, bool exact, bool wit) const {
-    load_keys(T, t0, exact);
-    load_rest(T, t0, wit);
-  }
-
-  // stored and exact keys with the key scale (what the logits need first)
-  __device__ __forceinline__ void load_keys(TileRegs &T, int t0, bool exact) const {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
-    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
-    if constexpr (KF == KVQ_FMT_FP8_E4M3 || KF == KVQ_FMT_INT8_DITHER) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * D + 32 * g);
-      T.k[0] = p[0];
-      T.k[1] = p[1];
-      T.ks = KF == KVQ_FMT_FP8_E4M3 ? ksb[rk] : 1.0f;   // INT8: block scales ride on q
-    } else {
-      const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.k[i] = p[i];
-      T.ks = 1.0f;
-    }
-    if (exact) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(keb + ra * (2 * D) + 64 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.ke[i] = p[i];
-    }
-  }
-
-  // witness, values and the value scale
-  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit) const {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
-    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
-    if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
-    if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + row_of(t0 + 4 * g + e) * D + 8 * j16);
-      T.vs = VF == KVQ_FMT_FP8_E4M3 ? vsb[rk] : 1.0f;
-    } else if constexpr (VF == KVQ_FMT_BF16) {
-      const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
-      const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
-      const uint4 *p1 = reinterpret_cast<const uint4 *>(vbb + r1 * (2 * D) + 32 * (lane & 7));
-      T.vb[0] = p0[0]; T.vb[1] = p0[1];
-      T.vb[2] = p1[0]; T.vb[3] = p1[1];
-      T.vs = 1.0f;
-    }
-  }
-};
-
-// One (request, KV head) chunk [c0, c1) of one region, run by the whole
-// work-group (4 wavefronts, tiles of 16 tokens dealt round-robin): leaves each
-// wavefront's softmax states and output accumulator in part_s[wv].  The
-// (l~, l) pairs go to the spill: SPILL_LDS = the chunk's own LDS buffer
-// (entry 64 ((t0 - c0) / 16) + lane), else the group's workspace rows.
-//
-// FULL: TV and meter requested and this region holds exact bf16 keys and a
-// witness (the common quantized case).  Then every load of a tile is issued
-// unconditionally, which lets the compiler keep the next tile's loads in
-// flight across the current tile's math (no load sits under a runtime branch).
-template <int KF, int VF, bool PAGED, bool FULL, bool SPILL_LDS>
-__device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh, int grp, int c0,
-                                           int c1, float2 *spill_s, float (*w_s)[64],
-                                           float (*part_s)[4][PART_STRIDE]) {
-  constexpr int G = 4;
-  const RegionDev &R = d.region;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int g = lane >> 4, j16 = lane & 15, hh = j16 >> 2, pp = lane & 3;
-
-  const bool do_tv = FULL || d.has_tv != 0;
-  const bool do_meter = FULL || d.has_meter != 0;
-  const bool has_exact = FULL || R.exact_fmt == EX_BF16;
-  const bool has_wit = FULL || R.witness != nullptr;
-  const float qs = d.sm_scale * LOG2E;
-
-  // ---- B operands of the logit contractions, column j16 = 4 hh + pp
-  bf16x8_t bq[4];
-  f16x4_t bw;
-  {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = qp[32 * g + 8 * s + e] * qs;
-        const float hi = bf16_round(x);
-        const float mid = bf16_round(x - hi);
-        const float lo = bf16_round(x - hi - mid);
-        const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
-        bq[s][e] = (__bf16)piece;                   // exact: piece is a bf16 value
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int bb = 4 * g + e;
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = qp[4 * bb + i], c = qp[64 + 4 * bb + i];
-        ss += a * a + c * c;
-      }
-      const float qn = sqrtf(ss) * qs;
-      const _Float16 h1 = (_Float16)qn;
-      const _Float16 h2 = (_Float16)(qn - (float)h1);
-      bw[e] = pp == 0 ? h1 : (pp == 1 ? h2 : (_Float16)0.0f);
-    }
-  }
-
-  // INT8 (subtractive dither): x^ = s_c (code - xi) with s_c per 256-token
-  // block and channel.  The logits take the block's scales on the query side:
-  // bqs = exact three-way bf16 split of q_c s_c (log2 units), against the
-  // codes and the two pieces of -xi.  Values are dequantized to fp16.
-  constexpr bool I8K = KF == KVQ_FMT_INT8_DITHER;
-  constexpr bool I8V = VF == KVQ_FMT_INT8_DITHER;
-  bf16x8_t bqs[4];
-  float sv8[8];                                    // value scales of dims 8 j16 + n
-  uint32_t i8_stream = 0, i8_ktag = 0, i8_vtag = 0;
-  size_t i8_scale_row0 = 0;
-  if constexpr (I8K || I8V) {
-    const size_t sh = R.is_prefix ? (size_t)kvh : (size_t)b * d.h_kv + kvh;
-    i8_scale_row0 = sh * (size_t)((R.length + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK);
-    i8_stream = (uint32_t)(R.is_prefix ? R.stream_id : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
-    i8_ktag = dither_tag(0, R.layer, kvh);
-    i8_vtag = dither_tag(1, R.layer, kvh);
-  }
-  auto set_block = [&](int blk) {
-    const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
-    if constexpr (I8K) {
-      const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
-      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
-#pragma unroll
-      for (int s8 = 0; s8 < 4; ++s8) {
-        const uint4 sc = *reinterpret_cast<const uint4 *>(ks + 32 * g + 8 * s8);
-        const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = qp[32 * g + 8 * s8 + e] * qs * fp16_bits_to_f32((sw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          const float hi = bf16_round(x);
-          const float mid = bf16_round(x - hi);
-          const float lo = bf16_round(x - hi - mid);
-          const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
-          bqs[s8][e] = (__bf16)piece;
-        }
-      }
-    }
-    if constexpr (I8V) {
-      const uint4 sc = *reinterpret_cast<const uint4 *>((const uint16_t *)R.v_scale + srow + 8 * j16);
-      const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-      for (int n = 0; n < 8; ++n) sv8[n] = fp16_bits_to_f32((sw[n >> 1] >> (16 * (n & 1))) & 0xffffu);
-    }
-  };
-
-  const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
-  float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
-  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit); };
-
-  // per-lane accumulator states (lane = one (token slot, head) pair)
-  float mq = NEG_INF, zq = 0.0f;     // attention softmax, maximum uniform per head
-  float mm = NEG_INF, zm = 0.0f;     // l~ + c (Theorem 1's A)
-  float me = NEG_INF, ze = 0.0f;     // exact logits (TV normalizer)
-  // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
-  // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
-  f32x4_t ov[8];
-#pragma unroll
-  for (int n = 0; n < 8; ++n) ov[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int NACC = (VF == KVQ_FMT_BF16) ? G : 1;
-  float acc[NACC][16];
-#pragma unroll
-  for (int h = 0; h < NACC; ++h)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
-
-  auto process = [&](const TileRegs &T, int t0) {
-    // ---- logit contractions on the matrix cores
-    f32x4_t dq = {0.0f, 0.0f, 0.0f, 0.0f}, de = dq, dc = dq;
-    if constexpr (KF == KVQ_FMT_FP8_E4M3) {
-      const uint32_t w[8] = {T.k[0].x, T.k[0].y, T.k[0].z, T.k[0].w,
-                             T.k[1].x, T.k[1].y, T.k[1].z, T.k[1].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(w[2 * s], w[2 * s + 1]), bq[s], dq, 0, 0, 0);
-    } else if constexpr (I8K) {
-      // row j16 = token t0 + j16, slice s = channels 32 g + 8 s .. + 7
-      const uint32_t w[8] = {T.k[0].x, T.k[0].y, T.k[0].z, T.k[0].w,
-                             T.k[1].x, T.k[1].y, T.k[1].z, T.k[1].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 cw = {i8x2_to_bf16x2(w[2 * s], 0), i8x2_to_bf16x2(w[2 * s], 2),
-                          i8x2_to_bf16x2(w[2 * s + 1], 0), i8x2_to_bf16x2(w[2 * s + 1], 2)};
-        bf16x8_t xh, xl;
-        neg_dither8_bf16((uint32_t)(t0 + j16), (uint32_t)(8 * g + 2 * s), i8_ktag, i8_stream, R.seed_lo,
-                         R.seed_hi, xh, xl);
-        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], dq, 0, 0, 0);
-        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], dq, 0, 0, 0);
-        dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bqs[s], dq, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.k[s]), bq[s], dq, 0, 0, 0);
-    }
-    if (do_tv && has_exact) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) de = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.ke[s]), bq[s], de, 0, 0, 0);
-    }
-    if (do_meter && has_wit)
-      dc = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, T.wit), bw, dc, 0, 0, 0);
-
-    const int tk = t0 + 4 * g + pp;
-    const bool valid = tk < c1;
-    float lq = collapse(dq, pp) * T.ks;
-    float le = (do_tv && has_exact) ? collapse(de, pp) : lq;
-    const float cc = (do_meter && has_wit) ? collapse(dc, pp) : 0.0f;
-    if (!valid) {
-      lq = NEG_INF;
-      le = NEG_INF;
-    }
-    // spill entry of (tk, hh) is 64 (t0 / 16) + lane: one contiguous 512-byte store
-    if constexpr (SPILL_LDS) {
-      if (do_tv) spill_s[64 * ((t0 - c0) >> 4) + lane] = make_float2(lq, le);
-    } else {
-      if (do_tv && valid)
-        st_pair(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane), lq, le, d.total_chunks > 1);
-    }
-
-    // ---- attention softmax (maximum uniform per head)
-    if (__any(lq > mq + LAZY)) {
-      float mx = lq;
-      mx = fmaxf(mx, dpp<DPP_QUAD_XOR1>(mx));
-      mx = fmaxf(mx, dpp<DPP_QUAD_XOR2>(mx));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = mx > mq + LAZY ? mx : mq;
-      const float f = merge_factor(mq, mnew);
-      zq *= f;
-      float fh[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
-      if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ov[n][r] *= fh[r];
-      } else if constexpr (VF == KVQ_FMT_BF16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[h][i] *= fh[h];
-      }
-      mq = mnew;
-    }
-    const float p = valid ? fast_exp2(lq - mq) : 0.0f;
-    zq += p;
-    if (do_tv) {
-      if (le > me + LAZY) {
-        ze *= merge_factor(me, le);
-        me = le;
-      }
-      ze += valid ? fast_exp2(le - me) : 0.0f;
-    }
-    if (do_meter) {
-      const float y = lq + cc;
-      if (y > mm + LAZY) {
-        zm *= merge_factor(mm, y);
-        mm = y;
-      }
-      zm += valid ? fast_exp2(y - mm) : 0.0f;
-    }
-
-    // ---- output accumulation
-    if constexpr (VF == KVQ_FMT_FP8_E4M3) {
-      // weights to the A layout: lane (16 g' + h) needs tokens 4g'..4g'+3 of head h
-      w_s[wv][16 * hh + 4 * g + pp] = p * T.vs;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const float4 wa = *reinterpret_cast<const float4 *>(&w_s[wv][16 * (j16 & 3) + 4 * g]);
-      const bool arow = j16 < 4;
-      const f16x4_t aw = {(_Float16)(arow ? wa.x : 0.0f), (_Float16)(arow ? wa.y : 0.0f),
-                          (_Float16)(arow ? wa.z : 0.0f), (_Float16)(arow ? wa.w : 0.0f)};
-      const uint32_t lo[4] = {T.v8[0].x, T.v8[1].x, T.v8[2].x, T.v8[3].x};
-      const uint32_t hi[4] = {T.v8[0].y, T.v8[1].y, T.v8[2].y, T.v8[3].y};
-      uint32_t tl[4], th[4];
-      transpose4x4(lo, tl);
-      transpose4x4(hi, th);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        ov[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(aw, fp8x4_to_f16(tl[n]), ov[n], 0, 0, 0);
-        ov[n + 4] = __builtin_amdgcn_mfma_f32_16x16x16f16(aw, fp8x4_to_f16(th[n]), ov[n + 4], 0, 0, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    } else if constexpr (I8V) {
-      // as FP8, with weights p and values s_c (code - xi) in fp16
-      w_s[wv][16 * hh + 4 * g + pp] = p;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const float4 wa = *reinterpret_cast<const float4 *>(&w_s[wv][16 * (j16 & 3) + 4 * g]);
-      const bool arow = j16 < 4;
-      const f16x4_t aw = {(_Float16)(arow ? wa.x : 0.0f), (_Float16)(arow ? wa.y : 0.0f),
-                          (_Float16)(arow ? wa.z : 0.0f), (_Float16)(arow ? wa.w : 0.0f)};
-      f16x4_t vb[8];                               // vb[n][e]: token t0 + 4 g + e, dim 8 j16 + n
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float xi[8];
-        const uint32_t tok = (uint32_t)(t0 + 4 * g + e);
-        dither4(tok, (uint32_t)(2 * j16), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi);
-        dither4(tok, (uint32_t)(2 * j16 + 1), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi + 4);
-        const uint32_t cw[2] = {T.v8[e].x, T.v8[e].y};
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const float code = (float)(int)(int8_t)(cw[n >> 2] >> (8 * (n & 3)));
-          vb[n][e] = (_Float16)(sv8[n] * (code - xi[n]));
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < 8; ++n) ov[n] = __builtin_amdgcn_mfma_f32_16x16x16f16(aw, vb[n], ov[n], 0, 0, 0);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    } else if constexpr (VF == KVQ_FMT_BF16) {
-      w_s[wv][4 * (4 * g + pp) + hh] = p;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const float4 w0 = *reinterpret_cast<const float4 *>(&w_s[wv][4 * (lane >> 3)]);
-      const float4 w1 = *reinterpret_cast<const float4 *>(&w_s[wv][4 * ((lane >> 3) + 8)]);
-      const float wa[G] = {w0.x, w0.y, w0.z, w0.w};
-      const float wb[G] = {w1.x, w1.y, w1.z, w1.w};
-      const uint32_t a[8] = {T.vb[0].x, T.vb[0].y, T.vb[0].z, T.vb[0].w,
-                             T.vb[1].x, T.vb[1].y, T.vb[1].z, T.vb[1].w};
-      const uint32_t c[8] = {T.vb[2].x, T.vb[2].y, T.vb[2].z, T.vb[2].w,
-                             T.vb[3].x, T.vb[3].y, T.vb[3].z, T.vb[3].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][2 * i] = fmaf(wa[h], bf16_lo(a[i]), fmaf(wb[h], bf16_lo(c[i]), acc[h][2 * i]));
-          acc[h][2 * i + 1] = fmaf(wa[h], bf16_hi(a[i]), fmaf(wb[h], bf16_hi(c[i]), acc[h][2 * i + 1]));
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-  };
-
-  // two register sets, no copies: the loads of one tile overlap the other's
-  // math.  The next tile is always loaded (rows clamp to the last valid
-  // token, so past the end this re-reads a valid row and the data is unused).
-  TileRegs ta, tb;
-  if constexpr (I8K || I8V) {
-    // INT8: wavefront wv takes whole 256-token blocks wv, wv + 4, ... of the
-    // chunk, so the block operands change once per 16 tiles
-    const int blk0 = c0 / KVQ_INT8_BLOCK;
-    for (int blk = blk0 + wv; blk * KVQ_INT8_BLOCK < c1; blk += WAVES) {
-      const int tb0 = max(blk * KVQ_INT8_BLOCK, c0), tb1 = min((blk + 1) * KVQ_INT8_BLOCK, c1);
-      set_block(blk);
-      int t0 = tb0;
-      load_tile(ta, t0);
-      while (t0 < tb1) {
-        load_tile(tb, t0 + 16);
-        process(ta, t0);
-        t0 += 16;
-        if (t0 >= tb1) break;
-        load_tile(ta, t0 + 16);
-        process(tb, t0);
-        t0 += 16;
-      }
-    }
-  } else {
-    constexpr int STEP = 16 * WAVES;
-    int t0 = c0 + 16 * wv;
-    if (t0 < c1) load_tile(ta, t0);
-    while (t0 < c1) {
-      load_tile(tb, t0 + STEP);
-      process(ta, t0);
-      t0 += STEP;
-      if (t0 >= c1) break;
-      load_tile(ta, t0 + STEP);
-      process(tb, t0);
-      t0 += STEP;
-    }
-  }
-
-  // ---- wavefront merge: lanes of one head differ in bits 0, 1, 4, 5
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    if (off == 4 || off == 8) continue;
-    zq += __shfl_xor(zq, off);
-    if (do_meter) {
-      const float m2 = __shfl_xor(mm, off), z2 = __shfl_xor(zm, off);
-      const float m = fmaxf(mm, m2);
-      zm = zm * merge_factor(mm, m) + z2 * merge_factor(m2, m);
-      mm = m;
-    }
-    if (do_tv) {
-      const float m2 = __shfl_xor(me, off), z2 = __shfl_xor(ze, off);
-      const float m = fmaxf(me, m2);
-      ze = ze * merge_factor(me, m) + z2 * merge_factor(m2, m);
-      me = m;
-    }
-  }
-  if constexpr (VF == KVQ_FMT_BF16) {
-#pragma unroll
-    for (int off = 8; off < 64; off <<= 1)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
-  }
-
-  if (lane < 16 && pp == 0) {                      // lane 4h holds head h
-    part_s[wv][hh][0] = mq; part_s[wv][hh][1] = zq;
-    part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
-    part_s[wv][hh][4] = me; part_s[wv][hh][5] = ze;
-  }
-  if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
-    if (lane < 16) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part_s[wv][r][8 + 8 * lane + n] = ov[n][r];
-    }
-  } else if constexpr (VF == KVQ_FMT_BF16) {
-    if (lane < 8) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];
-    }
-  } else {
-    if (lane < 16) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part_s[wv][r][8 + 8 * lane + n] = 0.0f;
-    }
-  }
-}
 
 template <int KF, int VF, bool PAGED, bool FULL>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch d) {
@@ -611,17 +13,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
   const unsigned n_work = (unsigned)d.batch * d.h_kv * d.n_chunks;
   if (L >= n_work) return;
-  const int chunk_idx = (int)(L % (unsigned)d.n_chunks);
-  const int grp = (int)(L / (unsigned)d.n_chunks);
-  const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
-  const RegionDev &R = d.region;
-  const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
-  const int c0 = chunk_idx * d.chunk;
-  const int c1 = min(c0 + d.chunk, len);
   __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
   __shared__ float part_s[WAVES][4][PART_STRIDE];
-  mfma_chunk<KF, VF, PAGED, FULL, false>(d, b, kvh, grp, c0, c1, nullptr, w_s, part_s);
-  chunk_epilogue<4>(d, part_s, grp, chunk_idx, b, kvh);
+  chunk_work<KF, VF, PAGED, FULL>(d, (int)(L / (unsigned)d.n_chunks), (int)(L % (unsigned)d.n_chunks), w_s,
+                                  part_s);
 }
 
 // ----------------------------------------------------------------- teams

@@ -78,6 +78,9 @@ hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 bool mfma_path_supports(const DecodeLaunch &d);
 hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t stream);
 hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t stream);
+// One launch over both regions (d1: prefix, d2: suffix; same shared fields).
+bool two_region_supported(const DecodeLaunch &d1, const DecodeLaunch &d2);
+hipError_t launch_decode_two(const DecodeLaunch &d1, const DecodeLaunch &d2, hipStream_t stream);
 
 // Team launch (matrix-core path, one region, TV requested): chunk <=
 // TEAM_MAX_CHUNK tokens per member, each kept in LDS; at most TEAM_MAX

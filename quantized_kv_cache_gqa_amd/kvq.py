@@ -68,12 +68,13 @@ _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("team", c_int32), ("n_teams", c_int32), ("rounds", c_int32), ("grid", c_int32),
-                ("chunk", c_int32), ("chunks", c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("chunk", c_int32), ("chunks", c_int32), ("launches", c_int32), ("reserved", c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 2
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 3
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -134,6 +134,30 @@ def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
     if not torch.cuda.is_available():
         assert d.team == 0
     assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, None) == 1
+
+
+@pytest.mark.parametrize("suffix_k,suffix_v,launches", [
+    ("bf16", "bf16", 1),     # K16 cartridge + BF16 suffix: one launch
+    ("bf16", "fp8", 1),
+    ("fp8", "fp8", 2),       # key formats differ: one launch per region
+])
+def test_two_region_calls_take_one_launch_where_formats_allow(lib, monkeypatch, suffix_k, suffix_v, launches):
+    """A shared BF16-key prefix and a suffix: one kernel over both regions
+    when the key formats agree, else one per region; KVQ_DECODE_TWO=0 (a test
+    hook) forces one per region; a one-region call is one launch."""
+    monkeypatch.delenv("KVQ_DECODE_TWO", raising=False)
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    a = _args(batch=16, prefix=632, suffix=1024, kf=suffix_k, vf=suffix_v, exact=False, witness=False)
+    m = kvq.MeterOut()
+    for meter_only in (0, 1):
+        info = _plan(lib, a, m, meter_only)
+        assert (info.team, info.launches, info.reserved) == (0, launches, 0)
+        assert info.chunks >= 2
+    monkeypatch.setenv("KVQ_DECODE_TWO", "0")
+    assert _plan(lib, a, m).launches == 2
+    monkeypatch.delenv("KVQ_DECODE_TWO")
+    one = _args(batch=16, suffix=1024, kf=suffix_k, vf=suffix_v, exact=False, witness=False)
+    assert _plan(lib, one, m).launches == 1
 
 
 @pytest.mark.parametrize("mutate,status", [

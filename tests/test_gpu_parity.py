@@ -318,3 +318,46 @@ def test_graph_capture_takes_the_per_chunk_plan(gpu_lib, monkeypatch):
         assert torch.equal(o2, o_team)
         for k in m_team:
             assert torch.equal(m2[k], m_team[k]), k
+
+
+def _two_region_fp8(paged):
+    """A shared FP8 cartridge (exact keys, witness) before an FP8 suffix, both
+    with the TV and the meter: the one-launch form with the full meter."""
+    from workloads.configs import RegionCfg
+    base = small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=1504, lens=(1504, 700))
+    suf = dataclasses.replace(base.suffix, paged=paged, page_size=16)
+    pre = RegionCfg(length=700, k_fmt="fp8", v_fmt="fp8", exact_k=True, witness=True)
+    return dataclasses.replace(base, prefix=pre, suffix=suf, name=base.name + "-cartridge")
+
+
+TWO_REGION = {
+    "cfg1": lambda: CONFIGS[1],
+    "cfg2": SMALL["cfg2"],
+    "fp8": lambda: _two_region_fp8(False),
+    "fp8-paged": lambda: _two_region_fp8(True),
+}
+
+
+@pytest.mark.parametrize("name", list(TWO_REGION))
+def test_two_regions_in_one_launch(gpu_lib, monkeypatch, name):
+    """Cartridge + suffix in one launch (every chunk of either region may be the
+    last to arrive and merge): every cell against the oracle, and bitwise the
+    results of one launch per region, for the decode and the meter-only call."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_DECODE_TWO", raising=False)
+    cfg = TWO_REGION[name]()
+    case = GpuCase(cfg, page_seed=5)
+    split = 128
+    p = plan(case, split_tokens=split)
+    assert (p["team"], p["launches"]) == (0, 1), p
+    assert plan(case, split_tokens=split, meter_only=True)["launches"] == 1
+    o1, m1, _ = _all_cells(case, split_tokens=split)
+    _, q1 = case.run(split_tokens=split, meter_only=True)
+    monkeypatch.setenv("KVQ_DECODE_TWO", "0")
+    assert plan(case, split_tokens=split)["launches"] == 2
+    o2, m2 = case.run(split_tokens=split)
+    _, q2 = case.run(split_tokens=split, meter_only=True)
+    assert torch.equal(o1, o2)
+    for k in m1:
+        assert torch.equal(m1[k], m2[k]), k
+        assert torch.equal(q1[k], q2[k]), k
