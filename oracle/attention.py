@@ -19,6 +19,14 @@ softmax), and each of the G query heads q_h sharing that KV head:
                 largest float32 (Sec. 6.2.4: overflow to +inf is sound)
     meter = min(1, bound_raw)                              (Sec. 3 / Sec. 4.3)
 
+Tier B, the sub-Gaussian certificate of a subtractively dithered cache
+(WitCert Sec. 4.2, Lemma 2; the in-kernel form of Sec. 6.2.3):
+    var_t   = sm_scale^2 / 12 * sum_c q_c^2 s_{c,t}^2    (s: the key's dither step
+              of channel c at token t; 0 for exact keys)
+    u_t     = sqrt(2 var_t log(2 S / delta_loc))          (S tokens, joint over t)
+    log A_B = logsumexp(l~ + u) - logsumexp(l~)           (A_B = E_p~[e^u])
+    bound_b = 1/2 expm1(2 log A_B), meter_b = min(1, bound_b)  (Thm. 1 applied to u)
+
 Everything is evaluated in float64; nothing is split or reordered beyond what
 the definitions state.
 """
@@ -63,13 +71,29 @@ def bound_from_log_a(log_a) -> np.ndarray:
     return np.where(b > FLT_MAX, np.inf, b)
 
 
-def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float):
+def tier_b_radius(q, s_key, sm_scale: float, n_tokens: int, delta_loc: float) -> np.ndarray:
+    """u_{h,t} of WitCert Sec. 4.2: the radius that bounds the logit error of
+    a subtractively dithered key with probability >= 1 - delta_loc jointly
+    over n_tokens tokens (Lemma 2: the dither residual of step s is
+    sub-Gaussian with proxy s^2 / 12).
+
+    q: (G, d); s_key: (S, d) dither step per token and channel.  Returns (G, S).
+    """
+    q = np.asarray(q, np.float64)
+    s = np.asarray(s_key, np.float64)
+    var = (float(sm_scale) ** 2 / 12.0) * ((q * q) @ (s * s).T)
+    return np.sqrt(2.0 * var * math.log(2.0 * n_tokens / float(delta_loc)))
+
+
+def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delta_loc=None):
     """One (layer, request, KV head) cell.
 
     q: (G, d) query heads sharing this KV head (float32 values).
     k_exact, k_hat, v_hat: (S, d) exact keys, reconstructed keys and values.
     w16: (S, B) stored witness (float16) or None when the stored keys are the
          exact keys (then c = 0).
+    s_key, delta_loc: (S, d) dither steps of the stored keys and the failure
+         probability of Tier B; both given adds u, log_a_b, bound_b_raw, meter_b.
     Returns a dict of float64 arrays: out (G, d), out_exact (G, d), tv, log_a,
     bound_raw, meter (G,), plus the per-token logits and bounds for checks.
     """
@@ -93,9 +117,15 @@ def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float):
     log_a = logsumexp(l_tilde + c) - logsumexp(l_tilde)
     bound_raw = bound_from_log_a(log_a)
     meter = np.minimum(1.0, bound_raw)
-    return dict(out=out, out_exact=out_exact, tv=tv, log_a=log_a,
-                bound_raw=bound_raw, meter=meter, l_exact=l_exact,
-                l_tilde=l_tilde, c=c, p=p, p_tilde=pt)
+    res = dict(out=out, out_exact=out_exact, tv=tv, log_a=log_a,
+               bound_raw=bound_raw, meter=meter, l_exact=l_exact,
+               l_tilde=l_tilde, c=c, p=p, p_tilde=pt)
+    if s_key is not None and delta_loc is not None:
+        u = tier_b_radius(q, s_key, sm, l_tilde.shape[1], delta_loc)
+        log_a_b = logsumexp(l_tilde + u) - logsumexp(l_tilde)
+        bound_b = bound_from_log_a(log_a_b)
+        res.update(u=u, log_a_b=log_a_b, bound_b_raw=bound_b, meter_b=np.minimum(1.0, bound_b))
+    return res
 
 
 def kv_head_view(per_qhead: np.ndarray, group: int) -> np.ndarray:

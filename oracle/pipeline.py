@@ -70,8 +70,20 @@ def encode_region(k, v, spec: RegionSpec, kv_head: int) -> EncodedRegion:
     return EncodedRegion(kc, ks, vc, vs, w, w16, kh, vh, c1 + c2)
 
 
-def decode_cell(q, regions, sm_scale: float):
-    """regions: list of (k_exact, EncodedRegion, RegionSpec) in logical order."""
+def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray:
+    """(n, d) dither step of the stored keys per token and channel: the
+    block's scale for INT8 (WitCert Sec. 4.2: the residual is uniform on
+    [-s/2, s/2]), 0 for keys stored exactly (BF16).  FP8 keys have no dither."""
+    if spec.k_fmt == "int8":
+        return np.asarray(enc.k_scale, np.float64)[np.arange(n) // quant.BLOCK]
+    if spec.k_fmt == "bf16":
+        return np.zeros((n, np.asarray(enc.k_hat).shape[1]))
+    raise ValueError("Tier B needs dithered INT8 keys or keys stored exactly")
+
+
+def decode_cell(q, regions, sm_scale: float, delta_loc=None):
+    """regions: list of (k_exact, EncodedRegion, RegionSpec) in logical order.
+    delta_loc: Tier B's failure probability (None: Tier B not computed)."""
     ke = np.concatenate([np.asarray(r[0], np.float64) for r in regions])
     kh = np.concatenate([r[1].k_hat for r in regions])
     vh = np.concatenate([r[1].v_hat for r in regions])
@@ -85,6 +97,10 @@ def decode_cell(q, regions, sm_scale: float):
     ke_used = np.concatenate([
         np.asarray(r[0], np.float64) if r[2].exact_k else r[1].k_hat
         for r in regions])
-    res = attention.decode_step(q, ke_used, kh, vh, w16, sm_scale)
+    s_key = None
+    if delta_loc is not None:
+        s_key = np.concatenate([key_dither_steps(r[1], r[2], np.asarray(r[0]).shape[0])
+                                for r in regions])
+    res = attention.decode_step(q, ke_used, kh, vh, w16, sm_scale, s_key=s_key, delta_loc=delta_loc)
     res["k_exact_all"] = ke
     return res
