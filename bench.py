@@ -245,13 +245,28 @@ def measure_workload(idx: int, reps: int, warmup: int):
         e1.record(stream)
     torch.cuda.synchronize()
     off_ms = sorted(e0.elapsed_time(e1) for e0, e1 in off_evs)[reps // 2]
+    # with Tier B as well (dithered INT8 keys: the sub-Gaussian certificate)
+    tier_b_ms = None
+    if sf.k_fmt == "int8":
+        tb = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev) for k in ("log_a_b", "bound_b_raw", "meter_b")}
+        meter_b = kvq.MeterOut(**{k: v.data_ptr() for k, v in list(mbuf.items()) + list(tb.items())}, delta_b=1e-9)
+        info_b = kvq.PlanInfo()
+        assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter_b), 0, ctypes.byref(info_b)) == 0
+        assert info_b.workspace_bytes <= ws.numel()
+        b_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in b_evs:
+            e0.record(stream)
+            assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(meter_b), ws.data_ptr(), ws.numel(), sp) == 0
+            e1.record(stream)
+        torch.cuda.synchronize()
+        tier_b_ms = sorted(e0.elapsed_time(e1) for e0, e1 in b_evs)[reps // 2]
     plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
             if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
     print(json.dumps({
         "workload": f"config {idx}: {cfg.description}",
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
-        "meter_off_launch_ms": off_ms,
+        "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS},
         "plan": plan}), flush=True)

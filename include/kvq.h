@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -133,12 +133,31 @@ typedef struct kvq_attn_args {
  *   tv        = 1/2 sum_t |p_t - p~_t|, p from exact keys, p~ from stored keys
  *   log_a     = log E_p~[e^{c_t}],  c_t = sm_scale * sum_b ||q_b|| w_{t,b}
  *   bound_raw = 1/2 (A^2 - 1), +inf when beyond the float range
- *   meter     = min(1, bound_raw) */
+ *   meter     = min(1, bound_raw)
+ * Tier B (WitCert Sec. 4.2, Lemma 2; Sec. 6.2.3): the sub-Gaussian certificate
+ * of subtractively dithered INT8 keys, from the stored scales and the query
+ * alone (no witness).  Requesting any of its outputs needs delta_b in (0, 1)
+ * and, in every region present, INT8-dithered keys or keys stored as BF16
+ * (radius 0); other key formats return KVQ_ERR_UNSUPPORTED.
+ *   u_t         = sqrt(2 var_t log(2 S / delta_b)),
+ *                 var_t = sm_scale^2 / 12 * sum_c q_c^2 s_{c,t}^2 (s: the key's
+ *                 block scale of channel c), S = the request's tokens
+ *   log_a_b     = log E_p~[e^{u_t}]
+ *   bound_b_raw = 1/2 (A_B^2 - 1), +inf when beyond the float range
+ *   meter_b     = min(1, bound_b_raw)
+ * TV <= bound_b_raw holds with probability >= 1 - delta_b jointly over the S
+ * tokens for a query that does not depend on the stored dither (a
+ * non-adaptive query); delta_b is the per-(layer, head, step) share of a
+ * request's budget, delta_req / (layers * heads * steps). */
 typedef struct kvq_meter_out {
   float *tv;
   float *bound_raw;
   float *meter;
   float *log_a;
+  float *log_a_b;
+  float *bound_b_raw;
+  float *meter_b;
+  double delta_b;
 } kvq_meter_out;
 
 /* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store

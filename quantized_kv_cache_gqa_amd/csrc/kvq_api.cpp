@@ -2,6 +2,7 @@
 // layout and kernel launches.  Nothing here touches device memory directly.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -34,7 +35,7 @@ inline bool is_store_fmt(int f) {
 struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
   int prefix_len = 0, suffix_cap = 0;
-  bool tv = false, meter = false, wit_any = false;
+  bool tv = false, meter = false, wit_any = false, tier_b = false;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
 };
@@ -72,7 +73,7 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || a->split_tokens != 0 || p.group != 4) return false;
+  if (!p.tv || p.tier_b || a->split_tokens != 0 || p.group != 4) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -204,6 +205,19 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
     p.tv = m->tv && any_exact;
     p.meter = (m->bound_raw || m->meter || m->log_a) && p.wit_any;
+    const void *mb[] = {m->log_a_b, m->bound_b_raw, m->meter_b};
+    for (const void *x : mb)
+      if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
+    p.tier_b = m->log_a_b || m->bound_b_raw || m->meter_b;
+    if (p.tier_b) {
+      // WitCert Sec. 4.2: a probability, and keys whose residual is the
+      // uniform dither residual (INT8) or zero (BF16)
+      if (!(m->delta_b > 0.0 && m->delta_b < 1.0)) return KVQ_ERR_SHAPE;
+      if (p.prefix_len > 0 && a->prefix.k_format != KVQ_FMT_INT8_DITHER && a->prefix.k_format != KVQ_FMT_BF16)
+        return KVQ_ERR_UNSUPPORTED;
+      if (p.suffix_cap > 0 && a->suffix.k_format != KVQ_FMT_INT8_DITHER && a->suffix.k_format != KVQ_FMT_BF16)
+        return KVQ_ERR_UNSUPPORTED;
+    }
   }
   if (allow_team && plan_team(a, meter_only, groups, p)) return KVQ_OK;
   p.off_counters = 0;
@@ -271,7 +285,10 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   d.has_wit_any = p.wit_any;
   if (m) {
     d.tv = m->tv; d.bound_raw = m->bound_raw; d.meter = m->meter; d.log_a = m->log_a;
+    d.log_a_b = m->log_a_b; d.bound_b_raw = m->bound_b_raw; d.meter_b = m->meter_b;
   }
+  d.has_tier_b = p.tier_b;
+  d.tier_b_log_inv_delta = p.tier_b ? (float)-log(m->delta_b) : 0.0f;
   if (ws) {
     char *w = static_cast<char *>(ws);
     d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);

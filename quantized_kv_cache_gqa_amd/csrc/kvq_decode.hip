@@ -58,6 +58,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   const bool do_meter = d.has_meter != 0;
   const bool has_exact = R.exact_fmt != EX_NONE;
   const bool has_wit = R.witness != nullptr;
+  // Tier B (WitCert Sec. 4.2): zb accumulates p~ e^{u} on the attention's
+  // maximum, tb_l = log(2 S / delta) with S the request's tokens
+  const bool do_b = d.has_tier_b != 0;
+  float tb_l = 0.0f;
+  if (do_b) {
+    const int sl = d.suffix_cap > 0
+                       ? (d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap)
+                       : 0;
+    tb_l = logf(2.0f * (float)(d.prefix_len + sl)) + d.tier_b_log_inv_delta;
+  }
 
   // query rows of this KV head, pre-scaled into log2 units
   const float qs = d.sm_scale * LOG2E;
@@ -88,12 +98,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     }
   }
 
-  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G];
+  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G];
   float acc[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mq[h] = mm[h] = me[h] = NEG_INF;
-    zq[h] = zm[h] = ze[h] = 0.0f;
+    zq[h] = zm[h] = ze[h] = zb[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
   }
@@ -180,6 +190,35 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         st_pair(spill_g + 2 * spill_entry<G>(t, h), lq[h], le[h], d.total_chunks > 1);
     }
 
+    // ---- Tier B radius of this token: u log2(e) = sqrt(sum_c (q_c s_c)^2 tb_l / 6)
+    //      in log2 units (INT8 keys: s = the block's scale; other keys: u = 0)
+    float eub[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) eub[h] = 1.0f;
+    if constexpr (KF == KVQ_FMT_INT8_DITHER) {
+      if (do_b) {
+        float sc[16];
+        const uint4 *sp = reinterpret_cast<const uint4 *>(ksc8 + 16 * j);
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+          const uint4 w = sp[v4];
+          const uint32_t sw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc[8 * v4 + i] = fp16_bits_to_f32((sw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = qv[h][i] * sc[i];
+            ss = fmaf(x, x, ss);
+          }
+          eub[h] = exp2f(sqrtf(sum8(ss) * tb_l * (1.0f / 6.0f)));
+        }
+      }
+    }
+
     // ---- online accumulators
     float p[G];
 #pragma unroll
@@ -188,12 +227,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       if (x > mq[h] + LAZY) {
         const float f = merge_factor(mq[h], x);
         zq[h] *= f;
+        zb[h] *= f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[h][i] *= f;
         mq[h] = x;
       }
       p[h] = valid ? fast_exp2(x - mq[h]) : 0.0f;
       zq[h] += p[h];
+      if (do_b) zb[h] = fmaf(p[h], eub[h], zb[h]);
     }
     if (do_meter) {
 #pragma unroll
@@ -247,6 +288,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         const float m = fmaxf(mq[h], m2);
         const float f1 = merge_factor(mq[h], m), f2 = merge_factor(m2, m);
         zq[h] = zq[h] * f1 + z2 * f2;
+        if (do_b) zb[h] = zb[h] * f1 + __shfl_xor(zb[h], off) * f2;
         if constexpr (VF != VF_NONE) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[h][i] = acc[h][i] * f1 + __shfl_xor(acc[h][i], off) * f2;
@@ -277,6 +319,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         part_s[wv][h][0] = mq[h]; part_s[wv][h][1] = zq[h];
         part_s[wv][h][2] = mm[h]; part_s[wv][h][3] = zm[h];
         part_s[wv][h][4] = me[h]; part_s[wv][h][5] = ze[h];
+        part_s[wv][h][6] = zb[h];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];

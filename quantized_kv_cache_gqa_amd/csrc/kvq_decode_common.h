@@ -120,8 +120,8 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
   }
 }
 
-// Per-wavefront states are in part_s[w][h][...] (m~, z~, m', z', m_e, z_e, -, -,
-// acc[128]).  Merges the wavefronts into this chunk's partial.  When the group
+// Per-wavefront states are in part_s[w][h][...] (m~, z~, m', z', m_e, z_e,
+// z_b, -, acc[128]); z_b (Tier B's sum of p~ e^u) and acc share m~.  Merges the wavefronts into this chunk's partial.  When the group
 // (b, kvh) has several chunks, the partial goes to the workspace and the
 // arrival is counted; the last arrival runs the finalize over all partials.  A
 // group with a single chunk finalizes from LDS directly (no cross-work-group
@@ -144,8 +144,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
                          : d.partials + ((size_t)grp * total_chunks + d.chunk_base + chunk_idx) * G * PART_STRIDE;
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if (k == 6 || k == 7) continue;
-    const int mk = (k >= 8) ? 0 : (k & ~1);          // which maximum governs this field
+    if (k == 7 || (k == 6 && !d.has_tier_b)) continue;
+    const int mk = (k >= 6) ? 0 : (k & ~1);          // which maximum governs this field
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
@@ -193,11 +193,12 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       Mm = fmaxf(Mm, rd(pc + 2));
       Me = fmaxf(Me, rd(pc + 4));
     }
-    float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
       const float fq = merge_factor(rd(pc + 0), Mq);
       Zq += rd(pc + 1) * fq;
+      if (d.has_tier_b) Zb += rd(pc + 6) * fq;
       Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
       Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
       o0 += rd(pc + 8 + lane) * fq;
@@ -218,6 +219,15 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       if (d.log_a) d.log_a[qh] = (float)log_a;
       if (d.bound_raw) d.bound_raw[qh] = bf;
       if (d.meter) d.meter[qh] = fminf(1.0f, bf);
+      if (d.has_tier_b) {
+        // log A_B = log(sum p~ e^u / sum p~), both sums on the maximum M~
+        const double log_ab = (Zq > 0.0f && Zb > 0.0f) ? log((double)Zb) - log((double)Zq) : 0.0;
+        const double bb = 0.5 * expm1(2.0 * log_ab);
+        const float bbf = bb > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bb;
+        if (d.log_a_b) d.log_a_b[qh] = (float)log_ab;
+        if (d.bound_b_raw) d.bound_b_raw[qh] = bbf;
+        if (d.meter_b) d.meter_b[qh] = fminf(1.0f, bbf);
+      }
       fin_s[h][0] = Mq;
       fin_s[h][1] = Zq > 0.0f ? 1.0f / Zq : 0.0f;
       fin_s[h][2] = Me;

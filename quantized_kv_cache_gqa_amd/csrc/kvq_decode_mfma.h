@@ -241,6 +241,18 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   const bool has_exact = FULL || R.exact_fmt == EX_BF16;
   const bool has_wit = FULL || R.witness != nullptr;
   const float qs = d.sm_scale * LOG2E;
+  // Tier B (WitCert Sec. 4.2): zb accumulates p~ e^{u} on the attention's
+  // maximum.  tb_l = log(2 S / delta) with S the request's tokens (both
+  // regions); eub = e^{u} of this lane's head, constant over a 256-token
+  // block of INT8 keys and 1 for keys stored as BF16 (u = 0).
+  const bool do_b = d.has_tier_b != 0;
+  float tb_l = 0.0f, eub = 1.0f;
+  if (do_b) {
+    const int sl = d.suffix_cap > 0
+                       ? (d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap)
+                       : 0;
+    tb_l = logf(2.0f * (float)(d.prefix_len + sl)) + d.tier_b_log_inv_delta;
+  }
 
   // ---- B operands of the logit contractions, column j16 = 4 hh + pp
   bf16x8_t bq[4];
@@ -297,6 +309,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     if constexpr (I8K) {
       const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
       const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+      float ss = 0.0f;                             // sum of (q_c s_c)^2 in log2 units
 #pragma unroll
       for (int s8 = 0; s8 < 4; ++s8) {
         const uint4 sc = *reinterpret_cast<const uint4 *>(ks + 32 * g + 8 * s8);
@@ -304,12 +317,20 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = qp[32 * g + 8 * s8 + e] * qs * fp16_bits_to_f32((sw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          ss = fmaf(x, x, ss);
           const float hi = bf16_round(x);
           const float mid = bf16_round(x - hi);
           const float lo = bf16_round(x - hi - mid);
           const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
           bqs[s8][e] = (__bf16)piece;
         }
+      }
+      if (do_b) {
+        // lanes 16 g + 4 hh + pp hold channels 32 g .. 32 g + 31 of head hh;
+        // u log2(e) = sqrt(2 var log(2S/delta)) log2(e) = sqrt(ss tb_l / 6)
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        eub = exp2f(sqrtf(ss * tb_l * (1.0f / 6.0f)));
       }
     }
     if constexpr (I8V) {
@@ -328,6 +349,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   float mq = NEG_INF, zq = 0.0f;     // attention softmax, maximum uniform per head
   float mm = NEG_INF, zm = 0.0f;     // l~ + c (Theorem 1's A)
   float me = NEG_INF, ze = 0.0f;     // exact logits (TV normalizer)
+  float zb = 0.0f;                   // Tier B: sum p~ e^u on the attention maximum
   // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
   // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
   f32x4_t ov[8];
@@ -402,6 +424,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       const float mnew = mx > mq + LAZY ? mx : mq;
       const float f = merge_factor(mq, mnew);
       zq *= f;
+      zb *= f;
       float fh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
@@ -420,6 +443,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
     const float p = valid ? fast_exp2(lq - mq) : 0.0f;
     zq += p;
+    if (do_b) zb = fmaf(p, eub, zb);
     if (do_tv) {
       if (le > me + LAZY) {
         ze *= merge_factor(me, le);
@@ -556,6 +580,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   for (int off = 1; off < 64; off <<= 1) {
     if (off == 4 || off == 8) continue;
     zq += __shfl_xor(zq, off);
+    if (do_b) zb += __shfl_xor(zb, off);
     if (do_meter) {
       const float m2 = __shfl_xor(mm, off), z2 = __shfl_xor(zm, off);
       const float m = fmaxf(mm, m2);
@@ -582,6 +607,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][0] = mq; part_s[wv][hh][1] = zq;
     part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
     part_s[wv][hh][4] = me; part_s[wv][hh][5] = ze;
+    part_s[wv][hh][6] = zb;
   }
   if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
     if (lane < 16) {

@@ -61,6 +61,9 @@ struct DecodeLaunch {
   const int32_t *suffix_lengths;// for the finalize (nullable: all = suffix_cap)
   int has_tv, has_meter, has_out, has_wit_any;
   float *tv, *bound_raw, *meter, *log_a;
+  float *log_a_b, *bound_b_raw, *meter_b;   // Tier B outputs (nullable)
+  int has_tier_b;               // Tier B requested: accumulate E_p~[e^u] (partial field 6)
+  float tier_b_log_inv_delta;   // log(1 / delta_b)
   uint32_t *counters;
   float *partials;
   float *spill;

@@ -104,21 +104,24 @@ class GpuCase:
                               page_size=ps, use_witness=st.witness is not None)
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
-            workspace=None):
+            workspace=None, tier_b_delta=None):
         out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
                                       self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
-                                      meter=meter, meter_only=meter_only, workspace=workspace)
+                                      meter=meter, meter_only=meter_only, workspace=workspace,
+                                      tier_b_delta=tier_b_delta)
         torch.cuda.synchronize()
         return out, m
 
 
-def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False) -> dict:
+def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None) -> dict:
     return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
-                         sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only)
+                         sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only,
+                         tier_b_delta=tier_b_delta)
 
 
-def oracle_cell(case: GpuCase, b: int, kvh: int):
-    """The oracle's view of cell (b, kvh): encoded regions and the decode result."""
+def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
+    """The oracle's view of cell (b, kvh): encoded regions and the decode result
+    (with Tier B when tier_b_delta is given)."""
     cfg, inp, layer = case.cfg, case.inp, case.layer
     G = cfg.group
     q = inp["q"][b, kvh * G:(kvh + 1) * G].double().cpu().numpy()
@@ -146,7 +149,7 @@ def oracle_cell(case: GpuCase, b: int, kvh: int):
     enc = encode_region(k, v, spec, kvh)
     regions.append((k, enc, spec))
     encs["suffix"] = enc
-    return encs, decode_cell(q, regions, SM_SCALE)
+    return encs, decode_cell(q, regions, SM_SCALE, delta_loc=tier_b_delta)
 
 
 def _bits(t: torch.Tensor) -> np.ndarray:
@@ -223,4 +226,17 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
             mg = float(meter["meter"][b, qh])
             assert abs(mg - float(ref["meter"][h])) <= TOL_METER
             worst["meter"] = max(worst["meter"], abs(mg - float(ref["meter"][h])))
+        if "bound_b_raw" in meter:
+            # Tier B: the same bar as Tier A (log A and bound within 1e-5,
+            # relative above 1; meter within 1e-5)
+            la = float(meter["log_a_b"][b, qh])
+            assert abs(la - float(ref["log_a_b"][h])) <= TOL_METER * max(1.0, abs(float(ref["log_a_b"][h]))), \
+                (b, qh, la, ref["log_a_b"][h])
+            bg, br = float(meter["bound_b_raw"][b, qh]), float(ref["bound_b_raw"][h])
+            if math.isinf(br) or math.isinf(bg):
+                assert math.isinf(br) == math.isinf(bg)
+            else:
+                assert abs(bg - br) / max(1.0, br) <= TOL_METER, (b, qh, bg, br)
+            assert abs(float(meter["meter_b"][b, qh]) - float(ref["meter_b"][h])) <= TOL_METER
+            worst["bound_b"] = max(worst.get("bound_b", 0.0), abs(bg - br) / max(1.0, br))
     return worst

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 3
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 4
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -158,6 +158,29 @@ def test_two_region_calls_take_one_launch_where_formats_allow(lib, monkeypatch, 
     monkeypatch.delenv("KVQ_DECODE_TWO")
     one = _args(batch=16, suffix=1024, kf=suffix_k, vf=suffix_v, exact=False, witness=False)
     assert _plan(lib, one, m).launches == 1
+
+
+def test_tier_b_arguments_are_checked(lib, monkeypatch):
+    """Tier B needs a failure probability in (0, 1) and keys whose residual is
+    the dither's (INT8) or zero (BF16); FP8 keys are rejected, never metered
+    with the wrong proxy.  A Tier B call never takes the team plan."""
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    good = _args(batch=8, suffix=32768, kf="int8", vf="int8")
+    bad = _args(batch=8, suffix=32768, kf="fp8", vf="fp8")
+    mk = lambda delta: kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE,
+                                    log_a_b=FAKE, bound_b_raw=FAKE, meter_b=FAKE, delta_b=delta)
+    assert _plan(lib, good, mk(1e-6)).team == 0
+    for delta, status in ((0.0, 2), (1.0, 2), (-1e-3, 2), (float("nan"), 2)):
+        info = kvq.PlanInfo()
+        assert lib.kvq_decode_plan(ctypes.byref(good), ctypes.byref(mk(delta)), 0, ctypes.byref(info)) == status
+    info = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(bad), ctypes.byref(mk(1e-6)), 0, ctypes.byref(info)) == 5
+    assert lib.kvq_decode_attn(ctypes.byref(bad), ctypes.byref(mk(1e-6)), FAKE, 1 << 40, None) == 5
+    two = _args(batch=8, prefix=632, suffix=4096, kf="int8", vf="int8")   # BF16 prefix keys: allowed
+    assert _plan(lib, two, mk(1e-6)).chunks >= 2
+    m_misaligned = mk(1e-6)
+    m_misaligned.meter_b = FAKE + 4
+    assert lib.kvq_decode_plan(ctypes.byref(good), ctypes.byref(m_misaligned), 0, ctypes.byref(info)) == 4
 
 
 @pytest.mark.parametrize("mutate,status", [

@@ -18,13 +18,13 @@ from workloads import CONFIGS, small_variant
 pytestmark = pytest.mark.gpu
 
 
-def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False):
+def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False, tier_b_delta=None):
     cfg = case.cfg
-    out, m = case.run(split_tokens=split_tokens, meter_only=meter_only)
+    out, m = case.run(split_tokens=split_tokens, meter_only=meter_only, tier_b_delta=tier_b_delta)
     cells = cells or [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
     worst = {}
     for b, kvh in cells:
-        encs, ref = oracle_cell(case, b, kvh)
+        encs, ref = oracle_cell(case, b, kvh, tier_b_delta=tier_b_delta)
         check_stored(case, b, kvh, encs)
         w = check_results(case, out, m, b, kvh, ref, check_out=check_out and not meter_only)
         for k, v in w.items():
@@ -361,3 +361,44 @@ def test_two_regions_in_one_launch(gpu_lib, monkeypatch, name):
     for k in m1:
         assert torch.equal(m1[k], m2[k]), k
         assert torch.equal(q1[k], q2[k]), k
+
+
+def _tier_b_two_region():
+    """A BF16 shared prefix (radius 0) before a dithered INT8 suffix: two
+    launches, one per key format, both accumulating E_p~[e^u]."""
+    from workloads.configs import RegionCfg
+    base = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=700, lens=(700, 300))
+    pre = RegionCfg(length=300, k_fmt="bf16", v_fmt="bf16", exact_k=False, witness=False)
+    return dataclasses.replace(base, prefix=pre, name=base.name + "-bf16-cartridge")
+
+
+TIER_B = {
+    "cfg4": SMALL["cfg4"],
+    "cfg4-long": lambda: small_variant(CONFIGS[4], batch=1, h_kv=2, suffix_len=3000, lens=(2900,)),
+    "cfg2-bf16": SMALL["cfg2"],
+    "bf16-int8": _tier_b_two_region,
+}
+
+
+@pytest.mark.parametrize("name", list(TIER_B))
+@pytest.mark.parametrize("delta", [1e-3, 1e-9])
+def test_tier_b_certificate_every_cell(gpu_lib, kernel, name, delta):
+    """Tier B (WitCert Sec. 4.2) on every cell against the oracle: log A_B,
+    bound and meter within 1e-5; Tier A, TV and the output unchanged; the team
+    launch is never planned with Tier B; TV <= bound_B on these (non-adaptive)
+    queries."""
+    cfg = TIER_B[name]()
+    case = GpuCase(cfg, page_seed=2)
+    assert plan(case, tier_b_delta=delta)["team"] == 0
+    split = 256 if name == "cfg4-long" else 0
+    out, m, worst = _all_cells(case, split_tokens=split, tier_b_delta=delta)
+    assert "bound_b" in worst
+    if cfg.suffix.k_fmt == "bf16" and (cfg.prefix is None or cfg.prefix.k_fmt == "bf16"):
+        assert torch.all(m["log_a_b"] == 0) and torch.all(m["bound_b_raw"] == 0)
+    else:
+        assert torch.all(m["log_a_b"] > 0)
+    assert torch.all(m["tv"] <= m["bound_b_raw"])
+    out2, m2 = case.run(split_tokens=split)
+    assert torch.equal(out, out2)
+    for k in m2:
+        assert torch.equal(m[k], m2[k]), k
