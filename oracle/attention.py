@@ -27,6 +27,15 @@ Tier B, the sub-Gaussian certificate of a subtractively dithered cache
     log A_B = logsumexp(l~ + u) - logsumexp(l~)           (A_B = E_p~[e^u])
     bound_b = 1/2 expm1(2 log A_B), meter_b = min(1, bound_b)  (Thm. 1 applied to u)
 
+Value side and the joint output bound (WitCert Sec. 3 and Sec. 4.2 "Value
+side and the joint event"), with rho_t = ||v^_t - v_t|| and ||v_t|| stored per
+token (rounded up):
+    value_err  = sum_t p~_t rho_t
+    v_norm_max = max_t ||v_t||
+    out_bound  = 2 meter v_norm_max + value_err  >= ||y - y^||,
+                 y = sum_t p_t v_t (exact keys and values), y^ = out
+  (meter = min(1, bound_raw) bounds TV; with keys stored exactly TV = 0).
+
 Everything is evaluated in float64; nothing is split or reordered beyond what
 the definitions state.
 """
@@ -85,7 +94,8 @@ def tier_b_radius(q, s_key, sm_scale: float, n_tokens: int, delta_loc: float) ->
     return np.sqrt(2.0 * var * math.log(2.0 * n_tokens / float(delta_loc)))
 
 
-def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delta_loc=None):
+def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delta_loc=None,
+                v_rec=None):
     """One (layer, request, KV head) cell.
 
     q: (G, d) query heads sharing this KV head (float32 values).
@@ -94,6 +104,8 @@ def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delt
          exact keys (then c = 0).
     s_key, delta_loc: (S, d) dither steps of the stored keys and the failure
          probability of Tier B; both given adds u, log_a_b, bound_b_raw, meter_b.
+    v_rec: (S, 2) stored value records (rho, ||v||); adds value_err,
+         v_norm_max and out_bound.
     Returns a dict of float64 arrays: out (G, d), out_exact (G, d), tv, log_a,
     bound_raw, meter (G,), plus the per-token logits and bounds for checks.
     """
@@ -125,6 +137,12 @@ def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delt
         log_a_b = logsumexp(l_tilde + u) - logsumexp(l_tilde)
         bound_b = bound_from_log_a(log_a_b)
         res.update(u=u, log_a_b=log_a_b, bound_b_raw=bound_b, meter_b=np.minimum(1.0, bound_b))
+    if v_rec is not None:
+        rec = np.asarray(v_rec, np.float64)
+        value_err = pt @ rec[:, 0]
+        v_norm_max = float(np.max(rec[:, 1])) if rec.shape[0] else 0.0
+        res.update(value_err=value_err, v_norm_max=np.full(value_err.shape, v_norm_max),
+                   out_bound=2.0 * meter * v_norm_max + value_err)
     return res
 
 

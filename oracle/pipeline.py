@@ -29,6 +29,7 @@ class RegionSpec:
     stream: int = 0           # dither stream id of this (region, request)
     witness: bool = True      # store/use a witness for the keys
     exact_k: bool = True      # the exact keys are available for TV
+    value_witness: bool = False   # store/use the value record (rho, ||v||)
 
 
 @dataclass
@@ -42,6 +43,7 @@ class EncodedRegion:
     k_hat: np.ndarray
     v_hat: np.ndarray
     clipped: int
+    v_rec: Optional[np.ndarray] = None   # float16 (T, 2): rho, ||v||
 
 
 def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int):
@@ -67,7 +69,8 @@ def encode_region(k, v, spec: RegionSpec, kv_head: int) -> EncodedRegion:
     w = w16 = None
     if spec.witness:
         w, w16 = quant.witness(kh, k)
-    return EncodedRegion(kc, ks, vc, vs, w, w16, kh, vh, c1 + c2)
+    v_rec = quant.value_witness(vh, v) if spec.value_witness else None
+    return EncodedRegion(kc, ks, vc, vs, w, w16, kh, vh, c1 + c2, v_rec)
 
 
 def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray:
@@ -101,6 +104,10 @@ def decode_cell(q, regions, sm_scale: float, delta_loc=None):
     if delta_loc is not None:
         s_key = np.concatenate([key_dither_steps(r[1], r[2], np.asarray(r[0]).shape[0])
                                 for r in regions])
-    res = attention.decode_step(q, ke_used, kh, vh, w16, sm_scale, s_key=s_key, delta_loc=delta_loc)
+    v_rec = None
+    if all(r[1].v_rec is not None for r in regions):
+        v_rec = np.concatenate([r[1].v_rec.astype(np.float64) for r in regions])
+    res = attention.decode_step(q, ke_used, kh, vh, w16, sm_scale, s_key=s_key, delta_loc=delta_loc,
+                                v_rec=v_rec)
     res["k_exact_all"] = ke
     return res

@@ -19,6 +19,9 @@ INT8 with subtractive dither, per (256-token block, channel) scales
     x^ = s * (code - xi)                              (exact in float64)
   with xi the Philox dither of oracle.philox.  s = 0 gives code 0 and x^ = 0.
 
+Value record: rho = ||v^ - v|| and ||v|| per token, the two norms of the output
+bound (WitCert Sec. 3), summed in coordinate order and rounded up the same way.
+
 Witness (WitCert, Sec. 4.1, Eq. (2)): r = x^ - x;  w_b = ||r_b|| over the 8
 coordinates of band b, stored as fp16 rounded toward +infinity.  Bands follow
 the rotate-half RoPE pairing (coordinate j pairs with j + d/2); band b holds
@@ -113,6 +116,22 @@ def int8_dither_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
 
 
 WITNESS_INFLATE = 1.0 + 2.0 ** -48
+
+
+def value_witness(v_hat: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Value record of each token (WitCert Sec. 3 output bound, Sec. 4.2
+    "Value side"): rho = ||v^_t - v_t|| and ||v_t||, each summed in float64 over
+    coordinates 0..d-1 in order (one rounding per square and per addition),
+    square-rooted, multiplied by 1 + 2^-48 and rounded up to fp16.
+    Returns float16 (T, 2): [:, 0] = rho, [:, 1] = ||v||."""
+    out = np.empty((np.asarray(v).shape[0], 2), np.float16)
+    for col, x in enumerate((np.asarray(v_hat, np.float64) - np.asarray(v, np.float64),
+                             np.asarray(v, np.float64))):
+        acc = x[:, 0] * x[:, 0]
+        for c in range(1, x.shape[1]):
+            acc = acc + x[:, c] * x[:, c]
+        out[:, col] = fp16_round_up(np.sqrt(acc) * WITNESS_INFLATE)
+    return out
 
 
 def witness(x_hat: np.ndarray, x: np.ndarray, n_bands: int = N_BANDS):
