@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -110,6 +110,8 @@ typedef struct kvq_region {
   int32_t layer;            /* INT8 dither: layer index, < 32768 */
   int32_t stream_id;        /* INT8 dither: prefix stream id; suffix: request b uses stream_id + b */
   const int32_t *stream_ids;/* suffix: optional device int32 [batch] stream ids (overrides) */
+  const uint16_t *v_witness;/* value records, fp16 bits [.., len, 2] laid out like the witness:
+                               (rho_t = ||v^_t - v_t||, ||v_t||), each rounded up; or NULL */
 } kvq_region;
 
 /* Decode-step attention over prefix ++ suffix for every (request, query head).
@@ -148,7 +150,16 @@ typedef struct kvq_attn_args {
  * TV <= bound_b_raw holds with probability >= 1 - delta_b jointly over the S
  * tokens for a query that does not depend on the stored dither (a
  * non-adaptive query); delta_b is the per-(layer, head, step) share of a
- * request's budget, delta_req / (layers * heads * steps). */
+ * request's budget, delta_req / (layers * heads * steps).
+ * Value side and the joint output bound (WitCert Sec. 3; Sec. 4.2 "Value side
+ * and the joint event"), from the regions' value records (every region present
+ * must have v_witness, else KVQ_ERR_NULL; keys stored as BF16 or with a
+ * witness, else KVQ_ERR_UNSUPPORTED):
+ *   value_err  = sum_t p~_t rho_t
+ *   v_norm_max = max_t ||v_t|| over the request's tokens
+ *   out_bound  = 2 meter v_norm_max + value_err, an upper bound of
+ *                ||y - out||, y the attention output with exact keys and values
+ *                (meter as above; 0 when every region's keys are stored exactly). */
 typedef struct kvq_meter_out {
   float *tv;
   float *bound_raw;
@@ -158,6 +169,9 @@ typedef struct kvq_meter_out {
   float *bound_b_raw;
   float *meter_b;
   double delta_b;
+  float *value_err;
+  float *v_norm_max;
+  float *out_bound;
 } kvq_meter_out;
 
 /* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store
@@ -190,6 +204,10 @@ typedef struct kvq_quant_args {
   int32_t layer;
   int32_t stream_id;
   const int32_t *stream_ids;
+  uint16_t *v_witness_out;  /* value records fp16 bits [n_seq, Hk, capacity, 2] =
+                               (||v^_t - v_t||, ||v_t||): norms in float64 summed over
+                               channels 0..127 in order, times 1 + 2^-48, rounded up
+                               to fp16; or NULL.  Needs v_in. */
 } kvq_quant_args;
 
 /* Library ABI version (KVQ_ABI_VERSION of the build). */

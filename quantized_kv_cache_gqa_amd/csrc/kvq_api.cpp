@@ -35,7 +35,7 @@ inline bool is_store_fmt(int f) {
 struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
   int prefix_len = 0, suffix_cap = 0;
-  bool tv = false, meter = false, wit_any = false, tier_b = false;
+  bool tv = false, meter = false, wit_any = false, tier_b = false, value = false;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
 };
@@ -73,7 +73,7 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || p.tier_b || a->split_tokens != 0 || p.group != 4) return false;
+  if (!p.tv || p.tier_b || p.value || a->split_tokens != 0 || p.group != 4) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -137,7 +137,7 @@ kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int ba
   if (r.k_exact && r.k_exact_format != KVQ_FMT_BF16 && r.k_exact_format != KVQ_FMT_FP32)
     return KVQ_ERR_FORMAT;
   const void *ptrs[] = {r.k, need_v ? r.v : nullptr, r.k_scale, need_v ? r.v_scale : nullptr,
-                        r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids};
+                        r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids, r.v_witness};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   const bool int8 = r.k_format == KVQ_FMT_INT8_DITHER || (need_v && r.v_format == KVQ_FMT_INT8_DITHER);
@@ -204,7 +204,24 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     for (const void *x : mp)
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
     p.tv = m->tv && any_exact;
-    p.meter = (m->bound_raw || m->meter || m->log_a) && p.wit_any;
+    const void *mv[] = {m->value_err, m->v_norm_max, m->out_bound};
+    for (const void *x : mv)
+      if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
+    p.value = m->value_err || m->v_norm_max || m->out_bound;
+    // every region's value records for the value side
+    if (p.value && p.prefix_len > 0 && !a->prefix.v_witness) return KVQ_ERR_NULL;
+    if (p.value && p.suffix_cap > 0 && !a->suffix.v_witness) return KVQ_ERR_NULL;
+    // Tier A (and the joint bound, which uses it): a region without a witness
+    // counts as holding the exact keys (c = 0), which only keys stored as BF16
+    // can; quantized keys without a witness are rejected, never metered as exact
+    const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound;
+    if (wants_a) {
+      if (p.prefix_len > 0 && a->prefix.k_format != KVQ_FMT_BF16 && !a->prefix.witness)
+        return KVQ_ERR_UNSUPPORTED;
+      if (p.suffix_cap > 0 && a->suffix.k_format != KVQ_FMT_BF16 && !a->suffix.witness)
+        return KVQ_ERR_UNSUPPORTED;
+    }
+    p.meter = wants_a && p.wit_any;
     const void *mb[] = {m->log_a_b, m->bound_b_raw, m->meter_b};
     for (const void *x : mb)
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
@@ -250,6 +267,7 @@ RegionDev region_dev(const kvq_region &r, bool is_prefix) {
   d.layer = r.layer;
   d.stream_id = r.stream_id;
   d.stream_ids = is_prefix ? nullptr : r.stream_ids;
+  d.v_witness = r.v_witness;
   return d;
 }
 
@@ -288,6 +306,10 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
     d.log_a_b = m->log_a_b; d.bound_b_raw = m->bound_b_raw; d.meter_b = m->meter_b;
   }
   d.has_tier_b = p.tier_b;
+  if (m) {
+    d.value_err = m->value_err; d.v_norm_max = m->v_norm_max; d.out_bound = m->out_bound;
+  }
+  d.has_value = p.value;
   d.tier_b_log_inv_delta = p.tier_b ? (float)-log(m->delta_b) : 0.0f;
   if (ws) {
     char *w = static_cast<char *>(ws);
@@ -401,7 +423,7 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   if (a->k_format != KVQ_FMT_BF16 && !a->k_scale_out) return KVQ_ERR_NULL;
   if (a->v_in && a->v_format != KVQ_FMT_BF16 && !a->v_scale_out) return KVQ_ERR_NULL;
   const void *ptrs[] = {a->k_in, a->v_in, a->k_out, a->v_out, a->k_scale_out, a->v_scale_out,
-                        a->witness_out, a->stream_ids};
+                        a->witness_out, a->stream_ids, a->v_witness_out};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   const bool int8 = a->k_format == KVQ_FMT_INT8_DITHER || (a->v_in && a->v_format == KVQ_FMT_INT8_DITHER);
@@ -417,6 +439,7 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   q.k_out = a->k_out; q.v_out = a->v_out; q.k_scale_out = a->k_scale_out; q.v_scale_out = a->v_scale_out;
   q.witness_out = a->witness_out;
   q.seed = a->seed; q.layer = a->layer; q.stream_id = a->stream_id; q.stream_ids = a->stream_ids;
+  q.v_witness_out = a->v_in ? a->v_witness_out : nullptr;
   return launch_quantize(q, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 

@@ -98,12 +98,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     }
   }
 
-  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G];
+  // value side (WitCert Sec. 3 output bound): zv = sum p~ rho on the attention
+  // maximum, vmax = the largest ||v|| of the chunk's tokens
+  const bool do_v = d.has_value != 0;
+  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G];
+  float vmax = 0.0f;
   float acc[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mq[h] = mm[h] = me[h] = NEG_INF;
-    zq[h] = zm[h] = ze[h] = zb[h] = 0.0f;
+    zq[h] = zm[h] = ze[h] = zb[h] = zv[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
   }
@@ -219,6 +223,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       }
     }
 
+    float rho = 0.0f;
+    if (do_v) {
+      const uint32_t vr = *reinterpret_cast<const uint32_t *>(R.v_witness + row * 2);
+      rho = fp16_bits_to_f32(vr & 0xffffu);
+      if (valid) vmax = fmaxf(vmax, fp16_bits_to_f32(vr >> 16));
+    }
+
     // ---- online accumulators
     float p[G];
 #pragma unroll
@@ -228,6 +239,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         const float f = merge_factor(mq[h], x);
         zq[h] *= f;
         zb[h] *= f;
+        zv[h] *= f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[h][i] *= f;
         mq[h] = x;
@@ -235,6 +247,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       p[h] = valid ? fast_exp2(x - mq[h]) : 0.0f;
       zq[h] += p[h];
       if (do_b) zb[h] = fmaf(p[h], eub[h], zb[h]);
+      if (do_v) zv[h] = fmaf(p[h], rho, zv[h]);
     }
     if (do_meter) {
 #pragma unroll
@@ -289,6 +302,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         const float f1 = merge_factor(mq[h], m), f2 = merge_factor(m2, m);
         zq[h] = zq[h] * f1 + z2 * f2;
         if (do_b) zb[h] = zb[h] * f1 + __shfl_xor(zb[h], off) * f2;
+        if (do_v) zv[h] = zv[h] * f1 + __shfl_xor(zv[h], off) * f2;
         if constexpr (VF != VF_NONE) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[h][i] = acc[h][i] * f1 + __shfl_xor(acc[h][i], off) * f2;
@@ -310,6 +324,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     }
   }
 
+  if (do_v) {
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  }
+
   // ---- per-wavefront states to LDS, then the shared chunk epilogue
   __shared__ float part_s[WAVES][G][PART_STRIDE];
   if (lane < 8) {
@@ -320,6 +339,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         part_s[wv][h][2] = mm[h]; part_s[wv][h][3] = zm[h];
         part_s[wv][h][4] = me[h]; part_s[wv][h][5] = ze[h];
         part_s[wv][h][6] = zb[h];
+        part_s[wv][h][7] = zv[h];
+        part_s[wv][h][PART_VMAX] = vmax;
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];

@@ -121,7 +121,8 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
 }
 
 // Per-wavefront states are in part_s[w][h][...] (m~, z~, m', z', m_e, z_e,
-// z_b, -, acc[128]); z_b (Tier B's sum of p~ e^u) and acc share m~.  Merges the wavefronts into this chunk's partial.  When the group
+// z_b, z_v, acc[128], max ||v||, pad); z_b (Tier B's sum of p~ e^u), z_v (the
+// value side's sum of p~ rho) and acc share m~.  Merges the wavefronts into this chunk's partial.  When the group
 // (b, kvh) has several chunks, the partial goes to the workspace and the
 // arrival is counted; the last arrival runs the finalize over all partials.  A
 // group with a single chunk finalizes from LDS directly (no cross-work-group
@@ -144,13 +145,19 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
                          : d.partials + ((size_t)grp * total_chunks + d.chunk_base + chunk_idx) * G * PART_STRIDE;
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if (k == 7 || (k == 6 && !d.has_tier_b)) continue;
+    if ((k == 6 && !d.has_tier_b) || (k == 7 && !d.has_value) || k > PART_VMAX ||
+        (k == PART_VMAX && !d.has_value))
+      continue;
     const int mk = (k >= 6) ? 0 : (k & ~1);          // which maximum governs this field
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
     float r;
-    if (k < 6 && (k & 1) == 0) {
+    if (k == PART_VMAX) {                            // a plain maximum
+      r = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) r = fmaxf(r, part_s[w][h][k]);
+    } else if (k < 6 && (k & 1) == 0) {
       r = M;
     } else {
       r = 0.0f;
@@ -193,12 +200,16 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       Mm = fmaxf(Mm, rd(pc + 2));
       Me = fmaxf(Me, rd(pc + 4));
     }
-    float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, Zv = 0.0f, Vmax = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
       const float fq = merge_factor(rd(pc + 0), Mq);
       Zq += rd(pc + 1) * fq;
       if (d.has_tier_b) Zb += rd(pc + 6) * fq;
+      if (d.has_value) {
+        Zv += rd(pc + 7) * fq;
+        Vmax = fmaxf(Vmax, rd(pc + PART_VMAX));
+      }
       Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
       Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
       o0 += rd(pc + 8 + lane) * fq;
@@ -219,6 +230,15 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       if (d.log_a) d.log_a[qh] = (float)log_a;
       if (d.bound_raw) d.bound_raw[qh] = bf;
       if (d.meter) d.meter[qh] = fminf(1.0f, bf);
+      if (d.has_value) {
+        // value side and the joint output bound (WitCert Sec. 3): the meter
+        // bounds TV (0 when every region's keys are stored exactly)
+        const float verr = Zq > 0.0f ? Zv / Zq : 0.0f;
+        const float tvb = do_meter ? fminf(1.0f, bf) : 0.0f;
+        if (d.value_err) d.value_err[qh] = verr;
+        if (d.v_norm_max) d.v_norm_max[qh] = Vmax;
+        if (d.out_bound) d.out_bound[qh] = 2.0f * tvb * Vmax + verr;
+      }
       if (d.has_tier_b) {
         // log A_B = log(sum p~ e^u / sum p~), both sums on the maximum M~
         const double log_ab = (Zq > 0.0f && Zb > 0.0f) ? log((double)Zb) - log((double)Zq) : 0.0;

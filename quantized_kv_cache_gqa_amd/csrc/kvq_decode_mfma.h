@@ -122,6 +122,7 @@ struct TileRegs {
   uint2 v8[4];     // FP8 values: 8 dims of 4 tokens (MFMA B layout)
   uint4 vb[4];     // BF16 values: 16 dims of 2 tokens (vector-ALU layout)
   float ks, vs;    // scales of this lane's compact (token, head) slot
+  uint32_t vrec;   // value record of this lane's token: fp16 (rho, ||v||)
 };
 
 // Addressing of one (request, KV head) region range ending at c1, and the
@@ -133,7 +134,7 @@ template <int KF, int VF, bool PAGED>
 struct TileSrc {
   using RowT = typename std::conditional<PAGED, size_t, uint32_t>::type;
   const uint8_t *kb, *keb, *vbb;
-  const uint16_t *wb;
+  const uint16_t *wb, *vwb;
   const float *ksb, *vsb;
   const int32_t *ptab;
   int pshift, page_size, h_kv, kvh, last;
@@ -151,6 +152,7 @@ struct TileSrc {
     kb = (const uint8_t *)R.k + row0 * (KF == KVQ_FMT_BF16 ? 2 * D : D);
     keb = (const uint8_t *)R.k_exact + row0 * (2 * D);
     wb = R.witness + row0 * NB;
+    vwb = R.v_witness + row0 * 2;
     ksb = (const float *)R.k_scale + row0;
     vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_BF16 ? 2 * D : D);
     vsb = (const float *)R.v_scale + row0;
@@ -166,9 +168,9 @@ struct TileSrc {
     }
   }
 
-  __device__ __forceinline__ void load(TileRegs &T, int t0, bool exact, bool wit) const {
+  __device__ __forceinline__ void load(TileRegs &T, int t0, bool exact, bool wit, bool vrec) const {
     load_keys(T, t0, exact);
-    load_rest(T, t0, wit);
+    load_rest(T, t0, wit, vrec);
   }
 
   // stored and exact keys with the key scale (what the logits need first)
@@ -195,11 +197,12 @@ struct TileSrc {
   }
 
   // witness, values and the value scale
-  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit) const {
+  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit, bool vrec) const {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
     if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
+    if (vrec) T.vrec = *reinterpret_cast<const uint32_t *>(vwb + rk * 2);
     if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -245,7 +248,12 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // maximum.  tb_l = log(2 S / delta) with S the request's tokens (both
   // regions); eub = e^{u} of this lane's head, constant over a 256-token
   // block of INT8 keys and 1 for keys stored as BF16 (u = 0).
-  const bool do_b = d.has_tier_b != 0;
+  // (the team launch never takes Tier B or the value side: SPILL_LDS compiles
+  // them out of its kernel)
+  const bool do_b = !SPILL_LDS && d.has_tier_b != 0;
+  // value side (WitCert Sec. 3 output bound): zv accumulates p~ rho on the
+  // attention maximum, vmax the largest ||v|| of the chunk's tokens
+  const bool do_v = !SPILL_LDS && d.has_value != 0;
   float tb_l = 0.0f, eub = 1.0f;
   if (do_b) {
     const int sl = d.suffix_cap > 0
@@ -343,13 +351,14 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 
   const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
   float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
-  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit); };
+  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit, do_v); };
 
   // per-lane accumulator states (lane = one (token slot, head) pair)
   float mq = NEG_INF, zq = 0.0f;     // attention softmax, maximum uniform per head
   float mm = NEG_INF, zm = 0.0f;     // l~ + c (Theorem 1's A)
   float me = NEG_INF, ze = 0.0f;     // exact logits (TV normalizer)
   float zb = 0.0f;                   // Tier B: sum p~ e^u on the attention maximum
+  float zv = 0.0f, vmax = 0.0f;      // value side: sum p~ rho, max ||v||
   // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
   // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
   f32x4_t ov[8];
@@ -425,6 +434,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       const float f = merge_factor(mq, mnew);
       zq *= f;
       zb *= f;
+      zv *= f;
       float fh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
@@ -444,6 +454,10 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const float p = valid ? fast_exp2(lq - mq) : 0.0f;
     zq += p;
     if (do_b) zb = fmaf(p, eub, zb);
+    if (do_v) {
+      zv = fmaf(p, fp16_bits_to_f32(T.vrec & 0xffffu), zv);
+      if (valid) vmax = fmaxf(vmax, fp16_bits_to_f32(T.vrec >> 16));
+    }
     if (do_tv) {
       if (le > me + LAZY) {
         ze *= merge_factor(me, le);
@@ -581,6 +595,10 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     if (off == 4 || off == 8) continue;
     zq += __shfl_xor(zq, off);
     if (do_b) zb += __shfl_xor(zb, off);
+    if (do_v) {
+      zv += __shfl_xor(zv, off);
+      vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+    }
     if (do_meter) {
       const float m2 = __shfl_xor(mm, off), z2 = __shfl_xor(zm, off);
       const float m = fmaxf(mm, m2);
@@ -608,6 +626,8 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
     part_s[wv][hh][4] = me; part_s[wv][hh][5] = ze;
     part_s[wv][hh][6] = zb;
+    part_s[wv][hh][7] = zv;
+    part_s[wv][hh][PART_VMAX] = vmax;
   }
   if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
     if (lane < 16) {

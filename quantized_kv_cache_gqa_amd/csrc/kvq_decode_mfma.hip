@@ -119,7 +119,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   __syncthreads();
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if (k == 6 || k == 7) continue;
+    if (k == 6 || k == 7 || k >= 8 + D) continue;   // states and accumulator only
     const int mk = (k >= 8) ? 0 : (k & ~1);
     float M = NEG_INF;
 #pragma unroll

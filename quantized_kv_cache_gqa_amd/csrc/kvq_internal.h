@@ -20,6 +20,7 @@ struct QuantLaunch {
   uint64_t seed;
   int layer, stream_id;
   const int32_t *stream_ids;
+  uint16_t *v_witness_out;  // value records (rho, ||v||) per token, nullable
 };
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
@@ -43,6 +44,7 @@ struct RegionDev {
   uint32_t seed_lo, seed_hi;
   int layer, stream_id;
   const int32_t *stream_ids;
+  const uint16_t *v_witness;    // value records (rho, ||v||) per token (nullable)
 };
 
 struct DecodeLaunch {
@@ -64,6 +66,8 @@ struct DecodeLaunch {
   float *log_a_b, *bound_b_raw, *meter_b;   // Tier B outputs (nullable)
   int has_tier_b;               // Tier B requested: accumulate E_p~[e^u] (partial field 6)
   float tier_b_log_inv_delta;   // log(1 / delta_b)
+  float *value_err, *v_norm_max, *out_bound;   // value side outputs (nullable)
+  int has_value;                // value side requested: sum p~ rho (field 7), max ||v|| (field 136)
   uint32_t *counters;
   float *partials;
   float *spill;
@@ -74,7 +78,9 @@ struct DecodeLaunch {
   int silent_member;            // team launch: member that never publishes (test hook; -1: none)
 };
 
-constexpr int PART_STRIDE = 136;  // m~, z~, m', z', m_e, z_e, 2 pad, acc[128]
+// m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, 7 pad
+constexpr int PART_STRIDE = 144;
+constexpr int PART_VMAX = 136;
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 // Matrix-core kernel for GQA group 4 with FP8/BF16 keys and values.

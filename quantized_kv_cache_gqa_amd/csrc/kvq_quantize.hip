@@ -12,6 +12,10 @@
 // float64; each band's squares are summed in coordinate order (4b..4b+3, then
 // 64+4b..64+4b+3) with one rounding per operation, square-rooted, multiplied by
 // 1 + 2^-48 and rounded up to fp16, so the stored value bounds the exact norm.
+//
+// Value records (WitCert Sec. 3, the output bound's two norms): per token,
+// rho = ||v^ - v|| and ||v||, each summed in float64 over channels 0..127 in
+// order, square-rooted, inflated and rounded up the same way.
 #include <hip/hip_runtime.h>
 
 #include "kvq_device.h"
@@ -41,13 +45,27 @@ __device__ __forceinline__ uint32_t band_witness(const double *r, int b) {
   return fp16_round_up_bits(w);
 }
 
+// Norm of 128 float64 values held in LDS, summed in channel order.
+__device__ __forceinline__ uint32_t full_norm_up(const double *x) {
+#pragma clang fp contract(off)
+  double acc = x[0] * x[0];
+  for (int c = 1; c < D; ++c) {
+    double t = x[c] * x[c];
+    acc = acc + t;
+  }
+  double w = sqrt(acc);
+  w = w * (1.0 + 0x1p-48);
+  return fp16_round_up_bits(w);
+}
+
 // One wavefront per token; handles FP8 per-token and BF16 targets.
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const void *__restrict__ in, int in_fmt, int target, int n_seq, int h_kv, int capacity,
     int tok_begin, int tok_end, uint8_t *__restrict__ out, float *__restrict__ scale_out,
-    uint16_t *__restrict__ wit_out) {
+    uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out) {
 #pragma clang fp contract(off)
   __shared__ double rbuf[4][D];
+  __shared__ double xbuf[4][D];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int ntok = tok_end - tok_begin;
@@ -90,6 +108,16 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < NB) wit_out[row * NB + lane] = (uint16_t)band_witness(rbuf[wv], lane);
   }
+  if (vrec_out) {                                        // values: (rho, ||v||)
+    rbuf[wv][lane] = h0 - (double)x0;
+    rbuf[wv][lane + 64] = h1 - (double)x1;
+    xbuf[wv][lane] = (double)x0;
+    xbuf[wv][lane + 64] = (double)x1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < 2) vrec_out[row * 2 + lane] = (uint16_t)full_norm_up(lane == 0 ? rbuf[wv] : xbuf[wv]);
+  }
 }
 
 // One work-group per (sequence, KV head, 256-token block): dithered INT8.
@@ -97,11 +125,12 @@ __global__ __launch_bounds__(256) void quant_int8_block_kernel(
     const void *__restrict__ in, int in_fmt, int kv, int n_seq, int h_kv, int capacity,
     int blk_begin, int n_blk, int tok_end, int8_t *__restrict__ out,
     uint16_t *__restrict__ scale_out, uint16_t *__restrict__ wit_out, uint32_t k0, uint32_t k1,
-    int layer, int stream_id, const int32_t *__restrict__ stream_ids) {
+    int layer, int stream_id, const int32_t *__restrict__ stream_ids, uint16_t *__restrict__ vrec_out) {
 #pragma clang fp contract(off)
   __shared__ float amax_s[2][D];
   __shared__ float scale_s[D];
   __shared__ double rbuf[8][D];
+  __shared__ double xbuf[8][D];
   const int tid = threadIdx.x;
   const int sh = blockIdx.x / n_blk;                     // (seq, kv head)
   const int blk = blk_begin + (int)(blockIdx.x - sh * n_blk);
@@ -150,18 +179,24 @@ __global__ __launch_bounds__(256) void quant_int8_block_kernel(
           code = fminf(fmaxf(rintf(z), -127.0f), 127.0f);
         }
         word |= ((uint32_t)(int)code & 0xffu) << (8 * e);
-        if (wit_out) {
+        if (wit_out || vrec_out) {
           double xh = (s != 0.0f) ? (double)s * ((double)code - (double)xi[e]) : 0.0;
           rbuf[ti][c] = xh - (double)x;
+          xbuf[ti][c] = (double)x;
         }
       }
       *reinterpret_cast<uint32_t *>(out + (base + t) * D + 4 * g) = word;
     }
-    if (wit_out) {
+    if (wit_out || vrec_out) {
       __syncthreads();
-      if (tid < 128) {
+      if (wit_out && tid < 128) {
         const int tt = tid >> 4, b = tid & 15;
         if (i0 + tt < nt) wit_out[(base + t0 + i0 + tt) * NB + b] = (uint16_t)band_witness(rbuf[tt], b);
+      }
+      if (vrec_out && tid >= 128 && tid < 144) {
+        const int tt = (tid - 128) >> 1, col = tid & 1;
+        if (i0 + tt < nt)
+          vrec_out[(base + t0 + i0 + tt) * 2 + col] = (uint16_t)full_norm_up(col == 0 ? rbuf[tt] : xbuf[tt]);
       }
       __syncthreads();
     }
@@ -174,6 +209,7 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
   void *out = which == 0 ? q.k_out : q.v_out;
   void *sc = which == 0 ? q.k_scale_out : q.v_scale_out;
   uint16_t *wit = which == 0 ? q.witness_out : nullptr;
+  uint16_t *vrec = which == 1 ? q.v_witness_out : nullptr;
   const int ntok = q.tok_end - q.tok_begin;
   if (ntok <= 0) return hipSuccess;
   if (fmt == KVQ_FMT_INT8_DITHER) {
@@ -183,13 +219,13 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
     hipLaunchKernelGGL(quant_int8_block_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
                        q.in_format, which, q.n_seq, q.h_kv, q.capacity, blk_begin, n_blk, q.tok_end,
                        (int8_t *)out, (uint16_t *)sc, wit, (uint32_t)q.seed,
-                       (uint32_t)(q.seed >> 32), q.layer, q.stream_id, q.stream_ids);
+                       (uint32_t)(q.seed >> 32), q.layer, q.stream_id, q.stream_ids, vrec);
   } else {
     const long total = (long)q.n_seq * q.h_kv * ntok;
     const long grid = (total + 3) / 4;
     hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
                        q.in_format, fmt, q.n_seq, q.h_kv, q.capacity, q.tok_begin, q.tok_end,
-                       (uint8_t *)out, (float *)sc, wit);
+                       (uint8_t *)out, (float *)sc, wit, vrec);
   }
   return hipGetLastError();
 }

@@ -41,7 +41,7 @@ class Region(ctypes.Structure):
                 ("k_exact", c_void_p), ("k_exact_format", c_int32), ("length", c_int32),
                 ("lengths", c_void_p), ("page_table", c_void_p), ("page_size", c_int32),
                 ("max_pages", c_int32), ("seed", ctypes.c_uint64), ("layer", c_int32),
-                ("stream_id", c_int32), ("stream_ids", c_void_p)]
+                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness", c_void_p)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -53,7 +53,8 @@ class AttnArgs(ctypes.Structure):
 class MeterOut(ctypes.Structure):
     _fields_ = [("tv", c_void_p), ("bound_raw", c_void_p), ("meter", c_void_p), ("log_a", c_void_p),
                 ("log_a_b", c_void_p), ("bound_b_raw", c_void_p), ("meter_b", c_void_p),
-                ("delta_b", ctypes.c_double)]
+                ("delta_b", ctypes.c_double), ("value_err", c_void_p), ("v_norm_max", c_void_p),
+                ("out_bound", c_void_p)]
 
 
 class QuantArgs(ctypes.Structure):
@@ -63,14 +64,14 @@ class QuantArgs(ctypes.Structure):
                 ("tok_begin", c_int32), ("tok_end", c_int32), ("k_out", c_void_p),
                 ("v_out", c_void_p), ("k_scale_out", c_void_p), ("v_scale_out", c_void_p),
                 ("witness_out", c_void_p), ("seed", ctypes.c_uint64), ("layer", c_int32),
-                ("stream_id", c_int32), ("stream_ids", c_void_p)]
+                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness_out", c_void_p)]
 
 
 _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class PlanInfo(ctypes.Structure):
@@ -142,10 +143,11 @@ class Stored:
     k_scale: Optional[torch.Tensor]
     v_scale: Optional[torch.Tensor]
     witness: Optional[torch.Tensor]
+    v_witness: Optional[torch.Tensor] = None   # fp16 [.., capacity, 2]: rho, ||v||
 
 
 def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Optional[str],
-                 witness: bool, device) -> Stored:
+                 witness: bool, device, value_witness: bool = False) -> Stored:
     def codes(fmt):
         dt = {"bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8}[fmt]
         return torch.zeros((n_seq, h_kv, capacity, HEAD_DIM), dtype=dt, device=device)
@@ -161,7 +163,9 @@ def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Option
     return Stored(fmt_k, fmt_v or "bf16", codes(fmt_k), codes(fmt_v) if fmt_v else None,
                   scale(fmt_k), scale(fmt_v) if fmt_v else None,
                   torch.zeros((n_seq, h_kv, capacity, N_BANDS), dtype=torch.float16, device=device)
-                  if witness else None)
+                  if witness else None,
+                  torch.zeros((n_seq, h_kv, capacity, 2), dtype=torch.float16, device=device)
+                  if value_witness and fmt_v else None)
 
 
 def quantize_into(st: Stored, k_in: torch.Tensor, v_in: Optional[torch.Tensor], *, tok_begin: int = 0,
@@ -180,7 +184,8 @@ def quantize_into(st: Stored, k_in: torch.Tensor, v_in: Optional[torch.Tensor], 
                   k_scale_out=_ptr(st.k_scale),
                   v_scale_out=_ptr(st.v_scale) if v_in is not None else None,
                   witness_out=_ptr(st.witness), seed=seed, layer=layer, stream_id=stream_id,
-                  stream_ids=_ptr(stream_ids))
+                  stream_ids=_ptr(stream_ids),
+                  v_witness_out=_ptr(st.v_witness) if v_in is not None else None)
     _check(lib.kvq_quantize(ctypes.byref(a), _stream(stream)), "kvq_quantize")
 
 
@@ -215,7 +220,7 @@ class RegionView:
                       page_size=self.page_size,
                       max_pages=self.page_table.shape[1] if self.page_table is not None else 0,
                       seed=self.seed, layer=self.layer, stream_id=self.stream_id,
-                      stream_ids=_ptr(self.stream_ids))
+                      stream_ids=_ptr(self.stream_ids), v_witness=_ptr(st.v_witness))
 
 
 def _attn_args(q, prefix: Optional[RegionView], suffix: Optional[RegionView], out, sm_scale,
@@ -248,15 +253,18 @@ class Workspace:
 
 METER_KEYS = ("tv", "bound_raw", "meter", "log_a")
 TIER_B_KEYS = ("log_a_b", "bound_b_raw", "meter_b")
+VALUE_KEYS = ("value_err", "v_norm_max", "out_bound")
 
 
 def plan(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
          suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
-         meter: bool = True, meter_only: bool = False, tier_b_delta: Optional[float] = None) -> dict:
+         meter: bool = True, meter_only: bool = False, tier_b_delta: Optional[float] = None,
+         value_bound: bool = False) -> dict:
     """kvq_decode_plan for the arguments decode_attn would pass (host only;
     the output and meter pointers only need to be non-NULL and aligned)."""
     dummy = _ptr(q) if meter else None
-    keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())) if meter else ()
+    keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
+            + (VALUE_KEYS if value_bound else ())) if meter else ()
     m = MeterOut(**{k: dummy for k in keys}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else q, sm_scale, split_tokens,
                       num_kv_heads, need_v=not meter_only)
@@ -270,16 +278,17 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
                 suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
                 meter: bool = True, workspace: Optional[Workspace] = None, out=None,
                 meter_bufs=None, stream=None, meter_only: bool = False,
-                tier_b_delta: Optional[float] = None):
+                tier_b_delta: Optional[float] = None, value_bound: bool = False):
     """kvq_decode_attn (or kvq_meter when meter_only).  Returns (out, dict of
     meter tensors); tier_b_delta adds the Tier B outputs with that failure
-    probability."""
+    probability, value_bound the value term and the joint output bound."""
     lib = load()
     batch, hq, d = q.shape
     if out is None and not meter_only:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     if meter_bufs is None:
-        keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())) if meter else ()
+        keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
+                + (VALUE_KEYS if value_bound else ())) if meter else ()
         meter_bufs = {k: torch.empty((batch, hq), dtype=torch.float32, device=q.device) for k in keys}
     m = MeterOut(**{k: _ptr(v) for k, v in meter_bufs.items()}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else out, sm_scale, split_tokens,

@@ -24,20 +24,22 @@ def dither_seed(cfg: Config) -> int:
     return (cfg.seed * 0x9E3779B97F4A7C15) % (1 << 64)
 
 
-def _spec(cfg: Config, region, layer: int, stream: int) -> RegionSpec:
+def _spec(cfg: Config, region, layer: int, stream: int, value_witness: bool = False) -> RegionSpec:
     return RegionSpec(k_fmt=region.k_fmt, v_fmt=region.v_fmt, seed=dither_seed(cfg), layer=layer,
-                      stream=stream, witness=region.witness, exact_k=region.exact_k)
+                      stream=stream, witness=region.witness, exact_k=region.exact_k,
+                      value_witness=value_witness)
 
 
 class GpuCase:
     """One layer of a workload quantized and stored by the HIP write path."""
 
     def __init__(self, cfg: Config, layer: int = 0, device="cuda", page_seed: int = 0,
-                 fp32_exact: bool = False):
+                 fp32_exact: bool = False, value_witness: bool = False):
         from quantized_kv_cache_gqa_amd import kvq
         self.kvq = kvq
         self.cfg, self.layer, self.device = cfg, layer, device
         self.fp32_exact = fp32_exact
+        self.value_witness = value_witness
         self.inp = gen_layer(cfg, layer, device, want_fp32_keys=fp32_exact)
         G, hkv = cfg.group, cfg.h_kv
         seed = dither_seed(cfg)
@@ -50,7 +52,8 @@ class GpuCase:
             vin = self.inp["prefix_v"][None].contiguous()
             if fp32_exact:
                 vin = vin.float()
-            st = kvq.alloc_stored(1, hkv, P, pr.k_fmt, pr.v_fmt, pr.witness or fp32_exact, device)
+            st = kvq.alloc_stored(1, hkv, P, pr.k_fmt, pr.v_fmt, pr.witness or fp32_exact, device,
+                                  value_witness=value_witness)
             kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=PREFIX_STREAM)
             exact = kin[0] if (pr.exact_k or fp32_exact) else None
             self.prefix_store = st
@@ -61,7 +64,8 @@ class GpuCase:
         cap = sf.length
         kin = self.inp["suffix_k32"] if fp32_exact else self.inp["suffix_k"]
         vin = self.inp["suffix_v"].float() if fp32_exact else self.inp["suffix_v"]
-        st = kvq.alloc_stored(cfg.batch, hkv, cap, sf.k_fmt, sf.v_fmt, sf.witness or fp32_exact, device)
+        st = kvq.alloc_stored(cfg.batch, hkv, cap, sf.k_fmt, sf.v_fmt, sf.witness or fp32_exact, device,
+                              value_witness=value_witness)
         kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=0)
         self.suffix_store = st
         exact = kin if (sf.exact_k or fp32_exact) else None
@@ -98,25 +102,26 @@ class GpuCase:
             return out.contiguous()
 
         paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
-                           scatter(st.v_scale), scatter(st.witness))
+                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
         self.page_table = table
         return kvq.RegionView(paged, cap, k_exact=scatter(exact), lengths=lens, page_table=table,
                               page_size=ps, use_witness=st.witness is not None)
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
-            workspace=None, tier_b_delta=None):
+            workspace=None, tier_b_delta=None, value_bound: bool = False):
         out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
                                       self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
                                       meter=meter, meter_only=meter_only, workspace=workspace,
-                                      tier_b_delta=tier_b_delta)
+                                      tier_b_delta=tier_b_delta, value_bound=value_bound)
         torch.cuda.synchronize()
         return out, m
 
 
-def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None) -> dict:
+def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None,
+         value_bound: bool = False) -> dict:
     return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
                          sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only,
-                         tier_b_delta=tier_b_delta)
+                         tier_b_delta=tier_b_delta, value_bound=value_bound)
 
 
 def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
@@ -131,7 +136,7 @@ def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
         key = "prefix_k32" if case.fp32_exact else "prefix_k"
         k = inp[key][kvh].double().cpu().numpy()
         v = inp["prefix_v"][kvh].double().cpu().numpy()
-        spec = _spec(cfg, cfg.prefix, layer, PREFIX_STREAM)
+        spec = _spec(cfg, cfg.prefix, layer, PREFIX_STREAM, case.value_witness)
         if case.fp32_exact:
             spec.witness = True
             spec.exact_k = True
@@ -142,7 +147,7 @@ def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
     key = "suffix_k32" if case.fp32_exact else "suffix_k"
     k = inp[key][b, kvh, :n].double().cpu().numpy()
     v = inp["suffix_v"][b, kvh, :n].double().cpu().numpy()
-    spec = _spec(cfg, cfg.suffix, layer, b)
+    spec = _spec(cfg, cfg.suffix, layer, b, case.value_witness)
     if case.fp32_exact:
         spec.witness = True
         spec.exact_k = True
@@ -188,6 +193,9 @@ def check_stored(case: GpuCase, b: int, kvh: int, encs) -> None:
         if enc.w16 is not None and st.witness is not None:
             np.testing.assert_array_equal(_bits(st.witness[bb, hh, :nn]), enc.w16.view(np.uint16),
                                           err_msg=f"{name} witness")
+        if enc.v_rec is not None and st.v_witness is not None:
+            np.testing.assert_array_equal(_bits(st.v_witness[bb, hh, :nn]), enc.v_rec.view(np.uint16),
+                                          err_msg=f"{name} value records")
         assert enc.clipped == 0
 
 
@@ -239,4 +247,15 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
                 assert abs(bg - br) / max(1.0, br) <= TOL_METER, (b, qh, bg, br)
             assert abs(float(meter["meter_b"][b, qh]) - float(ref["meter_b"][h])) <= TOL_METER
             worst["bound_b"] = max(worst.get("bound_b", 0.0), abs(bg - br) / max(1.0, br))
+        if "out_bound" in meter:
+            # value side: v_norm_max is a maximum of stored fp16 values (exact);
+            # value_err within 1e-5 relative; out_bound within what the meter's
+            # 1e-5 and value_err's 1e-5 allow
+            vm, vr = float(meter["v_norm_max"][b, qh]), float(ref["v_norm_max"][h])
+            assert vm == vr, (b, qh, vm, vr)
+            ve, vre = float(meter["value_err"][b, qh]), float(ref["value_err"][h])
+            assert abs(ve - vre) <= TOL_METER * max(vre, 1e-30), (b, qh, ve, vre)
+            ob, obr = float(meter["out_bound"][b, qh]), float(ref["out_bound"][h])
+            assert abs(ob - obr) <= 2 * TOL_METER * vr + TOL_METER * vre + 1e-30, (b, qh, ob, obr)
+            worst["value_err"] = max(worst.get("value_err", 0.0), abs(ve - vre) / max(vre, 1e-30))
     return worst

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 4
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 5
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -105,7 +105,7 @@ def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
     groups, chunks, G = 64 * 8, 1, 4        # 512 groups fill the GPU: one chunk each
     counters = 2048
-    partials = groups * chunks * G * 136 * 4
+    partials = groups * chunks * G * 144 * 4
     spill = groups * 12640 * G * 8                # 12628 tokens padded to 16-token tiles
     assert n == counters + partials + spill
     info = _plan(lib, a, m)
@@ -181,6 +181,32 @@ def test_tier_b_arguments_are_checked(lib, monkeypatch):
     m_misaligned = mk(1e-6)
     m_misaligned.meter_b = FAKE + 4
     assert lib.kvq_decode_plan(ctypes.byref(good), ctypes.byref(m_misaligned), 0, ctypes.byref(info)) == 4
+
+
+def test_value_side_and_tier_a_arguments_are_checked(lib):
+    """The value side needs every region's value records (KVQ_ERR_NULL
+    otherwise); Tier A and the joint bound reject quantized keys without a
+    witness instead of metering them as exact keys."""
+    a = _args(batch=4, suffix=4096)                       # FP8 keys with a witness
+    vals = dict(value_err=FAKE, v_norm_max=FAKE, out_bound=FAKE)
+    info = kvq.PlanInfo()
+    m = kvq.MeterOut(**vals)
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, ctypes.byref(info)) == 1
+    a.suffix.v_witness = FAKE
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, ctypes.byref(info)) == 0
+    assert info.team == 0
+    nowit = _args(batch=4, suffix=4096, witness=False)
+    nowit.suffix.v_witness = FAKE
+    for fields in ({"meter": FAKE}, {"log_a": FAKE}, {"out_bound": FAKE}):
+        assert lib.kvq_decode_plan(ctypes.byref(nowit), ctypes.byref(kvq.MeterOut(**fields)), 0,
+                                   ctypes.byref(info)) == 5
+    for fields in ({"value_err": FAKE}, {"tv": FAKE}):   # no TV bound needed
+        assert lib.kvq_decode_plan(ctypes.byref(nowit), ctypes.byref(kvq.MeterOut(**fields)), 0,
+                                   ctypes.byref(info)) == 0
+    k16 = _args(batch=4, suffix=4096, kf="bf16", vf="fp8", exact=False, witness=False)
+    k16.suffix.v_witness = FAKE
+    assert lib.kvq_decode_plan(ctypes.byref(k16), ctypes.byref(kvq.MeterOut(**vals)), 0,
+                               ctypes.byref(info)) == 0
 
 
 @pytest.mark.parametrize("mutate,status", [

@@ -18,9 +18,11 @@ from workloads import CONFIGS, small_variant
 pytestmark = pytest.mark.gpu
 
 
-def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False, tier_b_delta=None):
+def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False, tier_b_delta=None,
+               value_bound=False):
     cfg = case.cfg
-    out, m = case.run(split_tokens=split_tokens, meter_only=meter_only, tier_b_delta=tier_b_delta)
+    out, m = case.run(split_tokens=split_tokens, meter_only=meter_only, tier_b_delta=tier_b_delta,
+                      value_bound=value_bound)
     cells = cells or [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
     worst = {}
     for b, kvh in cells:
@@ -402,3 +404,36 @@ def test_tier_b_certificate_every_cell(gpu_lib, kernel, name, delta):
     assert torch.equal(out, out2)
     for k in m2:
         assert torch.equal(m[k], m2[k]), k
+
+
+VALUE = {
+    "cfg2": SMALL["cfg2"],
+    "cfg3": SMALL["cfg3"],
+    "cfg4": SMALL["cfg4"],
+    "cfg5": SMALL["cfg5"],
+    "fp8-paged-cartridge": lambda: _two_region_fp8(True),
+}
+
+
+@pytest.mark.parametrize("name", list(VALUE))
+def test_value_side_and_joint_output_bound_every_cell(gpu_lib, kernel, monkeypatch, name):
+    """Value records written bit-exactly; value_err, v_norm_max and the joint
+    output bound 2 meter max||v|| + sum p~ rho on every cell against the
+    oracle; no team plan, and the other results bitwise those of the same
+    (per-chunk) plan without the value side."""
+    cfg = VALUE[name]()
+    case = GpuCase(cfg, page_seed=4, value_witness=True)
+    assert plan(case, value_bound=True)["team"] == 0
+    out, m, worst = _all_cells(case, value_bound=True)
+    assert "value_err" in worst
+    assert torch.all(m["out_bound"] >= m["value_err"])
+    if cfg.suffix.v_fmt != "bf16":
+        assert torch.all(m["value_err"] > 0)
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    o2, m2 = case.run()
+    assert torch.equal(out, o2)
+    for k in m2:
+        assert torch.equal(m[k], m2[k]), k
+    _, mo = case.run(meter_only=True, value_bound=True)
+    for k in ("value_err", "v_norm_max", "out_bound"):
+        assert torch.equal(mo[k], m[k]), k
