@@ -19,6 +19,11 @@ softmax), and each of the G query heads q_h sharing that KV head:
                 largest float32 (Sec. 6.2.4: overflow to +inf is sound)
     meter = min(1, bound_raw)                              (Sec. 3 / Sec. 4.3)
 
+Two-sided form (WitCert Sec. 4.3, Proposition 1), with A- = E_p~[e^{-c}]:
+    log A-          = logsumexp(l~ - c) - logsumexp(l~)
+    bound_two_sided = 1/2 (A/A- - A-/A) = sinh(log A - log A-); +inf past float32
+    meter_two_sided = min(1, bound_raw, bound_two_sided)
+
 Tier B, the sub-Gaussian certificate of a subtractively dithered cache
 (WitCert Sec. 4.2, Lemma 2; the in-kernel form of Sec. 6.2.3):
     var_t   = sm_scale^2 / 12 * sum_c q_c^2 s_{c,t}^2    (s: the key's dither step
@@ -129,9 +134,14 @@ def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delt
     log_a = logsumexp(l_tilde + c) - logsumexp(l_tilde)
     bound_raw = bound_from_log_a(log_a)
     meter = np.minimum(1.0, bound_raw)
+    log_a_minus = logsumexp(l_tilde - c) - logsumexp(l_tilde)
+    with np.errstate(over="ignore"):
+        two = np.sinh(log_a - log_a_minus)
+    two = np.where(two > FLT_MAX, np.inf, two)
     res = dict(out=out, out_exact=out_exact, tv=tv, log_a=log_a,
                bound_raw=bound_raw, meter=meter, l_exact=l_exact,
-               l_tilde=l_tilde, c=c, p=p, p_tilde=pt)
+               l_tilde=l_tilde, c=c, p=p, p_tilde=pt, log_a_minus=log_a_minus,
+               bound_two_sided=two, meter_two_sided=np.minimum(np.minimum(1.0, bound_raw), two))
     if s_key is not None and delta_loc is not None:
         u = tier_b_radius(q, s_key, sm, l_tilde.shape[1], delta_loc)
         log_a_b = logsumexp(l_tilde + u) - logsumexp(l_tilde)
