@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 5
+#define KVQ_ABI_VERSION 6
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -159,7 +159,11 @@ typedef struct kvq_attn_args {
  *   v_norm_max = max_t ||v_t|| over the request's tokens
  *   out_bound  = 2 meter v_norm_max + value_err, an upper bound of
  *                ||y - out||, y the attention output with exact keys and values
- *                (meter as above; 0 when every region's keys are stored exactly). */
+ *                (meter as above; 0 when every region's keys are stored exactly).
+ * Two-sided form (WitCert Sec. 4.3, Proposition 1), same needs as Tier A:
+ *   log_a_minus     = log E_p~[e^{-c_t}]
+ *   bound_two_sided = 1/2 (A/A- - A-/A), +inf when beyond the float range
+ *   meter_two_sided = min(1, bound_raw, bound_two_sided) */
 typedef struct kvq_meter_out {
   float *tv;
   float *bound_raw;
@@ -172,6 +176,9 @@ typedef struct kvq_meter_out {
   float *value_err;
   float *v_norm_max;
   float *out_bound;
+  float *log_a_minus;
+  float *bound_two_sided;
+  float *meter_two_sided;
 } kvq_meter_out;
 
 /* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store

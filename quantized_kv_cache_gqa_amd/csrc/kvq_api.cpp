@@ -35,7 +35,7 @@ inline bool is_store_fmt(int f) {
 struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
   int prefix_len = 0, suffix_cap = 0;
-  bool tv = false, meter = false, wit_any = false, tier_b = false, value = false;
+  bool tv = false, meter = false, wit_any = false, tier_b = false, value = false, two_sided = false;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
 };
@@ -73,7 +73,7 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || p.tier_b || p.value || a->split_tokens != 0 || p.group != 4) return false;
+  if (!p.tv || p.tier_b || p.value || p.two_sided || a->split_tokens != 0 || p.group != 4) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -214,7 +214,11 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     // Tier A (and the joint bound, which uses it): a region without a witness
     // counts as holding the exact keys (c = 0), which only keys stored as BF16
     // can; quantized keys without a witness are rejected, never metered as exact
-    const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound;
+    const void *mn[] = {m->log_a_minus, m->bound_two_sided, m->meter_two_sided};
+    for (const void *x : mn)
+      if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
+    const bool wants_two = m->log_a_minus || m->bound_two_sided || m->meter_two_sided;
+    const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound || wants_two;
     if (wants_a) {
       if (p.prefix_len > 0 && a->prefix.k_format != KVQ_FMT_BF16 && !a->prefix.witness)
         return KVQ_ERR_UNSUPPORTED;
@@ -222,6 +226,7 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
         return KVQ_ERR_UNSUPPORTED;
     }
     p.meter = wants_a && p.wit_any;
+    p.two_sided = wants_two && p.wit_any;
     const void *mb[] = {m->log_a_b, m->bound_b_raw, m->meter_b};
     for (const void *x : mb)
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
@@ -310,6 +315,11 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
     d.value_err = m->value_err; d.v_norm_max = m->v_norm_max; d.out_bound = m->out_bound;
   }
   d.has_value = p.value;
+  if (m) {
+    d.log_a_minus = m->log_a_minus; d.bound_two_sided = m->bound_two_sided;
+    d.meter_two_sided = m->meter_two_sided;
+  }
+  d.has_two_sided = p.two_sided;
   d.tier_b_log_inv_delta = p.tier_b ? (float)-log(m->delta_b) : 0.0f;
   if (ws) {
     char *w = static_cast<char *>(ws);

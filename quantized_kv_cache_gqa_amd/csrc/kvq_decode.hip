@@ -101,13 +101,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   // value side (WitCert Sec. 3 output bound): zv = sum p~ rho on the attention
   // maximum, vmax = the largest ||v|| of the chunk's tokens
   const bool do_v = d.has_value != 0;
-  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G];
+  // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
+  const bool do_n = d.has_two_sided != 0;
+  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G], mn[G], zn[G];
   float vmax = 0.0f;
   float acc[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    mq[h] = mm[h] = me[h] = NEG_INF;
-    zq[h] = zm[h] = ze[h] = zb[h] = zv[h] = 0.0f;
+    mq[h] = mm[h] = me[h] = mn[h] = NEG_INF;
+    zq[h] = zm[h] = ze[h] = zb[h] = zv[h] = zn[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
   }
@@ -259,6 +261,14 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
           mm[h] = y;
         }
         zm[h] += valid ? fast_exp2(y - mm[h]) : 0.0f;
+        if (do_n) {
+          const float yn = valid ? lq[h] - c : NEG_INF;
+          if (yn > mn[h] + LAZY) {
+            zn[h] *= merge_factor(mn[h], yn);
+            mn[h] = yn;
+          }
+          zn[h] += valid ? fast_exp2(yn - mn[h]) : 0.0f;
+        }
       }
     }
     if (do_tv) {
@@ -315,6 +325,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         zm[h] = zm[h] * merge_factor(mm[h], m) + z2 * merge_factor(m2, m);
         mm[h] = m;
       }
+      if (do_n) {
+        const float m2 = __shfl_xor(mn[h], off), z2 = __shfl_xor(zn[h], off);
+        const float m = fmaxf(mn[h], m2);
+        zn[h] = zn[h] * merge_factor(mn[h], m) + z2 * merge_factor(m2, m);
+        mn[h] = m;
+      }
       if (do_tv) {
         const float m2 = __shfl_xor(me[h], off), z2 = __shfl_xor(ze[h], off);
         const float m = fmaxf(me[h], m2);
@@ -341,6 +357,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         part_s[wv][h][6] = zb[h];
         part_s[wv][h][7] = zv[h];
         part_s[wv][h][PART_VMAX] = vmax;
+        part_s[wv][h][PART_MN] = mn[h];
+        part_s[wv][h][PART_ZN] = zn[h];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];

@@ -121,8 +121,9 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
 }
 
 // Per-wavefront states are in part_s[w][h][...] (m~, z~, m', z', m_e, z_e,
-// z_b, z_v, acc[128], max ||v||, pad); z_b (Tier B's sum of p~ e^u), z_v (the
-// value side's sum of p~ rho) and acc share m~.  Merges the wavefronts into this chunk's partial.  When the group
+// z_b, z_v, acc[128], max ||v||, m-, z-, pad); z_b (Tier B's sum of p~ e^u),
+// z_v (the value side's sum of p~ rho) and acc share m~; (m-, z-) is the
+// running state over l~ - c of the two-sided form.  Merges the wavefronts into this chunk's partial.  When the group
 // (b, kvh) has several chunks, the partial goes to the workspace and the
 // arrival is counted; the last arrival runs the finalize over all partials.  A
 // group with a single chunk finalizes from LDS directly (no cross-work-group
@@ -145,10 +146,11 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
                          : d.partials + ((size_t)grp * total_chunks + d.chunk_base + chunk_idx) * G * PART_STRIDE;
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if ((k == 6 && !d.has_tier_b) || (k == 7 && !d.has_value) || k > PART_VMAX ||
-        (k == PART_VMAX && !d.has_value))
+    if ((k == 6 && !d.has_tier_b) || (k == 7 && !d.has_value) || k > PART_ZN ||
+        (k == PART_VMAX && !d.has_value) || (k >= PART_MN && !d.has_two_sided))
       continue;
-    const int mk = (k >= 6) ? 0 : (k & ~1);          // which maximum governs this field
+    // which maximum governs this field: its own (m~, m', m_e, m-) or m~
+    const int mk = k < 6 ? (k & ~1) : (k >= PART_MN ? PART_MN : 0);
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
@@ -157,7 +159,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       r = 0.0f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) r = fmaxf(r, part_s[w][h][k]);
-    } else if (k < 6 && (k & 1) == 0) {
+    } else if ((k < 6 && (k & 1) == 0) || k == PART_MN) {
       r = M;
     } else {
       r = 0.0f;
@@ -193,13 +195,15 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
   const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
   const int S = d.prefix_len + suf_len;
   for (int h = wv; h < G; h += WAVES) {
-    float Mq = NEG_INF, Mm = NEG_INF, Me = NEG_INF;
+    float Mq = NEG_INF, Mm = NEG_INF, Me = NEG_INF, Mn = NEG_INF;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
       Mq = fmaxf(Mq, rd(pc + 0));
       Mm = fmaxf(Mm, rd(pc + 2));
       Me = fmaxf(Me, rd(pc + 4));
+      if (d.has_two_sided) Mn = fmaxf(Mn, rd(pc + PART_MN));
     }
+    float Zn = 0.0f;
     float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, Zv = 0.0f, Vmax = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
@@ -210,6 +214,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         Zv += rd(pc + 7) * fq;
         Vmax = fmaxf(Vmax, rd(pc + PART_VMAX));
       }
+      if (d.has_two_sided) Zn += rd(pc + PART_ZN) * merge_factor(rd(pc + PART_MN), Mn);
       Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
       Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
       o0 += rd(pc + 8 + lane) * fq;
@@ -230,6 +235,17 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       if (d.log_a) d.log_a[qh] = (float)log_a;
       if (d.bound_raw) d.bound_raw[qh] = bf;
       if (d.meter) d.meter[qh] = fminf(1.0f, bf);
+      if (d.log_a_minus || d.bound_two_sided || d.meter_two_sided) {
+        // two-sided form (WitCert Prop. 1): 1/2 (A/A- - A-/A) = sinh(log A - log A-)
+        double log_am = 0.0;
+        if (d.has_two_sided && Zq > 0.0f && Zn > 0.0f)
+          log_am = ((double)Mn - (double)Mq) * 0.69314718055994530942 + log((double)Zn) - log((double)Zq);
+        const double two = sinh(log_a - log_am);
+        const float tf = two > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)two;
+        if (d.log_a_minus) d.log_a_minus[qh] = (float)log_am;
+        if (d.bound_two_sided) d.bound_two_sided[qh] = tf;
+        if (d.meter_two_sided) d.meter_two_sided[qh] = fminf(fminf(1.0f, bf), tf);
+      }
       if (d.has_value) {
         // value side and the joint output bound (WitCert Sec. 3): the meter
         // bounds TV (0 when every region's keys are stored exactly)

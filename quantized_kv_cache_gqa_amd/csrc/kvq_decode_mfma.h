@@ -254,6 +254,8 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // value side (WitCert Sec. 3 output bound): zv accumulates p~ rho on the
   // attention maximum, vmax the largest ||v|| of the chunk's tokens
   const bool do_v = !SPILL_LDS && d.has_value != 0;
+  // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
+  const bool do_n = !SPILL_LDS && d.has_two_sided != 0;
   float tb_l = 0.0f, eub = 1.0f;
   if (do_b) {
     const int sl = d.suffix_cap > 0
@@ -359,6 +361,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   float me = NEG_INF, ze = 0.0f;     // exact logits (TV normalizer)
   float zb = 0.0f;                   // Tier B: sum p~ e^u on the attention maximum
   float zv = 0.0f, vmax = 0.0f;      // value side: sum p~ rho, max ||v||
+  float mn = NEG_INF, zn = 0.0f;     // l~ - c (Prop. 1's A-)
   // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
   // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
   f32x4_t ov[8];
@@ -472,6 +475,14 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         mm = y;
       }
       zm += valid ? fast_exp2(y - mm) : 0.0f;
+    }
+    if (do_n) {
+      const float y = lq - cc;
+      if (y > mn + LAZY) {
+        zn *= merge_factor(mn, y);
+        mn = y;
+      }
+      zn += valid ? fast_exp2(y - mn) : 0.0f;
     }
 
     // ---- output accumulation
@@ -611,6 +622,12 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       ze = ze * merge_factor(me, m) + z2 * merge_factor(m2, m);
       me = m;
     }
+    if (do_n) {
+      const float m2 = __shfl_xor(mn, off), z2 = __shfl_xor(zn, off);
+      const float m = fmaxf(mn, m2);
+      zn = zn * merge_factor(mn, m) + z2 * merge_factor(m2, m);
+      mn = m;
+    }
   }
   if constexpr (VF == KVQ_FMT_BF16) {
 #pragma unroll
@@ -628,6 +645,8 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][6] = zb;
     part_s[wv][hh][7] = zv;
     part_s[wv][hh][PART_VMAX] = vmax;
+    part_s[wv][hh][PART_MN] = mn;
+    part_s[wv][hh][PART_ZN] = zn;
   }
   if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
     if (lane < 16) {

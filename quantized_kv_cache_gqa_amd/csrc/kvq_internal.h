@@ -68,6 +68,8 @@ struct DecodeLaunch {
   float tier_b_log_inv_delta;   // log(1 / delta_b)
   float *value_err, *v_norm_max, *out_bound;   // value side outputs (nullable)
   int has_value;                // value side requested: sum p~ rho (field 7), max ||v|| (field 136)
+  float *log_a_minus, *bound_two_sided, *meter_two_sided;   // two-sided form (nullable)
+  int has_two_sided;            // accumulate E_p~[e^{-c}] (fields 137, 138)
   uint32_t *counters;
   float *partials;
   float *spill;
@@ -78,9 +80,10 @@ struct DecodeLaunch {
   int silent_member;            // team launch: member that never publishes (test hook; -1: none)
 };
 
-// m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, 7 pad
+// m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, m-, z-, 5 pad
 constexpr int PART_STRIDE = 144;
 constexpr int PART_VMAX = 136;
+constexpr int PART_MN = 137, PART_ZN = 138;
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 // Matrix-core kernel for GQA group 4 with FP8/BF16 keys and values.

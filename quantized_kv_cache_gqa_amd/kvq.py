@@ -54,7 +54,8 @@ class MeterOut(ctypes.Structure):
     _fields_ = [("tv", c_void_p), ("bound_raw", c_void_p), ("meter", c_void_p), ("log_a", c_void_p),
                 ("log_a_b", c_void_p), ("bound_b_raw", c_void_p), ("meter_b", c_void_p),
                 ("delta_b", ctypes.c_double), ("value_err", c_void_p), ("v_norm_max", c_void_p),
-                ("out_bound", c_void_p)]
+                ("out_bound", c_void_p), ("log_a_minus", c_void_p), ("bound_two_sided", c_void_p),
+                ("meter_two_sided", c_void_p)]
 
 
 class QuantArgs(ctypes.Structure):
@@ -71,7 +72,7 @@ _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class PlanInfo(ctypes.Structure):
@@ -254,17 +255,18 @@ class Workspace:
 METER_KEYS = ("tv", "bound_raw", "meter", "log_a")
 TIER_B_KEYS = ("log_a_b", "bound_b_raw", "meter_b")
 VALUE_KEYS = ("value_err", "v_norm_max", "out_bound")
+TWO_SIDED_KEYS = ("log_a_minus", "bound_two_sided", "meter_two_sided")
 
 
 def plan(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
          suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
          meter: bool = True, meter_only: bool = False, tier_b_delta: Optional[float] = None,
-         value_bound: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False) -> dict:
     """kvq_decode_plan for the arguments decode_attn would pass (host only;
     the output and meter pointers only need to be non-NULL and aligned)."""
     dummy = _ptr(q) if meter else None
     keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
-            + (VALUE_KEYS if value_bound else ())) if meter else ()
+            + (VALUE_KEYS if value_bound else ()) + (TWO_SIDED_KEYS if two_sided else ())) if meter else ()
     m = MeterOut(**{k: dummy for k in keys}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else q, sm_scale, split_tokens,
                       num_kv_heads, need_v=not meter_only)
@@ -278,17 +280,19 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
                 suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
                 meter: bool = True, workspace: Optional[Workspace] = None, out=None,
                 meter_bufs=None, stream=None, meter_only: bool = False,
-                tier_b_delta: Optional[float] = None, value_bound: bool = False):
+                tier_b_delta: Optional[float] = None, value_bound: bool = False,
+                two_sided: bool = False):
     """kvq_decode_attn (or kvq_meter when meter_only).  Returns (out, dict of
     meter tensors); tier_b_delta adds the Tier B outputs with that failure
-    probability, value_bound the value term and the joint output bound."""
+    probability, value_bound the value term and the joint output bound,
+    two_sided the two-sided form of the meter."""
     lib = load()
     batch, hq, d = q.shape
     if out is None and not meter_only:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     if meter_bufs is None:
         keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
-                + (VALUE_KEYS if value_bound else ())) if meter else ()
+                + (VALUE_KEYS if value_bound else ()) + (TWO_SIDED_KEYS if two_sided else ())) if meter else ()
         meter_bufs = {k: torch.empty((batch, hq), dtype=torch.float32, device=q.device) for k in keys}
     m = MeterOut(**{k: _ptr(v) for k, v in meter_bufs.items()}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else out, sm_scale, split_tokens,

@@ -108,20 +108,21 @@ class GpuCase:
                               page_size=ps, use_witness=st.witness is not None)
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
-            workspace=None, tier_b_delta=None, value_bound: bool = False):
+            workspace=None, tier_b_delta=None, value_bound: bool = False, two_sided: bool = False):
         out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
                                       self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
                                       meter=meter, meter_only=meter_only, workspace=workspace,
-                                      tier_b_delta=tier_b_delta, value_bound=value_bound)
+                                      tier_b_delta=tier_b_delta, value_bound=value_bound,
+                                      two_sided=two_sided)
         torch.cuda.synchronize()
         return out, m
 
 
 def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None,
-         value_bound: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False) -> dict:
     return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
                          sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only,
-                         tier_b_delta=tier_b_delta, value_bound=value_bound)
+                         tier_b_delta=tier_b_delta, value_bound=value_bound, two_sided=two_sided)
 
 
 def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
@@ -258,4 +259,16 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
             ob, obr = float(meter["out_bound"][b, qh]), float(ref["out_bound"][h])
             assert abs(ob - obr) <= 2 * TOL_METER * vr + TOL_METER * vre + 1e-30, (b, qh, ob, obr)
             worst["value_err"] = max(worst.get("value_err", 0.0), abs(ve - vre) / max(vre, 1e-30))
+        if "bound_two_sided" in meter:
+            # two-sided form: the Tier A bar (1e-5, relative above 1)
+            lm, lmr = float(meter["log_a_minus"][b, qh]), float(ref["log_a_minus"][h])
+            assert abs(lm - lmr) <= TOL_METER * max(1.0, abs(lmr)), (b, qh, lm, lmr)
+            tg, tr = float(meter["bound_two_sided"][b, qh]), float(ref["bound_two_sided"][h])
+            if math.isinf(tr) or math.isinf(tg):
+                assert math.isinf(tr) == math.isinf(tg)
+            else:
+                assert abs(tg - tr) / max(1.0, tr) <= TOL_METER, (b, qh, tg, tr)
+            mt, mtr = float(meter["meter_two_sided"][b, qh]), float(ref["meter_two_sided"][h])
+            assert abs(mt - mtr) <= TOL_METER, (b, qh, mt, mtr)
+            worst["two_sided"] = max(worst.get("two_sided", 0.0), abs(tg - tr) / max(1.0, tr))
     return worst

@@ -19,10 +19,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _all_cells(case, cells=None, check_out=True, split_tokens=0, meter_only=False, tier_b_delta=None,
-               value_bound=False):
+               value_bound=False, two_sided=False):
     cfg = case.cfg
     out, m = case.run(split_tokens=split_tokens, meter_only=meter_only, tier_b_delta=tier_b_delta,
-                      value_bound=value_bound)
+                      value_bound=value_bound, two_sided=two_sided)
     cells = cells or [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
     worst = {}
     for b, kvh in cells:
@@ -437,3 +437,32 @@ def test_value_side_and_joint_output_bound_every_cell(gpu_lib, kernel, monkeypat
     _, mo = case.run(meter_only=True, value_bound=True)
     for k in ("value_err", "v_norm_max", "out_bound"):
         assert torch.equal(mo[k], m[k]), k
+
+
+TWO_SIDED = {
+    "cfg2": SMALL["cfg2"],
+    "cfg3": SMALL["cfg3"],
+    "cfg4": SMALL["cfg4"],
+    "cfg5": SMALL["cfg5"],
+    "fp8-cartridge": lambda: _two_region_fp8(False),
+}
+
+
+@pytest.mark.parametrize("name", list(TWO_SIDED))
+def test_two_sided_form_every_cell(gpu_lib, kernel, monkeypatch, name):
+    """Proposition 1's A- and the two-sided meter on every cell against the
+    oracle; TV <= bound_two_sided and meter_two_sided <= meter; the other
+    results bitwise those of the same per-chunk plan without it."""
+    cfg = TWO_SIDED[name]()
+    case = GpuCase(cfg, page_seed=6)
+    assert plan(case, two_sided=True)["team"] == 0
+    out, m, worst = _all_cells(case, two_sided=True)
+    assert "two_sided" in worst
+    assert torch.all(m["tv"] <= m["bound_two_sided"])
+    assert torch.all(m["meter_two_sided"] <= m["meter"])
+    assert torch.all(m["log_a_minus"] <= 0) and torch.all(m["log_a"] >= 0)
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    o2, m2 = case.run()
+    assert torch.equal(out, o2)
+    for k in m2:
+        assert torch.equal(m[k], m2[k]), k
