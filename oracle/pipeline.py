@@ -84,6 +84,41 @@ def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray
     raise ValueError("Tier B needs dithered INT8 keys or keys stored exactly")
 
 
+def block_report(res, region_lengths, region_capacities, block: int = quant.BLOCK):
+    """Block-decomposable risk report (WitCert Sec. 6.3.5): blocks of 256
+    tokens aligned at the start of each region (the INT8 scale blocks), in
+    logical order, numbered over the regions' capacities.  Per query head and
+    block j:
+        mass_j     = sum_{t in j} p~_t
+        excess_j   = sum_{t in j} p~_t (e^{c_t} - 1)    (sum_j excess_j = A - 1)
+        excess_b_j = mass_j (e^{u_j} - 1)              (Tier B; u shared by the block)
+        order      = blocks by decreasing excess (excess_b when Tier B was
+                     computed), ties by lower index.
+    res: a decode_step result; region_lengths: tokens present per region;
+    region_capacities: tokens per region that fix the block numbering."""
+    pt, c = res["p_tilde"], res["c"]
+    G = pt.shape[0]
+    n_blocks = sum(-(-cap // block) for cap in region_capacities)
+    mass = np.zeros((G, n_blocks))
+    excess = np.zeros((G, n_blocks))
+    excess_b = np.zeros((G, n_blocks))
+    t0 = 0
+    b0 = 0
+    for n, cap in zip(region_lengths, region_capacities):
+        for j in range(-(-n // block)):
+            sl = slice(t0 + j * block, t0 + min(n, (j + 1) * block))
+            mass[:, b0 + j] = np.sum(pt[:, sl], axis=1)
+            excess[:, b0 + j] = np.sum(pt[:, sl] * np.expm1(c[:, sl]), axis=1)
+            if "u" in res:
+                excess_b[:, b0 + j] = mass[:, b0 + j] * np.expm1(res["u"][:, sl.start])
+        t0 += n
+        b0 += -(-cap // block)
+    key = excess_b if "u" in res else excess
+    order = np.array([sorted(range(n_blocks), key=lambda j: (-key[h, j], j)) for h in range(G)],
+                     dtype=np.int64).reshape(G, n_blocks)
+    return dict(block_mass=mass, block_excess=excess, block_excess_b=excess_b, block_order=order)
+
+
 def decode_cell(q, regions, sm_scale: float, delta_loc=None):
     """regions: list of (k_exact, EncodedRegion, RegionSpec) in logical order.
     delta_loc: Tier B's failure probability (None: Tier B not computed)."""
