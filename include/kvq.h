@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 6
+#define KVQ_ABI_VERSION 7
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -163,7 +163,19 @@ typedef struct kvq_attn_args {
  * Two-sided form (WitCert Sec. 4.3, Proposition 1), same needs as Tier A:
  *   log_a_minus     = log E_p~[e^{-c_t}]
  *   bound_two_sided = 1/2 (A/A- - A-/A), +inf when beyond the float range
- *   meter_two_sided = min(1, bound_raw, bound_two_sided) */
+ *   meter_two_sided = min(1, bound_raw, bound_two_sided)
+ * Block-decomposable risk report (WitCert Sec. 6.3.5), device arrays
+ * [batch, num_q_heads, n_blocks] with n_blocks = ceil(prefix.length / 256) +
+ * ceil(suffix.length / 256): 256-token blocks aligned at the start of each
+ * region, prefix first; blocks past a request's tokens read 0.
+ *   block_mass     = sum_{t in j} p~_t
+ *   block_excess   = sum_{t in j} p~_t (e^{c_t} - 1)   (they add up to A - 1;
+ *                    same needs as Tier A)
+ *   block_excess_b = block_mass (e^{u_j} - 1), u_j the block's Tier B radius
+ *                    (needs the Tier B request; they add up to A_B - 1)
+ *   block_order    = int32 block indices by decreasing block_excess_b when
+ *                    Tier B is requested, else block_excess; ties by lower
+ *                    index (the page-in order); needs n_blocks <= 512. */
 typedef struct kvq_meter_out {
   float *tv;
   float *bound_raw;
@@ -179,6 +191,10 @@ typedef struct kvq_meter_out {
   float *log_a_minus;
   float *bound_two_sided;
   float *meter_two_sided;
+  float *block_mass;
+  float *block_excess;
+  float *block_excess_b;
+  int32_t *block_order;
 } kvq_meter_out;
 
 /* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store

@@ -36,8 +36,10 @@ struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
   int prefix_len = 0, suffix_cap = 0;
   bool tv = false, meter = false, wit_any = false, tier_b = false, value = false, two_sided = false;
+  bool report = false;          // per-block risk report
+  int n_blocks = 0, pre_blocks = 0;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
-  size_t off_counters = 0, off_partials = 0, off_spill = 0, bytes = 0;
+  size_t off_counters = 0, off_partials = 0, off_spill = 0, off_rspill = 0, off_ublk = 0, bytes = 0;
 };
 
 // Tags of a team launch: epoch + 1 .. epoch + rounds, never 0 (the value of
@@ -73,7 +75,8 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || p.tier_b || p.value || p.two_sided || a->split_tokens != 0 || p.group != 4) return false;
+  if (!p.tv || p.tier_b || p.value || p.two_sided || p.report || a->split_tokens != 0 || p.group != 4)
+    return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -218,7 +221,19 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     for (const void *x : mn)
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
     const bool wants_two = m->log_a_minus || m->bound_two_sided || m->meter_two_sided;
-    const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound || wants_two;
+    const bool tier_b_req = m->log_a_b || m->bound_b_raw || m->meter_b;
+    // the block report (WitCert Sec. 6.3.5): Tier A's contributions need c,
+    // Tier B's need the Tier B request; the order ranks Tier B when requested
+    const void *mr[] = {m->block_mass, m->block_excess, m->block_excess_b, m->block_order};
+    for (const void *x : mr)
+      if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
+    p.report = m->block_mass || m->block_excess || m->block_excess_b || m->block_order;
+    p.pre_blocks = (p.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
+    p.n_blocks = p.pre_blocks + (p.suffix_cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
+    if (m->block_excess_b && !tier_b_req) return KVQ_ERR_UNSUPPORTED;
+    if (m->block_order && p.n_blocks > 512) return KVQ_ERR_UNSUPPORTED;
+    const bool rep_a = m->block_excess || (m->block_order && !tier_b_req);
+    const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound || wants_two || rep_a;
     if (wants_a) {
       if (p.prefix_len > 0 && a->prefix.k_format != KVQ_FMT_BF16 && !a->prefix.witness)
         return KVQ_ERR_UNSUPPORTED;
@@ -249,7 +264,14 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   p.bytes = p.off_spill;
   // spill: each region padded to whole 16-token tiles
   const size_t spill_rows = round_up((size_t)p.prefix_len, 16) + round_up((size_t)p.suffix_cap, 16);
-  if (p.tv) p.bytes += round_up((size_t)groups * spill_rows * p.group * 2 * sizeof(float), kAlign);
+  if (p.tv || p.report) p.bytes += round_up((size_t)groups * spill_rows * p.group * 2 * sizeof(float), kAlign);
+  if (p.report) {
+    // c of every token-head, and the Tier B radius of every block and head
+    p.off_rspill = p.bytes;
+    p.bytes += round_up((size_t)groups * spill_rows * p.group * sizeof(float), kAlign);
+    p.off_ublk = p.bytes;
+    p.bytes += round_up((size_t)groups * p.n_blocks * p.group * sizeof(float), kAlign);
+  }
   return KVQ_OK;
 }
 
@@ -320,12 +342,23 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
     d.meter_two_sided = m->meter_two_sided;
   }
   d.has_two_sided = p.two_sided;
+  if (m) {
+    d.block_mass = m->block_mass; d.block_excess = m->block_excess;
+    d.block_excess_b = m->block_excess_b; d.block_order = m->block_order;
+  }
+  d.has_report = p.report;
+  d.n_blocks = p.n_blocks;
+  d.pre_blocks = p.pre_blocks;
+  d.pre_int8 = p.prefix_len > 0 && a->prefix.k_format == KVQ_FMT_INT8_DITHER;
+  d.suf_int8 = p.suffix_cap > 0 && a->suffix.k_format == KVQ_FMT_INT8_DITHER;
   d.tier_b_log_inv_delta = p.tier_b ? (float)-log(m->delta_b) : 0.0f;
   if (ws) {
     char *w = static_cast<char *>(ws);
     d.counters = reinterpret_cast<uint32_t *>(w + p.off_counters);
     d.partials = reinterpret_cast<float *>(w + p.off_partials);
-    d.spill = (p.tv && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+    d.spill = ((p.tv || p.report) && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
+    d.rspill = p.report ? reinterpret_cast<float *>(w + p.off_rspill) : nullptr;
+    d.ublk = p.report ? reinterpret_cast<float *>(w + p.off_ublk) : nullptr;
   }
   dp = d;
   ds = d;

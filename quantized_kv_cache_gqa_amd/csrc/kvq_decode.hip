@@ -103,6 +103,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   const bool do_v = d.has_value != 0;
   // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
   const bool do_n = d.has_two_sided != 0;
+  // block report: spill (l~, l) and c of every token-head, the Tier B radius
+  // of every INT8 block
+  const bool do_r = d.has_report != 0;
   float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G], mn[G], zn[G];
   float vmax = 0.0f;
   float acc[G][16];
@@ -122,7 +125,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
                                                  : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
   const uint32_t ktag = dither_tag(0, R.layer, kvh), vtag = dither_tag(1, R.layer, kvh);
   const int nblk_cap = (R.length + BLK - 1) / BLK;
-  float *spill_g = do_tv ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
+  float *spill_g = (do_tv || do_r) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
+  float *rspill_g = do_r ? rspill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
 
   for (int base = c0 + wv * 8; base < c1; base += 8 * WAVES) {
     const int t = base + slot;
@@ -189,11 +193,26 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       le[h] = (do_tv && has_exact) ? sum8(pe[h]) : lq[h];
     }
 
-    // ---- spill (l~, l) for the TV pass
-    if (do_tv && valid && j == 0) {
+    // ---- spill (l~, l) for the TV pass and the block report, c for the report
+    if ((do_tv || do_r) && valid && j == 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
         st_pair(spill_g + 2 * spill_entry<G>(t, h), lq[h], le[h], d.total_chunks > 1);
+    }
+    if (do_r) {
+      float cr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) cr[h] = (do_meter && has_wit) ? sum8(pc[h]) : 0.0f;
+      if (valid && j == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float *rp = rspill_g + spill_entry<G>(t, h);
+          if (d.total_chunks > 1)
+            st_dev(rp, cr[h]);
+          else
+            *rp = cr[h];
+        }
+      }
     }
 
     // ---- Tier B radius of this token: u log2(e) = sqrt(sum_c (q_c s_c)^2 tb_l / 6)
@@ -220,7 +239,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
             const float x = qv[h][i] * sc[i];
             ss = fmaf(x, x, ss);
           }
-          eub[h] = exp2f(sqrtf(sum8(ss) * tb_l * (1.0f / 6.0f)));
+          const float ub = sqrtf(sum8(ss) * tb_l * (1.0f / 6.0f));
+          eub[h] = exp2f(ub);
+          // the block's radius, once per block and chunk (first token of the block here)
+          if (do_r && valid && j == 0 && (t % BLK == 0 || t == c0)) {
+            float *up = d.ublk + ((size_t)grp * d.n_blocks + (R.is_prefix ? 0 : d.pre_blocks) + t / BLK) * G + h;
+            if (d.total_chunks > 1)
+              st_dev(up, ub);
+            else
+              *up = ub;
+          }
         }
       }
     }

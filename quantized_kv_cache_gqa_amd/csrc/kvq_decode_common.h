@@ -41,6 +41,13 @@ __device__ __forceinline__ float *spill_region(const DecodeLaunch &d, int grp, b
   return d.spill + ((size_t)grp * rows + (is_prefix ? 0 : round16(d.prefix_len))) * (2 * G);
 }
 
+// c (log2 units) of every spill entry, for the block report: one float per entry
+template <int G>
+__device__ __forceinline__ float *rspill_region(const DecodeLaunch &d, int grp, bool is_prefix) {
+  const size_t rows = (size_t)round16(d.prefix_len) + round16(d.suffix_cap);
+  return d.rspill + ((size_t)grp * rows + (is_prefix ? 0 : round16(d.prefix_len))) * G;
+}
+
 // Words that other work-groups read (partials, and the spill when a group
 // has several chunks) go through agent-scope stores and loads, each coherent
 // at device scope by itself, so no fence has to write back or invalidate a
@@ -116,6 +123,89 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
         const float s = fp16_bits_to_f32((sw[i >> 1] >> (16 * (i & 1))) & 0xffffu);
         v[i] = s * (code - xi[e]);
       }
+    }
+  }
+}
+
+// Block-decomposable risk report (WitCert Sec. 6.3.5), run by the finalizing
+// work-group after the normalizers are known: for every 256-token block j of
+// each region (aligned at the region's start) and head h, from the spilled
+// l~ and c of its tokens:
+//   mass_j = sum p~_t,  excess_j = sum p~_t (e^{c_t} - 1),
+//   excess_b_j = mass_j (e^{u_j} - 1) with the block's Tier B radius,
+// then the blocks ranked by decreasing excess (Tier B's when requested), ties
+// by lower index.  Thread tid takes entries tid + 256 i of the block, all of
+// head (tid % 4G) / 4; sums reduce over the other lane bits, then the
+// wavefronts in order (bitwise reproducible).
+template <int G>
+__device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh, bool single, int suf_len,
+                                  const float (*fin)[6]) {
+  constexpr float LN2 = 0.69314718055994530942f;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  __shared__ float rsum_s[WAVES][2][G];
+  __shared__ float rkey_s[G][512];
+  const int hmine = (tid % (4 * G)) / 4;
+  const float Mt = fin[hmine][0], iZt = fin[hmine][1];
+  auto rd = [&](const float *p) { return single ? *p : ld_dev(p); };
+  for (int region = 0; region < 2; ++region) {
+    const int cap = region == 0 ? d.prefix_len : d.suffix_cap;
+    const int n = region == 0 ? d.prefix_len : suf_len;
+    const int nb = (cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
+    const int gb0 = region == 0 ? 0 : d.pre_blocks;
+    const bool i8 = (region == 0 ? d.pre_int8 : d.suf_int8) != 0;
+    if (nb == 0) continue;
+    const float *sp = spill_region<G>(d, grp, region == 0);
+    const float *rp = rspill_region<G>(d, grp, region == 0);
+    for (int j = 0; j < nb; ++j) {                 // uniform over the work-group
+      float ms = 0.0f, ex = 0.0f;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int e = KVQ_INT8_BLOCK * G * j + tid + 256 * i;
+        const int tile = e / (16 * G), r = e % (16 * G);
+        const int t = 16 * tile + 4 * (r / (4 * G)) + (r & 3);
+        if (t < n) {
+          const float pt = fast_exp2(rd(sp + 2 * (size_t)e) - Mt) * iZt;
+          ms += pt;
+          ex += pt * expm1f(rd(rp + e) * LN2);
+        }
+      }
+      for (int off = 1; off < 64; off <<= 1) {
+        if (off >= 4 && off < 4 * G) continue;     // the head bits
+        ms += __shfl_xor(ms, off);
+        ex += __shfl_xor(ex, off);
+      }
+      if (lane < 4 * G && (lane & 3) == 0) {
+        rsum_s[wv][0][lane >> 2] = ms;
+        rsum_s[wv][1][lane >> 2] = ex;
+      }
+      __syncthreads();
+      if (tid < G) {
+        const float M = ((rsum_s[0][0][tid] + rsum_s[1][0][tid]) + rsum_s[2][0][tid]) + rsum_s[3][0][tid];
+        const float E = ((rsum_s[0][1][tid] + rsum_s[1][1][tid]) + rsum_s[2][1][tid]) + rsum_s[3][1][tid];
+        float Eb = 0.0f;
+        if (d.has_tier_b && i8 && M > 0.0f)
+          Eb = M * expm1f(rd(d.ublk + ((size_t)grp * d.n_blocks + gb0 + j) * G + tid) * LN2);
+        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + tid) * d.n_blocks + gb0 + j;
+        if (d.block_mass) d.block_mass[o] = M;
+        if (d.block_excess) d.block_excess[o] = E;
+        if (d.block_excess_b) d.block_excess_b[o] = Eb;
+        if (d.block_order) rkey_s[tid][gb0 + j] = d.has_tier_b ? Eb : E;
+      }
+      __syncthreads();
+    }
+  }
+  if (d.block_order) {                             // rank = blocks ahead of j
+    const int nbt = d.n_blocks;
+    for (int i = tid; i < G * nbt; i += 256) {
+      const int h = i / nbt, j = i - h * nbt;
+      const float kj = rkey_s[h][j];
+      int rank = 0;
+      for (int k = 0; k < nbt; ++k) {
+        const float kk = rkey_s[h][k];
+        rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
+      }
+      d.block_order[((size_t)b * d.h_q + (size_t)kvh * G + h) * nbt + rank] = j;
     }
   }
 }
@@ -320,6 +410,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * s;
     }
   }
+  if (d.has_report) block_report_pass<G>(d, grp, b, kvh, single, suf_len, fin_s);
   if (tid == 0 && !single)                          // ready for the next call
     __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -256,6 +256,9 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   const bool do_v = !SPILL_LDS && d.has_value != 0;
   // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
   const bool do_n = !SPILL_LDS && d.has_two_sided != 0;
+  // block report: spill (l~, l) and c of every token-head, the Tier B radius
+  // of every INT8 block
+  const bool do_r = !SPILL_LDS && d.has_report != 0;
   float tb_l = 0.0f, eub = 1.0f;
   if (do_b) {
     const int sl = d.suffix_cap > 0
@@ -340,7 +343,15 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         // u log2(e) = sqrt(2 var log(2S/delta)) log2(e) = sqrt(ss tb_l / 6)
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
-        eub = exp2f(sqrtf(ss * tb_l * (1.0f / 6.0f)));
+        const float ub = sqrtf(ss * tb_l * (1.0f / 6.0f));
+        eub = exp2f(ub);
+        if (do_r && g == 0 && pp == 0) {
+          float *up = d.ublk + ((size_t)grp * d.n_blocks + (R.is_prefix ? 0 : d.pre_blocks) + blk) * G + hh;
+          if (d.total_chunks > 1)
+            st_dev(up, ub);
+          else
+            *up = ub;
+        }
       }
     }
     if constexpr (I8V) {
@@ -352,7 +363,8 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   };
 
   const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
-  float *spill_g = (do_tv && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
+  float *spill_g = ((do_tv || do_r) && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
+  float *rspill_g = do_r ? rspill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
   auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit, do_v); };
 
   // per-lane accumulator states (lane = one (token slot, head) pair)
@@ -422,8 +434,15 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     if constexpr (SPILL_LDS) {
       if (do_tv) spill_s[64 * ((t0 - c0) >> 4) + lane] = make_float2(lq, le);
     } else {
-      if (do_tv && valid)
+      if ((do_tv || do_r) && valid)
         st_pair(spill_g + 2 * ((size_t)64 * (t0 >> 4) + lane), lq, le, d.total_chunks > 1);
+      if (do_r && valid) {
+        float *rp = rspill_g + (size_t)64 * (t0 >> 4) + lane;
+        if (d.total_chunks > 1)
+          st_dev(rp, cc);
+        else
+          *rp = cc;
+      }
     }
 
     // ---- attention softmax (maximum uniform per head)

@@ -70,6 +70,13 @@ struct DecodeLaunch {
   int has_value;                // value side requested: sum p~ rho (field 7), max ||v|| (field 136)
   float *log_a_minus, *bound_two_sided, *meter_two_sided;   // two-sided form (nullable)
   int has_two_sided;            // accumulate E_p~[e^{-c}] (fields 137, 138)
+  float *block_mass, *block_excess, *block_excess_b;   // block report outputs (nullable)
+  int32_t *block_order;
+  int has_report;               // spill (l~, l) and c per token-head, Tier B radius per block
+  int n_blocks, pre_blocks;     // report blocks of both regions, and of the prefix
+  int pre_int8, suf_int8;       // the region's keys are dithered INT8 (blocks have a radius)
+  float *rspill;                // c per (group, spill entry), log2 units
+  float *ublk;                  // Tier B radius per (group, block, head), log2 units
   uint32_t *counters;
   float *partials;
   float *spill;

@@ -55,7 +55,8 @@ class MeterOut(ctypes.Structure):
                 ("log_a_b", c_void_p), ("bound_b_raw", c_void_p), ("meter_b", c_void_p),
                 ("delta_b", ctypes.c_double), ("value_err", c_void_p), ("v_norm_max", c_void_p),
                 ("out_bound", c_void_p), ("log_a_minus", c_void_p), ("bound_two_sided", c_void_p),
-                ("meter_two_sided", c_void_p)]
+                ("meter_two_sided", c_void_p), ("block_mass", c_void_p), ("block_excess", c_void_p),
+                ("block_excess_b", c_void_p), ("block_order", c_void_p)]
 
 
 class QuantArgs(ctypes.Structure):
@@ -72,7 +73,7 @@ _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class PlanInfo(ctypes.Structure):
@@ -256,17 +257,34 @@ METER_KEYS = ("tv", "bound_raw", "meter", "log_a")
 TIER_B_KEYS = ("log_a_b", "bound_b_raw", "meter_b")
 VALUE_KEYS = ("value_err", "v_norm_max", "out_bound")
 TWO_SIDED_KEYS = ("log_a_minus", "bound_two_sided", "meter_two_sided")
+REPORT_KEYS = ("block_mass", "block_excess", "block_order")
+INT8_BLOCK_TOKENS = 256
+
+
+def n_report_blocks(prefix: Optional["RegionView"], suffix: Optional["RegionView"]) -> int:
+    """Blocks of the risk report: 256-token blocks per region, prefix first."""
+    return sum(-(-r.length // INT8_BLOCK_TOKENS) for r in (prefix, suffix) if r is not None)
+
+
+def _meter_keys(meter, tier_b_delta, value_bound, two_sided, report):
+    if not meter:
+        return ()
+    keys = METER_KEYS
+    keys += TIER_B_KEYS if tier_b_delta is not None else ()
+    keys += VALUE_KEYS if value_bound else ()
+    keys += TWO_SIDED_KEYS if two_sided else ()
+    keys += REPORT_KEYS + (("block_excess_b",) if tier_b_delta is not None else ()) if report else ()
+    return keys
 
 
 def plan(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
          suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
          meter: bool = True, meter_only: bool = False, tier_b_delta: Optional[float] = None,
-         value_bound: bool = False, two_sided: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False, report: bool = False) -> dict:
     """kvq_decode_plan for the arguments decode_attn would pass (host only;
     the output and meter pointers only need to be non-NULL and aligned)."""
     dummy = _ptr(q) if meter else None
-    keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
-            + (VALUE_KEYS if value_bound else ()) + (TWO_SIDED_KEYS if two_sided else ())) if meter else ()
+    keys = _meter_keys(meter, tier_b_delta, value_bound, two_sided, report)
     m = MeterOut(**{k: dummy for k in keys}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else q, sm_scale, split_tokens,
                       num_kv_heads, need_v=not meter_only)
@@ -281,19 +299,25 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
                 meter: bool = True, workspace: Optional[Workspace] = None, out=None,
                 meter_bufs=None, stream=None, meter_only: bool = False,
                 tier_b_delta: Optional[float] = None, value_bound: bool = False,
-                two_sided: bool = False):
+                two_sided: bool = False, report: bool = False):
     """kvq_decode_attn (or kvq_meter when meter_only).  Returns (out, dict of
     meter tensors); tier_b_delta adds the Tier B outputs with that failure
     probability, value_bound the value term and the joint output bound,
-    two_sided the two-sided form of the meter."""
+    two_sided the two-sided form of the meter, report the per-block risk
+    report ([batch, num_q_heads, n_blocks] arrays)."""
     lib = load()
     batch, hq, d = q.shape
     if out is None and not meter_only:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
     if meter_bufs is None:
-        keys = (METER_KEYS + (TIER_B_KEYS if tier_b_delta is not None else ())
-                + (VALUE_KEYS if value_bound else ()) + (TWO_SIDED_KEYS if two_sided else ())) if meter else ()
-        meter_bufs = {k: torch.empty((batch, hq), dtype=torch.float32, device=q.device) for k in keys}
+        nb = n_report_blocks(prefix, suffix)
+        meter_bufs = {}
+        for k in _meter_keys(meter, tier_b_delta, value_bound, two_sided, report):
+            if k.startswith("block_"):
+                meter_bufs[k] = torch.empty((batch, hq, nb), device=q.device,
+                                            dtype=torch.int32 if k == "block_order" else torch.float32)
+            else:
+                meter_bufs[k] = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
     m = MeterOut(**{k: _ptr(v) for k, v in meter_bufs.items()}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else out, sm_scale, split_tokens,
                       num_kv_heads, need_v=not meter_only)

@@ -108,21 +108,23 @@ class GpuCase:
                               page_size=ps, use_witness=st.witness is not None)
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
-            workspace=None, tier_b_delta=None, value_bound: bool = False, two_sided: bool = False):
+            workspace=None, tier_b_delta=None, value_bound: bool = False, two_sided: bool = False,
+            report: bool = False):
         out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
                                       self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
                                       meter=meter, meter_only=meter_only, workspace=workspace,
                                       tier_b_delta=tier_b_delta, value_bound=value_bound,
-                                      two_sided=two_sided)
+                                      two_sided=two_sided, report=report)
         torch.cuda.synchronize()
         return out, m
 
 
 def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None,
-         value_bound: bool = False, two_sided: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False, report: bool = False) -> dict:
     return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
                          sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only,
-                         tier_b_delta=tier_b_delta, value_bound=value_bound, two_sided=two_sided)
+                         tier_b_delta=tier_b_delta, value_bound=value_bound, two_sided=two_sided,
+                         report=report)
 
 
 def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):

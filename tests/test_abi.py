@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 6
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 7
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -206,6 +206,31 @@ def test_value_side_and_tier_a_arguments_are_checked(lib):
     k16 = _args(batch=4, suffix=4096, kf="bf16", vf="fp8", exact=False, witness=False)
     k16.suffix.v_witness = FAKE
     assert lib.kvq_decode_plan(ctypes.byref(k16), ctypes.byref(kvq.MeterOut(**vals)), 0,
+                               ctypes.byref(info)) == 0
+
+
+def test_block_report_arguments_and_workspace(lib, monkeypatch):
+    """The report adds the c spill and the per-block radii to the workspace,
+    never takes the team plan, needs the Tier B request for Tier B's
+    contributions, and ranks at most 512 blocks."""
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    a = _args(batch=64, suffix=12628)
+    info = kvq.PlanInfo()
+    base = kvq.MeterOut(tv=FAKE, meter=FAKE)
+    rep = kvq.MeterOut(tv=FAKE, meter=FAKE, block_mass=FAKE, block_excess=FAKE, block_order=FAKE)
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    n0 = _plan(lib, a, base).workspace_bytes
+    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    p = _plan(lib, a, rep)
+    groups, rows, nb = 64 * 8, 12640, 50
+    assert p.team == 0
+    assert p.workspace_bytes == n0 + groups * rows * 4 * 4 + groups * nb * 4 * 4
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(kvq.MeterOut(block_excess_b=FAKE)), 0,
+                               ctypes.byref(info)) == 5
+    long = _args(batch=1, suffix=131073)                   # 513 blocks
+    assert lib.kvq_decode_plan(ctypes.byref(long), ctypes.byref(kvq.MeterOut(block_order=FAKE)), 0,
+                               ctypes.byref(info)) == 5
+    assert lib.kvq_decode_plan(ctypes.byref(long), ctypes.byref(kvq.MeterOut(block_mass=FAKE)), 0,
                                ctypes.byref(info)) == 0
 
 
