@@ -274,3 +274,32 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
             assert abs(mt - mtr) <= TOL_METER, (b, qh, mt, mtr)
             worst["two_sided"] = max(worst.get("two_sided", 0.0), abs(tg - tr) / max(1.0, tr))
     return worst
+
+
+def check_block_report(case: GpuCase, meter, b: int, kvh: int, ref, with_b: bool) -> None:
+    """The block report of cell (b, kvh) against the oracle's: masses and
+    contributions within 1e-5 (relative above 1); the order ranks the GPU's
+    own keys and, along it, the oracle's keys do not increase beyond that
+    tolerance (near-equal blocks may swap)."""
+    from oracle.pipeline import block_report
+    cfg = case.cfg
+    pre = cfg.prefix.length if cfg.prefix is not None else 0
+    caps = ([pre] if pre else []) + [cfg.suffix.length]
+    lens = ([pre] if pre else []) + [int(case.inp["suffix_lens"][b])]
+    rep = block_report(ref, lens, caps)
+    nb = meter["block_mass"].shape[-1]
+    assert nb == sum(-(-c // 256) for c in caps)
+    for h in range(cfg.group):
+        qh = kvh * cfg.group + h
+        keys = ["block_mass", "block_excess"] + (["block_excess_b"] if with_b else [])
+        for k in keys:
+            g = meter[k][b, qh].double().cpu().numpy()
+            r = rep[k][h]
+            assert np.all(np.abs(g - r) <= 1e-5 * np.maximum(1.0, np.abs(r))), (k, b, qh)
+        kk = "block_excess_b" if with_b else "block_excess"
+        key = meter[kk][b, qh].double().cpu().numpy()
+        order = meter["block_order"][b, qh].cpu().numpy()
+        assert sorted(order.tolist()) == list(range(nb))
+        assert np.all(np.diff(key[order]) <= 0)
+        rkey = rep[kk][h][order]
+        assert np.all(np.diff(rkey) <= 2e-5 * np.maximum(1.0, np.abs(rkey[1:])))

@@ -4,7 +4,7 @@ oracle computes one by one."""
 import pytest
 import torch
 
-from cells import GpuCase, check_results, check_stored, oracle_cell
+from cells import GpuCase, check_block_report, check_results, check_stored, oracle_cell
 from workloads import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -35,5 +35,34 @@ def test_full_size_sampled_cells(gpu_lib, idx):
     assert torch.all(m["tv"] <= m["bound_raw"] + 1e-6)
     assert torch.all(torch.isfinite(out))
     print(f"[{cfg.name} layer {layer}] sampled={len(cells)} worst={worst}", flush=True)
+    del case
+    torch.cuda.empty_cache()
+
+
+EXTENSIONS = {4: 1e-9, 5: None}                   # Tier B's delta (INT8 keys only)
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_full_size_meter_extensions_sampled_cells(gpu_lib, idx):
+    """Tier B (INT8), the value side and joint output bound, the two-sided
+    form and the block report (512 blocks at 131,072 tokens) in one call at
+    full size, on sampled cells against the oracle."""
+    cfg = CONFIGS[idx]
+    layer = cfg.layers - 1
+    delta = EXTENSIONS[idx]
+    case = GpuCase(cfg, layer=layer, page_seed=1, value_witness=True)
+    out, m = case.run(split_tokens=cfg.split_tokens, tier_b_delta=delta, value_bound=True, two_sided=True,
+                      report=True)
+    worst = {}
+    for b, kvh in SAMPLES[idx]:
+        encs, ref = oracle_cell(case, b, kvh, tier_b_delta=delta)
+        check_stored(case, b, kvh, encs)
+        w = check_results(case, out, m, b, kvh, ref)
+        check_block_report(case, m, b, kvh, ref, with_b=delta is not None)
+        for k, v in w.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    assert {"value_err", "two_sided"} <= set(worst) and ("bound_b" in worst) == (delta is not None)
+    assert torch.all(m["tv"] <= m["bound_two_sided"] + 1e-6)
+    print(f"[{cfg.name} layer {layer} extensions] sampled={len(SAMPLES[idx])} worst={worst}", flush=True)
     del case
     torch.cuda.empty_cache()
