@@ -229,7 +229,10 @@ struct TileSrc {
 // witness (the common quantized case).  Then every load of a tile is issued
 // unconditionally, which lets the compiler keep the next tile's loads in
 // flight across the current tile's math (no load sits under a runtime branch).
-template <int KF, int VF, bool PAGED, bool FULL, bool SPILL_LDS>
+// EXT: Tier B, the value side, the two-sided form and the block report are
+// compiled in (they are tested at run time); without it the tile loop has
+// none of their code.
+template <int KF, int VF, bool PAGED, bool FULL, bool SPILL_LDS, bool EXT = false>
 __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh, int grp, int c0,
                                            int c1, float2 *spill_s, float (*w_s)[64],
                                            float (*part_s)[4][PART_STRIDE]) {
@@ -250,15 +253,15 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // block of INT8 keys and 1 for keys stored as BF16 (u = 0).
   // (the team launch never takes Tier B or the value side: SPILL_LDS compiles
   // them out of its kernel)
-  const bool do_b = !SPILL_LDS && d.has_tier_b != 0;
+  const bool do_b = EXT && !SPILL_LDS && d.has_tier_b != 0;
   // value side (WitCert Sec. 3 output bound): zv accumulates p~ rho on the
   // attention maximum, vmax the largest ||v|| of the chunk's tokens
-  const bool do_v = !SPILL_LDS && d.has_value != 0;
+  const bool do_v = EXT && !SPILL_LDS && d.has_value != 0;
   // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
-  const bool do_n = !SPILL_LDS && d.has_two_sided != 0;
+  const bool do_n = EXT && !SPILL_LDS && d.has_two_sided != 0;
   // block report: spill (l~, l) and c of every token-head, the Tier B radius
   // of every INT8 block
-  const bool do_r = !SPILL_LDS && d.has_report != 0;
+  const bool do_r = EXT && !SPILL_LDS && d.has_report != 0;
   float tb_l = 0.0f, eub = 1.0f;
   if (do_b) {
     const int sl = d.suffix_cap > 0
@@ -693,7 +696,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 
 // One work-group's share of the per-chunk plan: chunk `chunk_idx` of group
 // grp = (request, KV head) in the region d.region, then the chunk epilogue.
-template <int KF, int VF, bool PAGED, bool FULL>
+template <int KF, int VF, bool PAGED, bool FULL, bool EXT>
 __device__ __forceinline__ void chunk_work(const DecodeLaunch &d, int grp, int chunk_idx, float (*w_s)[64],
                                            float (*part_s)[4][PART_STRIDE]) {
   const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
@@ -701,7 +704,7 @@ __device__ __forceinline__ void chunk_work(const DecodeLaunch &d, int grp, int c
   const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
   const int c0 = chunk_idx * d.chunk;
   const int c1 = min(c0 + d.chunk, len);
-  mfma_chunk<KF, VF, PAGED, FULL, false>(d, b, kvh, grp, c0, c1, nullptr, w_s, part_s);
+  mfma_chunk<KF, VF, PAGED, FULL, false, EXT>(d, b, kvh, grp, c0, c1, nullptr, w_s, part_s);
   chunk_epilogue<4>(d, part_s, grp, chunk_idx, b, kvh);
 }
 

@@ -7,7 +7,7 @@
 
 namespace kvq {
 
-template <int KF, int VF, bool PAGED, bool FULL>
+template <int KF, int VF, bool PAGED, bool FULL, bool EXT>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch d) {
   const unsigned per_xcd = gridDim.x >> 3;
   const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
   if (L >= n_work) return;
   __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
   __shared__ float part_s[WAVES][4][PART_STRIDE];
-  chunk_work<KF, VF, PAGED, FULL>(d, (int)(L / (unsigned)d.n_chunks), (int)(L % (unsigned)d.n_chunks), w_s,
+  chunk_work<KF, VF, PAGED, FULL, EXT>(d, (int)(L / (unsigned)d.n_chunks), (int)(L % (unsigned)d.n_chunks), w_s,
                                   part_s);
 }
 
@@ -364,10 +364,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
 template <int KF, int VF, bool PAGED>
 static void launch_p(const DecodeLaunch &d, hipStream_t stream, dim3 grid) {
   const bool full = d.has_tv && d.has_meter && d.region.exact_fmt == EX_BF16 && d.region.witness;
-  if (full)
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, true>), grid, dim3(256), 0, stream, d);
+  const bool ext = launch_has_extensions(d);
+  if (full && ext)
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, true, true>), grid, dim3(256), 0, stream, d);
+  else if (full)
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, true, false>), grid, dim3(256), 0, stream, d);
+  else if (ext)
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, false, true>), grid, dim3(256), 0, stream, d);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, false>), grid, dim3(256), 0, stream, d);
+    hipLaunchKernelGGL((decode_mfma_kernel<KF, VF, PAGED, false, false>), grid, dim3(256), 0, stream, d);
 }
 
 template <int KF, int VF>

@@ -12,7 +12,7 @@
 
 namespace kvq {
 
-template <int KF, int VF1, int VF2, bool PAGED2, bool FULL>
+template <int KF, int VF1, int VF2, bool PAGED2, bool FULL, bool EXT>
 __global__ __launch_bounds__(256, 2) void decode_two_kernel(const DecodeLaunch d1, const DecodeLaunch d2) {
   const unsigned per_xcd = gridDim.x >> 3;
   const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
@@ -22,9 +22,9 @@ __global__ __launch_bounds__(256, 2) void decode_two_kernel(const DecodeLaunch d
   __shared__ float part_s[WAVES][4][PART_STRIDE];
   const int grp = (int)(L / nc), ci = (int)(L % nc);
   if (ci < d1.n_chunks)
-    chunk_work<KF, VF1, false, FULL>(d1, grp, ci, w_s, part_s);
+    chunk_work<KF, VF1, false, FULL, EXT>(d1, grp, ci, w_s, part_s);
   else
-    chunk_work<KF, VF2, PAGED2, FULL>(d2, grp, ci - d1.n_chunks, w_s, part_s);
+    chunk_work<KF, VF2, PAGED2, FULL, EXT>(d2, grp, ci - d1.n_chunks, w_s, part_s);
 }
 
 namespace {
@@ -38,11 +38,19 @@ hipError_t launch_2(const DecodeLaunch &d1, const DecodeLaunch &d2, hipStream_t 
   const long work = (long)d1.batch * d1.h_kv * (d1.n_chunks + d2.n_chunks);
   const dim3 grid((unsigned)((work + 7) / 8 * 8));
   // FULL = false is exact for every case (it tests the flags at run time)
-  if (KF == KVQ_FMT_FP8_E4M3 && full_region(d1) && full_region(d2))
-    hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, KF == KVQ_FMT_FP8_E4M3>), grid, dim3(256), 0, s,
-                       d1, d2);
-  else
-    hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, false>), grid, dim3(256), 0, s, d1, d2);
+  constexpr bool F8 = KF == KVQ_FMT_FP8_E4M3;
+  const bool full = F8 && full_region(d1) && full_region(d2);
+  if (launch_has_extensions(d1)) {
+    if (full)
+      hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, F8, true>), grid, dim3(256), 0, s, d1, d2);
+    else
+      hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, false, true>), grid, dim3(256), 0, s, d1, d2);
+  } else {
+    if (full)
+      hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, F8, false>), grid, dim3(256), 0, s, d1, d2);
+    else
+      hipLaunchKernelGGL((decode_two_kernel<KF, VF1, VF2, PAGED2, false, false>), grid, dim3(256), 0, s, d1, d2);
+  }
   return hipGetLastError();
 }
 

@@ -89,6 +89,11 @@ struct DecodeLaunch {
 
 // m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, m-, z-, 5 pad
 constexpr int PART_STRIDE = 144;
+// Tier B, the value side, the two-sided form or the block report requested:
+// the matrix-core kernels then take their instance with that code compiled in
+inline bool launch_has_extensions(const DecodeLaunch &d) {
+  return d.has_tier_b || d.has_value || d.has_two_sided || d.has_report;
+}
 constexpr int PART_VMAX = 136;
 constexpr int PART_MN = 137, PART_ZN = 138;
 
