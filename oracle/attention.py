@@ -24,6 +24,10 @@ Two-sided form (WitCert Sec. 4.3, Proposition 1), with A- = E_p~[e^{-c}]:
     bound_two_sided = 1/2 (A/A- - A-/A) = sinh(log A - log A-); +inf past float32
     meter_two_sided = min(1, bound_raw, bound_two_sided)
 
+Deterministic tanh shape (WitCert Sec. 6.4.2, the shape tanh(max_t Delta_t) of
+the compared system, evaluated with the same witness: Delta_t = c_t):
+    bound_tanh = tanh(max_t c_t)   (max-merged across splits)
+
 Tier B, the sub-Gaussian certificate of a subtractively dithered cache
 (WitCert Sec. 4.2, Lemma 2; the in-kernel form of Sec. 6.2.3):
     var_t   = sm_scale^2 / 12 * sum_c q_c^2 s_{c,t}^2    (s: the key's dither step
@@ -141,6 +145,7 @@ def decode_step(q, k_exact, k_hat, v_hat, w16, sm_scale: float, s_key=None, delt
     res = dict(out=out, out_exact=out_exact, tv=tv, log_a=log_a,
                bound_raw=bound_raw, meter=meter, l_exact=l_exact,
                l_tilde=l_tilde, c=c, p=p, p_tilde=pt, log_a_minus=log_a_minus,
+               bound_tanh=np.tanh(np.max(c, axis=1)) if c.shape[1] else np.zeros(c.shape[0]),
                bound_two_sided=two, meter_two_sided=np.minimum(np.minimum(1.0, bound_raw), two))
     if s_key is not None and delta_loc is not None:
         u = tier_b_radius(q, s_key, sm, l_tilde.shape[1], delta_loc)
