@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 7
+#define KVQ_ABI_VERSION 8
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -175,7 +175,11 @@ typedef struct kvq_attn_args {
  *                    (needs the Tier B request; they add up to A_B - 1)
  *   block_order    = int32 block indices by decreasing block_excess_b when
  *                    Tier B is requested, else block_excess; ties by lower
- *                    index (the page-in order); needs n_blocks <= 512. */
+ *                    index (the page-in order); needs n_blocks <= 512.
+ * Deterministic tanh shape (WitCert Sec. 6.4.2, the compared system's
+ * tanh(max_t Delta_t) with the same witness, Delta_t = c_t), same needs as
+ * Tier A:
+ *   bound_tanh = tanh(max_t c_t) */
 typedef struct kvq_meter_out {
   float *tv;
   float *bound_raw;
@@ -195,6 +199,7 @@ typedef struct kvq_meter_out {
   float *block_excess;
   float *block_excess_b;
   int32_t *block_order;
+  float *bound_tanh;
 } kvq_meter_out;
 
 /* Write path: quantize tokens [tok_begin, tok_end) of every sequence and store

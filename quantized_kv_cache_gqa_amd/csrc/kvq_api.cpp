@@ -217,10 +217,10 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     // Tier A (and the joint bound, which uses it): a region without a witness
     // counts as holding the exact keys (c = 0), which only keys stored as BF16
     // can; quantized keys without a witness are rejected, never metered as exact
-    const void *mn[] = {m->log_a_minus, m->bound_two_sided, m->meter_two_sided};
+    const void *mn[] = {m->log_a_minus, m->bound_two_sided, m->meter_two_sided, m->bound_tanh};
     for (const void *x : mn)
       if (x && !aligned16(x)) return KVQ_ERR_ALIGN;
-    const bool wants_two = m->log_a_minus || m->bound_two_sided || m->meter_two_sided;
+    const bool wants_two = m->log_a_minus || m->bound_two_sided || m->meter_two_sided || m->bound_tanh;
     const bool tier_b_req = m->log_a_b || m->bound_b_raw || m->meter_b;
     // the block report (WitCert Sec. 6.3.5): Tier A's contributions need c,
     // Tier B's need the Tier B request; the order ranks Tier B when requested
@@ -340,6 +340,7 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   if (m) {
     d.log_a_minus = m->log_a_minus; d.bound_two_sided = m->bound_two_sided;
     d.meter_two_sided = m->meter_two_sided;
+    d.bound_tanh = m->bound_tanh;
   }
   d.has_two_sided = p.two_sided;
   if (m) {

@@ -106,13 +106,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   // block report: spill (l~, l) and c of every token-head, the Tier B radius
   // of every INT8 block
   const bool do_r = d.has_report != 0;
-  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G], mn[G], zn[G];
+  float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G], mn[G], zn[G], cmx[G];
   float vmax = 0.0f;
   float acc[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     mq[h] = mm[h] = me[h] = mn[h] = NEG_INF;
-    zq[h] = zm[h] = ze[h] = zb[h] = zv[h] = zn[h] = 0.0f;
+    zq[h] = zm[h] = ze[h] = zb[h] = zv[h] = zn[h] = cmx[h] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
   }
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
             mn[h] = yn;
           }
           zn[h] += valid ? fast_exp2(yn - mn[h]) : 0.0f;
+          if (valid) cmx[h] = fmaxf(cmx[h], c);
         }
       }
     }
@@ -358,6 +359,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         const float m = fmaxf(mn[h], m2);
         zn[h] = zn[h] * merge_factor(mn[h], m) + z2 * merge_factor(m2, m);
         mn[h] = m;
+        cmx[h] = fmaxf(cmx[h], __shfl_xor(cmx[h], off));
       }
       if (do_tv) {
         const float m2 = __shfl_xor(me[h], off), z2 = __shfl_xor(ze[h], off);
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         part_s[wv][h][PART_VMAX] = vmax;
         part_s[wv][h][PART_MN] = mn[h];
         part_s[wv][h][PART_ZN] = zn[h];
+        part_s[wv][h][PART_CMAX] = cmx[h];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];

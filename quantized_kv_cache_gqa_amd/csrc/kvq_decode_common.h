@@ -236,16 +236,16 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
                          : d.partials + ((size_t)grp * total_chunks + d.chunk_base + chunk_idx) * G * PART_STRIDE;
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if ((k == 6 && !d.has_tier_b) || (k == 7 && !d.has_value) || k > PART_ZN ||
+    if ((k == 6 && !d.has_tier_b) || (k == 7 && !d.has_value) || k > PART_CMAX ||
         (k == PART_VMAX && !d.has_value) || (k >= PART_MN && !d.has_two_sided))
       continue;
     // which maximum governs this field: its own (m~, m', m_e, m-) or m~
-    const int mk = k < 6 ? (k & ~1) : (k >= PART_MN ? PART_MN : 0);
+    const int mk = k < 6 ? (k & ~1) : ((k == PART_MN || k == PART_ZN) ? PART_MN : 0);
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
     float r;
-    if (k == PART_VMAX) {                            // a plain maximum
+    if (k == PART_VMAX || k == PART_CMAX) {          // a plain maximum
       r = 0.0f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) r = fmaxf(r, part_s[w][h][k]);
@@ -293,7 +293,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       Me = fmaxf(Me, rd(pc + 4));
       if (d.has_two_sided) Mn = fmaxf(Mn, rd(pc + PART_MN));
     }
-    float Zn = 0.0f;
+    float Zn = 0.0f, Cmax = 0.0f;
     float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, Zv = 0.0f, Vmax = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c = 0; c < total_chunks; ++c) {
       const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
@@ -304,7 +304,10 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         Zv += rd(pc + 7) * fq;
         Vmax = fmaxf(Vmax, rd(pc + PART_VMAX));
       }
-      if (d.has_two_sided) Zn += rd(pc + PART_ZN) * merge_factor(rd(pc + PART_MN), Mn);
+      if (d.has_two_sided) {
+        Zn += rd(pc + PART_ZN) * merge_factor(rd(pc + PART_MN), Mn);
+        Cmax = fmaxf(Cmax, rd(pc + PART_CMAX));
+      }
       Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
       Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
       o0 += rd(pc + 8 + lane) * fq;
@@ -325,7 +328,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       if (d.log_a) d.log_a[qh] = (float)log_a;
       if (d.bound_raw) d.bound_raw[qh] = bf;
       if (d.meter) d.meter[qh] = fminf(1.0f, bf);
-      if (d.log_a_minus || d.bound_two_sided || d.meter_two_sided) {
+      if (d.log_a_minus || d.bound_two_sided || d.meter_two_sided || d.bound_tanh) {
         // two-sided form (WitCert Prop. 1): 1/2 (A/A- - A-/A) = sinh(log A - log A-)
         double log_am = 0.0;
         if (d.has_two_sided && Zq > 0.0f && Zn > 0.0f)
@@ -335,6 +338,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         if (d.log_a_minus) d.log_a_minus[qh] = (float)log_am;
         if (d.bound_two_sided) d.bound_two_sided[qh] = tf;
         if (d.meter_two_sided) d.meter_two_sided[qh] = fminf(fminf(1.0f, bf), tf);
+        // tanh shape: tanh(max_t c_t), c in natural units
+        if (d.bound_tanh) d.bound_tanh[qh] = (float)tanh((double)Cmax * 0.69314718055994530942);
       }
       if (d.has_value) {
         // value side and the joint output bound (WitCert Sec. 3): the meter

@@ -377,6 +377,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   float zb = 0.0f;                   // Tier B: sum p~ e^u on the attention maximum
   float zv = 0.0f, vmax = 0.0f;      // value side: sum p~ rho, max ||v||
   float mn = NEG_INF, zn = 0.0f;     // l~ - c (Prop. 1's A-)
+  float cmax = 0.0f;                 // max c (the tanh shape)
   // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
   // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
   f32x4_t ov[8];
@@ -505,6 +506,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         mn = y;
       }
       zn += valid ? fast_exp2(y - mn) : 0.0f;
+      if (valid) cmax = fmaxf(cmax, cc);
     }
 
     // ---- output accumulation
@@ -649,6 +651,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       const float m = fmaxf(mn, m2);
       zn = zn * merge_factor(mn, m) + z2 * merge_factor(m2, m);
       mn = m;
+      cmax = fmaxf(cmax, __shfl_xor(cmax, off));
     }
   }
   if constexpr (VF == KVQ_FMT_BF16) {
@@ -669,6 +672,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][PART_VMAX] = vmax;
     part_s[wv][hh][PART_MN] = mn;
     part_s[wv][hh][PART_ZN] = zn;
+    part_s[wv][hh][PART_CMAX] = cmax;
   }
   if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
     if (lane < 16) {

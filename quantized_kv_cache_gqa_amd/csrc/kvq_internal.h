@@ -69,7 +69,8 @@ struct DecodeLaunch {
   float *value_err, *v_norm_max, *out_bound;   // value side outputs (nullable)
   int has_value;                // value side requested: sum p~ rho (field 7), max ||v|| (field 136)
   float *log_a_minus, *bound_two_sided, *meter_two_sided;   // two-sided form (nullable)
-  int has_two_sided;            // accumulate E_p~[e^{-c}] (fields 137, 138)
+  int has_two_sided;            // accumulate E_p~[e^{-c}] (fields 137, 138) and max c (field 139)
+  float *bound_tanh;            // tanh(max_t c_t) (nullable)
   float *block_mass, *block_excess, *block_excess_b;   // block report outputs (nullable)
   int32_t *block_order;
   int has_report;               // spill (l~, l) and c per token-head, Tier B radius per block
@@ -87,15 +88,16 @@ struct DecodeLaunch {
   int silent_member;            // team launch: member that never publishes (test hook; -1: none)
 };
 
-// m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, m-, z-, 5 pad
+// m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, m-, z-, max c, 4 pad
 constexpr int PART_STRIDE = 144;
-// Tier B, the value side, the two-sided form or the block report requested:
-// the matrix-core kernels then take their instance with that code compiled in
+constexpr int PART_VMAX = 136;
+constexpr int PART_MN = 137, PART_ZN = 138, PART_CMAX = 139;
+// Tier B, the value side, the two-sided form, the tanh shape or the block
+// report requested: the matrix-core kernels then take their instance with
+// that code compiled in
 inline bool launch_has_extensions(const DecodeLaunch &d) {
   return d.has_tier_b || d.has_value || d.has_two_sided || d.has_report;
 }
-constexpr int PART_VMAX = 136;
-constexpr int PART_MN = 137, PART_ZN = 138;
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
 // Matrix-core kernel for GQA group 4 with FP8/BF16 keys and values.

@@ -56,7 +56,7 @@ class MeterOut(ctypes.Structure):
                 ("delta_b", ctypes.c_double), ("value_err", c_void_p), ("v_norm_max", c_void_p),
                 ("out_bound", c_void_p), ("log_a_minus", c_void_p), ("bound_two_sided", c_void_p),
                 ("meter_two_sided", c_void_p), ("block_mass", c_void_p), ("block_excess", c_void_p),
-                ("block_excess_b", c_void_p), ("block_order", c_void_p)]
+                ("block_excess_b", c_void_p), ("block_order", c_void_p), ("bound_tanh", c_void_p)]
 
 
 class QuantArgs(ctypes.Structure):
@@ -73,7 +73,7 @@ _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class PlanInfo(ctypes.Structure):
@@ -256,7 +256,7 @@ class Workspace:
 METER_KEYS = ("tv", "bound_raw", "meter", "log_a")
 TIER_B_KEYS = ("log_a_b", "bound_b_raw", "meter_b")
 VALUE_KEYS = ("value_err", "v_norm_max", "out_bound")
-TWO_SIDED_KEYS = ("log_a_minus", "bound_two_sided", "meter_two_sided")
+TWO_SIDED_KEYS = ("log_a_minus", "bound_two_sided", "meter_two_sided", "bound_tanh")
 REPORT_KEYS = ("block_mass", "block_excess", "block_order")
 INT8_BLOCK_TOKENS = 256
 

@@ -273,6 +273,8 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
             mt, mtr = float(meter["meter_two_sided"][b, qh]), float(ref["meter_two_sided"][h])
             assert abs(mt - mtr) <= TOL_METER, (b, qh, mt, mtr)
             worst["two_sided"] = max(worst.get("two_sided", 0.0), abs(tg - tr) / max(1.0, tr))
+            th, thr = float(meter["bound_tanh"][b, qh]), float(ref["bound_tanh"][h])
+            assert abs(th - thr) <= TOL_METER, (b, qh, th, thr)
     return worst
 
 

@@ -461,6 +461,7 @@ def test_two_sided_form_every_cell(gpu_lib, kernel, monkeypatch, name):
     assert torch.all(m["tv"] <= m["bound_two_sided"])
     assert torch.all(m["meter_two_sided"] <= m["meter"])
     assert torch.all(m["log_a_minus"] <= 0) and torch.all(m["log_a"] >= 0)
+    assert torch.all(m["tv"] <= m["bound_tanh"] + 1e-6) and torch.all(m["bound_tanh"] <= 1)
     monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
     o2, m2 = case.run()
     assert torch.equal(out, o2)
