@@ -73,9 +73,10 @@ def token_head_bytes(k_fmt, v_fmt, exact_k, witness, with_v=True):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--workload", type=int, default=3,
-                    help="3: the decode step (default); 1, 2, 4, 5: time one layer's decode launch of "
-                         "that workload against its roofline (a measurement aid, not the bench line)")
+    ap.add_argument("--workload", type=int, default=0,
+                    help="0: the 36-layer decode step of the batch-64 workload (the bench line); 1..5: "
+                         "time one layer's decode launch of that workload against its roofline, also "
+                         "with the meter off and with the meter extensions (a measurement aid)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
@@ -177,7 +178,7 @@ def measure_workload(idx: int, reps: int, warmup: int):
     bytes_launch = 0
     if cfg.prefix is not None and cfg.prefix.length > 0:
         pr = cfg.prefix
-        st = kvq.alloc_stored(1, HKV, pr.length, pr.k_fmt, pr.v_fmt, pr.witness, dev)
+        st = kvq.alloc_stored(1, HKV, pr.length, pr.k_fmt, pr.v_fmt, pr.witness, dev, value_witness=True)
         kvq.quantize_into(st, inp["prefix_k"][None].contiguous(), inp["prefix_v"][None].contiguous(),
                           seed=seed, layer=layer, stream_id=1_000_000)
         prefix = kvq.RegionView(st, pr.length, k_exact=inp["prefix_k"] if pr.exact_k else None, seed=seed,
@@ -185,7 +186,8 @@ def measure_workload(idx: int, reps: int, warmup: int):
         # the shared prefix counts once per launch (every request reads the same rows)
         bytes_launch += HKV * pr.length * token_head_bytes(pr.k_fmt, pr.v_fmt, pr.exact_k, pr.witness)
     sf = cfg.suffix
-    st = kvq.alloc_stored(B, HKV, sf.length, sf.k_fmt, sf.v_fmt, sf.witness, dev)
+    # value records too (the value side of the extensions timing)
+    st = kvq.alloc_stored(B, HKV, sf.length, sf.k_fmt, sf.v_fmt, sf.witness, dev, value_witness=True)
     kvq.quantize_into(st, inp["suffix_k"], inp["suffix_v"], seed=seed, layer=layer, stream_id=0)
     lens = inp["suffix_lens"]
     exact = inp["suffix_k"] if sf.exact_k else None
@@ -205,7 +207,7 @@ def measure_workload(idx: int, reps: int, warmup: int):
             return o.contiguous()
 
         paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
-                           scatter(st.v_scale), scatter(st.witness))
+                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
         suffix = kvq.RegionView(paged, sf.length, k_exact=scatter(exact), lengths=lens, page_table=table,
                                 page_size=ps, use_witness=sf.witness)
     else:
@@ -221,7 +223,20 @@ def measure_workload(idx: int, reps: int, warmup: int):
     a = kvq._attn_args(inp["q"], prefix, suffix, out, sm, 0, HKV)
     info = kvq.PlanInfo()
     assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter), 0, ctypes.byref(info)) == 0
-    ws = torch.empty(max(info.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    # every extension at once (per-chunk plan): value side, two-sided form,
+    # tanh shape, block report, and Tier B where the keys allow it
+    nb = kvq.n_report_blocks(prefix, suffix)
+    tier_b_ok = sf.k_fmt in ("int8", "bf16") and (cfg.prefix is None or cfg.prefix.k_fmt in ("int8", "bf16"))
+    ext = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev)
+           for k in kvq.VALUE_KEYS + kvq.TWO_SIDED_KEYS + (kvq.TIER_B_KEYS if tier_b_ok else ())}
+    ext.update({"block_mass": torch.empty((B, HQ, nb), dtype=torch.float32, device=dev),
+                "block_excess": torch.empty((B, HQ, nb), dtype=torch.float32, device=dev),
+                "block_order": torch.empty((B, HQ, nb), dtype=torch.int32, device=dev)})
+    meter_x = kvq.MeterOut(**{k: v.data_ptr() for k, v in list(mbuf.items()) + list(ext.items())},
+                           delta_b=1e-9 if tier_b_ok else 0.0)
+    info_x = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter_x), 0, ctypes.byref(info_x)) == 0
+    ws = torch.empty(max(info.workspace_bytes, info_x.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     assert lib.kvq_workspace_init(ws.data_ptr(), ws.numel(), sp) == 0
@@ -245,6 +260,13 @@ def measure_workload(idx: int, reps: int, warmup: int):
         e1.record(stream)
     torch.cuda.synchronize()
     off_ms = sorted(e0.elapsed_time(e1) for e0, e1 in off_evs)[reps // 2]
+    x_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in x_evs:
+        e0.record(stream)
+        assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(meter_x), ws.data_ptr(), ws.numel(), sp) == 0
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ext_ms = sorted(e0.elapsed_time(e1) for e0, e1 in x_evs)[reps // 2]
     # with Tier B as well (dithered INT8 keys: the sub-Gaussian certificate)
     tier_b_ms = None
     if sf.k_fmt == "int8":
@@ -267,6 +289,9 @@ def measure_workload(idx: int, reps: int, warmup: int):
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
         "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
+        "with_all_extensions_launch_ms": ext_ms,
+        "extensions": "value side, two-sided form, tanh shape, block report"
+                      + (", Tier B" if tier_b_ok else "") + f" (plan: {info_x.chunks} chunk(s), team {info_x.team})",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS},
         "plan": plan}), flush=True)
@@ -278,7 +303,7 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design doc describes how the step would shard)", file=sys.stderr)
         sys.exit(2)
-    if args.workload != 3:
+    if args.workload != 0:
         measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1))
         return
     import numpy as np

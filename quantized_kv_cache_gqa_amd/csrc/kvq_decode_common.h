@@ -134,18 +134,17 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
 //   mass_j = sum p~_t,  excess_j = sum p~_t (e^{c_t} - 1),
 //   excess_b_j = mass_j (e^{u_j} - 1) with the block's Tier B radius,
 // then the blocks ranked by decreasing excess (Tier B's when requested), ties
-// by lower index.  Thread tid takes entries tid + 256 i of the block, all of
-// head (tid % 4G) / 4; sums reduce over the other lane bits, then the
-// wavefronts in order (bitwise reproducible).
+// by lower index.  Wavefront w takes blocks w, w + 4, ...; lane l reads the
+// block's entries l + 64 i, all of head (l % 4G) / 4, and the sums reduce
+// over the other lane bits in a fixed order (bitwise reproducible).
 template <int G>
 __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh, bool single, int suf_len,
                                   const float (*fin)[6]) {
   constexpr float LN2 = 0.69314718055994530942f;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  __shared__ float rsum_s[WAVES][2][G];
   __shared__ float rkey_s[G][512];
-  const int hmine = (tid % (4 * G)) / 4;
+  const int hmine = (lane % (4 * G)) / 4;
   const float Mt = fin[hmine][0], iZt = fin[hmine][1];
   auto rd = [&](const float *p) { return single ? *p : ld_dev(p); };
   for (int region = 0; region < 2; ++region) {
@@ -157,11 +156,11 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
     if (nb == 0) continue;
     const float *sp = spill_region<G>(d, grp, region == 0);
     const float *rp = rspill_region<G>(d, grp, region == 0);
-    for (int j = 0; j < nb; ++j) {                 // uniform over the work-group
+    for (int j = wv; j < nb; j += WAVES) {         // uniform over the wavefront
       float ms = 0.0f, ex = 0.0f;
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const int e = KVQ_INT8_BLOCK * G * j + tid + 256 * i;
+#pragma unroll 4
+      for (int i = 0; i < 4 * G; ++i) {
+        const int e = KVQ_INT8_BLOCK * G * j + lane + 64 * i;
         const int tile = e / (16 * G), r = e % (16 * G);
         const int t = 16 * tile + 4 * (r / (4 * G)) + (r & 3);
         if (t < n) {
@@ -176,26 +175,20 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         ex += __shfl_xor(ex, off);
       }
       if (lane < 4 * G && (lane & 3) == 0) {
-        rsum_s[wv][0][lane >> 2] = ms;
-        rsum_s[wv][1][lane >> 2] = ex;
-      }
-      __syncthreads();
-      if (tid < G) {
-        const float M = ((rsum_s[0][0][tid] + rsum_s[1][0][tid]) + rsum_s[2][0][tid]) + rsum_s[3][0][tid];
-        const float E = ((rsum_s[0][1][tid] + rsum_s[1][1][tid]) + rsum_s[2][1][tid]) + rsum_s[3][1][tid];
+        const int h = lane >> 2;
         float Eb = 0.0f;
-        if (d.has_tier_b && i8 && M > 0.0f)
-          Eb = M * expm1f(rd(d.ublk + ((size_t)grp * d.n_blocks + gb0 + j) * G + tid) * LN2);
-        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + tid) * d.n_blocks + gb0 + j;
-        if (d.block_mass) d.block_mass[o] = M;
-        if (d.block_excess) d.block_excess[o] = E;
+        if (d.has_tier_b && i8 && ms > 0.0f)
+          Eb = ms * expm1f(rd(d.ublk + ((size_t)grp * d.n_blocks + gb0 + j) * G + h) * LN2);
+        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + h) * d.n_blocks + gb0 + j;
+        if (d.block_mass) d.block_mass[o] = ms;
+        if (d.block_excess) d.block_excess[o] = ex;
         if (d.block_excess_b) d.block_excess_b[o] = Eb;
-        if (d.block_order) rkey_s[tid][gb0 + j] = d.has_tier_b ? Eb : E;
+        if (d.block_order) rkey_s[h][gb0 + j] = d.has_tier_b ? Eb : ex;
       }
-      __syncthreads();
     }
   }
   if (d.block_order) {                             // rank = blocks ahead of j
+    __syncthreads();
     const int nbt = d.n_blocks;
     for (int i = tid; i < G * nbt; i += 256) {
       const int h = i / nbt, j = i - h * nbt;
