@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY: nothing on the product path imports this module.
 Chains the write path (oracle.quant) and the read path (oracle.attention) the
 way the WitCert meter loop (Sec. 6, "The meter loop") orders them: quantize and
 store the witness at write time, then attend and meter at read time.  Region
-formats: "bf16" (stored as is), "fp8" (E4M3 per-token scale) and "int8"
-(dithered INT8 with per-(256-token block, channel) scales).
+formats: "bf16" (stored as is), "fp8" (E4M3 per-token scale), "int8"
+(dithered INT8 with per-(256-token block, channel) scales) and "int8g32"
+(dithered INT8 with per-(token, 32-channel group) scales).
 """
 from __future__ import annotations
 
@@ -54,9 +55,12 @@ def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int):
     if fmt == "fp8":
         codes, s = quant.fp8_token_quantize(x)
         return codes, s, quant.fp8_token_dequant(codes, s), 0
-    if fmt == "int8":
+    if fmt in ("int8", "int8g32"):
         xi = dither(spec.seed, spec.layer, kv, kv_head, spec.stream,
                     np.arange(x.shape[0]), x.shape[1])
+        if fmt == "int8g32":
+            codes, s, clipped = quant.int8_dither_g32_quantize(x, xi)
+            return codes, s, quant.int8_dither_g32_dequant(codes, s, xi), clipped
         codes, s, clipped = quant.int8_dither_quantize(x, xi)
         return codes, s, quant.int8_dither_dequant(codes, s, xi), clipped
     raise ValueError(fmt)
@@ -79,6 +83,8 @@ def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray
     [-s/2, s/2]), 0 for keys stored exactly (BF16).  FP8 keys have no dither."""
     if spec.k_fmt == "int8":
         return np.asarray(enc.k_scale, np.float64)[np.arange(n) // quant.BLOCK]
+    if spec.k_fmt == "int8g32":
+        return np.repeat(np.asarray(enc.k_scale, np.float64)[:n], quant.GROUP, axis=1)
     if spec.k_fmt == "bf16":
         return np.zeros((n, np.asarray(enc.k_hat).shape[1]))
     raise ValueError("Tier B needs dithered INT8 keys or keys stored exactly")

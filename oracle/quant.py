@@ -115,6 +115,43 @@ def int8_dither_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
     return np.where(s == 0, 0.0, out)
 
 
+GROUP = 32
+
+
+def int8_dither_g32_quantize(x: np.ndarray, xi: np.ndarray, group: int = GROUP):
+    """Per-token channel-group scales (WitCert Sec. 6.2.3, Table 4: token x
+    G_c-channel groups, G_c = 32 the default; paging-safe): every token and
+    group of 32 channels has its own s = fp16(fp32(amax / 126.5)); the codes
+    are encoded exactly as in the block format, with the same dither.
+
+    x (T, d) exact values, xi (T, d) float32 dither.
+    Returns (codes int8 (T, d), scale float16 (T, d / group), clipped count)."""
+    x = np.asarray(x, dtype=np.float64)
+    x32 = x.astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), x):
+        raise ValueError("int8_dither_g32_quantize: inputs must be float32-exact")
+    xi = np.asarray(xi, dtype=np.float32)
+    T, d = x.shape
+    ng = d // group
+    amax = np.max(np.abs(x32.reshape(T, ng, group)), axis=2)
+    s16 = (amax / np.float32(INT8_DIV)).astype(np.float32).astype(np.float16)
+    s = np.repeat(s16.astype(np.float32), group, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = (x32 / s).astype(np.float32)
+        z = (y + xi).astype(np.float32)
+    c = np.rint(z)
+    c = np.where(s == 0, 0.0, c)
+    clipped = int(np.sum(np.abs(c) > INT8_Q))
+    return np.clip(c, -INT8_Q, INT8_Q).astype(np.int8), s16, clipped
+
+
+def int8_dither_g32_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
+                            group: int = GROUP) -> np.ndarray:
+    s = np.repeat(np.asarray(scales, np.float64), group, axis=1)
+    out = s * (np.asarray(codes, np.float64) - np.asarray(xi, np.float32).astype(np.float64))
+    return np.where(s == 0, 0.0, out)
+
+
 WITNESS_INFLATE = 1.0 + 2.0 ** -48
 
 
