@@ -13,6 +13,7 @@ Prints one JSON line (see the design doc for every field).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import json
 import math
@@ -56,10 +57,11 @@ def measured_traffic():
 def token_head_bytes(k_fmt, v_fmt, exact_k, witness, with_v=True):
     """Algorithmic bytes the read path moves per cached token of one KV head:
     key and value codes, their scales (FP8: fp32 per token; INT8: fp16 per
-    256-token block and channel, amortized), the witness (16 fp16 bands) and
-    the bf16 exact key the exact TV needs."""
-    code = {"bf16": 256, "fp8": 128, "int8": 128}
-    scale = {"bf16": 0, "fp8": 4, "int8": 1}
+    256-token block and channel, amortized; INT8 with group scales: four fp16
+    per token), the witness (16 fp16 bands) and the bf16 exact key the exact
+    TV needs."""
+    code = {"bf16": 256, "fp8": 128, "int8": 128, "int8g32": 128}
+    scale = {"bf16": 0, "fp8": 4, "int8": 1, "int8g32": 8}
     n = code[k_fmt] + scale[k_fmt]
     if with_v:
         n += code[v_fmt] + scale[v_fmt]
@@ -77,6 +79,9 @@ def parse():
                     help="0: the 36-layer decode step of the batch-64 workload (the bench line); 1..5: "
                          "time one layer's decode launch of that workload against its roofline, also "
                          "with the meter off and with the meter extensions (a measurement aid)")
+    ap.add_argument("--int8-scales", choices=("block", "group"), default="block",
+                    help="with --workload: store INT8 regions with per-(256-token block, channel) "
+                         "scales or per-(token, 32-channel group) scales")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
@@ -158,7 +163,7 @@ def _oracle_slice(lb):
     return time.perf_counter() - t
 
 
-def measure_workload(idx: int, reps: int, warmup: int):
+def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False):
     """One layer of workload `idx`: stage its caches through kvq_quantize, then
     time kvq_decode_attn (with TV, log A, bound and meter where the workload
     has exact keys and a witness) with HIP events on the launch stream."""
@@ -167,6 +172,13 @@ def measure_workload(idx: int, reps: int, warmup: int):
     from quantized_kv_cache_gqa_amd import kvq
     from workloads import CONFIGS, gen_layer
     cfg = CONFIGS[idx]
+    if group_scales:
+        def g32(r):
+            if r is None:
+                return None
+            sub = {"int8": "int8g32"}
+            return dataclasses.replace(r, k_fmt=sub.get(r.k_fmt, r.k_fmt), v_fmt=sub.get(r.v_fmt, r.v_fmt))
+        cfg = dataclasses.replace(cfg, prefix=g32(cfg.prefix), suffix=g32(cfg.suffix))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = kvq.load()
@@ -209,7 +221,7 @@ def measure_workload(idx: int, reps: int, warmup: int):
         paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
                            scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
         suffix = kvq.RegionView(paged, sf.length, k_exact=scatter(exact), lengths=lens, page_table=table,
-                                page_size=ps, use_witness=sf.witness)
+                                page_size=ps, seed=seed, layer=layer, stream_id=0, use_witness=sf.witness)
     else:
         suffix = kvq.RegionView(st, sf.length, k_exact=exact, lengths=lens, seed=seed, layer=layer,
                                 stream_id=0, use_witness=sf.witness)
@@ -226,12 +238,15 @@ def measure_workload(idx: int, reps: int, warmup: int):
     # every extension at once (per-chunk plan): value side, two-sided form,
     # tanh shape, block report, and Tier B where the keys allow it
     nb = kvq.n_report_blocks(prefix, suffix)
-    tier_b_ok = sf.k_fmt in ("int8", "bf16") and (cfg.prefix is None or cfg.prefix.k_fmt in ("int8", "bf16"))
+    i8b = ("int8", "int8g32", "bf16")
+    tier_b_ok = sf.k_fmt in i8b and (cfg.prefix is None or cfg.prefix.k_fmt in i8b)
+    any_g32 = "int8g32" in (sf.k_fmt, cfg.prefix.k_fmt if cfg.prefix is not None else None)
     ext = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev)
            for k in kvq.VALUE_KEYS + kvq.TWO_SIDED_KEYS + (kvq.TIER_B_KEYS if tier_b_ok else ())}
     ext.update({"block_mass": torch.empty((B, HQ, nb), dtype=torch.float32, device=dev),
-                "block_excess": torch.empty((B, HQ, nb), dtype=torch.float32, device=dev),
-                "block_order": torch.empty((B, HQ, nb), dtype=torch.int32, device=dev)})
+                "block_excess": torch.empty((B, HQ, nb), dtype=torch.float32, device=dev)})
+    if not (any_g32 and tier_b_ok):      # group-scale keys rank blocks by Tier A only
+        ext["block_order"] = torch.empty((B, HQ, nb), dtype=torch.int32, device=dev)
     meter_x = kvq.MeterOut(**{k: v.data_ptr() for k, v in list(mbuf.items()) + list(ext.items())},
                            delta_b=1e-9 if tier_b_ok else 0.0)
     info_x = kvq.PlanInfo()
@@ -269,7 +284,7 @@ def measure_workload(idx: int, reps: int, warmup: int):
     ext_ms = sorted(e0.elapsed_time(e1) for e0, e1 in x_evs)[reps // 2]
     # with Tier B as well (dithered INT8 keys: the sub-Gaussian certificate)
     tier_b_ms = None
-    if sf.k_fmt == "int8":
+    if sf.k_fmt in ("int8", "int8g32"):
         tb = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev) for k in ("log_a_b", "bound_b_raw", "meter_b")}
         meter_b = kvq.MeterOut(**{k: v.data_ptr() for k, v in list(mbuf.items()) + list(tb.items())}, delta_b=1e-9)
         info_b = kvq.PlanInfo()
@@ -285,7 +300,10 @@ def measure_workload(idx: int, reps: int, warmup: int):
     plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
             if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
     print(json.dumps({
-        "workload": f"config {idx}: {cfg.description}",
+        "workload": f"config {idx}: {cfg.description}".replace(
+            "per-(256-token block, channel) fp16 scales",
+            "per-(token, 32-channel group) fp16 scales" if group_scales else
+            "per-(256-token block, channel) fp16 scales"),
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
         "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
@@ -304,7 +322,8 @@ def main():
               "(the design doc describes how the step would shard)", file=sys.stderr)
         sys.exit(2)
     if args.workload != 0:
-        measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1))
+        measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1),
+                         group_scales=args.int8_scales == "group")
         return
     import numpy as np
     import torch

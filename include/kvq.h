@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 8
+#define KVQ_ABI_VERSION 9
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -68,12 +68,19 @@ typedef enum kvq_status {
  *                       (256-token block, KV head, channel): s = fp16(amax/126.5),
  *                       code = rint(x/s + xi), x^ = s (code - xi), xi regenerated from
  *                       Philox4x32-10 (WitCert Sec. 4.2, 6.1.1, 6.2.1).
- *  KVQ_FMT_FP32         exact keys / write-path input only. */
+ *  KVQ_FMT_FP32         exact keys / write-path input only.
+ *  KVQ_FMT_INT8_G32     int8 codes with the same subtractive dither and one fp16
+ *                       scale per (token, KV head, 32-channel group), 4 per row:
+ *                       scales [.., L, 4] laid out like the codes' rows (WitCert
+ *                       Sec. 6.2.3, Table 4: token x G_c-channel groups, G_c = 32,
+ *                       paging-safe).  Keys and values of a region use it together
+ *                       (or keys alone for kvq_meter); decoded on the vector ALUs. */
 typedef enum kvq_format {
   KVQ_FMT_BF16 = 0,
   KVQ_FMT_FP8_E4M3 = 1,
   KVQ_FMT_INT8_DITHER = 2,
-  KVQ_FMT_FP32 = 3
+  KVQ_FMT_FP32 = 3,
+  KVQ_FMT_INT8_G32 = 5
 } kvq_format;
 
 /* One KV region: the shared prefix ("cartridge", no batch dimension) or the
@@ -139,11 +146,11 @@ typedef struct kvq_attn_args {
  * Tier B (WitCert Sec. 4.2, Lemma 2; Sec. 6.2.3): the sub-Gaussian certificate
  * of subtractively dithered INT8 keys, from the stored scales and the query
  * alone (no witness).  Requesting any of its outputs needs delta_b in (0, 1)
- * and, in every region present, INT8-dithered keys or keys stored as BF16
- * (radius 0); other key formats return KVQ_ERR_UNSUPPORTED.
+ * and, in every region present, INT8-dithered keys (either scale layout) or
+ * keys stored as BF16 (radius 0); other key formats return KVQ_ERR_UNSUPPORTED.
  *   u_t         = sqrt(2 var_t log(2 S / delta_b)),
  *                 var_t = sm_scale^2 / 12 * sum_c q_c^2 s_{c,t}^2 (s: the key's
- *                 block scale of channel c), S = the request's tokens
+ *                 scale of channel c at token t), S = the request's tokens
  *   log_a_b     = log E_p~[e^{u_t}]
  *   bound_b_raw = 1/2 (A_B^2 - 1), +inf when beyond the float range
  *   meter_b     = min(1, bound_b_raw)
@@ -172,9 +179,11 @@ typedef struct kvq_attn_args {
  *   block_excess   = sum_{t in j} p~_t (e^{c_t} - 1)   (they add up to A - 1;
  *                    same needs as Tier A)
  *   block_excess_b = block_mass (e^{u_j} - 1), u_j the block's Tier B radius
- *                    (needs the Tier B request; they add up to A_B - 1)
+ *                    (needs the Tier B request and block-scale keys, whose
+ *                    radius a block shares; they add up to A_B - 1)
  *   block_order    = int32 block indices by decreasing block_excess_b when
- *                    Tier B is requested, else block_excess; ties by lower
+ *                    Tier B is requested (block-scale keys only), else
+ *                    block_excess; ties by lower
  *                    index (the page-in order); needs n_blocks <= 512.
  * Deterministic tanh shape (WitCert Sec. 6.4.2, the compared system's
  * tanh(max_t Delta_t) with the same witness, Delta_t = c_t), same needs as

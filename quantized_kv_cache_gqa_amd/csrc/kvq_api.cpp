@@ -29,7 +29,12 @@ constexpr size_t kCounterBytes = (size_t)1 << 20;
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool is_store_fmt(int f) {
-  return f == KVQ_FMT_BF16 || f == KVQ_FMT_FP8_E4M3 || f == KVQ_FMT_INT8_DITHER;
+  return f == KVQ_FMT_BF16 || f == KVQ_FMT_FP8_E4M3 || f == KVQ_FMT_INT8_DITHER || f == KVQ_FMT_INT8_G32;
+}
+inline bool is_int8(int f) { return f == KVQ_FMT_INT8_DITHER || f == KVQ_FMT_INT8_G32; }
+// keys and values of a region share the per-token group layout, or neither does
+inline bool g32_paired(int kf, int vf) {
+  return (kf == KVQ_FMT_INT8_G32) == (vf == KVQ_FMT_INT8_G32);
 }
 
 struct Plan {
@@ -143,8 +148,10 @@ kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int ba
                         r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids, r.v_witness};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
-  const bool int8 = r.k_format == KVQ_FMT_INT8_DITHER || (need_v && r.v_format == KVQ_FMT_INT8_DITHER);
-  if (int8 && (r.layer < 0 || r.layer >= (1 << 15) || h_kv > (1 << 16))) return KVQ_ERR_SHAPE;
+  const bool int8 = r.k_format == KVQ_FMT_INT8_DITHER || (need_v && r.v_format == KVQ_FMT_INT8_DITHER);   // block scales
+  const bool any_int8 = is_int8(r.k_format) || (need_v && is_int8(r.v_format));
+  if (any_int8 && (r.layer < 0 || r.layer >= (1 << 15) || h_kv > (1 << 16))) return KVQ_ERR_SHAPE;
+  if (need_v && !g32_paired(r.k_format, r.v_format)) return KVQ_ERR_UNSUPPORTED;
   if (is_prefix) {
     if (r.lengths || r.page_table || r.stream_ids) return KVQ_ERR_UNSUPPORTED;
   } else if (r.page_table) {
@@ -231,6 +238,10 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     p.pre_blocks = (p.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
     p.n_blocks = p.pre_blocks + (p.suffix_cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
     if (m->block_excess_b && !tier_b_req) return KVQ_ERR_UNSUPPORTED;
+    // Tier B's block contributions need a radius shared by the block
+    const bool g32_keys = (p.prefix_len > 0 && a->prefix.k_format == KVQ_FMT_INT8_G32) ||
+                          (p.suffix_cap > 0 && a->suffix.k_format == KVQ_FMT_INT8_G32);
+    if (g32_keys && (m->block_excess_b || (m->block_order && tier_b_req))) return KVQ_ERR_UNSUPPORTED;
     if (m->block_order && p.n_blocks > 512) return KVQ_ERR_UNSUPPORTED;
     const bool rep_a = m->block_excess || (m->block_order && !tier_b_req);
     const bool wants_a = m->bound_raw || m->meter || m->log_a || m->out_bound || wants_two || rep_a;
@@ -250,9 +261,9 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
       // WitCert Sec. 4.2: a probability, and keys whose residual is the
       // uniform dither residual (INT8) or zero (BF16)
       if (!(m->delta_b > 0.0 && m->delta_b < 1.0)) return KVQ_ERR_SHAPE;
-      if (p.prefix_len > 0 && a->prefix.k_format != KVQ_FMT_INT8_DITHER && a->prefix.k_format != KVQ_FMT_BF16)
+      if (p.prefix_len > 0 && !is_int8(a->prefix.k_format) && a->prefix.k_format != KVQ_FMT_BF16)
         return KVQ_ERR_UNSUPPORTED;
-      if (p.suffix_cap > 0 && a->suffix.k_format != KVQ_FMT_INT8_DITHER && a->suffix.k_format != KVQ_FMT_BF16)
+      if (p.suffix_cap > 0 && !is_int8(a->suffix.k_format) && a->suffix.k_format != KVQ_FMT_BF16)
         return KVQ_ERR_UNSUPPORTED;
     }
   }
@@ -471,8 +482,10 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   const bool int8 = a->k_format == KVQ_FMT_INT8_DITHER || (a->v_in && a->v_format == KVQ_FMT_INT8_DITHER);
-  if (int8) {
-    if (a->tok_begin % KVQ_INT8_BLOCK) return KVQ_ERR_UNSUPPORTED;
+  const bool any_int8 = is_int8(a->k_format) || (a->v_in && is_int8(a->v_format));
+  if (a->v_in && !g32_paired(a->k_format, a->v_format)) return KVQ_ERR_UNSUPPORTED;
+  if (int8 && a->tok_begin % KVQ_INT8_BLOCK) return KVQ_ERR_UNSUPPORTED;   // whole 256-token blocks
+  if (any_int8) {
     if (a->layer < 0 || a->layer >= (1 << 15) || a->num_kv_heads > (1 << 16)) return KVQ_ERR_SHAPE;
   }
   QuantLaunch q;

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     const uint16_t *ksc8 = nullptr;
     if constexpr (KF == KVQ_FMT_INT8_DITHER)
       ksc8 = (const uint16_t *)R.k_scale + ((sh * nblk_cap + tc / BLK) * D);
+    if constexpr (KF == KVQ_FMT_INT8_G32) ksc8 = (const uint16_t *)R.k_scale + row * 4;
     load_row16<KF>(R.k, row, j, kv, ksc8, (uint32_t)tc, ktag, stream, R.seed_lo, R.seed_hi);
     float ks = 1.0f;
     if constexpr (KF == KVQ_FMT_FP8_E4M3) ks = reinterpret_cast<const float *>(R.k_scale)[row];
@@ -216,10 +217,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
     }
 
     // ---- Tier B radius of this token: u log2(e) = sqrt(sum_c (q_c s_c)^2 tb_l / 6)
-    //      in log2 units (INT8 keys: s = the block's scale; other keys: u = 0)
+    //      in log2 units (INT8 keys: s = the key's scale; other keys: u = 0)
     float eub[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) eub[h] = 1.0f;
+    if constexpr (KF == KVQ_FMT_INT8_G32) {
+      if (do_b) {                                        // one scale on the lane's 16 channels
+        const float s = fp16_bits_to_f32(ksc8[j >> 1]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ss = fmaf(qv[h][i], qv[h][i], ss);
+          eub[h] = exp2f(sqrtf(sum8(ss * s * s) * tb_l * (1.0f / 6.0f)));
+        }
+      }
+    }
     if constexpr (KF == KVQ_FMT_INT8_DITHER) {
       if (do_b) {
         float sc[16];
@@ -318,6 +331,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       const uint16_t *vsc8 = nullptr;
       if constexpr (VF == KVQ_FMT_INT8_DITHER)
         vsc8 = (const uint16_t *)R.v_scale + ((sh * nblk_cap + tc / BLK) * D);
+      if constexpr (VF == KVQ_FMT_INT8_G32) vsc8 = (const uint16_t *)R.v_scale + row * 4;
       load_row16<VF>(R.v, row, j, vv, vsc8, (uint32_t)tc, vtag, stream, R.seed_lo, R.seed_hi);
       float vs = 1.0f;
       if constexpr (VF == KVQ_FMT_FP8_E4M3) vs = reinterpret_cast<const float *>(R.v_scale)[row];
@@ -425,6 +439,10 @@ static hipError_t launch_k(const DecodeLaunch &d, hipStream_t s) {
     case KVQ_FMT_BF16: return launch_v<G, KVQ_FMT_BF16>(d, s);
     case KVQ_FMT_FP8_E4M3: return launch_v<G, KVQ_FMT_FP8_E4M3>(d, s);
     case KVQ_FMT_INT8_DITHER: return launch_v<G, KVQ_FMT_INT8_DITHER>(d, s);
+    case KVQ_FMT_INT8_G32:                               // values in the same layout, or none
+      if (d.v_format == KVQ_FMT_INT8_G32) return launch_t<G, KVQ_FMT_INT8_G32, KVQ_FMT_INT8_G32>(d, s);
+      if (d.v_format == VF_NONE) return launch_t<G, KVQ_FMT_INT8_G32, VF_NONE>(d, s);
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -106,7 +106,21 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
       v[2 * i] = bf16_lo(w[i]);
       v[2 * i + 1] = bf16_hi(w[i]);
     }
-  } else {  // INT8 with subtractive dither
+  } else if constexpr (F == KVQ_FMT_INT8_G32) {  // i8_scale: the row's 4 group scales
+    const uint4 w = *reinterpret_cast<const uint4 *>((const uint8_t *)base + row * D + 16 * j);
+    const float s = fp16_bits_to_f32(i8_scale[j >> 1]);
+    const uint32_t cw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float xi[4];
+      dither4(tok, (uint32_t)(4 * j + g), tag, stream, k0, k1, xi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float code = (float)(int)(int8_t)(cw[g] >> (8 * e));
+        v[4 * g + e] = s * (code - xi[e]);
+      }
+    }
+  } else {  // INT8 with subtractive dither, block scales
     const uint4 w = *reinterpret_cast<const uint4 *>((const uint8_t *)base + row * D + 16 * j);
     const uint4 *sp = reinterpret_cast<const uint4 *>(i8_scale + 16 * j);
     const uint4 sa = sp[0], sb = sp[1];

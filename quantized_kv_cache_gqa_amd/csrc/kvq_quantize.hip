@@ -58,11 +58,16 @@ __device__ __forceinline__ uint32_t full_norm_up(const double *x) {
   return fp16_round_up_bits(w);
 }
 
-// One wavefront per token; handles FP8 per-token and BF16 targets.
+// One wavefront per token; handles FP8 per-token, BF16 and INT8 with
+// per-(token, 32-channel group) scales: lanes 0..31 hold group 0 (channels
+// 0..31) and group 2 (64..95), lanes 32..63 groups 1 and 3; the dither is the
+// block format's (the same Philox counters), so the codes differ from it only
+// through the scales.
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const void *__restrict__ in, int in_fmt, int target, int n_seq, int h_kv, int capacity,
-    int tok_begin, int tok_end, uint8_t *__restrict__ out, float *__restrict__ scale_out,
-    uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out) {
+    int tok_begin, int tok_end, uint8_t *__restrict__ out, void *__restrict__ scale_out,
+    uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out, int kv, uint32_t k0, uint32_t k1,
+    int layer, int stream_id, const int32_t *__restrict__ stream_ids) {
 #pragma clang fp contract(off)
   __shared__ double rbuf[4][D];
   __shared__ double xbuf[4][D];
@@ -88,9 +93,45 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
     uint32_t c0 = e4m3_encode(y0), c1 = e4m3_encode(y1);
     out[row * D + lane] = (uint8_t)c0;
     out[row * D + lane + 64] = (uint8_t)c1;
-    if (lane == 0) scale_out[row] = s;
+    if (lane == 0) reinterpret_cast<float *>(scale_out)[row] = s;
     h0 = (double)e4m3_decode_sw(c0) * (double)s;
     h1 = (double)e4m3_decode_sw(c1) * (double)s;
+  } else if (target == KVQ_FMT_INT8_G32) {
+    float a0 = fabsf(x0), a1 = fabsf(x1);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {             // maxima over each half-wavefront
+      a0 = fmaxf(a0, __shfl_xor(a0, off));
+      a1 = fmaxf(a1, __shfl_xor(a1, off));
+    }
+    const uint32_t s0b = f32_to_fp16_bits_rne(a0 / 126.5f), s1b = f32_to_fp16_bits_rne(a1 / 126.5f);
+    const float s0 = fp16_bits_to_f32(s0b), s1 = fp16_bits_to_f32(s1b);
+    uint16_t *sc = reinterpret_cast<uint16_t *>(scale_out) + row * 4;
+    if ((lane & 31) == 0) {
+      sc[lane >> 5] = (uint16_t)s0b;
+      sc[2 + (lane >> 5)] = (uint16_t)s1b;
+    }
+    const int seq = (int)(sh / h_kv), kvh = (int)(sh - (long)seq * h_kv);
+    const uint32_t tag = dither_tag(kv, layer, kvh);
+    const uint32_t stream = (uint32_t)(stream_ids ? stream_ids[seq] : stream_id + seq);
+    float xa[4], xb[4];
+    dither4((uint32_t)t, (uint32_t)(lane >> 2), tag, stream, k0, k1, xa);
+    dither4((uint32_t)t, (uint32_t)((lane + 64) >> 2), tag, stream, k0, k1, xb);
+    const float xi0 = xa[lane & 3], xi1 = xb[lane & 3];
+    float c0 = 0.0f, c1 = 0.0f;
+    if (s0 != 0.0f) {
+      float y = x0 / s0;                                 // correctly rounded
+      float z = y + xi0;
+      c0 = fminf(fmaxf(rintf(z), -127.0f), 127.0f);
+    }
+    if (s1 != 0.0f) {
+      float y = x1 / s1;
+      float z = y + xi1;
+      c1 = fminf(fmaxf(rintf(z), -127.0f), 127.0f);
+    }
+    out[row * D + lane] = (uint8_t)(int8_t)(int)c0;
+    out[row * D + lane + 64] = (uint8_t)(int8_t)(int)c1;
+    h0 = s0 != 0.0f ? (double)s0 * ((double)c0 - (double)xi0) : 0.0;
+    h1 = s1 != 0.0f ? (double)s1 * ((double)c1 - (double)xi1) : 0.0;
   } else {                                               // BF16 target
     uint32_t b0 = in_fmt == KVQ_FMT_FP32 ? f32_to_bf16_bits(x0) : (__float_as_uint(x0) >> 16);
     uint32_t b1 = in_fmt == KVQ_FMT_FP32 ? f32_to_bf16_bits(x1) : (__float_as_uint(x1) >> 16);
@@ -212,7 +253,7 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
   uint16_t *vrec = which == 1 ? q.v_witness_out : nullptr;
   const int ntok = q.tok_end - q.tok_begin;
   if (ntok <= 0) return hipSuccess;
-  if (fmt == KVQ_FMT_INT8_DITHER) {
+  if (fmt == KVQ_FMT_INT8_DITHER) {   // block scales (G32 takes the per-token kernel)
     const int blk_begin = q.tok_begin / BLK;
     const int n_blk = (q.tok_end - 1) / BLK - blk_begin + 1;
     const long grid = (long)q.n_seq * q.h_kv * n_blk;
@@ -225,7 +266,8 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
     const long grid = (total + 3) / 4;
     hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
                        q.in_format, fmt, q.n_seq, q.h_kv, q.capacity, q.tok_begin, q.tok_end,
-                       (uint8_t *)out, (float *)sc, wit, vrec);
+                       (uint8_t *)out, sc, wit, vrec, which, (uint32_t)q.seed, (uint32_t)(q.seed >> 32),
+                       q.layer, q.stream_id, q.stream_ids);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
 
-FMT = {"bf16": 0, "fp8": 1, "int8": 2, "fp32": 3}
+FMT = {"bf16": 0, "fp8": 1, "int8": 2, "fp32": 3, "int8g32": 5}
+INT8_GROUP = 32                # channels per scale of "int8g32"
 HEAD_DIM = 128
 N_BANDS = 16
 INT8_BLOCK = 256
@@ -73,7 +74,7 @@ _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class PlanInfo(ctypes.Structure):
@@ -151,7 +152,7 @@ class Stored:
 def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Optional[str],
                  witness: bool, device, value_witness: bool = False) -> Stored:
     def codes(fmt):
-        dt = {"bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8}[fmt]
+        dt = {"bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8, "int8g32": torch.int8}[fmt]
         return torch.zeros((n_seq, h_kv, capacity, HEAD_DIM), dtype=dt, device=device)
 
     def scale(fmt):
@@ -160,6 +161,9 @@ def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Option
         if fmt == "int8":
             nb = (capacity + INT8_BLOCK - 1) // INT8_BLOCK
             return torch.zeros((n_seq, h_kv, nb, HEAD_DIM), dtype=torch.float16, device=device)
+        if fmt == "int8g32":                    # per (token, 32-channel group)
+            return torch.zeros((n_seq, h_kv, capacity, HEAD_DIM // INT8_GROUP), dtype=torch.float16,
+                               device=device)
         return None
 
     return Stored(fmt_k, fmt_v or "bf16", codes(fmt_k), codes(fmt_v) if fmt_v else None,

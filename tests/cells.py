@@ -105,7 +105,8 @@ class GpuCase:
                            scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
         self.page_table = table
         return kvq.RegionView(paged, cap, k_exact=scatter(exact), lengths=lens, page_table=table,
-                              page_size=ps, use_witness=st.witness is not None)
+                              page_size=ps, seed=dither_seed(cfg), layer=self.layer, stream_id=0,
+                              use_witness=st.witness is not None)
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
             workspace=None, tier_b_delta=None, value_bound: bool = False, two_sided: bool = False,

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 8
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 9
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -286,3 +286,43 @@ def test_quantize_argument_checks(lib):
     qi.tok_begin = 100                                  # INT8 calls start on a block boundary
     assert lib.kvq_quantize(ctypes.byref(qi), None) == 5
     assert lib.kvq_quantize(None, None) == 1
+
+
+def test_int8_group_scale_format_arguments(lib, monkeypatch):
+    """INT8 with per-(token, 32-channel group) scales: keys and values of a
+    region share the layout (keys alone for the meter); pages are allowed
+    since a token's scales sit in its own row; Tier B accepts the keys but
+    not Tier B's per-block contributions (the radius is per token); the
+    write path needs no block-aligned start."""
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    g = _args(batch=8, suffix=32768, kf="int8g32", vf="int8g32")
+    tier_b = dict(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE, log_a_b=FAKE, bound_b_raw=FAKE,
+                  meter_b=FAKE, delta_b=1e-6)
+    info = kvq.PlanInfo()
+    assert _plan(lib, g, kvq.MeterOut(**tier_b)).team == 0
+    for kf, vf in (("int8g32", "int8"), ("int8", "int8g32"), ("int8g32", "fp8"), ("bf16", "int8g32")):
+        mixed = _args(batch=8, suffix=32768, kf=kf, vf=vf)
+        assert lib.kvq_decode_plan(ctypes.byref(mixed), ctypes.byref(kvq.MeterOut(tv=FAKE)), 0,
+                                   ctypes.byref(info)) == 5, (kf, vf)
+    keys = _args(batch=8, suffix=32768, kf="int8g32", vf="int8")
+    assert lib.kvq_decode_plan(ctypes.byref(keys), ctypes.byref(kvq.MeterOut(tv=FAKE)), 1,
+                               ctypes.byref(info)) == 0          # meter only: values unused
+    paged = _args(batch=8, suffix=32768, kf="int8g32", vf="int8g32")
+    paged.suffix.page_table = FAKE
+    paged.suffix.page_size = 16
+    paged.suffix.max_pages = 32768 // 16
+    assert lib.kvq_decode_plan(ctypes.byref(paged), ctypes.byref(kvq.MeterOut(tv=FAKE)), 0,
+                               ctypes.byref(info)) == 0
+    for fields, status in (({"block_excess_b": FAKE}, 5), ({"block_order": FAKE}, 5),
+                           ({"block_excess": FAKE}, 0)):
+        m = kvq.MeterOut(**tier_b, **fields)
+        assert lib.kvq_decode_plan(ctypes.byref(g), ctypes.byref(m), 0, ctypes.byref(info)) == status, fields
+    assert lib.kvq_decode_plan(ctypes.byref(g), ctypes.byref(kvq.MeterOut(tv=FAKE, block_order=FAKE)), 0,
+                               ctypes.byref(info)) == 0          # Tier A's page-in order
+    q = kvq.QuantArgs(k_format=5, v_format=2, in_format=0, k_in=FAKE, v_in=FAKE, n_seq=2,
+                      num_kv_heads=8, head_dim=128, capacity=1000, tok_begin=100, tok_end=1000,
+                      k_out=FAKE, v_out=FAKE, k_scale_out=FAKE, v_scale_out=FAKE)
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 5            # mixed scale layouts
+    q.layer = -1
+    q.v_format = 5
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 2            # dither tag range

@@ -506,3 +506,44 @@ def test_block_report_every_cell(gpu_lib, kernel, monkeypatch, name, with_b):
     assert torch.equal(out, o2)
     for k in m2:
         assert torch.equal(m[k], m2[k]), k
+
+
+def _g32(paged=False, cartridge=False):
+    """Dithered INT8 with per-(token, 32-channel group) scales (WitCert Sec.
+    6.2.3, Table 4), dense or in shuffled 16-token pages, with an INT8-G32
+    shared prefix when asked."""
+    from workloads.configs import RegionCfg
+    base = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=1024, lens=(1024, 513))
+    suf = dataclasses.replace(base.suffix, k_fmt="int8g32", v_fmt="int8g32", paged=paged, page_size=16)
+    pre = RegionCfg(length=300, k_fmt="int8g32", v_fmt="int8g32", exact_k=True, witness=True) \
+        if cartridge else None
+    tag = "-g32" + ("-paged" if paged else "") + ("-cartridge" if cartridge else "")
+    return dataclasses.replace(base, prefix=pre, suffix=suf, name=base.name + tag)
+
+
+G32 = {
+    "dense": lambda: _g32(),
+    "paged": lambda: _g32(paged=True),
+    "paged-cartridge": lambda: _g32(paged=True, cartridge=True),
+}
+
+
+@pytest.mark.parametrize("name", list(G32))
+def test_int8_group_scales_every_cell(gpu_lib, kernel, monkeypatch, name):
+    """Codes, per-(token, group) scales, witness and value records bit-exact;
+    output, Tier A, Tier B (radius from the token's group scales), the value
+    side and the two-sided form on every cell against the oracle; then the
+    same split over smaller chunks gives the same results within the bars."""
+    cfg = G32[name]()
+    case = GpuCase(cfg, page_seed=9, value_witness=True)
+    out, m, worst = _all_cells(case, tier_b_delta=1e-3, value_bound=True, two_sided=True)
+    assert {"bound_b", "value_err", "two_sided"} <= set(worst)
+    assert torch.all(m["log_a_b"] > 0) and torch.all(m["tv"] <= m["bound_b_raw"])
+    assert torch.all(m["tv"] <= m["bound_raw"])
+    _all_cells(case, split_tokens=128, tier_b_delta=1e-3)
+    _, mb = case.run(report=True)
+    for b in range(cfg.batch):
+        for kvh in range(cfg.h_kv):
+            _, ref = oracle_cell(case, b, kvh)
+            check_block_report(case, mb, b, kvh, ref, False)
+
