@@ -123,6 +123,8 @@ struct TileRegs {
   uint4 vb[4];     // BF16 values: 16 dims of 2 tokens (vector-ALU layout)
   float ks, vs;    // scales of this lane's compact (token, head) slot
   uint32_t vrec;   // value record of this lane's token: fp16 (rho, ||v||)
+  uint2 kg[4];     // INT8 group scales: the 4 fp16 key scales of token 4 g + e
+  uint32_t vg[4];  // INT8 group scales: value scale of token 4 g + e, dims 8 j16 ..
 };
 
 // Addressing of one (request, KV head) region range ending at c1, and the
@@ -136,6 +138,7 @@ struct TileSrc {
   const uint8_t *kb, *keb, *vbb;
   const uint16_t *wb, *vwb;
   const float *ksb, *vsb;
+  const uint16_t *ksg, *vsg;   // INT8 group scales: 4 per row
   const int32_t *ptab;
   int pshift, page_size, h_kv, kvh, last;
 
@@ -156,6 +159,8 @@ struct TileSrc {
     ksb = (const float *)R.k_scale + row0;
     vbb = (const uint8_t *)R.v + row0 * (VF == KVQ_FMT_BF16 ? 2 * D : D);
     vsb = (const float *)R.v_scale + row0;
+    ksg = (const uint16_t *)R.k_scale + row0 * 4;
+    vsg = (const uint16_t *)R.v_scale + row0 * 4;
   }
 
   __device__ __forceinline__ RowT row_of(int t) const {   // row index relative to row0
@@ -183,6 +188,17 @@ struct TileSrc {
       T.k[0] = p[0];
       T.k[1] = p[1];
       T.ks = KF == KVQ_FMT_FP8_E4M3 ? ksb[rk] : 1.0f;   // INT8: block scales ride on q
+    } else if constexpr (KF == KVQ_FMT_INT8_G32) {
+      // slice s of this lane: channels 32 s + 8 g .. + 7, so that one
+      // contraction covers one scale group
+      const uint8_t *p = kb + ra * D + 8 * g;
+      const uint2 a0 = *reinterpret_cast<const uint2 *>(p), a1 = *reinterpret_cast<const uint2 *>(p + 32);
+      const uint2 a2 = *reinterpret_cast<const uint2 *>(p + 64), a3 = *reinterpret_cast<const uint2 *>(p + 96);
+      T.k[0] = uint4{a0.x, a0.y, a1.x, a1.y};
+      T.k[1] = uint4{a2.x, a2.y, a3.x, a3.y};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T.kg[e] = *reinterpret_cast<const uint2 *>(ksg + row_of(t0 + 4 * g + e) * 4);
+      T.ks = 1.0f;
     } else {
       const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
 #pragma unroll
@@ -203,10 +219,13 @@ struct TileSrc {
     const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
     if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
     if (vrec) T.vrec = *reinterpret_cast<const uint32_t *>(vwb + rk * 2);
-    if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {
+    if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + row_of(t0 + 4 * g + e) * D + 8 * j16);
+      for (int e = 0; e < 4; ++e) {
+        const RowT re = row_of(t0 + 4 * g + e);
+        T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + re * D + 8 * j16);
+        if constexpr (VF == KVQ_FMT_INT8_G32) T.vg[e] = vsg[re * 4 + (j16 >> 2)];
+      }
       T.vs = VF == KVQ_FMT_FP8_E4M3 ? vsb[rk] : 1.0f;
     } else if constexpr (VF == KVQ_FMT_BF16) {
       const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
@@ -309,11 +328,17 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // codes and the two pieces of -xi.  Values are dequantized to fp16.
   constexpr bool I8K = KF == KVQ_FMT_INT8_DITHER;
   constexpr bool I8V = VF == KVQ_FMT_INT8_DITHER;
+  // INT8 with per-(token, 32-channel group) scales: the logits contract one
+  // group per MFMA (bqs = exact three-way split of q_c in log2 units over
+  // channels 32 s + 8 g ..) and scale the four partial sums per token; values
+  // are dequantized to fp16 with their token's group scale.
+  constexpr bool GK = KF == KVQ_FMT_INT8_G32;
+  constexpr bool GV = VF == KVQ_FMT_INT8_G32;
   bf16x8_t bqs[4];
   float sv8[8];                                    // value scales of dims 8 j16 + n
   uint32_t i8_stream = 0, i8_ktag = 0, i8_vtag = 0;
   size_t i8_scale_row0 = 0;
-  if constexpr (I8K || I8V) {
+  if constexpr (I8K || I8V || GK || GV) {
     const size_t sh = R.is_prefix ? (size_t)kvh : (size_t)b * d.h_kv + kvh;
     i8_scale_row0 = sh * (size_t)((R.length + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK);
     i8_stream = (uint32_t)(R.is_prefix ? R.stream_id : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
@@ -365,6 +390,26 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
   };
 
+  float qg2[4] = {0.0f, 0.0f, 0.0f, 0.0f};         // group sums of (q_c qs)^2 of head hh
+  if constexpr (GK) {
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = qp[32 * s8 + 8 * g + e] * qs;
+        qg2[s8] = fmaf(x, x, qg2[s8]);
+        const float hi = bf16_round(x);
+        const float mid = bf16_round(x - hi);
+        const float lo = bf16_round(x - hi - mid);
+        const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
+        bqs[s8][e] = (__bf16)piece;
+      }
+      qg2[s8] += __shfl_xor(qg2[s8], 16);
+      qg2[s8] += __shfl_xor(qg2[s8], 32);
+    }
+  }
+
   const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
   float *spill_g = ((do_tv || do_r) && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
   float *rspill_g = do_r ? rspill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
@@ -413,6 +458,46 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], dq, 0, 0, 0);
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], dq, 0, 0, 0);
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bqs[s], dq, 0, 0, 0);
+      }
+    } else if constexpr (GK) {
+      // row j16 = token t0 + j16, slice s = scale group s (channels 32 s + 8 g ..)
+      const uint32_t w[8] = {T.k[0].x, T.k[0].y, T.k[0].z, T.k[0].w,
+                             T.k[1].x, T.k[1].y, T.k[1].z, T.k[1].w};
+      f32x4_t ds[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 cw = {i8x2_to_bf16x2(w[2 * s], 0), i8x2_to_bf16x2(w[2 * s], 2),
+                          i8x2_to_bf16x2(w[2 * s + 1], 0), i8x2_to_bf16x2(w[2 * s + 1], 2)};
+        bf16x8_t xh, xl;
+        neg_dither8_bf16((uint32_t)(t0 + j16), (uint32_t)(8 * s + 2 * g), i8_ktag, i8_stream, R.seed_lo,
+                         R.seed_hi, xh, xl);
+        ds[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                                      0, 0, 0);
+        ds[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], ds[s], 0, 0, 0);
+        ds[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bqs[s], ds[s], 0, 0, 0);
+      }
+      // output row r = token t0 + 4 g + r: its four group scales; Tier B's
+      // sum_s s_s^2 qg2_s of the same token
+      float ssr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint2 sw = T.kg[r];
+        const float s0 = fp16_bits_to_f32(sw.x & 0xffffu), s1 = fp16_bits_to_f32(sw.x >> 16);
+        const float s2 = fp16_bits_to_f32(sw.y & 0xffffu), s3 = fp16_bits_to_f32(sw.y >> 16);
+        dq[r] = s0 * ds[0][r];
+        dq[r] = fmaf(s1, ds[1][r], dq[r]);
+        dq[r] = fmaf(s2, ds[2][r], dq[r]);
+        dq[r] = fmaf(s3, ds[3][r], dq[r]);
+        float ss = s0 * s0 * qg2[0];
+        ss = fmaf(s1 * s1, qg2[1], ss);
+        ss = fmaf(s2 * s2, qg2[2], ss);
+        ssr[r] = fmaf(s3 * s3, qg2[3], ss);
+      }
+      if (do_b) {
+        // this lane's token t0 + 4 g + pp: u log2(e) = sqrt(sum_s s_s^2 qg2_s tb_l / 6)
+        const float a01 = (pp & 1) ? ssr[1] : ssr[0];
+        const float a23 = (pp & 1) ? ssr[3] : ssr[2];
+        eub = exp2f(sqrtf(((pp & 2) ? a23 : a01) * tb_l * (1.0f / 6.0f)));
       }
     } else {
 #pragma unroll
@@ -464,7 +549,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       float fh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
-      if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
+      if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {   // MFMA accumulators
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
@@ -532,8 +617,9 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
-    } else if constexpr (I8V) {
-      // as FP8, with weights p and values s_c (code - xi) in fp16
+    } else if constexpr (I8V || GV) {
+      // as FP8, with weights p and values s (code - xi) in fp16 (s: the block's
+      // scale of the channel, or the token's scale of the channel's group)
       w_s[wv][16 * hh + 4 * g + pp] = p;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -553,7 +639,8 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           const float code = (float)(int)(int8_t)(cw[n >> 2] >> (8 * (n & 3)));
-          vb[n][e] = (_Float16)(sv8[n] * (code - xi[n]));
+          const float sc = GV ? fp16_bits_to_f32(T.vg[e]) : sv8[n];
+          vb[n][e] = (_Float16)(sc * (code - xi[n]));
         }
       }
 #pragma unroll
@@ -674,7 +761,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][PART_ZN] = zn;
     part_s[wv][hh][PART_CMAX] = cmax;
   }
-  if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER) {   // MFMA accumulators
+  if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {   // MFMA accumulators
     if (lane < 16) {
 #pragma unroll
       for (int n = 0; n < 8; ++n)

@@ -448,11 +448,17 @@ bool mfma_path_supports(const DecodeLaunch &d) {
   if (d.group != 4 || d.region.exact_fmt == EX_F32) return false;
   if (d.k_format == KVQ_FMT_INT8_DITHER)           // dense INT8 keys and INT8 (or no) values
     return !d.region.paged && (d.v_format == KVQ_FMT_INT8_DITHER || d.v_format == VF_NONE);
+  if (d.k_format == KVQ_FMT_INT8_G32)              // dense or paged, values alike (or none)
+    return d.v_format == KVQ_FMT_INT8_G32 || d.v_format == VF_NONE;
   return (d.k_format == KVQ_FMT_FP8_E4M3 || d.k_format == KVQ_FMT_BF16) &&
          (d.v_format == KVQ_FMT_FP8_E4M3 || d.v_format == KVQ_FMT_BF16 || d.v_format == VF_NONE);
 }
 
 hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t s) {
+  if (d.k_format == KVQ_FMT_INT8_G32) {
+    if (d.v_format == KVQ_FMT_INT8_G32) return launch_m<KVQ_FMT_INT8_G32, KVQ_FMT_INT8_G32>(d, s);
+    return launch_m<KVQ_FMT_INT8_G32, VF_NONE>(d, s);
+  }
   if (d.k_format == KVQ_FMT_INT8_DITHER) {
     if (d.v_format == KVQ_FMT_INT8_DITHER)
       return launch_m<KVQ_FMT_INT8_DITHER, KVQ_FMT_INT8_DITHER>(d, s);
