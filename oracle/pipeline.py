@@ -31,6 +31,9 @@ class RegionSpec:
     witness: bool = True      # store/use a witness for the keys
     exact_k: bool = True      # the exact keys are available for TV
     value_witness: bool = False   # store/use the value record (rho, ||v||)
+    # fixed outlier RoPE pairs of the keys (WitCert Sec. 6.2.5), "int8g32" keys
+    # only: (h_kv, m) pair indices, one set per KV head
+    outlier_pairs: Optional[np.ndarray] = None
 
 
 @dataclass
@@ -45,9 +48,11 @@ class EncodedRegion:
     v_hat: np.ndarray
     clipped: int
     v_rec: Optional[np.ndarray] = None   # float16 (T, 2): rho, ||v||
+    k_out: Optional[np.ndarray] = None   # (T, 2m) stored outlier values of the keys
+    k_bypass: Optional[np.ndarray] = None   # bool (d,) channels those values replace
 
 
-def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int):
+def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int, pairs=None):
     x = np.asarray(x, np.float64)
     if fmt == "bf16":
         codes = f64_to_bf16_bits(x)
@@ -59,6 +64,11 @@ def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int):
         xi = dither(spec.seed, spec.layer, kv, kv_head, spec.stream,
                     np.arange(x.shape[0]), x.shape[1])
         if fmt == "int8g32":
+            if pairs is not None and len(pairs) > 0:
+                mask, _ = quant.outlier_mask(pairs, x.shape[1])
+                quant.outlier_values(x, pairs)               # exactness check
+                codes, s, clipped = quant.int8_dither_g32_quantize(x, xi, bypass=mask)
+                return codes, s, quant.int8_dither_g32_dequant(codes, s, xi, bypass=mask, x_bypass=x), clipped
             codes, s, clipped = quant.int8_dither_g32_quantize(x, xi)
             return codes, s, quant.int8_dither_g32_dequant(codes, s, xi), clipped
         codes, s, clipped = quant.int8_dither_quantize(x, xi)
@@ -68,13 +78,22 @@ def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int):
 
 def encode_region(k, v, spec: RegionSpec, kv_head: int) -> EncodedRegion:
     """Quantize one (region, request, KV head) slice and store its witness."""
-    kc, ks, kh, c1 = _encode_one(k, spec.k_fmt, spec, 0, kv_head)
+    pairs = None
+    if spec.outlier_pairs is not None:
+        if spec.k_fmt != "int8g32":
+            raise ValueError("outlier pairs need int8g32 keys")
+        pairs = np.asarray(spec.outlier_pairs)[kv_head]
+    kc, ks, kh, c1 = _encode_one(k, spec.k_fmt, spec, 0, kv_head, pairs)
     vc, vs, vh, c2 = _encode_one(v, spec.v_fmt, spec, 1, kv_head)
     w = w16 = None
     if spec.witness:
         w, w16 = quant.witness(kh, k)
     v_rec = quant.value_witness(vh, v) if spec.value_witness else None
-    return EncodedRegion(kc, ks, vc, vs, w, w16, kh, vh, c1 + c2, v_rec)
+    k_out = k_bypass = None
+    if pairs is not None:
+        k_out = quant.outlier_values(k, pairs)
+        k_bypass = quant.outlier_mask(pairs, np.asarray(k).shape[1])[0]
+    return EncodedRegion(kc, ks, vc, vs, w, w16, kh, vh, c1 + c2, v_rec, k_out, k_bypass)
 
 
 def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray:
@@ -84,7 +103,10 @@ def key_dither_steps(enc: EncodedRegion, spec: RegionSpec, n: int) -> np.ndarray
     if spec.k_fmt == "int8":
         return np.asarray(enc.k_scale, np.float64)[np.arange(n) // quant.BLOCK]
     if spec.k_fmt == "int8g32":
-        return np.repeat(np.asarray(enc.k_scale, np.float64)[:n], quant.GROUP, axis=1)
+        steps = np.repeat(np.asarray(enc.k_scale, np.float64)[:n], quant.GROUP, axis=1)
+        if enc.k_bypass is not None:                     # stored exactly: no dither
+            steps[:, enc.k_bypass] = 0.0
+        return steps
     if spec.k_fmt == "bf16":
         return np.zeros((n, np.asarray(enc.k_hat).shape[1]))
     raise ValueError("Tier B needs dithered INT8 keys or keys stored exactly")

@@ -118,11 +118,55 @@ def int8_dither_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
 GROUP = 32
 
 
-def int8_dither_g32_quantize(x: np.ndarray, xi: np.ndarray, group: int = GROUP):
+def outlier_mask(pairs, d: int = 128):
+    """Channels of a fixed set of outlier RoPE pairs (WitCert Sec. 6.2.5: one
+    channel set per (layer, KV head), m pairs): under the rotate-half pairing
+    pair j is channels j and j + d/2.  Slot i is active when its index lies
+    in [0, d/2) and no earlier slot holds the same index; inactive slots
+    bypass nothing.
+    Returns (bool (d,) bypassed channels, list of active flags per slot)."""
+    mask = np.zeros(d, dtype=bool)
+    active = []
+    seen = set()
+    for j in (int(p) for p in (pairs if pairs is not None else ())):
+        ok = 0 <= j < d // 2 and j not in seen
+        active.append(ok)
+        if ok:
+            seen.add(j)
+            mask[j] = mask[j + d // 2] = True
+    return mask, active
+
+
+def outlier_values(x: np.ndarray, pairs) -> np.ndarray:
+    """The bypassed values of every token, slot by slot: (T, 2m) with
+    [:, 2i] = x[:, P_i] and [:, 2i + 1] = x[:, P_i + d/2] for an active slot,
+    0 for an inactive one.  They are stored exactly (the keys' own 16-bit
+    values), so they must be bf16-exact."""
+    x = np.asarray(x, np.float64)
+    d = x.shape[1]
+    _, active = outlier_mask(pairs, d)
+    out = np.zeros((x.shape[0], 2 * len(active)))
+    for i, (j, ok) in enumerate(zip(pairs if pairs is not None else (), active)):
+        if ok:
+            out[:, 2 * i] = x[:, int(j)]
+            out[:, 2 * i + 1] = x[:, int(j) + d // 2]
+    bf = out.astype(np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    if not np.array_equal(bf.view(np.float32).astype(np.float64), out):
+        raise ValueError("outlier_values: bypassed values must be bf16-exact")
+    return out
+
+
+def int8_dither_g32_quantize(x: np.ndarray, xi: np.ndarray, group: int = GROUP,
+                             bypass: np.ndarray = None, amax_excludes_bypass: bool = True):
     """Per-token channel-group scales (WitCert Sec. 6.2.3, Table 4: token x
     G_c-channel groups, G_c = 32 the default; paging-safe): every token and
     group of 32 channels has its own s = fp16(fp32(amax / 126.5)); the codes
     are encoded exactly as in the block format, with the same dither.
+
+    bypass: bool (d,) channels stored exactly beside the codes (the fixed
+    outlier pairs of Sec. 6.2.5); they leave the group maximum (the page's
+    second step; amax_excludes_bypass=False keeps them in, the "bypass, amax
+    unchanged" treatment of its Table 5) and their codes are 0.
 
     x (T, d) exact values, xi (T, d) float32 dither.
     Returns (codes int8 (T, d), scale float16 (T, d / group), clipped count)."""
@@ -133,23 +177,33 @@ def int8_dither_g32_quantize(x: np.ndarray, xi: np.ndarray, group: int = GROUP):
     xi = np.asarray(xi, dtype=np.float32)
     T, d = x.shape
     ng = d // group
-    amax = np.max(np.abs(x32.reshape(T, ng, group)), axis=2)
+    byp = np.zeros(d, dtype=bool) if bypass is None else np.asarray(bypass, dtype=bool)
+    a = np.abs(x32)
+    if amax_excludes_bypass:
+        a = np.where(byp[None, :], np.float32(0.0), a)
+    amax = np.max(a.reshape(T, ng, group), axis=2)
     s16 = (amax / np.float32(INT8_DIV)).astype(np.float32).astype(np.float16)
     s = np.repeat(s16.astype(np.float32), group, axis=1)
     with np.errstate(divide="ignore", invalid="ignore"):
         y = (x32 / s).astype(np.float32)
         z = (y + xi).astype(np.float32)
     c = np.rint(z)
-    c = np.where(s == 0, 0.0, c)
+    c = np.where((s == 0) | byp[None, :], 0.0, c)
     clipped = int(np.sum(np.abs(c) > INT8_Q))
     return np.clip(c, -INT8_Q, INT8_Q).astype(np.int8), s16, clipped
 
 
 def int8_dither_g32_dequant(codes: np.ndarray, scales: np.ndarray, xi: np.ndarray,
-                            group: int = GROUP) -> np.ndarray:
+                            group: int = GROUP, bypass: np.ndarray = None,
+                            x_bypass: np.ndarray = None) -> np.ndarray:
+    """x^ = s (code - xi) per group; bypassed channels take their stored
+    exact values x_bypass (T, d) instead."""
     s = np.repeat(np.asarray(scales, np.float64), group, axis=1)
     out = s * (np.asarray(codes, np.float64) - np.asarray(xi, np.float32).astype(np.float64))
-    return np.where(s == 0, 0.0, out)
+    out = np.where(s == 0, 0.0, out)
+    if bypass is not None:
+        out = np.where(np.asarray(bypass, bool)[None, :], np.asarray(x_bypass, np.float64), out)
+    return out
 
 
 WITNESS_INFLATE = 1.0 + 2.0 ** -48
