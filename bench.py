@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--int8-scales", choices=("block", "group"), default="block",
                     help="with --workload: store INT8 regions with per-(256-token block, channel) "
                          "scales or per-(token, 32-channel group) scales")
+    ap.add_argument("--outlier-pairs", type=int, default=0, metavar="M",
+                    help="with --int8-scales group: M fixed outlier RoPE pairs per KV head kept "
+                         "exactly beside the keys (the workload's heavy pairs first)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
@@ -163,7 +166,7 @@ def _oracle_slice(lb):
     return time.perf_counter() - t
 
 
-def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False):
+def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False, n_pairs: int = 0):
     """One layer of workload `idx`: stage its caches through kvq_quantize, then
     time kvq_decode_attn (with TV, log A, bound and meter where the workload
     has exact keys and a witness) with HIP events on the launch stream."""
@@ -182,6 +185,12 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = kvq.load()
+    pairs = None
+    if n_pairs:
+        from workloads import outlier_channels
+        row = sorted({int(c) % 64 for c in outlier_channels(cfg)})[:n_pairs]
+        row += [j for j in range(64) if j not in row][:n_pairs - len(row)]
+        pairs = torch.tensor([row] * cfg.h_kv, dtype=torch.int32, device=dev)
     layer = 0
     inp = gen_layer(cfg, layer, dev)
     seed = 0x5EED0000 + idx
@@ -190,16 +199,19 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
     bytes_launch = 0
     if cfg.prefix is not None and cfg.prefix.length > 0:
         pr = cfg.prefix
-        st = kvq.alloc_stored(1, HKV, pr.length, pr.k_fmt, pr.v_fmt, pr.witness, dev, value_witness=True)
+        st = kvq.alloc_stored(1, HKV, pr.length, pr.k_fmt, pr.v_fmt, pr.witness, dev, value_witness=True,
+                              outlier_pairs=pairs if pr.k_fmt == "int8g32" else None)
         kvq.quantize_into(st, inp["prefix_k"][None].contiguous(), inp["prefix_v"][None].contiguous(),
                           seed=seed, layer=layer, stream_id=1_000_000)
         prefix = kvq.RegionView(st, pr.length, k_exact=inp["prefix_k"] if pr.exact_k else None, seed=seed,
                                 layer=layer, stream_id=1_000_000, use_witness=pr.witness)
         # the shared prefix counts once per launch (every request reads the same rows)
-        bytes_launch += HKV * pr.length * token_head_bytes(pr.k_fmt, pr.v_fmt, pr.exact_k, pr.witness)
+        bytes_launch += HKV * pr.length * (token_head_bytes(pr.k_fmt, pr.v_fmt, pr.exact_k, pr.witness)
+                                           + (4 * n_pairs if pr.k_fmt == "int8g32" else 0))
     sf = cfg.suffix
     # value records too (the value side of the extensions timing)
-    st = kvq.alloc_stored(B, HKV, sf.length, sf.k_fmt, sf.v_fmt, sf.witness, dev, value_witness=True)
+    st = kvq.alloc_stored(B, HKV, sf.length, sf.k_fmt, sf.v_fmt, sf.witness, dev, value_witness=True,
+                          outlier_pairs=pairs if sf.k_fmt == "int8g32" else None)
     kvq.quantize_into(st, inp["suffix_k"], inp["suffix_v"], seed=seed, layer=layer, stream_id=0)
     lens = inp["suffix_lens"]
     exact = inp["suffix_k"] if sf.exact_k else None
@@ -219,14 +231,16 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
             return o.contiguous()
 
         paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
-                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
+                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness),
+                           scatter(st.k_outliers), st.outlier_pairs)
         suffix = kvq.RegionView(paged, sf.length, k_exact=scatter(exact), lengths=lens, page_table=table,
                                 page_size=ps, seed=seed, layer=layer, stream_id=0, use_witness=sf.witness)
     else:
         suffix = kvq.RegionView(st, sf.length, k_exact=exact, lengths=lens, seed=seed, layer=layer,
                                 stream_id=0, use_witness=sf.witness)
     n_tok = int(lens.sum()) if lens is not None else B * sf.length
-    bytes_launch += HKV * n_tok * token_head_bytes(sf.k_fmt, sf.v_fmt, sf.exact_k, sf.witness)
+    bytes_launch += HKV * n_tok * (token_head_bytes(sf.k_fmt, sf.v_fmt, sf.exact_k, sf.witness)
+                                   + (4 * n_pairs if sf.k_fmt == "int8g32" else 0))   # outlier values
     bytes_launch += B * HQ * 128 * 4 * 2 + 4 * B * HQ * 4                     # q, out, meter
     sm = float(np.float32(1.0 / math.sqrt(128.0)))
     out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
@@ -303,7 +317,8 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         "workload": f"config {idx}: {cfg.description}".replace(
             "per-(256-token block, channel) fp16 scales",
             "per-(token, 32-channel group) fp16 scales" if group_scales else
-            "per-(256-token block, channel) fp16 scales"),
+            "per-(256-token block, channel) fp16 scales")
+        + (f", {n_pairs} fixed outlier RoPE pairs per KV head kept in bf16" if n_pairs else ""),
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
         "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
@@ -321,9 +336,11 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design doc describes how the step would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.outlier_pairs and args.int8_scales != "group":
+        sys.exit("--outlier-pairs needs --int8-scales group (the pairs sit beside group-scale keys)")
     if args.workload != 0:
         measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1),
-                         group_scales=args.int8_scales == "group")
+                         group_scales=args.int8_scales == "group", n_pairs=args.outlier_pairs)
         return
     import numpy as np
     import torch

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 9
+#define KVQ_ABI_VERSION 10
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -119,6 +119,17 @@ typedef struct kvq_region {
   const int32_t *stream_ids;/* suffix: optional device int32 [batch] stream ids (overrides) */
   const uint16_t *v_witness;/* value records, fp16 bits [.., len, 2] laid out like the witness:
                                (rho_t = ||v^_t - v_t||, ||v_t||), each rounded up; or NULL */
+  /* Fixed outlier RoPE pairs of the keys (WitCert Sec. 6.2.5: one channel set
+   * per (layer, KV head), kept exactly and left out of the group maximum),
+   * KVQ_FMT_INT8_G32 keys only.  Slot i of KV head h names pair
+   * P = outlier_pairs[h * n_outlier_pairs + i], i.e. channels P and P + 64;
+   * a slot is active when 0 <= P < 64 and no earlier slot of that head names
+   * P (others bypass nothing).  A bypassed channel's code is 0 and its value
+   * is k_outliers[.., t, 2 i] (channel P) and [.., 2 i + 1] (channel P + 64),
+   * the key's own bf16 value; inactive slots hold 0. */
+  const int32_t *outlier_pairs; /* device int32 [num_kv_heads, n_outlier_pairs], or NULL */
+  const uint16_t *k_outliers;   /* bf16 bits [.., len, 2 n_outlier_pairs] laid out like the codes */
+  int32_t n_outlier_pairs;      /* m in [0, 16]; 0: no bypass */
 } kvq_region;
 
 /* Decode-step attention over prefix ++ suffix for every (request, query head).
@@ -245,6 +256,12 @@ typedef struct kvq_quant_args {
                                (||v^_t - v_t||, ||v_t||): norms in float64 summed over
                                channels 0..127 in order, times 1 + 2^-48, rounded up
                                to fp16; or NULL.  Needs v_in. */
+  const int32_t *outlier_pairs; /* fixed outlier pairs of the keys, as in kvq_region: their
+                                   channels leave the group maximum, get code 0 and are
+                                   stored exactly in k_outliers_out.  KVQ_FMT_INT8_G32 keys
+                                   and BF16 input only (the stored values are the inputs). */
+  uint16_t *k_outliers_out;     /* bf16 bits [n_seq, Hk, capacity, 2 n_outlier_pairs] */
+  int32_t n_outlier_pairs;      /* m in [0, 16] */
 } kvq_quant_args;
 
 /* Library ABI version (KVQ_ABI_VERSION of the build). */

@@ -144,8 +144,14 @@ kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int ba
   if (need_v && r.v_format != KVQ_FMT_BF16 && !r.v_scale) return KVQ_ERR_NULL;
   if (r.k_exact && r.k_exact_format != KVQ_FMT_BF16 && r.k_exact_format != KVQ_FMT_FP32)
     return KVQ_ERR_FORMAT;
+  // fixed outlier pairs (WitCert Sec. 6.2.5): group-scale keys only
+  if (r.n_outlier_pairs < 0 || r.n_outlier_pairs > 16) return KVQ_ERR_SHAPE;
+  const bool op = r.n_outlier_pairs > 0;
+  if (op && r.k_format != KVQ_FMT_INT8_G32) return KVQ_ERR_UNSUPPORTED;
+  if (op && (!r.outlier_pairs || !r.k_outliers)) return KVQ_ERR_NULL;
   const void *ptrs[] = {r.k, need_v ? r.v : nullptr, r.k_scale, need_v ? r.v_scale : nullptr,
-                        r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids, r.v_witness};
+                        r.witness, r.k_exact, r.lengths, r.page_table, r.stream_ids, r.v_witness,
+                        op ? r.outlier_pairs : nullptr, op ? r.k_outliers : nullptr};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   const bool int8 = r.k_format == KVQ_FMT_INT8_DITHER || (need_v && r.v_format == KVQ_FMT_INT8_DITHER);   // block scales
@@ -306,6 +312,9 @@ RegionDev region_dev(const kvq_region &r, bool is_prefix) {
   d.stream_id = r.stream_id;
   d.stream_ids = is_prefix ? nullptr : r.stream_ids;
   d.v_witness = r.v_witness;
+  d.n_op = r.n_outlier_pairs > 0 ? r.n_outlier_pairs : 0;
+  d.opairs = d.n_op ? r.outlier_pairs : nullptr;
+  d.kout = d.n_op ? r.k_outliers : nullptr;
   return d;
 }
 
@@ -477,8 +486,14 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   if (a->v_in && !a->v_out) return KVQ_ERR_NULL;
   if (a->k_format != KVQ_FMT_BF16 && !a->k_scale_out) return KVQ_ERR_NULL;
   if (a->v_in && a->v_format != KVQ_FMT_BF16 && !a->v_scale_out) return KVQ_ERR_NULL;
+  if (a->n_outlier_pairs < 0 || a->n_outlier_pairs > 16) return KVQ_ERR_SHAPE;
+  const bool op = a->n_outlier_pairs > 0;
+  // the bypassed channels are stored as the inputs' own bf16 values
+  if (op && (a->k_format != KVQ_FMT_INT8_G32 || a->in_format != KVQ_FMT_BF16)) return KVQ_ERR_UNSUPPORTED;
+  if (op && (!a->outlier_pairs || !a->k_outliers_out)) return KVQ_ERR_NULL;
   const void *ptrs[] = {a->k_in, a->v_in, a->k_out, a->v_out, a->k_scale_out, a->v_scale_out,
-                        a->witness_out, a->stream_ids, a->v_witness_out};
+                        a->witness_out, a->stream_ids, a->v_witness_out,
+                        op ? a->outlier_pairs : nullptr, op ? a->k_outliers_out : nullptr};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KVQ_ERR_ALIGN;
   const bool int8 = a->k_format == KVQ_FMT_INT8_DITHER || (a->v_in && a->v_format == KVQ_FMT_INT8_DITHER);
@@ -497,6 +512,9 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
   q.witness_out = a->witness_out;
   q.seed = a->seed; q.layer = a->layer; q.stream_id = a->stream_id; q.stream_ids = a->stream_ids;
   q.v_witness_out = a->v_in ? a->v_witness_out : nullptr;
+  q.n_op = op ? a->n_outlier_pairs : 0;
+  q.opairs = op ? a->outlier_pairs : nullptr;
+  q.k_outliers_out = op ? a->k_outliers_out : nullptr;
   return launch_quantize(q, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 

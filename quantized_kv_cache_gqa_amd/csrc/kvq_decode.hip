@@ -106,6 +106,38 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   // block report: spill (l~, l) and c of every token-head, the Tier B radius
   // of every INT8 block
   const bool do_r = d.has_report != 0;
+  // fixed outlier pairs of group-scale keys (WitCert Sec. 6.2.5): byp16 marks
+  // the bypassed channels among this lane's 16 (their dequantized value is
+  // replaced by 0), qo holds q at the channels of outlier values 4 j .. 4 j + 3
+  uint32_t byp16 = 0;
+  float qo[G][4];
+  const int n_op = KF == KVQ_FMT_INT8_G32 ? R.n_op : 0;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qo[h][e] = 0.0f;
+  if (n_op > 0) {
+    const int32_t *opp = R.opairs + (size_t)kvh * n_op;
+    for (int i = 0; i < n_op; ++i) {                     // pair P: channels P and P + 64
+      const int P = opp[i];
+      if (P >= 0 && P < 64 && (P >> 4) == (j & 3)) byp16 |= 1u << (P & 15);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 4 * j + e, slot = k >> 1;
+      if (k < 2 * n_op) {
+        const int P = opp[slot];
+        bool act = P >= 0 && P < 64;
+        for (int i = 0; i < slot; ++i) act = act && opp[i] != P;
+        if (act) {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            qo[h][e] = d.q[((size_t)b * d.h_q + (size_t)kvh * G + h) * D + P + 64 * (k & 1)] * qs;
+        }
+      }
+    }
+  }
+
   float mq[G], zq[G], mm[G], zm[G], me[G], ze[G], zb[G], zv[G], mn[G], zn[G], cmx[G];
   float vmax = 0.0f;
   float acc[G][16];
@@ -147,6 +179,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       ksc8 = (const uint16_t *)R.k_scale + ((sh * nblk_cap + tc / BLK) * D);
     if constexpr (KF == KVQ_FMT_INT8_G32) ksc8 = (const uint16_t *)R.k_scale + row * 4;
     load_row16<KF>(R.k, row, j, kv, ksc8, (uint32_t)tc, ktag, stream, R.seed_lo, R.seed_hi);
+    if (byp16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) kv[i] = ((byp16 >> i) & 1u) ? 0.0f : kv[i];
+    }
     float ks = 1.0f;
     if constexpr (KF == KVQ_FMT_FP8_E4M3) ks = reinterpret_cast<const float *>(R.k_scale)[row];
 
@@ -159,6 +195,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       pq[h] = s;
       pe[h] = 0.0f;
       pc[h] = 0.0f;
+    }
+    if (n_op > 0) {                                      // the bypassed channels, exact
+      const uint16_t *op = R.kout + row * (size_t)(2 * n_op);
+      float ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * j + e;
+        ov[e] = k < 2 * n_op ? __uint_as_float((uint32_t)op[k] << 16) : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pq[h] = fmaf(qo[h][e], ov[e], pq[h]);
     }
     if (do_tv && has_exact) {
       float ke[16];
@@ -226,9 +275,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         const float s = fp16_bits_to_f32(ksc8[j >> 1]);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          float ss = 0.0f;
+          float ss = 0.0f;                               // bypassed channels: no dither
 #pragma unroll
-          for (int i = 0; i < 16; ++i) ss = fmaf(qv[h][i], qv[h][i], ss);
+          for (int i = 0; i < 16; ++i) ss = ((byp16 >> i) & 1u) ? ss : fmaf(qv[h][i], qv[h][i], ss);
           eub[h] = exp2f(sqrtf(sum8(ss * s * s) * tb_l * (1.0f / 6.0f)));
         }
       }

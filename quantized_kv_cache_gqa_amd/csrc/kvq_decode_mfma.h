@@ -125,6 +125,7 @@ struct TileRegs {
   uint32_t vrec;   // value record of this lane's token: fp16 (rho, ||v||)
   uint2 kg[4];     // INT8 group scales: the 4 fp16 key scales of token 4 g + e
   uint32_t vg[4];  // INT8 group scales: value scale of token 4 g + e, dims 8 j16 ..
+  uint4 ko;        // outlier values 8 g .. 8 g + 7 of token j16 (bf16, 0 past 2 m)
 };
 
 // Addressing of one (request, KV head) region range ending at c1, and the
@@ -139,6 +140,8 @@ struct TileSrc {
   const uint16_t *wb, *vwb;
   const float *ksb, *vsb;
   const uint16_t *ksg, *vsg;   // INT8 group scales: 4 per row
+  const uint16_t *kob;         // outlier values of the keys: 2 n_op per row
+  int n_op;
   const int32_t *ptab;
   int pshift, page_size, h_kv, kvh, last;
 
@@ -161,6 +164,8 @@ struct TileSrc {
     vsb = (const float *)R.v_scale + row0;
     ksg = (const uint16_t *)R.k_scale + row0 * 4;
     vsg = (const uint16_t *)R.v_scale + row0 * 4;
+    n_op = R.n_op;
+    kob = R.kout + row0 * (size_t)(2 * R.n_op);
   }
 
   __device__ __forceinline__ RowT row_of(int t) const {   // row index relative to row0
@@ -199,6 +204,16 @@ struct TileSrc {
 #pragma unroll
       for (int e = 0; e < 4; ++e) T.kg[e] = *reinterpret_cast<const uint2 *>(ksg + row_of(t0 + 4 * g + e) * 4);
       T.ks = 1.0f;
+      if (n_op > 0) {
+        // values 8 g + 2 i, 8 g + 2 i + 1 (a pair's two channels) as one word;
+        // rows are 4 n_op bytes, so every word is aligned
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(kob + ra * (2 * n_op) + 8 * g);
+        const int nw = n_op - 4 * g;                     // words of this lane's 4 that exist
+        T.ko.x = nw > 0 ? p[0] : 0u;
+        T.ko.y = nw > 1 ? p[1] : 0u;
+        T.ko.z = nw > 2 ? p[2] : 0u;
+        T.ko.w = nw > 3 ? p[3] : 0u;
+      }
     } else {
       const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * (2 * D) + 64 * g);
 #pragma unroll
@@ -390,14 +405,47 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
   };
 
+  // fixed outlier pairs (WitCert Sec. 6.2.5): their channels leave the
+  // group contractions (q zeroed there) and enter one more contraction
+  // against the stored exact values (bqo: q at the channels of values
+  // 8 g .. 8 g + 7, three-way split by column)
   float qg2[4] = {0.0f, 0.0f, 0.0f, 0.0f};         // group sums of (q_c qs)^2 of head hh
+  bf16x8_t bqo;
+  const int n_op = R.n_op;
   if constexpr (GK) {
     const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
-#pragma unroll
-    for (int s8 = 0; s8 < 4; ++s8) {
+    uint32_t bm0 = 0, bm1 = 0;                       // bypassed pairs 0..31, 32..63
+    if (n_op > 0) {
+      const int32_t *opp = R.opairs + (size_t)kvh * n_op;
+      for (int i = 0; i < n_op; ++i) {
+        const int P = opp[i];
+        if (P >= 0 && P < 32) bm0 |= 1u << P;
+        if (P >= 32 && P < 64) bm1 |= 1u << (P - 32);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = qp[32 * s8 + 8 * g + e] * qs;
+        const int k = 8 * g + e, slot = k >> 1;
+        float x = 0.0f;
+        if (k < 2 * n_op) {
+          const int P = opp[slot];
+          bool act = P >= 0 && P < 64;
+          for (int i = 0; i < slot; ++i) act = act && opp[i] != P;
+          if (act) x = qp[P + 64 * (k & 1)] * qs;
+        }
+        const float hi = bf16_round(x);
+        const float mid = bf16_round(x - hi);
+        const float lo = bf16_round(x - hi - mid);
+        bqo[e] = (__bf16)(pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f)));
+      }
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8) {
+      // channels 32 s8 + 8 g + e: pair (32 s8 + 8 g + e) mod 64
+      const uint32_t bw_ = (s8 & 1) ? bm1 : bm0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool byp = (bw_ >> (8 * g + e)) & 1u;
+        const float x = byp ? 0.0f : qp[32 * s8 + 8 * g + e] * qs;
         qg2[s8] = fmaf(x, x, qg2[s8]);
         const float hi = bf16_round(x);
         const float mid = bf16_round(x - hi);
@@ -492,6 +540,12 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         ss = fmaf(s1 * s1, qg2[1], ss);
         ss = fmaf(s2 * s2, qg2[2], ss);
         ssr[r] = fmaf(s3 * s3, qg2[3], ss);
+      }
+      if (n_op > 0) {                                // the bypassed channels, exact
+        const f32x4_t dov = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(T.ko), bqo,
+                                                                    f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dq[r] += dov[r];
       }
       if (do_b) {
         // this lane's token t0 + 4 g + pp: u log2(e) = sqrt(sum_s s_s^2 qg2_s tb_l / 6)

@@ -21,6 +21,9 @@ struct QuantLaunch {
   int layer, stream_id;
   const int32_t *stream_ids;
   uint16_t *v_witness_out;  // value records (rho, ||v||) per token, nullable
+  const int32_t *opairs;    // fixed outlier pairs of the keys [h_kv, n_op] (n_op > 0)
+  uint16_t *k_outliers_out; // bf16 [.., capacity, 2 n_op]
+  int n_op;
 };
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t stream);
@@ -45,6 +48,9 @@ struct RegionDev {
   int layer, stream_id;
   const int32_t *stream_ids;
   const uint16_t *v_witness;    // value records (rho, ||v||) per token (nullable)
+  const int32_t *opairs;        // fixed outlier pairs of the keys [h_kv, n_op]
+  const uint16_t *kout;         // their exact values, bf16 [.., len, 2 n_op]
+  int n_op;                     // outlier pairs per KV head (0: none)
 };
 
 struct DecodeLaunch {

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
     const void *__restrict__ in, int in_fmt, int target, int n_seq, int h_kv, int capacity,
     int tok_begin, int tok_end, uint8_t *__restrict__ out, void *__restrict__ scale_out,
     uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out, int kv, uint32_t k0, uint32_t k1,
-    int layer, int stream_id, const int32_t *__restrict__ stream_ids) {
+    int layer, int stream_id, const int32_t *__restrict__ stream_ids, const int32_t *__restrict__ opairs,
+    int n_op, uint16_t *__restrict__ kout) {
 #pragma clang fp contract(off)
   __shared__ double rbuf[4][D];
   __shared__ double xbuf[4][D];
@@ -97,7 +98,32 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
     h0 = (double)e4m3_decode_sw(c0) * (double)s;
     h1 = (double)e4m3_decode_sw(c1) * (double)s;
   } else if (target == KVQ_FMT_INT8_G32) {
-    float a0 = fabsf(x0), a1 = fabsf(x1);
+    const int seq = (int)(sh / h_kv), kvh = (int)(sh - (long)seq * h_kv);
+    // fixed outlier pairs (WitCert Sec. 6.2.5): pair `lane` (channels lane and
+    // lane + 64) is bypassed when a slot names it; it keeps its bf16 value,
+    // gets code 0 and leaves the group maximum
+    int oslot = -1;
+    if (n_op > 0) {
+      const int32_t *pp = opairs + (size_t)kvh * n_op;
+      for (int i = n_op - 1; i >= 0; --i)
+        if (pp[i] == lane) oslot = i;                    // the first slot naming the pair
+      uint16_t *orow = kout + row * (size_t)(2 * n_op);
+      if (lane < n_op) {                                 // slots that bypass nothing hold 0
+        const int P = pp[lane];
+        bool act = P >= 0 && P < 64;
+        for (int i = 0; i < lane; ++i) act = act && pp[i] != P;
+        if (!act) {
+          orow[2 * lane] = 0;
+          orow[2 * lane + 1] = 0;
+        }
+      }
+      if (oslot >= 0) {
+        orow[2 * oslot] = (uint16_t)(__float_as_uint(x0) >> 16);   // bf16 input: exact
+        orow[2 * oslot + 1] = (uint16_t)(__float_as_uint(x1) >> 16);
+      }
+    }
+    const bool byp = oslot >= 0;
+    float a0 = byp ? 0.0f : fabsf(x0), a1 = byp ? 0.0f : fabsf(x1);
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) {             // maxima over each half-wavefront
       a0 = fmaxf(a0, __shfl_xor(a0, off));
@@ -110,7 +136,6 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
       sc[lane >> 5] = (uint16_t)s0b;
       sc[2 + (lane >> 5)] = (uint16_t)s1b;
     }
-    const int seq = (int)(sh / h_kv), kvh = (int)(sh - (long)seq * h_kv);
     const uint32_t tag = dither_tag(kv, layer, kvh);
     const uint32_t stream = (uint32_t)(stream_ids ? stream_ids[seq] : stream_id + seq);
     float xa[4], xb[4];
@@ -128,10 +153,15 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
       float z = y + xi1;
       c1 = fminf(fmaxf(rintf(z), -127.0f), 127.0f);
     }
+    if (byp) c0 = c1 = 0.0f;
     out[row * D + lane] = (uint8_t)(int8_t)(int)c0;
     out[row * D + lane + 64] = (uint8_t)(int8_t)(int)c1;
     h0 = s0 != 0.0f ? (double)s0 * ((double)c0 - (double)xi0) : 0.0;
     h1 = s1 != 0.0f ? (double)s1 * ((double)c1 - (double)xi1) : 0.0;
+    if (byp) {
+      h0 = (double)x0;
+      h1 = (double)x1;
+    }
   } else {                                               // BF16 target
     uint32_t b0 = in_fmt == KVQ_FMT_FP32 ? f32_to_bf16_bits(x0) : (__float_as_uint(x0) >> 16);
     uint32_t b1 = in_fmt == KVQ_FMT_FP32 ? f32_to_bf16_bits(x1) : (__float_as_uint(x1) >> 16);
@@ -267,7 +297,8 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
     hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
                        q.in_format, fmt, q.n_seq, q.h_kv, q.capacity, q.tok_begin, q.tok_end,
                        (uint8_t *)out, sc, wit, vrec, which, (uint32_t)q.seed, (uint32_t)(q.seed >> 32),
-                       q.layer, q.stream_id, q.stream_ids);
+                       q.layer, q.stream_id, q.stream_ids, which == 0 ? q.opairs : nullptr,
+                       which == 0 ? q.n_op : 0, which == 0 ? q.k_outliers_out : nullptr);
   }
   return hipGetLastError();
 }

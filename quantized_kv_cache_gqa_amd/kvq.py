@@ -42,7 +42,8 @@ class Region(ctypes.Structure):
                 ("k_exact", c_void_p), ("k_exact_format", c_int32), ("length", c_int32),
                 ("lengths", c_void_p), ("page_table", c_void_p), ("page_size", c_int32),
                 ("max_pages", c_int32), ("seed", ctypes.c_uint64), ("layer", c_int32),
-                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness", c_void_p)]
+                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness", c_void_p),
+                ("outlier_pairs", c_void_p), ("k_outliers", c_void_p), ("n_outlier_pairs", c_int32)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -67,14 +68,15 @@ class QuantArgs(ctypes.Structure):
                 ("tok_begin", c_int32), ("tok_end", c_int32), ("k_out", c_void_p),
                 ("v_out", c_void_p), ("k_scale_out", c_void_p), ("v_scale_out", c_void_p),
                 ("witness_out", c_void_p), ("seed", ctypes.c_uint64), ("layer", c_int32),
-                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness_out", c_void_p)]
+                ("stream_id", c_int32), ("stream_ids", c_void_p), ("v_witness_out", c_void_p),
+                ("outlier_pairs", c_void_p), ("k_outliers_out", c_void_p), ("n_outlier_pairs", c_int32)]
 
 
 _lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class PlanInfo(ctypes.Structure):
@@ -147,10 +149,19 @@ class Stored:
     v_scale: Optional[torch.Tensor]
     witness: Optional[torch.Tensor]
     v_witness: Optional[torch.Tensor] = None   # fp16 [.., capacity, 2]: rho, ||v||
+    k_outliers: Optional[torch.Tensor] = None  # bf16 bits [.., capacity, 2 m]: the bypassed key values
+    outlier_pairs: Optional[torch.Tensor] = None   # int32 [h_kv, m]: fixed outlier RoPE pairs
+
+    @property
+    def n_outlier_pairs(self) -> int:
+        return 0 if self.outlier_pairs is None else int(self.outlier_pairs.shape[1])
 
 
 def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Optional[str],
-                 witness: bool, device, value_witness: bool = False) -> Stored:
+                 witness: bool, device, value_witness: bool = False,
+                 outlier_pairs: Optional[torch.Tensor] = None) -> Stored:
+    """outlier_pairs: int32 [h_kv, m] fixed outlier RoPE pairs of "int8g32" keys
+    (kept exactly, left out of the group maximum), or None."""
     def codes(fmt):
         dt = {"bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8, "int8g32": torch.int8}[fmt]
         return torch.zeros((n_seq, h_kv, capacity, HEAD_DIM), dtype=dt, device=device)
@@ -171,7 +182,10 @@ def alloc_stored(n_seq: int, h_kv: int, capacity: int, fmt_k: str, fmt_v: Option
                   torch.zeros((n_seq, h_kv, capacity, N_BANDS), dtype=torch.float16, device=device)
                   if witness else None,
                   torch.zeros((n_seq, h_kv, capacity, 2), dtype=torch.float16, device=device)
-                  if value_witness and fmt_v else None)
+                  if value_witness and fmt_v else None,
+                  torch.zeros((n_seq, h_kv, capacity, 2 * outlier_pairs.shape[1]), dtype=torch.int16,
+                              device=device) if outlier_pairs is not None else None,
+                  outlier_pairs)
 
 
 def quantize_into(st: Stored, k_in: torch.Tensor, v_in: Optional[torch.Tensor], *, tok_begin: int = 0,
@@ -191,7 +205,9 @@ def quantize_into(st: Stored, k_in: torch.Tensor, v_in: Optional[torch.Tensor], 
                   v_scale_out=_ptr(st.v_scale) if v_in is not None else None,
                   witness_out=_ptr(st.witness), seed=seed, layer=layer, stream_id=stream_id,
                   stream_ids=_ptr(stream_ids),
-                  v_witness_out=_ptr(st.v_witness) if v_in is not None else None)
+                  v_witness_out=_ptr(st.v_witness) if v_in is not None else None,
+                  outlier_pairs=_ptr(st.outlier_pairs), k_outliers_out=_ptr(st.k_outliers),
+                  n_outlier_pairs=st.n_outlier_pairs)
     _check(lib.kvq_quantize(ctypes.byref(a), _stream(stream)), "kvq_quantize")
 
 
@@ -226,7 +242,9 @@ class RegionView:
                       page_size=self.page_size,
                       max_pages=self.page_table.shape[1] if self.page_table is not None else 0,
                       seed=self.seed, layer=self.layer, stream_id=self.stream_id,
-                      stream_ids=_ptr(self.stream_ids), v_witness=_ptr(st.v_witness))
+                      stream_ids=_ptr(self.stream_ids), v_witness=_ptr(st.v_witness),
+                      outlier_pairs=_ptr(st.outlier_pairs), k_outliers=_ptr(st.k_outliers),
+                      n_outlier_pairs=st.n_outlier_pairs)
 
 
 def _attn_args(q, prefix: Optional[RegionView], suffix: Optional[RegionView], out, sm_scale,

@@ -13,6 +13,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 import torch
 
+from oracle.numerics import f64_to_bf16_bits
 from oracle.pipeline import RegionSpec, decode_cell, encode_region
 from workloads import Config, gen_layer
 
@@ -24,22 +25,47 @@ def dither_seed(cfg: Config) -> int:
     return (cfg.seed * 0x9E3779B97F4A7C15) % (1 << 64)
 
 
-def _spec(cfg: Config, region, layer: int, stream: int, value_witness: bool = False) -> RegionSpec:
+def _spec(cfg: Config, region, layer: int, stream: int, value_witness: bool = False,
+          outlier_pairs=None) -> RegionSpec:
     return RegionSpec(k_fmt=region.k_fmt, v_fmt=region.v_fmt, seed=dither_seed(cfg), layer=layer,
                       stream=stream, witness=region.witness, exact_k=region.exact_k,
-                      value_witness=value_witness)
+                      value_witness=value_witness,
+                      outlier_pairs=outlier_pairs if region.k_fmt == "int8g32" else None)
+
+
+def outlier_pairs(cfg: Config, m: int) -> np.ndarray:
+    """(h_kv, m) fixed outlier RoPE pairs per KV head: the workload's heavy
+    channels' pairs first, then other pairs, a different filler per head; KV
+    head 1 also carries a repeated and an out-of-range slot (inactive)."""
+    from workloads import outlier_channels
+    heavy = sorted({int(c) % 64 for c in outlier_channels(cfg)})
+    out = np.zeros((cfg.h_kv, m), np.int32)
+    for h in range(cfg.h_kv):
+        row = heavy[:m]
+        j = 5 + 11 * h
+        while len(row) < m:
+            if j % 64 not in row:
+                row.append(j % 64)
+            j += 7
+        out[h] = row
+        if h == 1 and m >= 4:
+            out[h, m - 2] = out[h, 0]                     # repeats slot 0
+            out[h, m - 1] = 64 + h                        # no such pair
+    return out
 
 
 class GpuCase:
     """One layer of a workload quantized and stored by the HIP write path."""
 
     def __init__(self, cfg: Config, layer: int = 0, device="cuda", page_seed: int = 0,
-                 fp32_exact: bool = False, value_witness: bool = False):
+                 fp32_exact: bool = False, value_witness: bool = False, n_outlier_pairs: int = 0):
         from quantized_kv_cache_gqa_amd import kvq
         self.kvq = kvq
         self.cfg, self.layer, self.device = cfg, layer, device
         self.fp32_exact = fp32_exact
         self.value_witness = value_witness
+        self.opairs = outlier_pairs(cfg, n_outlier_pairs) if n_outlier_pairs else None
+        op_dev = torch.from_numpy(self.opairs).to(device) if n_outlier_pairs else None
         self.inp = gen_layer(cfg, layer, device, want_fp32_keys=fp32_exact)
         G, hkv = cfg.group, cfg.h_kv
         seed = dither_seed(cfg)
@@ -53,7 +79,8 @@ class GpuCase:
             if fp32_exact:
                 vin = vin.float()
             st = kvq.alloc_stored(1, hkv, P, pr.k_fmt, pr.v_fmt, pr.witness or fp32_exact, device,
-                                  value_witness=value_witness)
+                                  value_witness=value_witness,
+                                  outlier_pairs=op_dev if pr.k_fmt == "int8g32" else None)
             kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=PREFIX_STREAM)
             exact = kin[0] if (pr.exact_k or fp32_exact) else None
             self.prefix_store = st
@@ -65,7 +92,8 @@ class GpuCase:
         kin = self.inp["suffix_k32"] if fp32_exact else self.inp["suffix_k"]
         vin = self.inp["suffix_v"].float() if fp32_exact else self.inp["suffix_v"]
         st = kvq.alloc_stored(cfg.batch, hkv, cap, sf.k_fmt, sf.v_fmt, sf.witness or fp32_exact, device,
-                              value_witness=value_witness)
+                              value_witness=value_witness,
+                              outlier_pairs=op_dev if sf.k_fmt == "int8g32" else None)
         kvq.quantize_into(st, kin, vin, seed=seed, layer=layer, stream_id=0)
         self.suffix_store = st
         exact = kin if (sf.exact_k or fp32_exact) else None
@@ -102,7 +130,8 @@ class GpuCase:
             return out.contiguous()
 
         paged = kvq.Stored(st.fmt_k, st.fmt_v, scatter(st.k), scatter(st.v), scatter(st.k_scale),
-                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness))
+                           scatter(st.v_scale), scatter(st.witness), scatter(st.v_witness),
+                           scatter(st.k_outliers), st.outlier_pairs)
         self.page_table = table
         return kvq.RegionView(paged, cap, k_exact=scatter(exact), lengths=lens, page_table=table,
                               page_size=ps, seed=dither_seed(cfg), layer=self.layer, stream_id=0,
@@ -140,7 +169,7 @@ def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
         key = "prefix_k32" if case.fp32_exact else "prefix_k"
         k = inp[key][kvh].double().cpu().numpy()
         v = inp["prefix_v"][kvh].double().cpu().numpy()
-        spec = _spec(cfg, cfg.prefix, layer, PREFIX_STREAM, case.value_witness)
+        spec = _spec(cfg, cfg.prefix, layer, PREFIX_STREAM, case.value_witness, case.opairs)
         if case.fp32_exact:
             spec.witness = True
             spec.exact_k = True
@@ -151,7 +180,7 @@ def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):
     key = "suffix_k32" if case.fp32_exact else "suffix_k"
     k = inp[key][b, kvh, :n].double().cpu().numpy()
     v = inp["suffix_v"][b, kvh, :n].double().cpu().numpy()
-    spec = _spec(cfg, cfg.suffix, layer, b, case.value_witness)
+    spec = _spec(cfg, cfg.suffix, layer, b, case.value_witness, case.opairs)
     if case.fp32_exact:
         spec.witness = True
         spec.exact_k = True
@@ -197,6 +226,11 @@ def check_stored(case: GpuCase, b: int, kvh: int, encs) -> None:
         if enc.w16 is not None and st.witness is not None:
             np.testing.assert_array_equal(_bits(st.witness[bb, hh, :nn]), enc.w16.view(np.uint16),
                                           err_msg=f"{name} witness")
+        assert (enc.k_out is None) == (st.k_outliers is None)
+        if enc.k_out is not None:
+            ref = f64_to_bf16_bits(enc.k_out).astype(np.uint16)
+            np.testing.assert_array_equal(_bits(st.k_outliers[bb, hh, :nn]).view(np.uint16), ref,
+                                          err_msg=f"{name} outlier values")
         if enc.v_rec is not None and st.v_witness is not None:
             np.testing.assert_array_equal(_bits(st.v_witness[bb, hh, :nn]), enc.v_rec.view(np.uint16),
                                           err_msg=f"{name} value records")

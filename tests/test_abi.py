@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 9
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 10
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -326,3 +326,46 @@ def test_int8_group_scale_format_arguments(lib, monkeypatch):
     q.layer = -1
     q.v_format = 5
     assert lib.kvq_quantize(ctypes.byref(q), None) == 2            # dither tag range
+
+
+def test_outlier_pair_arguments(lib, monkeypatch):
+    """Fixed outlier pairs need group-scale keys, at most 16 pairs, both
+    pointers, and (write path) bf16 input, since the stored values are the
+    inputs themselves."""
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    info = kvq.PlanInfo()
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    for kf, n, pairs, vals, status in (("int8g32", 4, FAKE, FAKE, 0), ("int8g32", 16, FAKE, FAKE, 0),
+                                       ("int8g32", 17, FAKE, FAKE, 2), ("int8g32", -1, FAKE, FAKE, 2),
+                                       ("int8g32", 4, None, FAKE, 1), ("int8g32", 4, FAKE, None, 1),
+                                       ("int8g32", 4, FAKE + 4, FAKE, 4), ("int8", 4, FAKE, FAKE, 5),
+                                       ("fp8", 4, FAKE, FAKE, 5), ("int8g32", 0, None, None, 0)):
+        vf = "int8g32" if kf == "int8g32" else kf
+        a = _args(batch=8, suffix=4096, kf=kf, vf=vf)
+        a.suffix.n_outlier_pairs, a.suffix.outlier_pairs, a.suffix.k_outliers = n, pairs, vals
+        assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, ctypes.byref(info)) == status, (kf, n)
+    q = kvq.QuantArgs(k_format=5, v_format=5, in_format=3, k_in=FAKE, v_in=FAKE, n_seq=2,
+                      num_kv_heads=8, head_dim=128, capacity=1000, tok_begin=0, tok_end=1000,
+                      k_out=FAKE, v_out=FAKE, k_scale_out=FAKE, v_scale_out=FAKE,
+                      outlier_pairs=FAKE, k_outliers_out=FAKE, n_outlier_pairs=4)
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 5             # fp32 input
+    q.in_format, q.k_format, q.v_format = 0, 2, 2
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 5             # block-scale keys
+    q.k_format, q.v_format, q.k_outliers_out = 5, 5, None
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 1
+    q.k_outliers_out, q.n_outlier_pairs = FAKE, 17
+    assert lib.kvq_quantize(ctypes.byref(q), None) == 2
+
+
+def test_outlier_store_bytes_match_the_page(tmp_path):
+    """The binding's key store for group-scale INT8 with m outlier pairs
+    takes 136 + 4 m bytes per token and KV head (WitCert Sec. 6.2.5, Table 6:
+    136, 144, 152, 168, 200 B/tok/head for m = 0, 2, 4, 8, 16)."""
+    import torch
+    for m, b in ((0, 136), (2, 144), (4, 152), (8, 168), (16, 200)):
+        pairs = torch.arange(m, dtype=torch.int32).view(1, m) if m else None
+        st = kvq.alloc_stored(1, 1, 10, "int8g32", None, False, "cpu", outlier_pairs=pairs)
+        n = st.k.element_size() * st.k.numel() + st.k_scale.element_size() * st.k_scale.numel()
+        if st.k_outliers is not None:
+            n += st.k_outliers.element_size() * st.k_outliers.numel()
+        assert n == 10 * b, (m, n)

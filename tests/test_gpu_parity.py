@@ -547,3 +547,31 @@ def test_int8_group_scales_every_cell(gpu_lib, kernel, monkeypatch, name):
             _, ref = oracle_cell(case, b, kvh)
             check_block_report(case, mb, b, kvh, ref, False)
 
+
+
+OUTLIERS = {
+    "dense-m4": (lambda: _g32(), 4),
+    "paged-m8": (lambda: _g32(paged=True), 8),
+    "paged-cartridge-m2": (lambda: _g32(paged=True, cartridge=True), 2),
+    "dense-m16": (lambda: _g32(), 16),
+}
+
+
+@pytest.mark.parametrize("name", list(OUTLIERS))
+def test_outlier_pairs_every_cell(gpu_lib, kernel, name):
+    """Fixed outlier RoPE pairs beside group-scale INT8 keys (WitCert Sec.
+    6.2.5): codes, scales (the pairs left out of the group maximum) and the
+    stored exact values bit-exact; output, Tier A, Tier B (no dither on the
+    bypassed channels) and the value side on every cell against the oracle,
+    KV head 1 with a repeated and an out-of-range slot; the bypass lowers
+    Tier B's log A_B on these keys with heavy RoPE pairs."""
+    make, m = OUTLIERS[name]
+    cfg = make()
+    case = GpuCase(cfg, page_seed=10, value_witness=True, n_outlier_pairs=m)
+    out, mo, worst = _all_cells(case, tier_b_delta=1e-3, value_bound=True)
+    assert {"bound_b", "value_err"} <= set(worst)
+    assert torch.all(mo["tv"] <= mo["bound_b_raw"]) and torch.all(mo["tv"] <= mo["bound_raw"])
+    _all_cells(case, split_tokens=128)                  # the kernels without the extensions
+    plain = GpuCase(cfg, page_seed=10)
+    _, mp = plain.run(tier_b_delta=1e-3)
+    assert float(mo["log_a_b"].median()) < float(mp["log_a_b"].median())
