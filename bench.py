@@ -296,6 +296,20 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         e1.record(stream)
     torch.cuda.synchronize()
     ext_ms = sorted(e0.elapsed_time(e1) for e0, e1 in x_evs)[reps // 2]
+    # the value side and the two-sided form (with the tanh shape) alone: no
+    # block report, so the plan is the plain call's (a team where one applies)
+    vt = {k: ext[k] for k in kvq.VALUE_KEYS + kvq.TWO_SIDED_KEYS}
+    meter_vt = kvq.MeterOut(**{k: v.data_ptr() for k, v in list(mbuf.items()) + list(vt.items())})
+    info_vt = kvq.PlanInfo()
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter_vt), 0, ctypes.byref(info_vt)) == 0
+    assert info_vt.workspace_bytes <= ws.numel()
+    vt_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in vt_evs:
+        e0.record(stream)
+        assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(meter_vt), ws.data_ptr(), ws.numel(), sp) == 0
+        e1.record(stream)
+    torch.cuda.synchronize()
+    vt_ms = sorted(e0.elapsed_time(e1) for e0, e1 in vt_evs)[reps // 2]
     # with Tier B as well (dithered INT8 keys: the sub-Gaussian certificate)
     tier_b_ms = None
     if sf.k_fmt in ("int8", "int8g32"):
@@ -323,6 +337,8 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
         "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
         "with_all_extensions_launch_ms": ext_ms,
+        "with_value_and_two_sided_launch_ms": vt_ms,
+        "value_and_two_sided_plan": f"team {info_vt.team}" if info_vt.team else f"{info_vt.chunks} chunk(s)",
         "extensions": "value side, two-sided form, tanh shape, block report"
                       + (", Tier B" if tier_b_ok else "") + f" (plan: {info_x.chunks} chunk(s), team {info_x.team})",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

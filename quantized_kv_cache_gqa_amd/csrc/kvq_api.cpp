@@ -80,8 +80,7 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || p.tier_b || p.value || p.two_sided || p.report || a->split_tokens != 0 || p.group != 4)
-    return false;
+  if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || p.group != 4) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -89,12 +88,15 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (!meter_only && vf != KVQ_FMT_BF16 && vf != KVQ_FMT_FP8_E4M3) return false;
   if (!r.k_exact || r.k_exact_format != KVQ_FMT_BF16) return false;
   const bool full = p.tv && p.meter && r.witness;
+  // the value side and the two-sided form ride on the exchange (full meter only)
+  const bool ext = p.value || p.two_sided;
+  if (ext && !full) return false;
   // one plan for the decode and the meter call on the same arguments (so
   // kvq_workspace_bytes fits both): the smaller capacity of the two kernels
   const bool paged = p.prefix_len == 0 && r.page_table;
   const int vf_dec = (r.v_format == KVQ_FMT_BF16 || r.v_format == KVQ_FMT_FP8_E4M3) ? r.v_format : VF_NONE;
-  const int cap = std::min(team_capacity(r.k_format, VF_NONE, paged, full),
-                           team_capacity(r.k_format, vf_dec, paged, full));
+  const int cap = std::min(team_capacity(r.k_format, VF_NONE, paged, full, ext),
+                           team_capacity(r.k_format, vf_dec, paged, full, ext));
   (void)vf;
   if (cap <= 0) return false;
   const int64_t len = r.length;

@@ -285,14 +285,14 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   // maximum.  tb_l = log(2 S / delta) with S the request's tokens (both
   // regions); eub = e^{u} of this lane's head, constant over a 256-token
   // block of INT8 keys and 1 for keys stored as BF16 (u = 0).
-  // (the team launch never takes Tier B or the value side: SPILL_LDS compiles
-  // them out of its kernel)
+  // (the team launch never takes Tier B or the block report: SPILL_LDS
+  // compiles them out of its kernel)
   const bool do_b = EXT && !SPILL_LDS && d.has_tier_b != 0;
   // value side (WitCert Sec. 3 output bound): zv accumulates p~ rho on the
   // attention maximum, vmax the largest ||v|| of the chunk's tokens
-  const bool do_v = EXT && !SPILL_LDS && d.has_value != 0;
+  const bool do_v = EXT && d.has_value != 0;
   // two-sided form (WitCert Prop. 1): a running state over l~ - c for A-
-  const bool do_n = EXT && !SPILL_LDS && d.has_two_sided != 0;
+  const bool do_n = EXT && d.has_two_sided != 0;
   // block report: spill (l~, l) and c of every token-head, the Tier B radius
   // of every INT8 block
   const bool do_r = EXT && !SPILL_LDS && d.has_report != 0;

@@ -39,8 +39,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeLaunch 
 // All reductions run in a fixed order (bitwise reproducible).  The grid fits
 // the device at once, so all members are resident; a bounded wait leaves NaN
 // in the group's results instead of hanging.
-constexpr int SLOT_WORDS = 544;    // 24 states (6 per head), 4 TV shares, 4 pad, 512 accumulator words
-constexpr int SLOT_TV = 24, SLOT_ACC = 32;
+// Slot of one member: per head SLOT_ST words (the six states M~, Z~, M, Z,
+// M_e, Z_e; then, with the meter extensions, z_v, max ||v||, M-, Z-, max c),
+// 4 TV shares, 512 accumulator words.
+constexpr int SLOT_ST = 11;
+constexpr int SLOT_TV = 4 * SLOT_ST, SLOT_ACC = SLOT_TV + 4;
+constexpr int SLOT_WORDS = SLOT_ACC + 512;
+static_assert(SLOT_WORDS * 8 == (int)TEAM_SLOT_BYTES, "team slot size");
 
 __device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -95,6 +100,9 @@ __device__ __forceinline__ float wave_sum_fixed(float x, int n) {
   return x;
 }
 
+// EXT: the value side and the two-sided form (with the tanh shape) ride on
+// the exchange: z_v merges like Z~, (M-, Z-) like (M, Z), the maxima by max.
+template <bool EXT>
 __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*part_s)[4][PART_STRIDE],
                               const float2 *spill_s, int team, int member, int round,
                               bool last_round, int b, int kvh, int c0, int c1) {
@@ -119,21 +127,37 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   __syncthreads();
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
-    if (k == 6 || k == 7 || k >= 8 + D) continue;   // states and accumulator only
-    const int mk = (k >= 8) ? 0 : (k & ~1);
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
-    float r;
-    if (k < 6 && (k & 1) == 0) {
-      r = M;
+    int word, mk;                                   // slot word; sum merged on field mk's maximum (-1: a maximum)
+    if (k < 6) {
+      word = SLOT_ST * h + k;
+      mk = (k & 1) ? k - 1 : -1;
+    } else if (k >= 8 && k < 8 + D) {
+      word = SLOT_ACC + 128 * h + (k - 8);
+      mk = 0;
+    } else if (EXT && k == 7) {
+      word = SLOT_ST * h + 6;
+      mk = 0;
+    } else if (EXT && k >= PART_VMAX && k <= PART_CMAX) {
+      word = SLOT_ST * h + 7 + (k - PART_VMAX);
+      mk = k == PART_ZN ? PART_MN : -1;
     } else {
+      continue;
+    }
+    float r;
+    if (mk < 0) {
+      r = part_s[0][h][k];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) r = fmaxf(r, part_s[w][h][k]);
+    } else {
+      float M = NEG_INF;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) M = fmaxf(M, part_s[w][h][mk]);
       r = 0.0f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) r += part_s[w][h][k] * merge_factor(part_s[w][h][mk], M);
     }
     if (member != d.silent_member)                 // (a test hook silences one member)
-      st_tagged(mine + (k < 6 ? 6 * h + k : SLOT_ACC + 128 * h + (k - 8)), tag, r);
+      st_tagged(mine + word, tag, r);
   }
 
   // 2. the group's normalizers: wavefront h reads head h of every member
@@ -142,12 +166,19 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   const int h = __builtin_amdgcn_readfirstlane(wv);   // uniform: scalar slot bases
   bool ok = true;
   float Mq = NEG_INF, Zq = 0.0f, Mm = NEG_INF, Zm = 0.0f, Me = NEG_INF, Ze = 0.0f;
+  float Zv = 0.0f, Vm = 0.0f, Mn = NEG_INF, Zn = 0.0f, Cm = 0.0f;
   if (lane < T) {
-    const uint64_t *s = slots + (size_t)lane * SLOT_WORDS + 6 * h;
-    const uint64_t *const p[6] = {s, s + 1, s + 2, s + 3, s + 4, s + 5};
-    float v[6];
-    ok = read_tagged<6>(p, tag, v, d.spin_limit);
+    constexpr int NS = EXT ? SLOT_ST : 6;
+    const uint64_t *s = slots + (size_t)lane * SLOT_WORDS + SLOT_ST * h;
+    const uint64_t *p[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) p[i] = s + i;
+    float v[NS];
+    ok = read_tagged<NS>(p, tag, v, d.spin_limit);
     Mq = v[0]; Zq = v[1]; Mm = v[2]; Zm = v[3]; Me = v[4]; Ze = v[5];
+    if constexpr (EXT) {
+      Zv = v[6]; Vm = v[7]; Mn = v[8]; Zn = v[9]; Cm = v[10];
+    }
   }
   // one member's words missing makes the whole group's states unknown: NaN
   // then flows into every result of the group (never a stale value)
@@ -155,6 +186,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   if (!ok) {
     const float qnan_s = __builtin_nanf("");
     Mq = Zq = Mm = Zm = Me = Ze = qnan_s;
+    Zv = Vm = Mn = Zn = Cm = qnan_s;
     if (lane == 0) bad_s = 1;
   }
   mq_s[h][lane] = Mq;
@@ -162,6 +194,15 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     const float a0 = __shfl_xor(Mq, off), a1 = __shfl_xor(Zq, off);
     const float b0 = __shfl_xor(Mm, off), b1 = __shfl_xor(Zm, off);
     const float e0 = __shfl_xor(Me, off), e1 = __shfl_xor(Ze, off);
+    if constexpr (EXT) {
+      const float v1 = __shfl_xor(Zv, off), vm = __shfl_xor(Vm, off);
+      const float n0 = __shfl_xor(Mn, off), n1 = __shfl_xor(Zn, off), cm = __shfl_xor(Cm, off);
+      const float mx = fmaxf(Mq, a0);                // z_v rides on the attention maximum
+      Zv = Zv * merge_factor(Mq, mx) + v1 * merge_factor(a0, mx);
+      Vm = fmaxf(Vm, vm);
+      mz_merge(Mn, Zn, n0, n1);
+      Cm = fmaxf(Cm, cm);
+    }
     mz_merge(Mq, Zq, a0, a1);
     mz_merge(Mm, Zm, b0, b1);
     mz_merge(Me, Ze, e0, e1);
@@ -296,6 +337,26 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (d.log_a) d.log_a[qh] = ok ? (float)log_a : qnan;
     if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
     if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
+    if constexpr (EXT) {                             // as the per-chunk finalize
+      if (d.has_two_sided) {
+        double log_am = 0.0;
+        if (Zq > 0.0f && Zn > 0.0f)
+          log_am = ((double)Mn - (double)Mq) * 0.69314718055994530942 + log((double)Zn) - log((double)Zq);
+        const double two = sinh(log_a - log_am);
+        const float tf = two > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)two;
+        if (d.log_a_minus) d.log_a_minus[qh] = ok ? (float)log_am : qnan;
+        if (d.bound_two_sided) d.bound_two_sided[qh] = ok ? tf : qnan;
+        if (d.meter_two_sided) d.meter_two_sided[qh] = ok ? fminf(fminf(1.0f, bf), tf) : qnan;
+        if (d.bound_tanh) d.bound_tanh[qh] = ok ? (float)tanh((double)Cm * 0.69314718055994530942) : qnan;
+      }
+      if (d.has_value) {
+        const float verr = Zq > 0.0f ? Zv / Zq : 0.0f;
+        const float tvb = do_meter ? fminf(1.0f, bf) : 0.0f;
+        if (d.value_err) d.value_err[qh] = ok ? verr : qnan;
+        if (d.v_norm_max) d.v_norm_max[qh] = ok ? Vm : qnan;
+        if (d.out_bound) d.out_bound[qh] = ok ? 2.0f * tvb * Vm + verr : qnan;
+      }
+    }
   }
   if (tv_duty && round > 0) {
     float sh = 0.0f;
@@ -335,7 +396,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   __syncthreads();                  // LDS buffers are reused by the next round
 }
 
-template <int KF, int VF, bool PAGED, bool FULL>
+template <int KF, int VF, bool PAGED, bool FULL, bool EXT>
 __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLaunch d) {
   extern __shared__ __attribute__((aligned(16))) float2 spill_s[];   // d.chunk * 4 entries
   __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
@@ -356,8 +417,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
     const int c1 = min(c0 + d.chunk, len);
     // (the next round's first tile is not loaded ahead: its loads would sit
     // ahead of the exchange's polls in the in-order load counter)
-    mfma_chunk<KF, VF, PAGED, FULL, true>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
-    team_epilogue(d, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh, c0, c1);
+    mfma_chunk<KF, VF, PAGED, FULL, true, EXT>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
+    team_epilogue<EXT>(d, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh, c0, c1);
   }
 }
 
@@ -390,41 +451,44 @@ static hipError_t launch_m(const DecodeLaunch &d, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KF, int VF, bool PAGED, bool FULL>
+template <int KF, int VF, bool PAGED, bool FULL, bool EXT>
 static const void *team_fn() {
-  return reinterpret_cast<const void *>(&decode_mfma_team_kernel<KF, VF, PAGED, FULL>);
+  return reinterpret_cast<const void *>(&decode_mfma_team_kernel<KF, VF, PAGED, FULL, EXT>);
 }
 
+// the meter extensions come with the full meter only (TV, meter, witness)
 template <int KF, int VF>
-static const void *team_fn_kv(bool paged, bool full) {
-  if (paged) return full ? team_fn<KF, VF, true, true>() : team_fn<KF, VF, true, false>();
-  return full ? team_fn<KF, VF, false, true>() : team_fn<KF, VF, false, false>();
+static const void *team_fn_kv(bool paged, bool full, bool ext) {
+  if (ext) return paged ? team_fn<KF, VF, true, true, true>() : team_fn<KF, VF, false, true, true>();
+  if (paged) return full ? team_fn<KF, VF, true, true, false>() : team_fn<KF, VF, true, false, false>();
+  return full ? team_fn<KF, VF, false, true, false>() : team_fn<KF, VF, false, false, false>();
 }
 
-static const void *team_kernel(int k_format, int v_format, bool paged, bool full) {
+static const void *team_kernel(int k_format, int v_format, bool paged, bool full, bool ext) {
   if (k_format == KVQ_FMT_FP8_E4M3) {
-    if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_FP8_E4M3>(paged, full);
-    if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16>(paged, full);
-    return team_fn_kv<KVQ_FMT_FP8_E4M3, VF_NONE>(paged, full);
+    if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_FP8_E4M3>(paged, full, ext);
+    if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16>(paged, full, ext);
+    return team_fn_kv<KVQ_FMT_FP8_E4M3, VF_NONE>(paged, full, ext);
   }
-  if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_FP8_E4M3>(paged, full);
-  if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_BF16>(paged, full);
-  return team_fn_kv<KVQ_FMT_BF16, VF_NONE>(paged, full);
+  if (v_format == KVQ_FMT_FP8_E4M3) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_FP8_E4M3>(paged, full, ext);
+  if (v_format == KVQ_FMT_BF16) return team_fn_kv<KVQ_FMT_BF16, KVQ_FMT_BF16>(paged, full, ext);
+  return team_fn_kv<KVQ_FMT_BF16, VF_NONE>(paged, full, ext);
 }
 
-int team_capacity(int k_format, int v_format, bool paged, bool full) {
+int team_capacity(int k_format, int v_format, bool paged, bool full, bool ext) {
   // resident work-groups of the team kernel with the largest LDS chunk;
   // cached per device and kernel instance, 0 when the device cannot tell
-  static int cache[16][2][3][2][2];
+  if (ext && !full) return 0;
+  static int cache[16][2][3][2][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
   const int ki = k_format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
   const int vi = v_format == KVQ_FMT_FP8_E4M3 ? 1 : (v_format == KVQ_FMT_BF16 ? 2 : 0);
-  int &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0];
+  int &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0][ext ? 1 : 0];
   if (c > 0) return c;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, team_kernel(k_format, v_format, paged, full),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, team_kernel(k_format, v_format, paged, full, ext),
                                                    256, (size_t)TEAM_MAX_CHUNK * 4 * sizeof(float2)) != hipSuccess)
     return 0;
   c = per_cu * cus;
@@ -433,7 +497,9 @@ int team_capacity(int k_format, int v_format, bool paged, bool full) {
 
 hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream) {
   const bool full = d.has_tv && d.has_meter && d.region.exact_fmt == EX_BF16 && d.region.witness;
-  const void *fn = team_kernel(d.k_format, d.v_format, d.region.paged != 0, full);
+  const bool ext = d.has_value || d.has_two_sided;   // (Tier B and the report never plan a team)
+  if (ext && !full) return hipErrorInvalidValue;
+  const void *fn = team_kernel(d.k_format, d.v_format, d.region.paged != 0, full, ext);
   DecodeLaunch arg = d;
   void *args[] = {&arg};
   // A plain launch: members wait only for members of their own team, and a

@@ -119,10 +119,10 @@ hipError_t launch_decode_two(const DecodeLaunch &d1, const DecodeLaunch &d2, hip
 // members; TEAM_SLOT_BYTES of workspace per member and round parity.
 constexpr int TEAM_MAX_CHUNK = 2048;
 constexpr int TEAM_MAX = 64;
-constexpr size_t TEAM_SLOT_BYTES = 544 * 8;
+constexpr size_t TEAM_SLOT_BYTES = 560 * 8;
 // Resident work-groups of the team kernel on the current device (0: no team
 // launch possible).
-int team_capacity(int k_format, int v_format, bool paged, bool full);
+int team_capacity(int k_format, int v_format, bool paged, bool full, bool ext);
 hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream);
 
 }  // namespace kvq
