@@ -112,6 +112,9 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   const int T = d.team;
   const bool do_tv = d.has_tv != 0;
   const bool do_meter = d.has_meter != 0;
+  // the exchange is the round's critical path: its waves issue ahead of the
+  // co-resident work-group's streaming waves (wave priority only)
+  __builtin_amdgcn_s_setprio(1);
   const uint32_t tag = d.epoch + (uint32_t)round + 1u;
   uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(team * 2 + (round & 1)) * T * SLOT_WORDS;
   uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
@@ -394,6 +397,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
     if (lane == 0) d.tv[qh] = okp ? 0.5f * sh : qnan;
   }
   __syncthreads();                  // LDS buffers are reused by the next round
+  __builtin_amdgcn_s_setprio(0);
 }
 
 template <int KF, int VF, bool PAGED, bool FULL, bool EXT>
