@@ -296,11 +296,12 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    one work-group each, in one launch (cartridge page: one kernel spans the
  *    shared cartridge and the live suffix) when both regions have keys of one
  *    format and, with FP8 keys, values of one format; else one launch per
- *    region.  The TV's logit pairs go through the workspace.  Calls on a
- *    stream under graph capture always run this way (a team launch's tags
- *    are chosen per call on the host, which a replay would repeat).
+ *    region.  The TV's logit pairs go through the workspace.
+ * Both plans may be captured into a HIP graph: a team launch takes its tags
+ * from an epoch kept in the workspace, which the launch's last work-group
+ * moves past every tag it used, so each replay waits for fresh tags.
  * workspace_bytes is what this plan needs; kvq_workspace_bytes may return
- * more (it also covers the capture case). */
+ * more (it covers the per-chunk plan of the same arguments too). */
 typedef struct kvq_plan_info {
   int32_t team;             /* work-groups per (request, KV head); 0: no team launch */
   int32_t n_teams;
@@ -318,13 +319,15 @@ kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter
 
 /* Prepare a workspace for first use: clears all of it (one fill kernel on
  * `stream`).  A workspace stays ready after every successful kvq_decode_attn /
- * kvq_meter call: the per-chunk plan's arrival counters (in the first MiB)
- * are reset by the last work-group of each (request, KV head), and team
- * launches tag their exchange words with a per-call epoch instead of
+ * kvq_meter call: the per-chunk plan's arrival counters (after the first 256
+ * bytes) are reset by the last work-group of each (request, KV head); team
+ * launches tag their exchange words with an epoch kept in the first 256
+ * bytes, which each launch advances past its tags on the device, instead of
  * clearing them.  Calls of other shapes may share the workspace; clearing it
  * again when the shape changes also removes the small chance (2^-32 per
- * word) that a word left by another plan carries the tag a team launch
- * waits for.  Calls that share a workspace must not overlap in time. */
+ * word) that a word left by the other plan's partial results carries the
+ * tag a team launch waits for.  Calls that share a workspace must not
+ * overlap in time. */
 kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, kvq_stream stream);
 
 /* Decode attention with the fused meter (WitCert Sec. 6 meter loop, read path;

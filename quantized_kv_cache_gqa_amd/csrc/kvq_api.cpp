@@ -7,11 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <time.h>
-#include <unistd.h>
-
 #include <algorithm>
-#include <atomic>
 
 #include "kvq_internal.h"
 
@@ -20,10 +16,13 @@ namespace {
 using namespace kvq;
 
 constexpr size_t kAlign = 256;
-// The per-chunk plan's arrival counters (one per (request, KV head), at most
-// 2^18) sit in the workspace's first MiB, which must read zero at rest; the
-// team plan's slots start after it, so neither plan's words land on the
-// other's counters when calls of different shapes share a workspace.
+// Workspace layout: the team launch's control words (epoch, finished count)
+// in the first 256 bytes, which no plan uses otherwise; then the per-chunk
+// plan's arrival counters (one per (request, KV head), at most 2^18, zero at
+// rest); the team plan's slots start after the counters' MiB, so neither
+// plan's words land on the other's counters or on the control words when
+// calls of different shapes share a workspace.
+constexpr size_t kCtlBytes = 256;
 constexpr size_t kCounterBytes = (size_t)1 << 20;
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -46,18 +45,6 @@ struct Plan {
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, off_rspill = 0, off_ublk = 0, bytes = 0;
 };
-
-// Tags of a team launch: epoch + 1 .. epoch + rounds, never 0 (the value of
-// cleared workspace) and never reused by another launch of this process
-// (the first epoch depends on the process and the clock, so a workspace left
-// by another process is unlikely to hold a matching tag).
-uint32_t next_epoch(uint32_t rounds) {
-  static std::atomic<uint32_t> next{(uint32_t)(time(nullptr) * 2654435761u) ^ ((uint32_t)getpid() << 16)};
-  for (;;) {
-    const uint32_t e = next.fetch_add(rounds + 1u);
-    if ((uint64_t)e + rounds < ((uint64_t)1 << 32)) return e;   // e + 1 .. e + rounds do not wrap to 0
-  }
-}
 
 // decimal value of an environment variable in [lo, 2^32), else dflt
 unsigned env_uint(const char *name, unsigned dflt, unsigned long lo) {
@@ -128,8 +115,8 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   p.suf_chunks = p.suffix_cap > 0 ? p.team : 0;
   p.total_chunks = p.team;
   p.rounds = (groups + p.n_teams - 1) / p.n_teams;
-  p.off_counters = 0;
-  p.off_partials = kCounterBytes;
+  p.off_counters = kCtlBytes;
+  p.off_partials = kCtlBytes + kCounterBytes;
   p.off_spill = p.off_partials + round_up((size_t)p.n_teams * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
   p.bytes = p.off_spill;
   return true;
@@ -276,8 +263,8 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     }
   }
   if (allow_team && plan_team(a, meter_only, groups, p)) return KVQ_OK;
-  p.off_counters = 0;
-  p.off_partials = round_up((size_t)groups * sizeof(uint32_t), kAlign);
+  p.off_counters = kCtlBytes;
+  p.off_partials = round_up(kCtlBytes + (size_t)groups * sizeof(uint32_t), kAlign);
   p.off_spill = p.off_partials +
                 round_up((size_t)groups * p.total_chunks * p.group * PART_STRIDE * sizeof(float), kAlign);
   p.bytes = p.off_spill;
@@ -318,14 +305,6 @@ RegionDev region_dev(const kvq_region &r, bool is_prefix) {
   d.opairs = d.n_op ? r.outlier_pairs : nullptr;
   d.kout = d.n_op ? r.k_outliers : nullptr;
   return d;
-}
-
-// A stream being captured into a graph gets the per-chunk plan: a team
-// launch's tags are chosen on the host per call, and a replayed graph would
-// repeat them.  A failed query counts as capturing.
-bool stream_capturing(hipStream_t stream) {
-  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-  return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
 }
 
 // The per-chunk plan's launch arguments: the fields every launch shares, and
@@ -412,7 +391,7 @@ int chunk_launch_count(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch
 kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
                       hipStream_t stream, bool meter_only) {
   Plan p;
-  kvq_status s = make_plan(a, m, meter_only, p, !stream_capturing(stream));
+  kvq_status s = make_plan(a, m, meter_only, p);
   if (s != KVQ_OK) return s;
   if (!ws) return KVQ_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVQ_ERR_ALIGN;
@@ -430,7 +409,7 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     d.chunk_base = 0;
     d.team = p.team;
     d.n_teams = p.n_teams;
-    d.epoch = next_epoch((uint32_t)p.rounds);
+    d.team_ctl = reinterpret_cast<uint32_t *>(ws);
     // Bounded waits of the team exchange.  Two test hooks, read from the
     // environment: KVQ_TEAM_SPIN_LIMIT (polls per batch of words, default
     // 2^18) and KVQ_TEAM_SILENT_MEMBER (that member of every team never
@@ -521,8 +500,8 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
 }
 
 size_t kvq_workspace_bytes(const kvq_attn_args *a, const kvq_meter_out *m) {
-  // the size does not depend on out/v; it covers the per-chunk plan too,
-  // which a call under stream capture uses
+  // the size does not depend on out/v; it also covers the per-chunk plan of
+  // the same arguments, so one workspace serves both whichever is taken
   Plan p, q;
   if (make_plan(a, m, true, p) != KVQ_OK) return 0;
   if (p.team && make_plan(a, m, true, q, false) == KVQ_OK) return std::max(p.bytes, q.bytes);

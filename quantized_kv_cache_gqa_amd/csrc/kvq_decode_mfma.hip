@@ -103,7 +103,7 @@ __device__ __forceinline__ float wave_sum_fixed(float x, int n) {
 // EXT: the value side and the two-sided form (with the tanh shape) ride on
 // the exchange: z_v merges like Z~, (M-, Z-) like (M, Z), the maxima by max.
 template <bool EXT>
-__device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*part_s)[4][PART_STRIDE],
+__device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t epoch, float (*part_s)[4][PART_STRIDE],
                               const float2 *spill_s, int team, int member, int round,
                               bool last_round, int b, int kvh, int c0, int c1) {
   constexpr int G = 4;
@@ -115,7 +115,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, float (*par
   // the exchange is the round's critical path: its waves issue ahead of the
   // co-resident work-group's streaming waves (wave priority only)
   __builtin_amdgcn_s_setprio(1);
-  const uint32_t tag = d.epoch + (uint32_t)round + 1u;
+  const uint32_t tag = epoch + (uint32_t)round + 1u;
   uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(team * 2 + (round & 1)) * T * SLOT_WORDS;
   uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
   __shared__ float mq_s[G][64];
@@ -409,10 +409,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
   const unsigned per_xcd = gridDim.x >> 3;
   const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
   const int team = (int)(L / (unsigned)T), member = (int)(L % (unsigned)T);
-  if (team >= d.n_teams) return;                     // grid padding: member of no team
   const int groups = d.batch * d.h_kv;
   const RegionDev &R = d.region;
-  for (int round = 0;; ++round) {
+  // this launch's epoch, kept in the workspace: round r's tag is epoch + r + 1
+  __shared__ uint32_t epoch_s;
+  if (threadIdx.x == 0) epoch_s = __hip_atomic_load(d.team_ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t epoch = epoch_s;
+  for (int round = 0; team < d.n_teams; ++round) {  // (grid padding: member of no team)
     const int grp = team + round * d.n_teams;
     if (grp >= groups) break;
     const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
@@ -422,7 +426,22 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
     // (the next round's first tile is not loaded ahead: its loads would sit
     // ahead of the exchange's polls in the in-order load counter)
     mfma_chunk<KF, VF, PAGED, FULL, true, EXT>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
-    team_epilogue<EXT>(d, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh, c0, c1);
+    team_epilogue<EXT>(d, epoch, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh,
+                       c0, c1);
+  }
+  // Every work-group counts itself out after reading the epoch; the last one
+  // moves the epoch past all of this launch's tags and rearms the count, so
+  // the next launch on this workspace (a graph replay included) waits for
+  // tags no earlier launch wrote.
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(d.team_ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1) {
+      const uint32_t rounds = (uint32_t)((groups + d.n_teams - 1) / d.n_teams);
+      uint32_t next = epoch + rounds + 1u;
+      if (next > 0xF0000000u) next = 0u;             // tags stay in [1, 2^32)
+      __hip_atomic_store(d.team_ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(d.team_ctl, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

@@ -89,7 +89,8 @@ struct DecodeLaunch {
   float *spill;
   int team;                     // > 0: team launch, work-groups per (request, KV head)
   int n_teams;                  // teams in the grid
-  uint32_t epoch;               // team launch: tag of round r is epoch + r + 1
+  uint32_t *team_ctl;           // team launch: [0] epoch (round r's tag is epoch + r + 1),
+                                // [1] work-groups finished (0 at rest)
   unsigned spin_limit;          // team launch: polls per batch of words before giving up
   int silent_member;            // team launch: member that never publishes (test hook; -1: none)
 };

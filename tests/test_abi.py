@@ -104,7 +104,7 @@ def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
     groups, chunks, G = 64 * 8, 1, 4        # 512 groups fill the GPU: one chunk each
-    counters = 2048
+    counters = 256 + 2048                   # team control words, then one counter per group
     partials = groups * chunks * G * 144 * 4
     spill = groups * 12640 * G * 8                # 12628 tokens padded to 16-token tiles
     assert n == counters + partials + spill
@@ -117,8 +117,8 @@ def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
 
 def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
     """kvq_decode_plan reports one size for the decode and the meter call;
-    kvq_workspace_bytes covers it and the per-chunk plan (taken under graph
-    capture); without a device there is no team plan and the sizes agree."""
+    kvq_workspace_bytes covers it and the per-chunk plan of the same
+    arguments; without a device there is no team plan and the sizes agree."""
     a = _args()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
@@ -128,7 +128,7 @@ def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
     assert _plan(lib, a, m, 0).workspace_bytes <= n
     monkeypatch.delenv("KVQ_DECODE_TEAM")
     if d.team:
-        assert d.workspace_bytes >= (1 << 20)          # slots after the counters' MiB
+        assert d.workspace_bytes >= 256 + (1 << 20)    # slots after the control words and counters
     else:
         assert d.workspace_bytes == n
     if not torch.cuda.is_available():

@@ -286,12 +286,12 @@ def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
     _all_cells(case, value_bound=True, two_sided=True)
 
 
-def test_graph_capture_takes_the_per_chunk_plan(gpu_lib, monkeypatch):
-    """A call captured into a graph runs the per-chunk plan (a team launch's
-    tags are chosen per call on the host, and a replay would repeat them).
-    Every replay equals the eager per-chunk result bit for bit, with eager
-    team calls on the same workspace between the replays, which in turn keep
-    equal to the first eager team call."""
+def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch):
+    """A call captured into a graph keeps the team plan: the launch takes its
+    tags from the epoch in the workspace, which every launch advances on the
+    device.  Every replay equals the eager team result bit for bit, with
+    eager team calls on the same workspace between the replays; a
+    per-chunk call on that workspace between them changes nothing either."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     from quantized_kv_cache_gqa_amd import kvq
     cfg = small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
@@ -313,20 +313,31 @@ def test_graph_capture_takes_the_per_chunk_plan(gpu_lib, monkeypatch):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         call(out=og, meter_bufs=mg)
-    for _ in range(3):
+    for it in range(4):
         og.fill_(float("nan"))
         for v in mg.values():
             v.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(og, o_chunk)
-        for k in m_chunk:
-            assert torch.equal(mg[k], m_chunk[k]), k
+        assert torch.equal(og, o_team)
+        for k in m_team:
+            assert torch.equal(mg[k], m_team[k]), k
+        g.replay()                                  # twice in a row: fresh tags again
+        torch.cuda.synchronize()
+        assert torch.equal(og, o_team)
         o2, m2 = call()
         torch.cuda.synchronize()
         assert torch.equal(o2, o_team)
         for k in m_team:
             assert torch.equal(m2[k], m_team[k]), k
+        if it == 1:                                 # the per-chunk plan on the same workspace
+            monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+            o3, m3 = call()
+            monkeypatch.delenv("KVQ_DECODE_TEAM")
+            torch.cuda.synchronize()
+            assert torch.equal(o3, o_chunk)
+            for k in m_chunk:
+                assert torch.equal(m3[k], m_chunk[k]), k
 
 
 def _two_region_fp8(paged):
