@@ -148,8 +148,8 @@ def _oracle_slice(lb):
     import torch
     torch.set_num_threads(1)
     from oracle.pipeline import RegionSpec, decode_cell, encode_region
-    from workloads import CONFIGS, gen_layer
-    cfg = CONFIGS[3]
+    from workloads import QWEN3_B64_S12628_K8V8, gen_layer
+    cfg = QWEN3_B64_S12628_K8V8
     layer, b = lb
     inp = gen_layer(cfg, layer, "cpu", requests=[b])           # input synthesis, not timed
     q = inp["q"][0].double().numpy()
@@ -361,9 +361,9 @@ def main():
     import numpy as np
     import torch
     from quantized_kv_cache_gqa_amd import kvq
-    from workloads import CONFIGS, gen_layer
+    from workloads import QWEN3_B64_S12628_K8V8, gen_layer
 
-    cfg = CONFIGS[3]
+    cfg = QWEN3_B64_S12628_K8V8
     L = args.layers or cfg.layers
     B, HQ, HKV, S, D = cfg.batch, cfg.h_q, cfg.h_kv, cfg.suffix.length, 128
     dev = torch.device("cuda:0")

@@ -13,7 +13,8 @@ import torch
 
 from cells import GpuCase, SM_SCALE, check_block_report, check_results, check_stored, oracle_cell, plan
 from oracle.numerics import e4m3_table
-from workloads import CONFIGS, small_variant
+from workloads import (CONFIGS, INT8_DITHER_B8_S32K, LONG_B4_S128K_SPLIT, QWEN3_B64_S12628_K8V8,
+                       QWEN3_SHARED_CARTRIDGE_PAGED, TINY_K16V8_CARTRIDGE, small_variant)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,11 +106,11 @@ def test_write_path_edge_values_bit_exact(gpu_lib):
 
 
 SMALL = {
-    "cfg1": lambda: CONFIGS[1],
-    "cfg2": lambda: small_variant(CONFIGS[2], batch=3, h_kv=2, lens=(1024, 1000, 17)),
-    "cfg3": lambda: small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1234)),
-    "cfg4": lambda: small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=1000, lens=(1000, 513)),
-    "cfg5": lambda: small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=5000, lens=(5000, 4097)),
+    "tiny-cartridge": lambda: TINY_K16V8_CARTRIDGE,
+    "shared-cartridge-paged": lambda: small_variant(QWEN3_SHARED_CARTRIDGE_PAGED, batch=3, h_kv=2, lens=(1024, 1000, 17)),
+    "fp8-b64": lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1234)),
+    "int8-dither": lambda: small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=1000, lens=(1000, 513)),
+    "long-split": lambda: small_variant(LONG_B4_S128K_SPLIT, batch=2, h_kv=2, suffix_len=5000, lens=(5000, 4097)),
 }
 
 
@@ -138,7 +139,7 @@ def test_small_config_parity_all_cells(gpu_lib, kernel, name):
 
 def test_cfg1_fp32_exact_cache_meter_nonzero(gpu_lib):
     """BF16 storage of fp32 keys as the quantizer: nonzero TV and witness bound."""
-    case = GpuCase(CONFIGS[1], fp32_exact=True)
+    case = GpuCase(TINY_K16V8_CARTRIDGE, fp32_exact=True)
     out, m, worst = _all_cells(case)
     assert float(m["tv"].max()) > 0 and float(m["bound_raw"].min()) > 0
     assert torch.all(m["tv"] <= m["bound_raw"])
@@ -146,27 +147,27 @@ def test_cfg1_fp32_exact_cache_meter_nonzero(gpu_lib):
 
 @pytest.mark.parametrize("split", [64, 256, 1024])
 def test_split_size_does_not_change_results(gpu_lib, kernel, split):
-    cfg = small_variant(CONFIGS[3], batch=2, h_kv=1, suffix_len=2500, lens=(2500, 70))
+    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=1, suffix_len=2500, lens=(2500, 70))
     case = GpuCase(cfg)
     _all_cells(case, split_tokens=split)
 
 
 def test_group_sizes_and_tiny_lengths(gpu_lib):
     for hq, lens in ((8, (1, 2)), (16, (63, 65)), (64, (129, 1))):
-        cfg = dataclasses.replace(small_variant(CONFIGS[3], batch=2, h_kv=8, suffix_len=130, lens=lens),
+        cfg = dataclasses.replace(small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=8, suffix_len=130, lens=lens),
                                   h_q=hq)
         case = GpuCase(cfg)
         _all_cells(case, cells=[(0, 0), (1, 7), (1, 3)])
 
 
 def test_prefix_only_request_and_empty_suffix(gpu_lib, kernel):
-    cfg = small_variant(CONFIGS[2], batch=2, h_kv=1, lens=(0, 16))
+    cfg = small_variant(QWEN3_SHARED_CARTRIDGE_PAGED, batch=2, h_kv=1, lens=(0, 16))
     case = GpuCase(cfg, page_seed=9)
     _all_cells(case)
 
 
 def test_meter_only_matches_decode(gpu_lib, kernel):
-    cfg = small_variant(CONFIGS[5], batch=1, h_kv=2, suffix_len=3000)
+    cfg = small_variant(LONG_B4_S128K_SPLIT, batch=1, h_kv=2, suffix_len=3000)
     case = GpuCase(cfg)
     _, m1 = case.run(split_tokens=1024)
     _, m2 = case.run(split_tokens=1024, meter_only=True)
@@ -223,7 +224,7 @@ def test_team_many_members_and_empty_chunks(gpu_lib, monkeypatch):
     with empty chunks; parity on every cell and agreement with the
     spill-to-workspace path."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    cfg = small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=5000, lens=(5000, 1500))
+    cfg = small_variant(LONG_B4_S128K_SPLIT, batch=2, h_kv=2, suffix_len=5000, lens=(5000, 1500))
     case = GpuCase(cfg)
     p = _team_plan(case, monkeypatch)
     assert p["team"] >= 16 and p["chunk"] * (p["team"] - 1) >= 1500, p   # members with no tokens
@@ -244,7 +245,7 @@ def test_team_several_rounds_sampled_cells(gpu_lib, monkeypatch):
     parity reuse); sampled cells against the oracle, bitwise repeatable."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     lens = tuple(3000 - 37 * i for i in range(80))
-    cfg = small_variant(CONFIGS[3], batch=80, h_kv=8, suffix_len=3000, lens=lens)
+    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=80, h_kv=8, suffix_len=3000, lens=lens)
     case = GpuCase(cfg)
     p = _team_plan(case, monkeypatch)
     assert p["rounds"] >= 3, p
@@ -262,7 +263,7 @@ def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
     result of the affected groups is NaN (never a stale or partial value),
     and the next call without the hooks is correct again."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    cfg = small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
     case = GpuCase(cfg, value_witness=True)
     p = _team_plan(case, monkeypatch)
     assert p["team"] >= 2, p
@@ -294,7 +295,7 @@ def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch):
     per-chunk call on that workspace between them changes nothing either."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     from quantized_kv_cache_gqa_amd import kvq
-    cfg = small_variant(CONFIGS[3], batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
     case = GpuCase(cfg)
     _team_plan(case, monkeypatch)
     ws = kvq.Workspace(torch.device("cuda"))
@@ -344,15 +345,15 @@ def _two_region_fp8(paged):
     """A shared FP8 cartridge (exact keys, witness) before an FP8 suffix, both
     with the TV and the meter: the one-launch form with the full meter."""
     from workloads.configs import RegionCfg
-    base = small_variant(CONFIGS[5], batch=2, h_kv=2, suffix_len=1504, lens=(1504, 700))
+    base = small_variant(LONG_B4_S128K_SPLIT, batch=2, h_kv=2, suffix_len=1504, lens=(1504, 700))
     suf = dataclasses.replace(base.suffix, paged=paged, page_size=16)
     pre = RegionCfg(length=700, k_fmt="fp8", v_fmt="fp8", exact_k=True, witness=True)
     return dataclasses.replace(base, prefix=pre, suffix=suf, name=base.name + "-cartridge")
 
 
 TWO_REGION = {
-    "cfg1": lambda: CONFIGS[1],
-    "cfg2": SMALL["cfg2"],
+    "tiny-cartridge": lambda: TINY_K16V8_CARTRIDGE,
+    "shared-cartridge-paged": SMALL["shared-cartridge-paged"],
     "fp8": lambda: _two_region_fp8(False),
     "fp8-paged": lambda: _two_region_fp8(True),
 }
@@ -387,15 +388,15 @@ def _tier_b_two_region():
     """A BF16 shared prefix (radius 0) before a dithered INT8 suffix: two
     launches, one per key format, both accumulating E_p~[e^u]."""
     from workloads.configs import RegionCfg
-    base = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=700, lens=(700, 300))
+    base = small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=700, lens=(700, 300))
     pre = RegionCfg(length=300, k_fmt="bf16", v_fmt="bf16", exact_k=False, witness=False)
     return dataclasses.replace(base, prefix=pre, name=base.name + "-bf16-cartridge")
 
 
 TIER_B = {
-    "cfg4": SMALL["cfg4"],
-    "cfg4-long": lambda: small_variant(CONFIGS[4], batch=1, h_kv=2, suffix_len=3000, lens=(2900,)),
-    "cfg2-bf16": SMALL["cfg2"],
+    "int8-dither": SMALL["int8-dither"],
+    "int8-dither-long": lambda: small_variant(INT8_DITHER_B8_S32K, batch=1, h_kv=2, suffix_len=3000, lens=(2900,)),
+    "shared-cartridge-paged-bf16": SMALL["shared-cartridge-paged"],
     "bf16-int8": _tier_b_two_region,
 }
 
@@ -410,7 +411,7 @@ def test_tier_b_certificate_every_cell(gpu_lib, kernel, name, delta):
     cfg = TIER_B[name]()
     case = GpuCase(cfg, page_seed=2)
     assert plan(case, tier_b_delta=delta)["team"] == 0
-    split = 256 if name == "cfg4-long" else 0
+    split = 256 if name == "int8-dither-long" else 0
     out, m, worst = _all_cells(case, split_tokens=split, tier_b_delta=delta)
     assert "bound_b" in worst
     if cfg.suffix.k_fmt == "bf16" and (cfg.prefix is None or cfg.prefix.k_fmt == "bf16"):
@@ -425,10 +426,10 @@ def test_tier_b_certificate_every_cell(gpu_lib, kernel, name, delta):
 
 
 VALUE = {
-    "cfg2": SMALL["cfg2"],
-    "cfg3": SMALL["cfg3"],
-    "cfg4": SMALL["cfg4"],
-    "cfg5": SMALL["cfg5"],
+    "shared-cartridge-paged": SMALL["shared-cartridge-paged"],
+    "fp8-b64": SMALL["fp8-b64"],
+    "int8-dither": SMALL["int8-dither"],
+    "long-split": SMALL["long-split"],
     "fp8-paged-cartridge": lambda: _two_region_fp8(True),
 }
 
@@ -443,7 +444,7 @@ def test_value_side_and_joint_output_bound_every_cell(gpu_lib, kernel, monkeypat
     case = GpuCase(cfg, page_seed=4, value_witness=True)
     pv = plan(case, value_bound=True)
     assert pv["team"] == plan(case)["team"]
-    if kernel == "auto" and name in ("cfg3", "cfg5"):
+    if kernel == "auto" and name in ("fp8-b64", "long-split"):
         assert pv["team"] > 0
     out, m, worst = _all_cells(case, value_bound=True)
     assert "value_err" in worst
@@ -460,10 +461,10 @@ def test_value_side_and_joint_output_bound_every_cell(gpu_lib, kernel, monkeypat
 
 
 TWO_SIDED = {
-    "cfg2": SMALL["cfg2"],
-    "cfg3": SMALL["cfg3"],
-    "cfg4": SMALL["cfg4"],
-    "cfg5": SMALL["cfg5"],
+    "shared-cartridge-paged": SMALL["shared-cartridge-paged"],
+    "fp8-b64": SMALL["fp8-b64"],
+    "int8-dither": SMALL["int8-dither"],
+    "long-split": SMALL["long-split"],
     "fp8-cartridge": lambda: _two_region_fp8(False),
 }
 
@@ -478,7 +479,7 @@ def test_two_sided_form_every_cell(gpu_lib, kernel, monkeypatch, name):
     case = GpuCase(cfg, page_seed=6)
     pt = plan(case, two_sided=True)
     assert pt["team"] == plan(case)["team"]
-    if kernel == "auto" and name in ("cfg3", "cfg5"):
+    if kernel == "auto" and name in ("fp8-b64", "long-split"):
         assert pt["team"] > 0
     out, m, worst = _all_cells(case, two_sided=True)
     assert "two_sided" in worst
@@ -493,9 +494,9 @@ def test_two_sided_form_every_cell(gpu_lib, kernel, monkeypatch, name):
 
 
 REPORT = {
-    "cfg2": (SMALL["cfg2"], True),
-    "cfg4": (SMALL["cfg4"], True),
-    "cfg5": (SMALL["cfg5"], False),
+    "shared-cartridge-paged": (SMALL["shared-cartridge-paged"], True),
+    "int8-dither": (SMALL["int8-dither"], True),
+    "long-split": (SMALL["long-split"], False),
     "bf16-int8": (_tier_b_two_region, True),
 }
 
@@ -536,7 +537,7 @@ def _g32(paged=False, cartridge=False):
     6.2.3, Table 4), dense or in shuffled 16-token pages, with an INT8-G32
     shared prefix when asked."""
     from workloads.configs import RegionCfg
-    base = small_variant(CONFIGS[4], batch=2, h_kv=2, suffix_len=1024, lens=(1024, 513))
+    base = small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=1024, lens=(1024, 513))
     suf = dataclasses.replace(base.suffix, k_fmt="int8g32", v_fmt="int8g32", paged=paged, page_size=16)
     pre = RegionCfg(length=300, k_fmt="int8g32", v_fmt="int8g32", exact_k=True, witness=True) \
         if cartridge else None

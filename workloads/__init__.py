@@ -6,5 +6,6 @@ the method's arithmetic (no quantization, witness, attention or meter) and
 imports neither the oracle nor the HIP library; both sides receive the same
 tensors from here.
 """
-from .configs import CONFIGS, Config, RegionCfg, small_variant  # noqa: F401
+from .configs import (CONFIGS, INT8_DITHER_B8_S32K, LONG_B4_S128K_SPLIT, QWEN3_B64_S12628_K8V8,  # noqa: F401
+                      QWEN3_SHARED_CARTRIDGE_PAGED, TINY_K16V8_CARTRIDGE, Config, RegionCfg, small_variant)
 from .gen import gen_layer, outlier_channels  # noqa: F401

@@ -97,6 +97,14 @@ CONFIGS = {
 }
 
 
+# the workloads by name (CONFIGS is keyed by workload number)
+TINY_K16V8_CARTRIDGE = CONFIGS[1]
+QWEN3_SHARED_CARTRIDGE_PAGED = CONFIGS[2]
+QWEN3_B64_S12628_K8V8 = CONFIGS[3]
+INT8_DITHER_B8_S32K = CONFIGS[4]
+LONG_B4_S128K_SPLIT = CONFIGS[5]
+
+
 def small_variant(cfg: Config, *, batch: int = 2, layers: int = 1, prefix_len: Optional[int] = None,
                   suffix_len: Optional[int] = None, lens: Optional[tuple] = None,
                   h_kv: Optional[int] = None, **kw) -> Config:
