@@ -349,8 +349,8 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the design doc describes how the step would shard)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(one GPU holds a whole layer's cache; sharding is by request or KV head)", file=sys.stderr)
         sys.exit(2)
     if args.outlier_pairs and args.int8_scales != "group":
         sys.exit("--outlier-pairs needs --int8-scales group (the pairs sit beside group-scale keys)")
