@@ -172,15 +172,24 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
     const float *rp = rspill_region<G>(d, grp, region == 0);
     for (int j = wv; j < nb; j += WAVES) {         // uniform over the wavefront
       float ms = 0.0f, ex = 0.0f;
-#pragma unroll 4
+      // all of the block's loads first (one work-group streams the whole
+      // group's spill: its loads in flight set the time)
+      float lt[4 * G], cr[4 * G];
+#pragma unroll
+      for (int i = 0; i < 4 * G; ++i) {
+        const int e = min(KVQ_INT8_BLOCK * G * j + lane + 64 * i, round16(cap) * G - 1);   // within the region's rows
+        lt[i] = rd(sp + 2 * (size_t)e);
+        cr[i] = rd(rp + e);
+      }
+#pragma unroll
       for (int i = 0; i < 4 * G; ++i) {
         const int e = KVQ_INT8_BLOCK * G * j + lane + 64 * i;
         const int tile = e / (16 * G), r = e % (16 * G);
         const int t = 16 * tile + 4 * (r / (4 * G)) + (r & 3);
         if (t < n) {
-          const float pt = fast_exp2(rd(sp + 2 * (size_t)e) - Mt) * iZt;
+          const float pt = fast_exp2(lt[i] - Mt) * iZt;
           ms += pt;
-          ex += pt * expm1f(rd(rp + e) * LN2);
+          ex += pt * expm1f(cr[i] * LN2);
         }
       }
       for (int off = 1; off < 64; off <<= 1) {
@@ -376,6 +385,9 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
   if (d.tv) {
     // Thread tid reads entries 2 tid + 512 k (a float4: two entries of one
     // head); 512 is a multiple of 4G, so the head of its entries never changes.
+    // TV_U float4 per thread are in flight at once: one work-group streams the
+    // whole group's spill here, so its memory-level parallelism sets the time.
+    constexpr int TV_U = 16;
     __shared__ float tvpart_s[256];
     const int hmine = ((2 * tid) % (4 * G)) / 4;
     float acc_tv = 0.0f;
@@ -388,10 +400,10 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         if (n == 0) continue;
         const float *sp = spill_region<G>(d, grp, region == 0);
         const int n_entries = round16(n) * G;
-        for (int e0 = 2 * tid; e0 < n_entries; e0 += 4 * 512) {
-          float4 x[4];
+        for (int e0 = 2 * tid; e0 < n_entries; e0 += TV_U * 512) {
+          float4 x[TV_U];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < TV_U; ++u) {
             const int e = min(e0 + 512 * u, n_entries - 2);
             if (single) {
               x[u] = *reinterpret_cast<const float4 *>(sp + 2 * (size_t)e);
@@ -401,7 +413,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
             }
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < TV_U; ++u) {
             const int e = e0 + 512 * u;
             if (e >= n_entries) break;
             // entries e and e + 1: tokens of the same head
