@@ -369,3 +369,18 @@ def test_outlier_store_bytes_match_the_page(tmp_path):
         if st.k_outliers is not None:
             n += st.k_outliers.element_size() * st.k_outliers.numel()
         assert n == 10 * b, (m, n)
+
+
+def test_automatic_chunks_are_at_least_640_tokens(lib, monkeypatch):
+    """The per-chunk plan fills about 512 work-groups, but no automatic chunk is
+    shorter than 640 tokens (a multiple of 64): fewer, longer chunks won on
+    small steps.  An explicit split_tokens is taken as given."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    for batch, hkv, suffix, chunk in ((64, 8, 12628, 12672), (8, 8, 32768, 4096), (4, 8, 131072, 8192),
+                                      (16, 8, 1024, 640), (1, 1, 64, 640), (1, 1, 100000, 640)):
+        info = _plan(lib, _args(batch=batch, hkv=hkv, hq=4 * hkv, suffix=suffix), m)
+        assert info.chunk == chunk, (batch, hkv, suffix, info.chunk)
+        assert info.chunks == -(-suffix // chunk)
+    info = _plan(lib, _args(batch=16, suffix=1024, split=128), m)
+    assert (info.chunk, info.chunks) == (128, 8)
