@@ -310,7 +310,10 @@ typedef struct kvq_plan_info {
   int32_t chunk;            /* tokens per chunk */
   int32_t chunks;           /* chunks per (request, KV head), both regions */
   int32_t launches;         /* kernel launches of the call: 1, or 2 when the
-                               two regions' formats need separate kernels */
+                               two regions' formats need separate kernels; one
+                               more when a per-chunk plan with several chunks
+                               per (request, KV head) runs the TV and the block
+                               report in a finish launch over many work-groups */
   int32_t reserved;         /* 0 */
   uint64_t workspace_bytes;
 } kvq_plan_info;

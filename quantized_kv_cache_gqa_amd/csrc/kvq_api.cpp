@@ -42,6 +42,9 @@ struct Plan {
   bool tv = false, meter = false, wit_any = false, tier_b = false, value = false, two_sided = false;
   bool report = false;          // per-block risk report
   int n_blocks = 0, pre_blocks = 0;
+  bool defer = false;           // per-chunk plan: TV and report in a finish launch
+  int fin_blocks = 0, fin_ranges = 0;
+  size_t off_fin = 0, off_tvp = 0, off_rkey = 0;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, off_rspill = 0, off_ublk = 0, bytes = 0;
 };
@@ -281,6 +284,24 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     p.off_ublk = p.bytes;
     p.bytes += round_up((size_t)groups * p.n_blocks * p.group * sizeof(float), kAlign);
   }
+  // Several chunks per group: the last work-group of a group would stream the
+  // whole group's spill alone for the TV and the report; a finish launch
+  // spreads that over FIN_BLOCKS-block ranges instead (KVQ_DEFER_FINISH=0, a
+  // test hook, keeps it in the decode launch).
+  p.defer = p.total_chunks > 1 && (p.tv || p.report) && !env_is("KVQ_DEFER_FINISH", '0');
+  if (p.defer) {
+    p.fin_blocks = (p.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK +
+                   (p.suffix_cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
+    p.fin_ranges = (p.fin_blocks + FIN_BLOCKS - 1) / FIN_BLOCKS;
+    p.off_fin = p.bytes;
+    p.bytes += round_up((size_t)groups * p.group * 4 * sizeof(float), kAlign);
+    p.off_tvp = p.bytes;
+    p.bytes += round_up((size_t)groups * p.fin_ranges * p.group * sizeof(float), kAlign);
+    if (p.report) {
+      p.off_rkey = p.bytes;
+      p.bytes += round_up((size_t)groups * p.group * p.fin_blocks * sizeof(float), kAlign);
+    }
+  }
   return KVQ_OK;
 }
 
@@ -364,7 +385,15 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
     d.spill = ((p.tv || p.report) && !p.team) ? reinterpret_cast<float *>(w + p.off_spill) : nullptr;
     d.rspill = p.report ? reinterpret_cast<float *>(w + p.off_rspill) : nullptr;
     d.ublk = p.report ? reinterpret_cast<float *>(w + p.off_ublk) : nullptr;
+    if (p.defer) {
+      d.fin = reinterpret_cast<float *>(w + p.off_fin);
+      d.tvp = reinterpret_cast<float *>(w + p.off_tvp);
+      d.rkey = p.report ? reinterpret_cast<float *>(w + p.off_rkey) : nullptr;
+    }
   }
+  d.defer_tv = p.defer ? 1 : 0;
+  d.fin_blocks = p.fin_blocks;
+  d.fin_ranges = p.fin_ranges;
   dp = d;
   ds = d;
   if (p.pre_chunks > 0) {
@@ -424,14 +453,19 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
   }
   if (chunk_launch_count(p, dp, ds) == 1 && p.pre_chunks > 0 && p.suf_chunks > 0) {
     e = launch_decode_two(dp, ds, stream);
-    return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
-  }
-  if (p.pre_chunks > 0) {
-    e = launch_decode(dp, stream);
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  } else {
+    if (p.pre_chunks > 0) {
+      e = launch_decode(dp, stream);
+      if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+    }
+    if (p.suf_chunks > 0) {
+      e = launch_decode(ds, stream);
+      if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+    }
   }
-  if (p.suf_chunks > 0) {
-    e = launch_decode(ds, stream);
+  if (p.defer) {
+    e = launch_finish(d, stream);
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
   }
   return KVQ_OK;
@@ -529,7 +563,7 @@ kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int m
   } else {
     DecodeLaunch d, dp, ds;
     chunk_launches(a, m, p, meter_only != 0, nullptr, d, dp, ds);
-    info->launches = chunk_launch_count(p, dp, ds);
+    info->launches = chunk_launch_count(p, dp, ds) + (p.defer ? 1 : 0);
   }
   info->reserved = 0;
   return KVQ_OK;

@@ -461,6 +461,189 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   chunk_epilogue<G>(d, part_s, grp, chunk_idx, b, kvh);
 }
 
+// ------------------------------------------------------------- finish launch
+// Deferred finalize of the per-chunk plan (several chunks per group): the
+// decode launch's last work-group per group published the normalizers; here
+// work-group (group, range r) takes the range's FIN_BLOCKS 256-token blocks
+// (the prefix's blocks first, then the suffix's, as the block report numbers
+// them), adds its tokens' TV terms and, for the report, each block's mass
+// and contribution (WitCert Sec. 6.3.5).  The group's last arrival sums the
+// ranges' TV partials in range order and ranks the blocks.  One work-group
+// per group would stream the whole spill alone; spread this way the pass
+// runs at the device's bandwidth.
+template <int G>
+__global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
+  constexpr float LN2 = 0.69314718055994530942f;
+  constexpr int NIT = (256 * G + 511) / 512;         // float4 loads per thread and block
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int groups = d.batch * d.h_kv;
+  const int grp = (int)(blockIdx.x / (unsigned)d.fin_ranges);
+  const int r = (int)(blockIdx.x - (unsigned)grp * d.fin_ranges);
+  if (grp >= groups) return;                          // (the grid is exact)
+  const int b = grp / d.h_kv, kvh = grp - b * d.h_kv;
+  const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
+  const int pre_nb = (d.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
+  __shared__ float fin_s[G][4];
+  __shared__ float tvpart_s[256];
+  __shared__ int last_s;
+  if (tid < 4 * G) fin_s[tid >> 2][tid & 3] = d.fin[(size_t)grp * 4 * G + tid];
+  __syncthreads();
+
+  // ---- TV terms of the range's tokens: thread tid reads entries
+  //      2 tid + 512 k of each block (two entries of head hmine per float4)
+  // TV requested (0 where no region holds exact keys: stored keys are exact)
+  const bool do_tv = d.tv != nullptr;
+  if (do_tv) {
+    const int hmine = ((2 * tid) % (4 * G)) / 4;
+    const float Mt = fin_s[hmine][0], iZt = fin_s[hmine][1];
+    const float Me = fin_s[hmine][2], iZe = fin_s[hmine][3];
+    float4 x[FIN_BLOCKS][NIT];
+#pragma unroll
+    for (int i = 0; i < FIN_BLOCKS; ++i) {           // all loads first
+      const int j = r * FIN_BLOCKS + i;
+      const bool pre = j < pre_nb;
+      const int jj = pre ? j : j - pre_nb;
+      const int cap = pre ? d.prefix_len : d.suffix_cap;
+      const float *sp = spill_region<G>(d, grp, pre);
+      const int e_max = round16(cap) * G - 2;        // the region's last entry pair
+#pragma unroll
+      for (int k = 0; k < NIT; ++k) {
+        const int e = min(KVQ_INT8_BLOCK * G * jj + 2 * tid + 512 * k, e_max);
+        x[i][k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (d.has_tv && j < d.fin_blocks && e >= 0) x[i][k] = *reinterpret_cast<const float4 *>(sp + 2 * (size_t)e);
+      }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FIN_BLOCKS; ++i) {
+      const int j = r * FIN_BLOCKS + i;
+      if (j >= d.fin_blocks || !d.has_tv) break;
+      const bool pre = j < pre_nb;
+      const int jj = pre ? j : j - pre_nb;
+      const int n = pre ? d.prefix_len : suf_len;
+#pragma unroll
+      for (int k = 0; k < NIT; ++k) {
+        const int el = 2 * tid + 512 * k;            // entry within the block
+        if (el >= KVQ_INT8_BLOCK * G) break;
+        const int e = KVQ_INT8_BLOCK * G * jj + el;
+        const int tile = e / (16 * G), rr = e % (16 * G);
+        const int t = 16 * tile + 4 * (rr / (4 * G)) + (rr & 3);
+        if (t < n) tvp_add(acc, x[i][k].x, x[i][k].y, Mt, iZt, Me, iZe);
+        if (t + 1 < n) tvp_add(acc, x[i][k].z, x[i][k].w, Mt, iZt, Me, iZe);
+      }
+    }
+    tvpart_s[tid] = acc;
+    __syncthreads();
+    if (tid < G) {
+      float sum = 0.0f;
+      for (int t = 0; t < 256; ++t)                   // fixed order
+        if (((2 * t) % (4 * G)) / 4 == tid) sum += tvpart_s[t];
+      st_dev(d.tvp + ((size_t)grp * d.fin_ranges + r) * G + tid, sum);
+    }
+  }
+
+  // ---- block report: wavefront w takes block r FIN_BLOCKS + w
+  if (d.has_report) {
+    const int j = r * FIN_BLOCKS + wv;
+    if (j < d.fin_blocks) {
+      const bool pre = j < pre_nb;
+      const int jj = pre ? j : j - pre_nb;
+      const int cap = pre ? d.prefix_len : d.suffix_cap;
+      const int n = pre ? d.prefix_len : suf_len;
+      const bool i8 = (pre ? d.pre_int8 : d.suf_int8) != 0;
+      const float *sp = spill_region<G>(d, grp, pre);
+      const float *rp = rspill_region<G>(d, grp, pre);
+      const int hmine = (lane % (4 * G)) / 4;
+      const float Mt = fin_s[hmine][0], iZt = fin_s[hmine][1];
+      float lt[4 * G], cr[4 * G];
+#pragma unroll
+      for (int i = 0; i < 4 * G; ++i) {
+        const int e = min(KVQ_INT8_BLOCK * G * jj + lane + 64 * i, round16(cap) * G - 1);
+        lt[i] = sp[2 * (size_t)e];
+        cr[i] = rp[e];
+      }
+      float ms = 0.0f, ex = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4 * G; ++i) {
+        const int e = KVQ_INT8_BLOCK * G * jj + lane + 64 * i;
+        const int tile = e / (16 * G), rr = e % (16 * G);
+        const int t = 16 * tile + 4 * (rr / (4 * G)) + (rr & 3);
+        if (t < n) {
+          const float pt = fast_exp2(lt[i] - Mt) * iZt;
+          ms += pt;
+          ex += pt * expm1f(cr[i] * LN2);
+        }
+      }
+      for (int off = 1; off < 64; off <<= 1) {
+        if (off >= 4 && off < 4 * G) continue;       // the head bits
+        ms += __shfl_xor(ms, off);
+        ex += __shfl_xor(ex, off);
+      }
+      if (lane < 4 * G && (lane & 3) == 0) {
+        const int h = lane >> 2;
+        float Eb = 0.0f;
+        if (d.has_tier_b && i8 && ms > 0.0f)
+          Eb = ms * expm1f(d.ublk[((size_t)grp * d.n_blocks + j) * G + h] * LN2);
+        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + h) * d.n_blocks + j;
+        if (d.block_mass) d.block_mass[o] = ms;
+        if (d.block_excess) d.block_excess[o] = ex;
+        if (d.block_excess_b) d.block_excess_b[o] = Eb;
+        if (d.block_order) st_dev(d.rkey + ((size_t)grp * G + h) * d.n_blocks + j, d.has_tier_b ? Eb : ex);
+      }
+    }
+  }
+
+  // ---- the group's last arrival: TV sum in range order, block ranking
+  wait_own_stores();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned old = __hip_atomic_fetch_add(d.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = (old == (unsigned)(d.fin_ranges - 1));
+  }
+  __syncthreads();
+  if (!last_s) return;
+  if (do_tv && tid < G) {
+    float sum = 0.0f;
+    for (int q = 0; q < d.fin_ranges; ++q) sum += ld_dev(d.tvp + ((size_t)grp * d.fin_ranges + q) * G + tid);
+    d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * sum;
+  }
+  if (d.has_report && d.block_order) {               // rank = blocks ahead of j
+    __shared__ float rkey_s[G][512];
+    const int nbt = d.n_blocks;
+    for (int i = tid; i < G * nbt; i += 256) rkey_s[i / nbt][i % nbt] = ld_dev(d.rkey + (size_t)grp * G * nbt + i);
+    __syncthreads();
+    for (int i = tid; i < G * nbt; i += 256) {
+      const int h = i / nbt, j = i - h * nbt;
+      const float kj = rkey_s[h][j];
+      int rank = 0;
+      for (int k = 0; k < nbt; ++k) {
+        const float kk = rkey_s[h][k];
+        rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
+      }
+      d.block_order[((size_t)b * d.h_q + (size_t)kvh * G + h) * nbt + rank] = j;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int G>
+static hipError_t launch_finish_g(const DecodeLaunch &d, hipStream_t s) {
+  const long grid = (long)d.batch * d.h_kv * d.fin_ranges;
+  hipLaunchKernelGGL((finish_kernel<G>), dim3((unsigned)grid), dim3(256), 0, s, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const DecodeLaunch &d, hipStream_t s) {
+  switch (d.group) {
+    case 1: return launch_finish_g<1>(d, s);
+    case 2: return launch_finish_g<2>(d, s);
+    case 4: return launch_finish_g<4>(d, s);
+    case 8: return launch_finish_g<8>(d, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <int G, int KF, int VF>

@@ -382,6 +382,13 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
     }
   }
   __syncthreads();
+  if (d.defer_tv) {
+    // the TV and the block report run in the finish launch, spread over many
+    // work-groups: publish this group's normalizers for it
+    if (tid < 4 * G) d.fin[(size_t)grp * 4 * G + tid] = fin_s[tid >> 2][tid & 3];
+    if (tid == 0) __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   if (d.tv) {
     // Thread tid reads entries 2 tid + 512 k (a float4: two entries of one
     // head); 512 is a multiple of 4G, so the head of its entries never changes.

@@ -89,6 +89,15 @@ struct DecodeLaunch {
   float *spill;
   int team;                     // > 0: team launch, work-groups per (request, KV head)
   int n_teams;                  // teams in the grid
+  // deferred finalize (per-chunk plan, several chunks per group): the
+  // finalizer publishes the normalizers (M~, 1/Z~, M_e, 1/Z_e per head) and a
+  // finish launch runs the TV and the block report over FIN_BLOCKS-block ranges
+  int defer_tv;
+  float *fin;                   // [groups][G][4]
+  float *tvp;                   // [groups][fin_ranges][G] TV partial sums
+  float *rkey;                  // [groups][G][n_blocks] page-in keys
+  int fin_ranges;               // ranges per group
+  int fin_blocks;               // 256-token blocks per group over both regions
   uint32_t *team_ctl;           // team launch: [0] epoch (round r's tag is epoch + r + 1),
                                 // [1] work-groups finished (0 at rest)
   unsigned spin_limit;          // team launch: polls per batch of words before giving up
@@ -107,6 +116,9 @@ inline bool launch_has_extensions(const DecodeLaunch &d) {
 }
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t stream);
+// The finish launch of a deferred finalize (TV and block report).
+constexpr int FIN_BLOCKS = 4;
+hipError_t launch_finish(const DecodeLaunch &d, hipStream_t stream);
 // Matrix-core kernel for GQA group 4 with FP8/BF16 keys and values.
 bool mfma_path_supports(const DecodeLaunch &d);
 hipError_t launch_decode_mfma(const DecodeLaunch &d, hipStream_t stream);

@@ -384,3 +384,22 @@ def test_automatic_chunks_are_at_least_640_tokens(lib, monkeypatch):
         assert info.chunks == -(-suffix // chunk)
     info = _plan(lib, _args(batch=16, suffix=1024, split=128), m)
     assert (info.chunk, info.chunks) == (128, 8)
+
+
+def test_several_chunks_per_group_add_a_finish_launch(lib, monkeypatch):
+    """With several chunks per (request, KV head) and a TV or block report,
+    the per-chunk plan runs those passes in one more launch (its normalizers
+    and partial sums in the workspace); KVQ_DEFER_FINISH=0 (a test hook) keeps
+    them in the decode launch's last work-group."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+    tv = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    one_chunk = _plan(lib, _args(), tv)                          # 512 groups: one chunk each
+    assert (one_chunk.chunks, one_chunk.launches) == (1, 1)
+    a = _args(batch=4, suffix=131072)
+    info = _plan(lib, a, tv)
+    assert info.chunks > 1 and info.launches == 2
+    assert _plan(lib, a, kvq.MeterOut(meter=FAKE)).launches == 1  # no TV, no report: nothing to finish
+    monkeypatch.setenv("KVQ_DEFER_FINISH", "0")
+    kept = _plan(lib, a, tv)
+    assert kept.launches == 1 and kept.workspace_bytes < info.workspace_bytes

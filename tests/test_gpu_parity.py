@@ -369,7 +369,8 @@ def test_two_regions_in_one_launch(gpu_lib, monkeypatch, name):
     cfg = TWO_REGION[name]()
     case = GpuCase(cfg, page_seed=5)
     split = 128
-    p = plan(case, split_tokens=split)
+    monkeypatch.setenv("KVQ_DEFER_FINISH", "0")      # decode launches only (the finish
+    p = plan(case, split_tokens=split)              # launch has its own test)
     assert (p["team"], p["launches"]) == (0, 1), p
     assert plan(case, split_tokens=split, meter_only=True)["launches"] == 1
     o1, m1, _ = _all_cells(case, split_tokens=split)
@@ -599,3 +600,44 @@ def test_outlier_pairs_every_cell(gpu_lib, kernel, name):
     plain = GpuCase(cfg, page_seed=10)
     _, mp = plain.run(tier_b_delta=1e-3)
     assert float(mo["log_a_b"].median()) < float(mp["log_a_b"].median())
+
+
+FINISH = {
+    "int8-dither": (lambda: small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1000)),
+                    1e-6),
+    "long-split": (lambda: small_variant(LONG_B4_S128K_SPLIT, batch=2, h_kv=2, suffix_len=9000, lens=(9000, 4097)),
+                   None),
+    "fp8-cartridge": (lambda: _two_region_fp8(False), None),
+}
+
+
+@pytest.mark.parametrize("name", list(FINISH))
+def test_finish_launch_matches_the_oracle_and_the_in_kernel_finalize(gpu_lib, monkeypatch, name):
+    """Several chunks per group: the TV and the block report run in the finish
+    launch.  Both that and the decode launch's own finalize (KVQ_DEFER_FINISH=0)
+    match the oracle on every cell; the page-in order is the same, the TV
+    differs by summation order only."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    make, delta = FINISH[name]
+    cfg = make()
+    case = GpuCase(cfg, page_seed=12)
+    res = {}
+    for mode in ("finish", "kept"):
+        if mode == "kept":
+            monkeypatch.setenv("KVQ_DEFER_FINISH", "0")
+        else:
+            monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+        p = plan(case, split_tokens=512, report=True, tier_b_delta=delta)
+        assert p["chunks"] > 1 and (p["launches"] >= 2) == (mode == "finish"), p
+        out, m = case.run(split_tokens=512, report=True, tier_b_delta=delta)
+        for b in range(cfg.batch):
+            for kvh in range(cfg.h_kv):
+                encs, ref = oracle_cell(case, b, kvh, tier_b_delta=delta)
+                check_results(case, out, m, b, kvh, ref)
+                check_block_report(case, m, b, kvh, ref, delta is not None)
+        res[mode] = (out, m)
+    (o1, m1), (o2, m2) = res["finish"], res["kept"]
+    assert torch.equal(o1, o2)
+    assert torch.equal(m1["block_order"], m2["block_order"])
+    assert torch.equal(m1["block_mass"], m2["block_mass"])
+    torch.testing.assert_close(m1["tv"], m2["tv"], rtol=0, atol=1e-6)
