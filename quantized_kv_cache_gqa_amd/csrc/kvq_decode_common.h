@@ -172,24 +172,15 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
     const float *rp = rspill_region<G>(d, grp, region == 0);
     for (int j = wv; j < nb; j += WAVES) {         // uniform over the wavefront
       float ms = 0.0f, ex = 0.0f;
-      // all of the block's loads first (one work-group streams the whole
-      // group's spill: its loads in flight set the time)
-      float lt[4 * G], cr[4 * G];
-#pragma unroll
-      for (int i = 0; i < 4 * G; ++i) {
-        const int e = min(KVQ_INT8_BLOCK * G * j + lane + 64 * i, round16(cap) * G - 1);   // within the region's rows
-        lt[i] = rd(sp + 2 * (size_t)e);
-        cr[i] = rd(rp + e);
-      }
-#pragma unroll
+#pragma unroll 4
       for (int i = 0; i < 4 * G; ++i) {
         const int e = KVQ_INT8_BLOCK * G * j + lane + 64 * i;
         const int tile = e / (16 * G), r = e % (16 * G);
         const int t = 16 * tile + 4 * (r / (4 * G)) + (r & 3);
         if (t < n) {
-          const float pt = fast_exp2(lt[i] - Mt) * iZt;
+          const float pt = fast_exp2(rd(sp + 2 * (size_t)e) - Mt) * iZt;
           ms += pt;
-          ex += pt * expm1f(cr[i] * LN2);
+          ex += pt * expm1f(rd(rp + e) * LN2);
         }
       }
       for (int off = 1; off < 64; off <<= 1) {
@@ -392,9 +383,9 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
   if (d.tv) {
     // Thread tid reads entries 2 tid + 512 k (a float4: two entries of one
     // head); 512 is a multiple of 4G, so the head of its entries never changes.
-    // TV_U float4 per thread are in flight at once: one work-group streams the
-    // whole group's spill here, so its memory-level parallelism sets the time.
-    constexpr int TV_U = 16;
+    // (a group with several chunks runs this pass in the finish launch
+    // instead, spread over many work-groups)
+    constexpr int TV_U = 4;
     __shared__ float tvpart_s[256];
     const int hmine = ((2 * tid) % (4 * G)) / 4;
     float acc_tv = 0.0f;
