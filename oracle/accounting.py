@@ -13,7 +13,7 @@ and, when the exact TV is measured, the exact bf16 key.
 """
 from __future__ import annotations
 
-ELEM_BYTES = {"bf16": 2, "fp8": 1, "int8": 1, "fp32": 4}
+ELEM_BYTES = {"bf16": 2, "fp8": 1, "int8": 1, "int8g32": 1, "fp32": 4}
 KIB = 1024
 MIB = 1024 ** 2
 GIB = 1024 ** 3
@@ -45,6 +45,8 @@ def token_head_bytes(k_fmt: str, v_fmt: str, *, exact_k: bool, witness: bool,
             total += 4.0                              # fp32 per-token scale
         elif fmt == "int8":
             total += 2.0 * head_dim / block           # fp16 per (block, channel)
+        elif fmt == "int8g32":
+            total += 2.0 * head_dim / 32              # fp16 per (token, 32-channel group)
     if witness:
         total += 2.0 * n_bands
     if exact_k:

@@ -29,3 +29,32 @@ def test_token_head_bytes_of_the_workloads():
     assert token_head_bytes("bf16", "bf16", exact_k=False, witness=False) == 512
     # dithered INT8 with per-(256-token block, channel) fp16 scales
     assert token_head_bytes("int8", "int8", exact_k=True, witness=True) == 546
+
+
+def test_group_scale_keys_match_table6_without_pairs():
+    """Keys of the per-token group-scale INT8 format: 128 codes + 4 fp16
+    scales = 136 B per token-head, Table 6's m = 0 row (WitCert Sec. 6.2.5)."""
+    g = json.load(open(os.path.join(GOLDEN, "witcert_table6_outlier_bytes.json")))
+    k_only = token_head_bytes("int8g32", "int8g32", exact_k=False, witness=False) / 2
+    assert k_only == g["printed"]["0"]
+
+
+def test_bench_byte_count_agrees_with_the_accounting():
+    """bench.py's algorithmic bytes per token-head (its own count) agree with
+    the accounting here for every stored format."""
+    import bench
+    for kf in ("bf16", "fp8", "int8", "int8g32"):
+        for vf in ("bf16", "fp8", "int8", "int8g32"):
+            for ex in (False, True):
+                for wit in (False, True):
+                    assert bench.token_head_bytes(kf, vf, ex, wit) == token_head_bytes(kf, vf, exact_k=ex,
+                                                                                        witness=wit), (kf, vf)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr
