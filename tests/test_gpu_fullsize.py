@@ -66,3 +66,30 @@ def test_full_size_meter_extensions_sampled_cells(gpu_lib, idx):
     print(f"[{cfg.name} layer {layer} extensions] sampled={len(SAMPLES[idx])} worst={worst}", flush=True)
     del case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pairs", [0, 4])
+def test_full_size_group_scales_and_outlier_pairs_sampled_cells(gpu_lib, pairs):
+    """The 32,768-token INT8 workload stored with per-(token, 32-channel
+    group) scales, without and with 4 fixed outlier RoPE pairs (WitCert Sec.
+    6.2.3, 6.2.5), in 16-token pages: Tier A, Tier B and the value side at
+    full size on sampled cells against the oracle."""
+    import dataclasses
+    base = CONFIGS[4]
+    suf = dataclasses.replace(base.suffix, k_fmt="int8g32", v_fmt="int8g32", paged=True, page_size=16)
+    cfg = dataclasses.replace(base, suffix=suf, name=base.name + f"-g32-paged-m{pairs}")
+    layer = cfg.layers - 1
+    case = GpuCase(cfg, layer=layer, page_seed=1, value_witness=True, n_outlier_pairs=pairs)
+    out, m = case.run(tier_b_delta=1e-9, value_bound=True)
+    worst = {}
+    for b, kvh in SAMPLES[4]:
+        encs, ref = oracle_cell(case, b, kvh, tier_b_delta=1e-9)
+        check_stored(case, b, kvh, encs)
+        w = check_results(case, out, m, b, kvh, ref)
+        for k, v in w.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    assert {"bound_b", "value_err"} <= set(worst)
+    assert torch.all(m["tv"] <= m["bound_raw"] + 1e-6) and torch.all(m["tv"] <= m["bound_b_raw"] + 1e-6)
+    print(f"[{cfg.name} layer {layer}] sampled={len(SAMPLES[4])} worst={worst}", flush=True)
+    del case
+    torch.cuda.empty_cache()
