@@ -293,6 +293,11 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     p.fin_blocks = (p.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK +
                    (p.suffix_cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
     p.fin_ranges = (p.fin_blocks + FIN_BLOCKS - 1) / FIN_BLOCKS;
+    if ((int64_t)groups * p.fin_ranges > ((int64_t)1 << 30)) {   // grid too large: keep the passes in place
+      p.defer = false;
+      p.fin_blocks = p.fin_ranges = 0;
+      return KVQ_OK;
+    }
     p.off_fin = p.bytes;
     p.bytes += round_up((size_t)groups * p.group * 4 * sizeof(float), kAlign);
     p.off_tvp = p.bytes;
