@@ -70,7 +70,9 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || p.group != 4) return false;
+  // (a group of 8 runs as two team launches of 4 query heads each)
+  if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || (p.group != 4 && p.group != 8)) return false;
+  if (p.group == 8 && env_is("KVQ_DECODE_KERNEL", 'g')) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -346,6 +348,8 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   d.h_q = a->num_q_heads;
   d.h_kv = a->num_kv_heads;
   d.group = p.group;
+  d.qg = p.group;
+  d.qh0 = 0;
   d.sm_scale = a->sm_scale;
   d.q = a->q;
   d.out = meter_only ? nullptr : a->out;
@@ -425,6 +429,39 @@ int chunk_launch_count(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch
   return 1;
 }
 
+// A GQA group of 8 whose regions all take the matrix-core kernels runs as two
+// launch sets of 4 query heads each (the group-4 kernels; each reads the
+// cache once), instead of the vector-ALU kernel.
+bool split_halves(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch &ds) {
+  if (p.group != 8 || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
+  DecodeLaunch hp = dp, hs = ds;
+  hp.group = hs.group = 4;
+  if (p.pre_chunks > 0 && !mfma_path_supports(hp)) return false;
+  if (p.suf_chunks > 0 && !mfma_path_supports(hs)) return false;
+  return true;
+}
+
+void make_half(DecodeLaunch &x, int half) {
+  x.group = 4;
+  x.qh0 = 4 * half;
+}
+
+// The per-chunk plan's launches: both regions in one launch where the kernels
+// allow it, else one per region; then the finish launch when deferred.
+hipError_t launch_chunks(const Plan &p, const DecodeLaunch &d, const DecodeLaunch &dp, const DecodeLaunch &ds,
+                         hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (chunk_launch_count(p, dp, ds) == 1 && p.pre_chunks > 0 && p.suf_chunks > 0) {
+    e = launch_decode_two(dp, ds, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    if (p.pre_chunks > 0 && (e = launch_decode(dp, stream)) != hipSuccess) return e;
+    if (p.suf_chunks > 0 && (e = launch_decode(ds, stream)) != hipSuccess) return e;
+  }
+  if (p.defer) e = launch_finish(d, stream);
+  return e;
+}
+
 kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
                       hipStream_t stream, bool meter_only) {
   Plan p;
@@ -453,27 +490,29 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     // publishes, so the others' waits run out and the results turn to NaN).
     d.spin_limit = env_uint("KVQ_TEAM_SPIN_LIMIT", 1u << 18, 1);
     d.silent_member = (int)env_uint("KVQ_TEAM_SILENT_MEMBER", 0xffffffffu, 0);
-    e = launch_decode_team(d, p.grid, stream);
+    if (p.group == 8) {                             // two launches of 4 query heads
+      for (int half = 0; half < 2 && e == hipSuccess; ++half) {
+        DecodeLaunch hd = d;
+        make_half(hd, half);
+        e = launch_decode_team(hd, p.grid, stream);
+      }
+    } else {
+      e = launch_decode_team(d, p.grid, stream);
+    }
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
   }
-  if (chunk_launch_count(p, dp, ds) == 1 && p.pre_chunks > 0 && p.suf_chunks > 0) {
-    e = launch_decode_two(dp, ds, stream);
-    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  if (split_halves(p, dp, ds)) {
+    for (int half = 0; half < 2 && e == hipSuccess; ++half) {
+      DecodeLaunch hd = d, hp = dp, hs = ds;
+      make_half(hd, half);
+      make_half(hp, half);
+      make_half(hs, half);
+      e = launch_chunks(p, hd, hp, hs, stream);
+    }
   } else {
-    if (p.pre_chunks > 0) {
-      e = launch_decode(dp, stream);
-      if (e != hipSuccess) return KVQ_ERR_LAUNCH;
-    }
-    if (p.suf_chunks > 0) {
-      e = launch_decode(ds, stream);
-      if (e != hipSuccess) return KVQ_ERR_LAUNCH;
-    }
+    e = launch_chunks(p, d, dp, ds, stream);
   }
-  if (p.defer) {
-    e = launch_finish(d, stream);
-    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
-  }
-  return KVQ_OK;
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -564,11 +603,18 @@ kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int m
   info->chunks = p.total_chunks;
   info->workspace_bytes = p.bytes;
   if (p.team) {
-    info->launches = 1;
+    info->launches = p.group == 8 ? 2 : 1;
   } else {
     DecodeLaunch d, dp, ds;
     chunk_launches(a, m, p, meter_only != 0, nullptr, d, dp, ds);
-    info->launches = chunk_launch_count(p, dp, ds) + (p.defer ? 1 : 0);
+    if (split_halves(p, dp, ds)) {
+      DecodeLaunch hp = dp, hs = ds;
+      make_half(hp, 0);
+      make_half(hs, 0);
+      info->launches = 2 * (chunk_launch_count(p, hp, hs) + (p.defer ? 1 : 0));
+    } else {
+      info->launches = chunk_launch_count(p, dp, ds) + (p.defer ? 1 : 0);
+    }
   }
   info->reserved = 0;
   return KVQ_OK;

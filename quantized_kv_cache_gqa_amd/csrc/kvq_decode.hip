@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   float qn[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + h) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * D;
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
       const float4 t = *reinterpret_cast<const float4 *>(qp + 16 * j + i);
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
         if (act) {
 #pragma unroll
           for (int h = 0; h < G; ++h)
-            qo[h][e] = d.q[((size_t)b * d.h_q + (size_t)kvh * G + h) * D + P + 64 * (k & 1)] * qs;
+            qo[h][e] = d.q[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * D + P + 64 * (k & 1)] * qs;
         }
       }
     }
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         float Eb = 0.0f;
         if (d.has_tier_b && i8 && ms > 0.0f)
           Eb = ms * expm1f(d.ublk[((size_t)grp * d.n_blocks + j) * G + h] * LN2);
-        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + h) * d.n_blocks + j;
+        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * d.n_blocks + j;
         if (d.block_mass) d.block_mass[o] = ms;
         if (d.block_excess) d.block_excess[o] = ex;
         if (d.block_excess_b) d.block_excess_b[o] = Eb;
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
   if (do_tv && tid < G) {
     float sum = 0.0f;
     for (int q = 0; q < d.fin_ranges; ++q) sum += ld_dev(d.tvp + ((size_t)grp * d.fin_ranges + q) * G + tid);
-    d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * sum;
+    d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * sum;
   }
   if (d.has_report && d.block_order) {               // rank = blocks ahead of j
     __shared__ float rkey_s[G][512];
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         const float kk = rkey_s[h][k];
         rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
       }
-      d.block_order[((size_t)b * d.h_q + (size_t)kvh * G + h) * nbt + rank] = j;
+      d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
     }
   }
   if (tid == 0) __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -193,7 +193,7 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         float Eb = 0.0f;
         if (d.has_tier_b && i8 && ms > 0.0f)
           Eb = ms * expm1f(rd(d.ublk + ((size_t)grp * d.n_blocks + gb0 + j) * G + h) * LN2);
-        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * G + h) * d.n_blocks + gb0 + j;
+        const size_t o = ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * d.n_blocks + gb0 + j;
         if (d.block_mass) d.block_mass[o] = ms;
         if (d.block_excess) d.block_excess[o] = ex;
         if (d.block_excess_b) d.block_excess_b[o] = Eb;
@@ -212,7 +212,7 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         const float kk = rkey_s[h][k];
         rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
       }
-      d.block_order[((size_t)b * d.h_q + (size_t)kvh * G + h) * nbt + rank] = j;
+      d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
     }
   }
 }
@@ -320,7 +320,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       o0 += rd(pc + 8 + lane) * fq;
       o1 += rd(pc + 8 + 64 + lane) * fq;
     }
-    const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
+    const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
     if (d.has_out) {
       const float inv = Zq > 0.0f ? 1.0f / Zq : 0.0f;
       d.out[qh * D + lane] = o0 * inv;
@@ -429,7 +429,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       float s = 0.0f;
       for (int t = 0; t < 256; ++t)                   // fixed order: bitwise reproducible
         if (((2 * t) % (4 * G)) / 4 == tid) s += tvpart_s[t];
-      d.tv[(size_t)b * d.h_q + (size_t)kvh * G + tid] = 0.5f * s;
+      d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * s;
     }
   }
   if (d.has_report) block_report_pass<G>(d, grp, b, kvh, single, suf_len, fin_s);

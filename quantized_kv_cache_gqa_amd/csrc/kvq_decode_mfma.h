@@ -308,7 +308,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bq[4];
   f16x4_t bw;
   {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -364,7 +364,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
     if constexpr (I8K) {
       const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
-      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
       float ss = 0.0f;                             // sum of (q_c s_c)^2 in log2 units
 #pragma unroll
       for (int s8 = 0; s8 < 4; ++s8) {
@@ -413,7 +413,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bqo;
   const int n_op = R.n_op;
   if constexpr (GK) {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * G + hh) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
     uint32_t bm0 = 0, bm1 = 0;                       // bypassed pairs 0..31, 32..63
     if (n_op > 0) {
       const int32_t *opp = R.opairs + (size_t)kvh * n_op;

@@ -227,7 +227,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   //    The first batch of accumulator words of this wavefront and the
   //    previous round's TV shares are requested first; the TV pass (4.)
   //    runs while they travel.
-  const size_t qh = (size_t)b * d.h_q + (size_t)kvh * G + h;
+  const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
   // T >= 8: unit u = member, its batches of 8 members dealt to the 4
   // wavefronts in turn, partial sums added in wavefront order through LDS
   const bool split = T >= 8;
@@ -312,7 +312,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
         for (int i = 0; i < 8; ++i)
           if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
       }
-      const size_t qu = (size_t)b * d.h_q + (size_t)kvh * G + hu;
+      const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hu;
       if (split) {
         unit_s[h][lane] = o;
         if (!oku) bad_s = 1;
@@ -326,7 +326,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
       if (h == 0) {
         const int hu = member >> 1, dim = 64 * (member & 1) + lane;
         const float o = ((unit_s[0][lane] + unit_s[1][lane]) + unit_s[2][lane]) + unit_s[3][lane];
-        const size_t qu = (size_t)b * d.h_q + (size_t)kvh * G + hu;
+        const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hu;
         d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
       }
     }
@@ -373,7 +373,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     okp = __all(okp);
     const int pg = team + (round - 1) * d.n_teams;
     const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
-    if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * G + h] = okp ? 0.5f * sh : qnan;
+    if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + d.qh0 + h] = okp ? 0.5f * sh : qnan;
   }
   if (!ok) bad_s = 1;
   __syncthreads();

@@ -55,6 +55,10 @@ struct RegionDev {
 
 struct DecodeLaunch {
   int batch, h_q, h_kv, group;
+  // query heads of KV head kvh in q / out / the meter arrays: kvh * qg + qh0 +
+  // h for h < group (qg = group, qh0 = 0, unless a group of 8 runs as two
+  // launches of 4 heads each)
+  int qg, qh0;
   float sm_scale;
   const float *q;
   float *out;

@@ -403,3 +403,22 @@ def test_several_chunks_per_group_add_a_finish_launch(lib, monkeypatch):
     monkeypatch.setenv("KVQ_DEFER_FINISH", "0")
     kept = _plan(lib, a, tv)
     assert kept.launches == 1 and kept.workspace_bytes < info.workspace_bytes
+
+
+def test_group_of_eight_takes_two_launch_sets_on_the_matrix_cores(lib, monkeypatch):
+    """8 query heads per KV head with formats the matrix-core kernels take:
+    two launch sets of 4 heads (the planner reports twice the launches);
+    KVQ_DECODE_KERNEL=generic keeps one vector-ALU launch."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    g4 = _plan(lib, _args(batch=2, hq=16, hkv=4, suffix=4096), m)
+    g8 = _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096), m)
+    assert g8.launches == 2 * g4.launches
+    monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
+    assert _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096), m).launches == g4.launches
+    monkeypatch.delenv("KVQ_DECODE_KERNEL")
+    f32 = _args(batch=2, hq=32, hkv=4, suffix=4096)
+    f32.suffix.k_exact_format = 3                                 # fp32 exact keys: vector ALUs
+    assert _plan(lib, f32, m).launches == g4.launches

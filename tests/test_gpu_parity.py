@@ -641,3 +641,42 @@ def test_finish_launch_matches_the_oracle_and_the_in_kernel_finalize(gpu_lib, mo
     assert torch.equal(m1["block_order"], m2["block_order"])
     assert torch.equal(m1["block_mass"], m2["block_mass"])
     torch.testing.assert_close(m1["tv"], m2["tv"], rtol=0, atol=1e-6)
+
+
+def _g8(make):
+    """The same cells with 8 query heads per KV head (h_q = 8 h_kv)."""
+    def f():
+        cfg = make()
+        return dataclasses.replace(cfg, h_q=8 * cfg.h_kv, name=cfg.name + "-g8")
+    return f
+
+
+GROUP8 = {
+    "fp8": _g8(lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1234))),
+    "int8-dither": _g8(lambda: small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=1000, lens=(1000, 513))),
+    "int8g32-paged-m4": _g8(lambda: _g32(paged=True)),
+    "fp8-cartridge": _g8(lambda: _two_region_fp8(False)),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP8))
+def test_group_of_eight_every_cell(gpu_lib, kernel, name):
+    """GQA groups of 8: on the matrix cores as two launch sets of 4 query
+    heads (library choice), or on the vector-ALU kernel; every cell against
+    the oracle with Tier A, the value side, the two-sided form and, for INT8
+    keys, Tier B; the block report where the plan takes it."""
+    cfg = GROUP8[name]()
+    m = 4 if name.endswith("m4") else 0
+    case = GpuCase(cfg, page_seed=13, value_witness=True, n_outlier_pairs=m)
+    delta = 1e-4 if "int8" in name else None
+    p = plan(case, tier_b_delta=delta, value_bound=True, two_sided=True)
+    if kernel != "generic":
+        assert p["launches"] % 2 == 0, p                 # two sets of launches
+    _all_cells(case, tier_b_delta=delta, value_bound=True, two_sided=True)
+    _all_cells(case, split_tokens=256)
+    if "g32" not in name:
+        _, mr = case.run(report=True)
+        for b in range(cfg.batch):
+            for kvh in range(cfg.h_kv):
+                _, ref = oracle_cell(case, b, kvh)
+                check_block_report(case, mr, b, kvh, ref, False)
