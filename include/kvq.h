@@ -287,8 +287,10 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    (request, KV head), each keeping its chunk's logit pairs in LDS for the
  *    TV (WitCert Sec. 3 target), `n_teams` teams take the (request, KV head)
  *    pairs in `rounds` rounds.  Chosen when the TV is requested for a single
- *    region of at most 131,072 tokens with GQA group 4, FP8/BF16 keys and
- *    values and bf16 exact keys, and split_tokens is 0.  Members wait only
+ *    region of at most 131,072 tokens with GQA group 4 or 8, FP8/BF16 keys
+ *    and values and bf16 exact keys, split_tokens 0, and neither Tier B nor
+ *    the block report.  A group of 8 runs as two such launches of 4 query
+ *    heads each (as does the per-chunk plan where its kernels allow).  Members wait only
  *    for members of their own team, with a bounded wait: a wait that runs
  *    out (another kernel holding the device for longer) leaves NaN in that
  *    (request, KV head)'s results, never a hang.
