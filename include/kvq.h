@@ -274,14 +274,14 @@ const char *kvq_status_string(kvq_status status);
 kvq_status kvq_quantize(const kvq_quant_args *args, kvq_stream stream);
 
 /* Bytes of device workspace kvq_decode_attn / kvq_meter need for these
- * arguments, with or without stream capture.  Host-only: reads the current
+ * arguments, captured into a graph or not.  Host-only: reads the current
  * device's properties, never its memory.  The decode and the meter call on
  * the same arguments need the same size.  Returns 0 on invalid arguments. */
 size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter);
 
 /* How kvq_decode_attn (meter_only = 0) or kvq_meter (meter_only != 0) will
- * run for these arguments on the current device, on a stream that is not
- * being captured (host-only, as above).
+ * run for these arguments on the current device, captured into a graph or not
+ * (host-only, as above).
  *  - team > 0: one launch of at most as many work-groups as the device holds
  *    at once; `team` work-groups share each
  *    (request, KV head), each keeping its chunk's logit pairs in LDS for the
