@@ -323,7 +323,10 @@ kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter
                            kvq_plan_info *info);
 
 /* Prepare a workspace for first use: clears all of it (one fill kernel on
- * `stream`).  A workspace stays ready after every successful kvq_decode_attn /
+ * `stream`).  The team epoch restarts from 0 after about 2^32 / (rounds + 1)
+ * team launches on one workspace (some 4 * 10^8 for the batch-64 step); a
+ * caller that runs that many should clear the workspace again before then, so
+ * that no word of a launch that long ago can carry a tag being waited for.  A workspace stays ready after every successful kvq_decode_attn /
  * kvq_meter call: the per-chunk plan's arrival counters (after the first 256
  * bytes) are reset by the last work-group of each (request, KV head); team
  * launches tag their exchange words with an epoch kept in the first 256

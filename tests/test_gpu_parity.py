@@ -680,3 +680,34 @@ def test_group_of_eight_every_cell(gpu_lib, kernel, name):
             for kvh in range(cfg.h_kv):
                 _, ref = oracle_cell(case, b, kvh)
                 check_block_report(case, mr, b, kvh, ref, False)
+
+
+def test_team_epoch_restarts_below_its_limit(gpu_lib, monkeypatch):
+    """The team epoch kept in the workspace's first word moves past each
+    launch's tags and restarts from 0 before the tags could wrap; results stay
+    exact across the restart (the control word is caller memory, set here
+    from the host)."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    from quantized_kv_cache_gqa_amd import kvq
+    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    case = GpuCase(cfg)
+    p = _team_plan(case, monkeypatch)
+    ws = kvq.Workspace(torch.device("cuda"))
+
+    def call():
+        return kvq.decode_attn(case.inp["q"], cfg.h_kv, case.prefix_view, case.suffix_view,
+                               sm_scale=SM_SCALE, workspace=ws)
+
+    o_ref, m_ref = call()
+    torch.cuda.synchronize()
+    ctl = ws.buf[:8].view(torch.int32)
+    assert int(ctl[0]) == p["rounds"] + 1 and int(ctl[1]) == 0
+    ctl[0] = int(0xF0000000 - p["rounds"]) - (1 << 32)          # the last epoch below the limit
+    torch.cuda.synchronize()
+    for expect in (0, p["rounds"] + 1):
+        o, m = call()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
+        for k in m_ref:
+            assert torch.equal(m[k], m_ref[k]), k
+        assert int(ctl[0]) == expect and int(ctl[1]) == 0
