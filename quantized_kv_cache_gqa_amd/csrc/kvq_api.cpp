@@ -38,6 +38,7 @@ inline bool g32_paired(int kf, int vf) {
 
 struct Plan {
   int group = 0, chunk = 0, pre_chunks = 0, suf_chunks = 0, total_chunks = 0;
+  int kgroup = 0;               // query heads per tile of the kernels: group, or 4 padding a group of 1 or 2
   int prefix_len = 0, suffix_cap = 0;
   bool tv = false, meter = false, wit_any = false, tier_b = false, value = false, two_sided = false;
   bool report = false;          // per-block risk report
@@ -71,7 +72,7 @@ bool env_is(const char *name, char c) {
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
   // (a group of 8 runs as two team launches of 4 query heads each)
-  if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || (p.group != 4 && p.group != 8)) return false;
+  if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || (p.kgroup != 4 && p.group != 8)) return false;
   if (p.group == 8 && env_is("KVQ_DECODE_KERNEL", 'g')) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
@@ -163,6 +164,8 @@ kvq_status check_region(const kvq_region &r, bool is_prefix, bool need_v, int ba
   return KVQ_OK;
 }
 
+RegionDev region_dev(const kvq_region &r, bool is_prefix);
+
 // allow_team = false: the per-chunk plan even where a team launch applies
 kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_only, Plan &p,
                      bool allow_team = true) {
@@ -173,6 +176,7 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   if (a->num_q_heads % a->num_kv_heads) return KVQ_ERR_SHAPE;
   p.group = a->num_q_heads / a->num_kv_heads;
   if (p.group != 1 && p.group != 2 && p.group != 4 && p.group != 8) return KVQ_ERR_UNSUPPORTED;
+  p.kgroup = p.group;
   if (!a->q) return KVQ_ERR_NULL;
   if (!aligned16(a->q)) return KVQ_ERR_ALIGN;
   if (!meter_only) {
@@ -186,6 +190,23 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   if (s != KVQ_OK) return s;
   p.prefix_len = a->prefix.length;
   p.suffix_cap = a->suffix.length;
+  // a group of 1 or 2 query heads runs on the matrix-core kernels as a tile of
+  // 4 heads (the rest copies of the last, never written) where they apply
+  if ((p.group == 1 || p.group == 2) && !env_is("KVQ_DECODE_KERNEL", 'g')) {
+    bool ok = true;
+    for (int pre = 0; pre < 2; ++pre) {
+      const kvq_region &r = pre ? a->prefix : a->suffix;
+      if (r.length <= 0) continue;
+      DecodeLaunch t;
+      memset(&t, 0, sizeof(t));
+      t.group = 4;
+      t.region = region_dev(r, pre != 0);
+      t.k_format = r.k_format;
+      t.v_format = meter_only ? VF_NONE : r.v_format;
+      ok = ok && mfma_path_supports(t);
+    }
+    if (ok) p.kgroup = 4;
+  }
   if (p.prefix_len + (int64_t)p.suffix_cap <= 0) return KVQ_ERR_SHAPE;
   if (a->split_tokens < 0 || (a->split_tokens % 64) != 0) return KVQ_ERR_SHAPE;
 
@@ -271,20 +292,21 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     }
   }
   if (allow_team && plan_team(a, meter_only, groups, p)) return KVQ_OK;
+  const int wg = std::max(p.group, p.kgroup);      // heads per group in the workspace
   p.off_counters = kCtlBytes;
   p.off_partials = round_up(kCtlBytes + (size_t)groups * sizeof(uint32_t), kAlign);
   p.off_spill = p.off_partials +
-                round_up((size_t)groups * p.total_chunks * p.group * PART_STRIDE * sizeof(float), kAlign);
+                round_up((size_t)groups * p.total_chunks * wg * PART_STRIDE * sizeof(float), kAlign);
   p.bytes = p.off_spill;
   // spill: each region padded to whole 16-token tiles
   const size_t spill_rows = round_up((size_t)p.prefix_len, 16) + round_up((size_t)p.suffix_cap, 16);
-  if (p.tv || p.report) p.bytes += round_up((size_t)groups * spill_rows * p.group * 2 * sizeof(float), kAlign);
+  if (p.tv || p.report) p.bytes += round_up((size_t)groups * spill_rows * wg * 2 * sizeof(float), kAlign);
   if (p.report) {
     // c of every token-head, and the Tier B radius of every block and head
     p.off_rspill = p.bytes;
-    p.bytes += round_up((size_t)groups * spill_rows * p.group * sizeof(float), kAlign);
+    p.bytes += round_up((size_t)groups * spill_rows * wg * sizeof(float), kAlign);
     p.off_ublk = p.bytes;
-    p.bytes += round_up((size_t)groups * p.n_blocks * p.group * sizeof(float), kAlign);
+    p.bytes += round_up((size_t)groups * p.n_blocks * wg * sizeof(float), kAlign);
   }
   // Several chunks per group: the last work-group of a group would stream the
   // whole group's spill alone for the TV and the report; a finish launch
@@ -301,12 +323,12 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
       return KVQ_OK;
     }
     p.off_fin = p.bytes;
-    p.bytes += round_up((size_t)groups * p.group * 4 * sizeof(float), kAlign);
+    p.bytes += round_up((size_t)groups * wg * 4 * sizeof(float), kAlign);
     p.off_tvp = p.bytes;
-    p.bytes += round_up((size_t)groups * p.fin_ranges * p.group * sizeof(float), kAlign);
+    p.bytes += round_up((size_t)groups * p.fin_ranges * wg * sizeof(float), kAlign);
     if (p.report) {
       p.off_rkey = p.bytes;
-      p.bytes += round_up((size_t)groups * p.group * p.fin_blocks * sizeof(float), kAlign);
+      p.bytes += round_up((size_t)groups * wg * p.fin_blocks * sizeof(float), kAlign);
     }
   }
   return KVQ_OK;
@@ -347,7 +369,7 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   d.batch = a->batch;
   d.h_q = a->num_q_heads;
   d.h_kv = a->num_kv_heads;
-  d.group = p.group;
+  d.group = p.kgroup;
   d.qg = p.group;
   d.qh0 = 0;
   d.sm_scale = a->sm_scale;

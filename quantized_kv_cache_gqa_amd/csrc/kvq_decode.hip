@@ -586,9 +586,10 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         if (d.has_tier_b && i8 && ms > 0.0f)
           Eb = ms * expm1f(d.ublk[((size_t)grp * d.n_blocks + j) * G + h] * LN2);
         const size_t o = ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * d.n_blocks + j;
-        if (d.block_mass) d.block_mass[o] = ms;
-        if (d.block_excess) d.block_excess[o] = ex;
-        if (d.block_excess_b) d.block_excess_b[o] = Eb;
+        const bool hv = d.qh0 + h < d.qg;              // a query head (not a padding head)
+        if (d.block_mass && hv) d.block_mass[o] = ms;
+        if (d.block_excess && hv) d.block_excess[o] = ex;
+        if (d.block_excess_b && hv) d.block_excess_b[o] = Eb;
         if (d.block_order) st_dev(d.rkey + ((size_t)grp * G + h) * d.n_blocks + j, d.has_tier_b ? Eb : ex);
       }
     }
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
   if (do_tv && tid < G) {
     float sum = 0.0f;
     for (int q = 0; q < d.fin_ranges; ++q) sum += ld_dev(d.tvp + ((size_t)grp * d.fin_ranges + q) * G + tid);
-    d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * sum;
+    if (d.qh0 + tid < d.qg) d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * sum;
   }
   if (d.has_report && d.block_order) {               // rank = blocks ahead of j
     __shared__ float rkey_s[G][512];
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         const float kk = rkey_s[h][k];
         rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
       }
-      d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
+      if (d.qh0 + h < d.qg) d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
     }
   }
   if (tid == 0) __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

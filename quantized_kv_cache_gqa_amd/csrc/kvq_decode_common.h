@@ -194,9 +194,10 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         if (d.has_tier_b && i8 && ms > 0.0f)
           Eb = ms * expm1f(rd(d.ublk + ((size_t)grp * d.n_blocks + gb0 + j) * G + h) * LN2);
         const size_t o = ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * d.n_blocks + gb0 + j;
-        if (d.block_mass) d.block_mass[o] = ms;
-        if (d.block_excess) d.block_excess[o] = ex;
-        if (d.block_excess_b) d.block_excess_b[o] = Eb;
+        const bool hv = d.qh0 + h < d.qg;
+        if (d.block_mass && hv) d.block_mass[o] = ms;
+        if (d.block_excess && hv) d.block_excess[o] = ex;
+        if (d.block_excess_b && hv) d.block_excess_b[o] = Eb;
         if (d.block_order) rkey_s[h][gb0 + j] = d.has_tier_b ? Eb : ex;
       }
     }
@@ -212,7 +213,7 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         const float kk = rkey_s[h][k];
         rank += (kk > kj || (kk == kj && k < j)) ? 1 : 0;
       }
-      d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
+      if (d.qh0 + h < d.qg) d.block_order[((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h) * nbt + rank] = j;
     }
   }
 }
@@ -321,7 +322,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       o1 += rd(pc + 8 + 64 + lane) * fq;
     }
     const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
-    if (d.has_out) {
+    const bool hv = d.qh0 + h < d.qg;               // a query head (not a padding head)
+    if (d.has_out && hv) {
       const float inv = Zq > 0.0f ? 1.0f / Zq : 0.0f;
       d.out[qh * D + lane] = o0 * inv;
       d.out[qh * D + 64 + lane] = o1 * inv;
@@ -332,9 +334,9 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
       double bound = 0.5 * expm1(2.0 * log_a);
       const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
-      if (d.log_a) d.log_a[qh] = (float)log_a;
-      if (d.bound_raw) d.bound_raw[qh] = bf;
-      if (d.meter) d.meter[qh] = fminf(1.0f, bf);
+      if (d.log_a && hv) d.log_a[qh] = (float)log_a;
+      if (d.bound_raw && hv) d.bound_raw[qh] = bf;
+      if (d.meter && hv) d.meter[qh] = fminf(1.0f, bf);
       if (d.log_a_minus || d.bound_two_sided || d.meter_two_sided || d.bound_tanh) {
         // two-sided form (WitCert Prop. 1): 1/2 (A/A- - A-/A) = sinh(log A - log A-)
         double log_am = 0.0;
@@ -342,29 +344,29 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
           log_am = ((double)Mn - (double)Mq) * 0.69314718055994530942 + log((double)Zn) - log((double)Zq);
         const double two = sinh(log_a - log_am);
         const float tf = two > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)two;
-        if (d.log_a_minus) d.log_a_minus[qh] = (float)log_am;
-        if (d.bound_two_sided) d.bound_two_sided[qh] = tf;
-        if (d.meter_two_sided) d.meter_two_sided[qh] = fminf(fminf(1.0f, bf), tf);
+        if (d.log_a_minus && hv) d.log_a_minus[qh] = (float)log_am;
+        if (d.bound_two_sided && hv) d.bound_two_sided[qh] = tf;
+        if (d.meter_two_sided && hv) d.meter_two_sided[qh] = fminf(fminf(1.0f, bf), tf);
         // tanh shape: tanh(max_t c_t), c in natural units
-        if (d.bound_tanh) d.bound_tanh[qh] = (float)tanh((double)Cmax * 0.69314718055994530942);
+        if (d.bound_tanh && hv) d.bound_tanh[qh] = (float)tanh((double)Cmax * 0.69314718055994530942);
       }
       if (d.has_value) {
         // value side and the joint output bound (WitCert Sec. 3): the meter
         // bounds TV (0 when every region's keys are stored exactly)
         const float verr = Zq > 0.0f ? Zv / Zq : 0.0f;
         const float tvb = do_meter ? fminf(1.0f, bf) : 0.0f;
-        if (d.value_err) d.value_err[qh] = verr;
-        if (d.v_norm_max) d.v_norm_max[qh] = Vmax;
-        if (d.out_bound) d.out_bound[qh] = 2.0f * tvb * Vmax + verr;
+        if (d.value_err && hv) d.value_err[qh] = verr;
+        if (d.v_norm_max && hv) d.v_norm_max[qh] = Vmax;
+        if (d.out_bound && hv) d.out_bound[qh] = 2.0f * tvb * Vmax + verr;
       }
       if (d.has_tier_b) {
         // log A_B = log(sum p~ e^u / sum p~), both sums on the maximum M~
         const double log_ab = (Zq > 0.0f && Zb > 0.0f) ? log((double)Zb) - log((double)Zq) : 0.0;
         const double bb = 0.5 * expm1(2.0 * log_ab);
         const float bbf = bb > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bb;
-        if (d.log_a_b) d.log_a_b[qh] = (float)log_ab;
-        if (d.bound_b_raw) d.bound_b_raw[qh] = bbf;
-        if (d.meter_b) d.meter_b[qh] = fminf(1.0f, bbf);
+        if (d.log_a_b && hv) d.log_a_b[qh] = (float)log_ab;
+        if (d.bound_b_raw && hv) d.bound_b_raw[qh] = bbf;
+        if (d.meter_b && hv) d.meter_b[qh] = fminf(1.0f, bbf);
       }
       fin_s[h][0] = Mq;
       fin_s[h][1] = Zq > 0.0f ? 1.0f / Zq : 0.0f;
@@ -429,7 +431,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       float s = 0.0f;
       for (int t = 0; t < 256; ++t)                   // fixed order: bitwise reproducible
         if (((2 * t) % (4 * G)) / 4 == tid) s += tvpart_s[t];
-      d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * s;
+      if (d.qh0 + tid < d.qg) d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * s;
     }
   }
   if (d.has_report) block_report_pass<G>(d, grp, b, kvh, single, suf_len, fin_s);

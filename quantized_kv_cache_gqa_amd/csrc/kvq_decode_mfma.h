@@ -304,11 +304,13 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     tb_l = logf(2.0f * (float)(d.prefix_len + sl)) + d.tier_b_log_inv_delta;
   }
 
-  // ---- B operands of the logit contractions, column j16 = 4 hh + pp
+  // ---- B operands of the logit contractions, column j16 = 4 hh + pp (a
+  //      group of 1 or 2 query heads pads the tile with copies of its last
+  //      head, whose results are not written)
   bf16x8_t bq[4];
   f16x4_t bw;
   {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -364,7 +366,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
     if constexpr (I8K) {
       const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
-      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
+      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
       float ss = 0.0f;                             // sum of (q_c s_c)^2 in log2 units
 #pragma unroll
       for (int s8 = 0; s8 < 4; ++s8) {
@@ -413,7 +415,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bqo;
   const int n_op = R.n_op;
   if constexpr (GK) {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hh) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
     uint32_t bm0 = 0, bm1 = 0;                       // bypassed pairs 0..31, 32..63
     if (n_op > 0) {
       const int32_t *opp = R.opairs + (size_t)kvh * n_op;

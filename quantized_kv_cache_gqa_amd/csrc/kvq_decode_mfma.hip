@@ -228,6 +228,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   //    previous round's TV shares are requested first; the TV pass (4.)
   //    runs while they travel.
   const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
+  const bool hv = d.qh0 + h < d.qg;                 // a query head (not a padding head)
   // T >= 8: unit u = member, its batches of 8 members dealt to the 4
   // wavefronts in turn, partial sums added in wavefront order through LDS
   const bool split = T >= 8;
@@ -317,7 +318,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
         unit_s[h][lane] = o;
         if (!oku) bad_s = 1;
       } else {
-        d.out[qu * D + dim] = oku ? o * iZu : qnan;
+        if (d.qh0 + hu < d.qg) d.out[qu * D + dim] = oku ? o * iZu : qnan;
         ok = ok && oku;
       }
     }
@@ -327,7 +328,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
         const int hu = member >> 1, dim = 64 * (member & 1) + lane;
         const float o = ((unit_s[0][lane] + unit_s[1][lane]) + unit_s[2][lane]) + unit_s[3][lane];
         const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hu;
-        d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
+        if (d.qh0 + hu < d.qg) d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
       }
     }
   }
@@ -337,9 +338,9 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
       log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
     const double bound = 0.5 * expm1(2.0 * log_a);
     const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
-    if (d.log_a) d.log_a[qh] = ok ? (float)log_a : qnan;
-    if (d.bound_raw) d.bound_raw[qh] = ok ? bf : qnan;
-    if (d.meter) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
+    if (d.log_a && hv) d.log_a[qh] = ok ? (float)log_a : qnan;
+    if (d.bound_raw && hv) d.bound_raw[qh] = ok ? bf : qnan;
+    if (d.meter && hv) d.meter[qh] = ok ? fminf(1.0f, bf) : qnan;
     if constexpr (EXT) {                             // as the per-chunk finalize
       if (d.has_two_sided) {
         double log_am = 0.0;
@@ -347,17 +348,17 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
           log_am = ((double)Mn - (double)Mq) * 0.69314718055994530942 + log((double)Zn) - log((double)Zq);
         const double two = sinh(log_a - log_am);
         const float tf = two > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)two;
-        if (d.log_a_minus) d.log_a_minus[qh] = ok ? (float)log_am : qnan;
-        if (d.bound_two_sided) d.bound_two_sided[qh] = ok ? tf : qnan;
-        if (d.meter_two_sided) d.meter_two_sided[qh] = ok ? fminf(fminf(1.0f, bf), tf) : qnan;
-        if (d.bound_tanh) d.bound_tanh[qh] = ok ? (float)tanh((double)Cm * 0.69314718055994530942) : qnan;
+        if (d.log_a_minus && hv) d.log_a_minus[qh] = ok ? (float)log_am : qnan;
+        if (d.bound_two_sided && hv) d.bound_two_sided[qh] = ok ? tf : qnan;
+        if (d.meter_two_sided && hv) d.meter_two_sided[qh] = ok ? fminf(fminf(1.0f, bf), tf) : qnan;
+        if (d.bound_tanh && hv) d.bound_tanh[qh] = ok ? (float)tanh((double)Cm * 0.69314718055994530942) : qnan;
       }
       if (d.has_value) {
         const float verr = Zq > 0.0f ? Zv / Zq : 0.0f;
         const float tvb = do_meter ? fminf(1.0f, bf) : 0.0f;
-        if (d.value_err) d.value_err[qh] = ok ? verr : qnan;
-        if (d.v_norm_max) d.v_norm_max[qh] = ok ? Vm : qnan;
-        if (d.out_bound) d.out_bound[qh] = ok ? 2.0f * tvb * Vm + verr : qnan;
+        if (d.value_err && hv) d.value_err[qh] = ok ? verr : qnan;
+        if (d.v_norm_max && hv) d.v_norm_max[qh] = ok ? Vm : qnan;
+        if (d.out_bound && hv) d.out_bound[qh] = ok ? 2.0f * tvb * Vm + verr : qnan;
       }
     }
   }
@@ -373,7 +374,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     okp = __all(okp);
     const int pg = team + (round - 1) * d.n_teams;
     const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
-    if (lane == 0) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + d.qh0 + h] = okp ? 0.5f * sh : qnan;
+    if (lane == 0 && hv) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + d.qh0 + h] = okp ? 0.5f * sh : qnan;
   }
   if (!ok) bad_s = 1;
   __syncthreads();
@@ -394,7 +395,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     }
     sh = wave_sum_fixed(sh, T);
     okp = __all(okp) && bad_s == 0;
-    if (lane == 0) d.tv[qh] = okp ? 0.5f * sh : qnan;
+    if (lane == 0 && hv) d.tv[qh] = okp ? 0.5f * sh : qnan;
   }
   __syncthreads();                  // LDS buffers are reused by the next round
   __builtin_amdgcn_s_setprio(0);

@@ -711,3 +711,41 @@ def test_team_epoch_restarts_below_its_limit(gpu_lib, monkeypatch):
         for k in m_ref:
             assert torch.equal(m[k], m_ref[k]), k
         assert int(ctl[0]) == expect and int(ctl[1]) == 0
+
+
+def _gq(make, g):
+    def f():
+        cfg = make()
+        return dataclasses.replace(cfg, h_q=g * cfg.h_kv, name=cfg.name + f"-g{g}")
+    return f
+
+
+SMALL_GROUPS = {f"{name}-g{g}": (_gq(make, g), g) for g in (1, 2) for name, make in (
+    ("fp8", lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 1234))),
+    ("int8-dither", lambda: small_variant(INT8_DITHER_B8_S32K, batch=2, h_kv=2, suffix_len=1000, lens=(1000, 513))),
+    ("int8g32-paged-m4", lambda: _g32(paged=True)),
+    ("fp8-cartridge", lambda: _two_region_fp8(False)),
+)}
+
+
+@pytest.mark.parametrize("name", list(SMALL_GROUPS))
+def test_groups_of_one_and_two_every_cell(gpu_lib, kernel, name):
+    """1 or 2 query heads per KV head: on the matrix cores as a 4-head tile
+    padded with copies of the last head (library choice; the padding heads'
+    results are never written), or on the vector-ALU kernel; every cell
+    against the oracle with Tier A, the value side, the two-sided form and,
+    for INT8 keys, Tier B; the block report where the plan takes it."""
+    make, g = SMALL_GROUPS[name]
+    cfg = make()
+    m = 4 if "m4" in name else 0
+    case = GpuCase(cfg, page_seed=14, value_witness=True, n_outlier_pairs=m)
+    delta = 1e-4 if "int8" in name else None
+    out, mm, _ = _all_cells(case, tier_b_delta=delta, value_bound=True, two_sided=True)
+    assert out.shape[1] == cfg.h_q and mm["tv"].shape[1] == cfg.h_q
+    _all_cells(case, split_tokens=256)
+    if "g32" not in name:
+        _, mr = case.run(report=True)
+        for b in range(cfg.batch):
+            for kvh in range(cfg.h_kv):
+                _, ref = oracle_cell(case, b, kvh)
+                check_block_report(case, mr, b, kvh, ref, False)
