@@ -422,3 +422,20 @@ def test_group_of_eight_takes_two_launch_sets_on_the_matrix_cores(lib, monkeypat
     f32 = _args(batch=2, hq=32, hkv=4, suffix=4096)
     f32.suffix.k_exact_format = 3                                 # fp32 exact keys: vector ALUs
     assert _plan(lib, f32, m).launches == g4.launches
+
+
+def test_groups_of_one_and_two_plan_the_padded_tile(lib, monkeypatch):
+    """1 or 2 query heads per KV head on matrix-core formats: the per-chunk
+    workspace is sized for the 4-head tile (as for a group of 4 with the same
+    KV heads); on the vector-ALU kernel it is sized for the group itself."""
+    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    g4 = _plan(lib, _args(batch=4, hq=32, hkv=8, suffix=4096), m)
+    for hq in (8, 16):
+        padded = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096), m)
+        assert (padded.workspace_bytes, padded.launches) == (g4.workspace_bytes, g4.launches), hq
+        monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
+        own = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096), m)
+        monkeypatch.delenv("KVQ_DECODE_KERNEL")
+        assert own.workspace_bytes < padded.workspace_bytes, hq
