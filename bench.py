@@ -355,7 +355,9 @@ def main():
     if args.outlier_pairs and args.int8_scales != "group":
         sys.exit("--outlier-pairs needs --int8-scales group (the pairs sit beside group-scale keys)")
     if args.workload != 0:
-        measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 1),
+        # at least 30 untimed launches first: the clocks settle over some
+        # milliseconds, longer than a few sub-millisecond launches take
+        measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 30),
                          group_scales=args.int8_scales == "group", n_pairs=args.outlier_pairs)
         return
     import numpy as np
