@@ -749,3 +749,30 @@ def test_groups_of_one_and_two_every_cell(gpu_lib, kernel, name):
             for kvh in range(cfg.h_kv):
                 _, ref = oracle_cell(case, b, kvh)
                 check_block_report(case, mr, b, kvh, ref, False)
+
+
+def test_group_scale_append_matches_a_whole_write(gpu_lib):
+    """The per-token group-scale format is written token by token (paging-safe,
+    WitCert Sec. 6.2.3): appending the newest tokens one call at a time, at
+    any position, stores the same codes, scales, witness, value records and
+    outlier values as one call over the whole range; and the meter-only call
+    gives the decode call's meter bitwise."""
+    from quantized_kv_cache_gqa_amd import kvq
+    cfg = _g32()
+    case = GpuCase(cfg, page_seed=15, value_witness=True, n_outlier_pairs=4)
+    st = case.suffix_store
+    kin, vin = case.inp["suffix_k"], case.inp["suffix_v"]
+    op = torch.from_numpy(case.opairs).to("cuda")
+    inc = kvq.alloc_stored(cfg.batch, cfg.h_kv, cfg.suffix.length, "int8g32", "int8g32", True, "cuda",
+                           value_witness=True, outlier_pairs=op)
+    from cells import dither_seed
+    cuts = [0, 1, 17, 300, 301, cfg.suffix.length - 1, cfg.suffix.length]
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        kvq.quantize_into(inc, kin, vin, tok_begin=t0, tok_end=t1, seed=dither_seed(cfg), layer=0, stream_id=0)
+    torch.cuda.synchronize()
+    for name in ("k", "v", "k_scale", "v_scale", "witness", "v_witness", "k_outliers"):
+        assert torch.equal(getattr(inc, name), getattr(st, name)), name
+    out, m = case.run()
+    _, mo = case.run(meter_only=True)
+    for k in mo:
+        assert torch.equal(mo[k], m[k]), k
