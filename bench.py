@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--outlier-pairs", type=int, default=0, metavar="M",
                     help="with --int8-scales group: M fixed outlier RoPE pairs per KV head kept "
                          "exactly beside the keys (the workload's heavy pairs first)")
+    ap.add_argument("--q-heads", type=int, default=0, metavar="H",
+                    help="with --workload: H query heads instead of the workload's own (GQA group "
+                         "H / KV heads: 1, 2, 4 or 8)")
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=0, help="debug: fewer layers (0 = all)")
@@ -166,7 +169,8 @@ def _oracle_slice(lb):
     return time.perf_counter() - t
 
 
-def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False, n_pairs: int = 0):
+def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False, n_pairs: int = 0,
+                     q_heads: int = 0):
     """One layer of workload `idx`: stage its caches through kvq_quantize, then
     time kvq_decode_attn (with TV, log A, bound and meter where the workload
     has exact keys and a witness) with HIP events on the launch stream."""
@@ -182,6 +186,8 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
             sub = {"int8": "int8g32"}
             return dataclasses.replace(r, k_fmt=sub.get(r.k_fmt, r.k_fmt), v_fmt=sub.get(r.v_fmt, r.v_fmt))
         cfg = dataclasses.replace(cfg, prefix=g32(cfg.prefix), suffix=g32(cfg.suffix))
+    if q_heads:
+        cfg = dataclasses.replace(cfg, h_q=q_heads)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lib = kvq.load()
@@ -332,7 +338,8 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
             "per-(256-token block, channel) fp16 scales",
             "per-(token, 32-channel group) fp16 scales" if group_scales else
             "per-(256-token block, channel) fp16 scales")
-        + (f", {n_pairs} fixed outlier RoPE pairs per KV head kept in bf16" if n_pairs else ""),
+        + (f", {n_pairs} fixed outlier RoPE pairs per KV head kept in bf16" if n_pairs else "")
+        + (f", {q_heads} query heads (GQA group {q_heads // cfg.h_kv})" if q_heads else ""),
         "measure": "one layer's kvq_decode_attn launch (median of HIP-event pairs on the launch stream)",
         "launch_ms": med, "min_ms": ms[0], "reps": reps, "bytes_per_launch": bytes_launch,
         "meter_off_launch_ms": off_ms, "with_tier_b_launch_ms": tier_b_ms,
@@ -358,7 +365,8 @@ def main():
         # at least 30 untimed launches first: the clocks settle over some
         # milliseconds, longer than a few sub-millisecond launches take
         measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 30),
-                         group_scales=args.int8_scales == "group", n_pairs=args.outlier_pairs)
+                         group_scales=args.int8_scales == "group", n_pairs=args.outlier_pairs,
+                         q_heads=args.q_heads)
         return
     import numpy as np
     import torch
