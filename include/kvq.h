@@ -289,8 +289,11 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    pairs in `rounds` rounds.  Chosen when the TV is requested for a single
  *    region of at most 131,072 tokens with GQA group 4 or 8, FP8/BF16 keys
  *    and values and bf16 exact keys, split_tokens 0, and neither Tier B nor
- *    the block report.  A group of 8 runs as two such launches of 4 query
- *    heads each (as does the per-chunk plan where its kernels allow).  Members wait only
+ *    the block report.  A group of 8 runs in one launch whose teams come in
+ *    pairs, one raw team per 4 query heads (grid = 2 * n_teams * team,
+ *    rounded up to a multiple of 8), so each tile is fetched from HBM about
+ *    once; the per-chunk plan runs it as two launches of 4 query heads each
+ *    where its kernels allow, each reading the cache.  Members wait only
  *    for members of their own team, with a bounded wait: a wait that runs
  *    out (another kernel holding the device for longer) leaves NaN in that
  *    (request, KV head)'s results, never a hang.
@@ -315,7 +318,8 @@ typedef struct kvq_plan_info {
                                two regions' formats need separate kernels; one
                                more when a per-chunk plan with several chunks
                                per (request, KV head) runs the TV and the block
-                               report in a finish launch over many work-groups */
+                               report in a finish launch over many work-groups;
+                               a per-chunk plan of a group of 8 doubles all that */
   int32_t reserved;         /* 0 */
   uint64_t workspace_bytes;
 } kvq_plan_info;

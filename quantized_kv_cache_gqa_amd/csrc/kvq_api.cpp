@@ -47,6 +47,7 @@ struct Plan {
   int fin_blocks = 0, fin_ranges = 0;
   size_t off_fin = 0, off_tvp = 0, off_rkey = 0;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
+  int halves = 1;               // team launch of a group of 8: 2 = pairs of raw teams in one launch
   size_t off_counters = 0, off_partials = 0, off_spill = 0, off_rspill = 0, off_ublk = 0, bytes = 0;
 };
 
@@ -71,7 +72,8 @@ bool env_is(const char *name, char c) {
 // 256 tokens).  Returns false when no team launch applies.
 bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  // (a group of 8 runs as two team launches of 4 query heads each)
+  // A group of 8 runs as one launch of paired raw teams of 4 query heads each
+  // (KVQ_TEAM_HALVES=0: two launches, one per 4 heads, each reading the cache).
   if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || (p.kgroup != 4 && p.group != 8)) return false;
   if (p.group == 8 && env_is("KVQ_DECODE_KERNEL", 'g')) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
@@ -92,12 +94,15 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
                            team_capacity(r.k_format, vf_dec, paged, full, ext));
   (void)vf;
   if (cap <= 0) return false;
+  const int hv = (p.group == 8 && !env_is("KVQ_TEAM_HALVES", '0')) ? 2 : 1;
+  const int capg = cap / hv;                       // resident work-groups per logical team slot
+  if (capg <= 0) return false;
   const int64_t len = r.length;
   const int64_t tmin = (len + TEAM_MAX_CHUNK - 1) / TEAM_MAX_CHUNK;
-  const int64_t tmax = std::min<int64_t>(std::min<int64_t>(cap, TEAM_MAX), (len + 63) / 64);
+  const int64_t tmax = std::min<int64_t>(std::min<int64_t>(capg, TEAM_MAX), (len + 63) / 64);
   int64_t best_cost = -1;
   for (int64_t T = tmin; T <= tmax; ++T) {
-    const int64_t n_teams = std::min<int64_t>(cap / T, groups);
+    const int64_t n_teams = std::min<int64_t>(capg / T, groups);
     if (n_teams <= 0) break;
     const int64_t rounds = (groups + n_teams - 1) / n_teams;
     const int64_t chunk = ((len + T - 1) / T + 15) / 16 * 16;      // whole tiles
@@ -111,8 +116,9 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   }
   if (p.team <= 0) return false;
   // the grid is padded to whole XCD slices (8) and must stay resident
-  while (p.n_teams > 1 && (int64_t)round_up((size_t)p.n_teams * p.team, 8) > cap) --p.n_teams;
-  p.grid = (int)round_up((size_t)p.n_teams * p.team, 8);
+  while (p.n_teams > 1 && (int64_t)round_up((size_t)p.n_teams * hv * p.team, 8) > cap) --p.n_teams;
+  p.grid = (int)round_up((size_t)p.n_teams * hv * p.team, 8);
+  p.halves = hv;
   if (p.grid > cap) {
     p.team = 0;
     return false;
@@ -123,7 +129,7 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   p.rounds = (groups + p.n_teams - 1) / p.n_teams;
   p.off_counters = kCtlBytes;
   p.off_partials = kCtlBytes + kCounterBytes;
-  p.off_spill = p.off_partials + round_up((size_t)p.n_teams * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
+  p.off_spill = p.off_partials + round_up((size_t)p.n_teams * hv * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
   p.bytes = p.off_spill;
   return true;
 }
@@ -512,7 +518,11 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     // publishes, so the others' waits run out and the results turn to NaN).
     d.spin_limit = env_uint("KVQ_TEAM_SPIN_LIMIT", 1u << 18, 1);
     d.silent_member = (int)env_uint("KVQ_TEAM_SILENT_MEMBER", 0xffffffffu, 0);
-    if (p.group == 8) {                             // two launches of 4 query heads
+    if (p.group == 8 && p.halves == 2) {           // one launch, paired raw teams of 4 heads
+      make_half(d, 0);
+      d.halves = 2;
+      e = launch_decode_team(d, p.grid, stream);
+    } else if (p.group == 8) {                      // two launches of 4 query heads
       for (int half = 0; half < 2 && e == hipSuccess; ++half) {
         DecodeLaunch hd = d;
         make_half(hd, half);
@@ -625,7 +635,7 @@ kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int m
   info->chunks = p.total_chunks;
   info->workspace_bytes = p.bytes;
   if (p.team) {
-    info->launches = p.group == 8 ? 2 : 1;
+    info->launches = (p.group == 8 && p.halves != 2) ? 2 : 1;
   } else {
     DecodeLaunch d, dp, ds;
     chunk_launches(a, m, p, meter_only != 0, nullptr, d, dp, ds);

@@ -267,7 +267,7 @@ struct TileSrc {
 // compiled in (they are tested at run time); without it the tile loop has
 // none of their code.
 template <int KF, int VF, bool PAGED, bool FULL, bool SPILL_LDS, bool EXT = false>
-__device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh, int grp, int c0,
+__device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh, int grp, int qh0, int c0,
                                            int c1, float2 *spill_s, float (*w_s)[64],
                                            float (*part_s)[4][PART_STRIDE]) {
   constexpr int G = 4;
@@ -310,7 +310,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bq[4];
   f16x4_t bw;
   {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -366,7 +366,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
     if constexpr (I8K) {
       const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
-      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
+      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
       float ss = 0.0f;                             // sum of (q_c s_c)^2 in log2 units
 #pragma unroll
       for (int s8 = 0; s8 < 4; ++s8) {
@@ -415,7 +415,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bqo;
   const int n_op = R.n_op;
   if constexpr (GK) {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(d.qh0 + hh, d.qg - 1)) * D;
+    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
     uint32_t bm0 = 0, bm1 = 0;                       // bypassed pairs 0..31, 32..63
     if (n_op > 0) {
       const int32_t *opp = R.opairs + (size_t)kvh * n_op;
@@ -851,7 +851,7 @@ __device__ __forceinline__ void chunk_work(const DecodeLaunch &d, int grp, int c
   const int len = R.is_prefix ? R.length : (R.lengths ? min(max(R.lengths[b], 0), R.length) : R.length);
   const int c0 = chunk_idx * d.chunk;
   const int c1 = min(c0 + d.chunk, len);
-  mfma_chunk<KF, VF, PAGED, FULL, false, EXT>(d, b, kvh, grp, c0, c1, nullptr, w_s, part_s);
+  mfma_chunk<KF, VF, PAGED, FULL, false, EXT>(d, b, kvh, grp, d.qh0, c0, c1, nullptr, w_s, part_s);
   chunk_epilogue<4>(d, part_s, grp, chunk_idx, b, kvh);
 }
 

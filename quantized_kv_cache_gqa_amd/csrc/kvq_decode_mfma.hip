@@ -104,8 +104,8 @@ __device__ __forceinline__ float wave_sum_fixed(float x, int n) {
 // the exchange: z_v merges like Z~, (M-, Z-) like (M, Z), the maxima by max.
 template <bool EXT>
 __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t epoch, float (*part_s)[4][PART_STRIDE],
-                              const float2 *spill_s, int team, int member, int round,
-                              bool last_round, int b, int kvh, int c0, int c1) {
+                              const float2 *spill_s, int team, int slot_team, int qh0, int member,
+                              int round, bool last_round, int b, int kvh, int c0, int c1) {
   constexpr int G = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -116,7 +116,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   // co-resident work-group's streaming waves (wave priority only)
   __builtin_amdgcn_s_setprio(1);
   const uint32_t tag = epoch + (uint32_t)round + 1u;
-  uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(team * 2 + (round & 1)) * T * SLOT_WORDS;
+  uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(slot_team * 2 + (round & 1)) * T * SLOT_WORDS;
   uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
   __shared__ float mq_s[G][64];
   __shared__ float unit_s[WAVES][64];
@@ -227,8 +227,8 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   //    The first batch of accumulator words of this wavefront and the
   //    previous round's TV shares are requested first; the TV pass (4.)
   //    runs while they travel.
-  const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
-  const bool hv = d.qh0 + h < d.qg;                 // a query head (not a padding head)
+  const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + qh0 + h;
+  const bool hv = qh0 + h < d.qg;                 // a query head (not a padding head)
   // T >= 8: unit u = member, its batches of 8 members dealt to the 4
   // wavefronts in turn, partial sums added in wavefront order through LDS
   const bool split = T >= 8;
@@ -250,7 +250,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   const bool tv_duty = do_tv && d.tv && member == (h + 4) % T;
   // shares of round - 1 sit in the other parity's slots
   const uint64_t *prev_tv = reinterpret_cast<const uint64_t *>(d.partials) +
-                            (size_t)(team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS +
+                            (size_t)(slot_team * 2 + ((round - 1) & 1)) * T * SLOT_WORDS +
                             (size_t)min(lane, T - 1) * SLOT_WORDS + SLOT_TV + h;
   uint64_t pre_tv[1] = {0};
   if (tv_duty && round > 0 && lane < T) pre_tv[0] = ld_tagged(prev_tv);
@@ -313,12 +313,12 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
         for (int i = 0; i < 8; ++i)
           if (cb + i < T) o += v[i] * merge_factor(mq_s[hu][cb + i], Mu);
       }
-      const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hu;
+      const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + qh0 + hu;
       if (split) {
         unit_s[h][lane] = o;
         if (!oku) bad_s = 1;
       } else {
-        if (d.qh0 + hu < d.qg) d.out[qu * D + dim] = oku ? o * iZu : qnan;
+        if (qh0 + hu < d.qg) d.out[qu * D + dim] = oku ? o * iZu : qnan;
         ok = ok && oku;
       }
     }
@@ -327,8 +327,8 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
       if (h == 0) {
         const int hu = member >> 1, dim = 64 * (member & 1) + lane;
         const float o = ((unit_s[0][lane] + unit_s[1][lane]) + unit_s[2][lane]) + unit_s[3][lane];
-        const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + hu;
-        if (d.qh0 + hu < d.qg) d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
+        const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + qh0 + hu;
+        if (qh0 + hu < d.qg) d.out[qu * D + dim] = bad_s == 0 ? o * fin_s[hu][1] : qnan;
       }
     }
   }
@@ -374,7 +374,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     okp = __all(okp);
     const int pg = team + (round - 1) * d.n_teams;
     const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
-    if (lane == 0 && hv) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + d.qh0 + h] = okp ? 0.5f * sh : qnan;
+    if (lane == 0 && hv) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + qh0 + h] = okp ? 0.5f * sh : qnan;
   }
   if (!ok) bad_s = 1;
   __syncthreads();
@@ -409,7 +409,13 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
   const int T = d.team;
   const unsigned per_xcd = gridDim.x >> 3;
   const unsigned L = (blockIdx.x & 7u) * per_xcd + (blockIdx.x >> 3);
-  const int team = (int)(L / (unsigned)T), member = (int)(L % (unsigned)T);
+  const int rt = (int)(L / (unsigned)T), member = (int)(L % (unsigned)T);
+  // A group of 8 query heads: raw teams 2t and 2t + 1 (neighbours in L, so on
+  // one XCD) take heads 0-3 and 4-7 of team t's groups in step, and the second
+  // read of each tile is served by the caches rather than HBM.
+  const bool pairs = d.halves == 2;
+  const int team = pairs ? rt >> 1 : rt;
+  const int qh0 = d.qh0 + (pairs ? 4 * (rt & 1) : 0);
   const int groups = d.batch * d.h_kv;
   const RegionDev &R = d.region;
   // this launch's epoch, kept in the workspace: round r's tag is epoch + r + 1
@@ -426,9 +432,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
     const int c1 = min(c0 + d.chunk, len);
     // (the next round's first tile is not loaded ahead: its loads would sit
     // ahead of the exchange's polls in the in-order load counter)
-    mfma_chunk<KF, VF, PAGED, FULL, true, EXT>(d, b, kvh, grp, c0, c1, spill_s, w_s, part_s);
-    team_epilogue<EXT>(d, epoch, part_s, spill_s, team, member, round, grp + d.n_teams >= groups, b, kvh,
-                       c0, c1);
+    mfma_chunk<KF, VF, PAGED, FULL, true, EXT>(d, b, kvh, grp, qh0, c0, c1, spill_s, w_s, part_s);
+    team_epilogue<EXT>(d, epoch, part_s, spill_s, team, rt, qh0, member, round, grp + d.n_teams >= groups,
+                       b, kvh, c0, c1);
   }
   // Every work-group counts itself out after reading the epoch; the last one
   // moves the epoch past all of this launch's tags and rearms the count, so

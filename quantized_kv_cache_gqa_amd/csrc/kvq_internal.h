@@ -93,6 +93,8 @@ struct DecodeLaunch {
   float *spill;
   int team;                     // > 0: team launch, work-groups per (request, KV head)
   int n_teams;                  // teams in the grid
+  int halves;                   // team launch: 2 when a group of 8 runs as pairs of raw teams
+                                // (raw team 2t + h takes query heads 4h..4h+3 of team t's groups)
   // deferred finalize (per-chunk plan, several chunks per group): the
   // finalizer publishes the normalizers (M~, 1/Z~, M_e, 1/Z_e per head) and a
   // finish launch runs the TV and the block report over FIN_BLOCKS-block ranges

@@ -661,16 +661,19 @@ GROUP8 = {
 
 @pytest.mark.parametrize("name", list(GROUP8))
 def test_group_of_eight_every_cell(gpu_lib, kernel, name):
-    """GQA groups of 8: on the matrix cores as two launch sets of 4 query
-    heads (library choice), or on the vector-ALU kernel; every cell against
-    the oracle with Tier A, the value side, the two-sided form and, for INT8
-    keys, Tier B; the block report where the plan takes it."""
+    """GQA groups of 8: on the matrix cores as one team launch of paired
+    4-head teams, or as two per-chunk launch sets of 4 query heads, or on the
+    vector-ALU kernel; every cell against the oracle with Tier A, the value
+    side, the two-sided form and, for INT8 keys, Tier B; the block report
+    where the plan takes it."""
     cfg = GROUP8[name]()
     m = 4 if name.endswith("m4") else 0
     case = GpuCase(cfg, page_seed=13, value_witness=True, n_outlier_pairs=m)
     delta = 1e-4 if "int8" in name else None
     p = plan(case, tier_b_delta=delta, value_bound=True, two_sided=True)
-    if kernel != "generic":
+    if p["team"]:
+        assert p["launches"] == 1 and p["grid"] >= 2 * p["team"] * p["n_teams"], p
+    elif kernel != "generic":
         assert p["launches"] % 2 == 0, p                 # two sets of launches
     _all_cells(case, tier_b_delta=delta, value_bound=True, two_sided=True)
     _all_cells(case, split_tokens=256)
@@ -680,6 +683,41 @@ def test_group_of_eight_every_cell(gpu_lib, kernel, name):
             for kvh in range(cfg.h_kv):
                 _, ref = oracle_cell(case, b, kvh)
                 check_block_report(case, mr, b, kvh, ref, False)
+
+
+def test_group_of_eight_team_pairs_against_two_launches(gpu_lib, monkeypatch):
+    """A group of 8 on the team plan: one launch whose raw teams 2t and 2t + 1
+    take query heads 0-3 and 4-7, on a shape with several rounds, ragged
+    requests, the value side and the two-sided form; sampled cells against the
+    oracle, bitwise repeatable, and within rounding of two launches of 4 heads
+    (KVQ_TEAM_HALVES=0, whose plan has its own team size and chunk)."""
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
+    lens = tuple(3000 - 61 * i for i in range(40))
+    cfg = _g8(lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=40, h_kv=8, suffix_len=3000, lens=lens))()
+    case = GpuCase(cfg, value_witness=True)
+    kw = dict(value_bound=True, two_sided=True)
+    p = _team_plan(case, monkeypatch)
+    assert p["rounds"] >= 3, p
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    pe = plan(case, **kw)
+    assert pe["team"] and pe["launches"] == 1, pe
+    assert pe["grid"] >= 2 * pe["team"] * pe["n_teams"] and pe["grid"] % 8 == 0, pe
+    o1, m1, _ = _all_cells(case, cells=[(0, 0), (13, 7), (39, 3), (39, 0)], **kw)
+    o1b, m1b = case.run(**kw)
+    assert torch.equal(o1, o1b)
+    monkeypatch.setenv("KVQ_TEAM_HALVES", "0")
+    q = plan(case, **kw)
+    assert q["team"] and q["launches"] == 2, q
+    o2, m2 = case.run(**kw)
+    # the same bars as against the oracle: rows within 2e-3 of their norm,
+    # meter fields within 1e-5
+    rel = (o1 - o2).norm(dim=-1) / o2.norm(dim=-1).clamp_min(1e-30)
+    assert rel.max().item() <= 2e-3, rel.max().item()
+    for k in m1:
+        if m1[k] is not None:
+            assert torch.equal(m1[k], m1b[k]), k
+            torch.testing.assert_close(m1[k], m2[k], rtol=1e-5, atol=1e-5, msg=k)
 
 
 def test_team_epoch_restarts_below_its_limit(gpu_lib, monkeypatch):
