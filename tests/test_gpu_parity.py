@@ -287,17 +287,23 @@ def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
     _all_cells(case, value_bound=True, two_sided=True)
 
 
-def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch):
+@pytest.mark.parametrize("group", [4, 8])
+def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch, group):
     """A call captured into a graph keeps the team plan: the launch takes its
     tags from the epoch in the workspace, which every launch advances on the
     device.  Every replay equals the eager team result bit for bit, with
     eager team calls on the same workspace between the replays; a
-    per-chunk call on that workspace between them changes nothing either."""
+    per-chunk call on that workspace between them changes nothing either.
+    A group of 8 captures its one launch of paired 4-head teams."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
     from quantized_kv_cache_gqa_amd import kvq
-    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    make = lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    cfg = make() if group == 4 else _g8(make)()
     case = GpuCase(cfg)
-    _team_plan(case, monkeypatch)
+    p = _team_plan(case, monkeypatch)
+    if group == 8:
+        assert p["launches"] == 1 and p["grid"] >= 2 * p["team"] * p["n_teams"], p
     ws = kvq.Workspace(torch.device("cuda"))
 
     def call(out=None, meter_bufs=None):
