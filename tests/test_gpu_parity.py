@@ -257,13 +257,17 @@ def test_team_several_rounds_sampled_cells(gpu_lib, monkeypatch):
         assert torch.equal(m1[k], m2[k]), k
 
 
-def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch):
+@pytest.mark.parametrize("group", [4, 8])
+def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch, group):
     """Fault injected from the host: one member of every team never publishes
     and the wait budget is small.  The launch still ends promptly, every
     result of the affected groups is NaN (never a stale or partial value),
-    and the next call without the hooks is correct again."""
+    and the next call without the hooks is correct again.  A group of 8 runs
+    its paired 4-head teams in one launch."""
     monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
+    make = lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
+    cfg = make() if group == 4 else _g8(make)()
     case = GpuCase(cfg, value_witness=True)
     p = _team_plan(case, monkeypatch)
     assert p["team"] >= 2, p
