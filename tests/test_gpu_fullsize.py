@@ -93,3 +93,36 @@ def test_full_size_group_scales_and_outlier_pairs_sampled_cells(gpu_lib, pairs):
     print(f"[{cfg.name} layer {layer}] sampled={len(SAMPLES[4])} worst={worst}", flush=True)
     del case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("q_heads", [8, 64])
+def test_full_size_gqa_groups_sampled_cells(gpu_lib, monkeypatch, q_heads):
+    """The batch-64 x 12,628-token FP8 workload with 8 or 64 query heads over
+    its 8 KV heads (GQA groups 1 and 8), in the launch the library plans for
+    it: the 4-head tile padded with copies of the last head, or paired 4-head
+    teams in one launch.  Sampled cells against the oracle."""
+    import dataclasses
+    from cells import plan
+    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
+    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
+    base = CONFIGS[3]
+    cfg = dataclasses.replace(base, h_q=q_heads, name=base.name + f"-hq{q_heads}")
+    layer = cfg.layers - 1
+    case = GpuCase(cfg, layer=layer, page_seed=1)
+    p = plan(case)
+    if q_heads == 64 and p["team"]:
+        assert p["launches"] == 1 and p["grid"] >= 2 * p["team"] * p["n_teams"], p
+    out, m = case.run()
+    worst = {}
+    for b, kvh in SAMPLES[3]:
+        encs, ref = oracle_cell(case, b, kvh)
+        check_stored(case, b, kvh, encs)
+        w = check_results(case, out, m, b, kvh, ref)
+        for k, v in w.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    assert torch.all(m["tv"] <= m["bound_raw"] + 1e-6)
+    assert torch.all(torch.isfinite(out))
+    print(f"[{cfg.name} layer {layer}] plan={p} sampled={len(SAMPLES[3])} worst={worst}", flush=True)
+    del case
+    torch.cuda.empty_cache()
