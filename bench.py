@@ -361,6 +361,11 @@ def main():
         sys.exit(2)
     if args.outlier_pairs and args.int8_scales != "group":
         sys.exit("--outlier-pairs needs --int8-scales group (the pairs sit beside group-scale keys)")
+    if args.q_heads:
+        from workloads import CONFIGS
+        h_kv = CONFIGS[args.workload].h_kv if args.workload else 0
+        if not h_kv or args.q_heads % h_kv or args.q_heads // h_kv not in (1, 2, 4, 8):
+            sys.exit("--q-heads needs --workload and 1, 2, 4 or 8 query heads per KV head")
     if args.workload != 0:
         # at least 30 untimed launches first: the clocks settle over some
         # milliseconds, longer than a few sub-millisecond launches take

@@ -58,3 +58,16 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bench_rejects_a_gqa_group_the_kernels_do_not_take():
+    """--q-heads must give 1, 2, 4 or 8 query heads per KV head of the
+    workload; the check runs before any device work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for extra in (["--workload", "3", "--q-heads", "24"], ["--workload", "3", "--q-heads", "12"],
+                  ["--q-heads", "64"]):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + extra, capture_output=True,
+                           text=True, timeout=300)
+        assert r.returncode == 1 and "--q-heads needs" in r.stderr, (extra, r.stderr[-300:])
