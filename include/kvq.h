@@ -309,8 +309,8 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  * more (it covers the per-chunk plan of the same arguments too). */
 typedef struct kvq_plan_info {
   int32_t team;             /* work-groups per (request, KV head); 0: no team launch */
-  int32_t n_teams;
-  int32_t rounds;
+  int32_t n_teams;          /* teams; a group of 8 runs two raw teams (4 query heads each) per team */
+  int32_t rounds;           /* (request, KV head) pairs each team takes in turn */
   int32_t grid;             /* work-groups of the team launch */
   int32_t chunk;            /* tokens per chunk */
   int32_t chunks;           /* chunks per (request, KV head), both regions */
