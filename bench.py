@@ -127,7 +127,7 @@ def cpu_baseline(cfg, budget_s: float):
             done += len(batch)
     kv_tokens = done * cfg.suffix.length                         # one token of one layer, all KV heads
     return dict(value=kv_tokens * n_workers / busy, unit="KV tokens/s", cores=n_workers,
-                kind="oracle",
+                kind="oracle", cpu=cpu_model(),
                 sample=f"{done} (layer, request) slices x {cfg.h_kv} KV heads x {cfg.suffix.length} "
                        f"tokens: newest-token write + decode with TV and bound in fp64; "
                        f"{busy:.1f} s of oracle time over {n_workers} single-threaded workers")
@@ -169,8 +169,132 @@ def _oracle_slice(lb):
     return time.perf_counter() - t
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# cells of the batch-64 step compared with the oracle after timing
+# (layer, request, KV head): first and last layer, corners and inner cells
+CHECK_CELLS = [(0, 0, 0), (17, 31, 3), (35, 63, 7), (35, 5, 2)]
+
+
+def validate_step(cfg, L, layers, out, mbuf, status):
+    """The last timed step's results: finite outputs, TV <= bound_raw on every
+    (layer, request, query head), the status word clear, and a few cells
+    against the oracle (attention output within 2e-3 of its norm, TV and
+    bound within 1e-5).  Raises on any failure."""
+    import numpy as np
+    import torch
+    from oracle.pipeline import RegionSpec, decode_cell, encode_region
+    torch.cuda.synchronize()
+    st = int(status[0].item())
+    if st != 0:
+        raise RuntimeError(f"status word {st:#x}: a team wait ran out during the timed steps")
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("non-finite attention output in the timed step")
+    for k in ("tv", "bound_raw", "meter", "log_a"):
+        if not bool(torch.isfinite(mbuf[k]).all()):
+            raise RuntimeError(f"non-finite {k} in the timed step")
+    if not bool((mbuf["tv"] <= mbuf["bound_raw"] + 1e-6).all()):
+        raise RuntimeError("TV above its bound in the timed step")
+    G = cfg.group
+    sm = float(np.float32(128 ** -0.5))
+    worst = dict(out_rel=0.0, tv=0.0, bound=0.0)
+    n = 0
+    for layer, b, kvh in CHECK_CELLS:
+        if layer >= L:
+            continue
+        Ld = layers[layer]
+        q = Ld["q"][b, kvh * G:(kvh + 1) * G].double().cpu().numpy()
+        k = Ld["k"][b, kvh].double().cpu().numpy()
+        v = Ld["v"][b, kvh].double().cpu().numpy()
+        spec = RegionSpec("fp8", "fp8", layer=layer, stream=b)
+        ref = decode_cell(q, [(k, encode_region(k, v, spec, kvh), spec)], sm)
+        for h in range(G):
+            qh = kvh * G + h
+            og = out[layer, b, qh].double().cpu().numpy()
+            rel = float(np.linalg.norm(og - ref["out"][h]) / np.linalg.norm(ref["out"][h]))
+            tv_err = abs(float(mbuf["tv"][layer, b, qh]) - float(ref["tv"][h]))
+            br = float(ref["bound_raw"][h])
+            b_err = abs(float(mbuf["bound_raw"][layer, b, qh]) - br) / max(1.0, br)
+            if rel > 2e-3 or tv_err > 1e-5 or b_err > 1e-5:
+                raise RuntimeError(f"cell (layer {layer}, request {b}, query head {qh}) off the oracle: "
+                                   f"out {rel:.2e}, tv {tv_err:.2e}, bound {b_err:.2e}")
+            worst = dict(out_rel=max(worst["out_rel"], rel), tv=max(worst["tv"], tv_err),
+                         bound=max(worst["bound"], b_err))
+        n += 1
+    return {"finite": True, "tv_le_bound_all": int(mbuf["tv"].numel()), "status": st,
+            "oracle_cells": n, "worst_vs_oracle": worst}
+
+
+def workload_cpu_baseline(cfg, budget_s: float):
+    """The oracle on whole (request, KV head) cells of one layer of a workload,
+    run in a spawn pool like cpu_baseline, until about budget_s is used;
+    KV tokens/s = cells' tokens x the workers / their oracle time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    n_workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    cells = [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
+    done, busy, toks = 0, 0.0, 0
+    with cf.ProcessPoolExecutor(max_workers=n_workers, mp_context=ctx, initializer=_pool_init) as ex:
+        list(ex.map(_oracle_warm, range(n_workers)))
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < budget_s and i < len(cells):
+            batch = cells[i:i + n_workers]
+            i += len(batch)
+            for sec, nt in ex.map(_oracle_cell_time, [(cfg.index, b, h) for b, h in batch]):
+                busy += sec
+                toks += nt
+            done += len(batch)
+    per_kvh = toks / cfg.h_kv                       # one token of one layer with all its KV heads
+    return dict(value=per_kvh * n_workers / busy, unit="KV tokens/s", cores=n_workers, kind="oracle",
+                cpu=cpu_model(),
+                sample=f"{done} of {len(cells)} (request, KV head) cells of one layer ({toks} token-heads): "
+                       f"encode + decode with the meter in fp64; {busy:.1f} s of oracle time over "
+                       f"{n_workers} single-threaded workers")
+
+
+def _oracle_cell_time(arg):
+    import numpy as np
+    import torch
+    torch.set_num_threads(1)
+    from oracle.pipeline import RegionSpec, decode_cell, encode_region
+    from workloads import CONFIGS, gen_layer
+    idx, b, kvh = arg
+    cfg = CONFIGS[idx]
+    inp = gen_layer(cfg, 0, "cpu", requests=[b])               # input synthesis, not timed
+    G = cfg.group
+    q = inp["q"][0, kvh * G:(kvh + 1) * G].double().numpy()
+    regions = []
+    n_tok = 0
+    if cfg.prefix is not None and cfg.prefix.length > 0:
+        pr = cfg.prefix
+        regions.append((inp["prefix_k"][kvh].double().numpy(), inp["prefix_v"][kvh].double().numpy(),
+                        RegionSpec(pr.k_fmt, pr.v_fmt, layer=0, stream=1_000_000, witness=pr.witness,
+                                   exact_k=pr.exact_k)))
+        n_tok += pr.length
+    n = int(inp["suffix_lens"][0])
+    sf = cfg.suffix
+    regions.append((inp["suffix_k"][0, kvh, :n].double().numpy(), inp["suffix_v"][0, kvh, :n].double().numpy(),
+                    RegionSpec(sf.k_fmt, sf.v_fmt, layer=0, stream=b, witness=sf.witness, exact_k=sf.exact_k)))
+    n_tok += n
+    sm = float(np.float32(128 ** -0.5))
+    t = time.perf_counter()
+    encs = [(k, encode_region(k, v, spec, kvh), spec) for k, v, spec in regions]
+    decode_cell(q, encs, sm)
+    return time.perf_counter() - t, n_tok
+
+
 def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = False, n_pairs: int = 0,
-                     q_heads: int = 0):
+                     q_heads: int = 0, cpu_seconds: float = 0.0):
     """One layer of workload `idx`: stage its caches through kvq_quantize, then
     time kvq_decode_attn (with TV, log A, bound and meter where the workload
     has exact keys and a witness) with HIP events on the launch stream."""
@@ -250,9 +374,11 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
     bytes_launch += B * HQ * 128 * 4 * 2 + 4 * B * HQ * 4                     # q, out, meter
     sm = float(np.float32(1.0 / math.sqrt(128.0)))
     out = torch.empty((B, HQ, 128), dtype=torch.float32, device=dev)
-    mbuf = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev) for k in ("tv", "bound_raw", "meter", "log_a")}
+    # (zeros: fields a workload without exact keys or witness leaves unwritten)
+    mbuf = {k: torch.zeros((B, HQ), dtype=torch.float32, device=dev) for k in ("tv", "bound_raw", "meter", "log_a")}
     meter = kvq.MeterOut(**{k: v.data_ptr() for k, v in mbuf.items()})
-    a = kvq._attn_args(inp["q"], prefix, suffix, out, sm, 0, HKV)
+    status = torch.zeros(4, dtype=torch.int32, device=dev)
+    a = kvq._attn_args(inp["q"], prefix, suffix, out, sm, 0, HKV, status=status)
     info = kvq.PlanInfo()
     assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(meter), 0, ctypes.byref(info)) == 0
     # every extension at once (per-chunk plan): value side, two-sided form,
@@ -333,6 +459,15 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         tier_b_ms = sorted(e0.elapsed_time(e1) for e0, e1 in b_evs)[reps // 2]
     plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
             if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
+    torch.cuda.synchronize()
+    if int(status[0].item()) != 0:
+        raise RuntimeError(f"status word {int(status[0].item()):#x}: a team wait ran out")
+    if not bool(torch.isfinite(out).all()) or not bool((mbuf["tv"] <= mbuf["bound_raw"] + 1e-6).all()):
+        raise RuntimeError("non-finite output or TV above its bound")
+    base = None
+    if cpu_seconds > 0:
+        log("timing the oracle on host cores")
+        base = workload_cpu_baseline(cfg, cpu_seconds)
     print(json.dumps({
         "workload": f"config {idx}: {cfg.description}".replace(
             "per-(256-token block, channel) fp16 scales",
@@ -350,7 +485,9 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
                       + (", Tier B" if tier_b_ok else "") + f" (plan: {info_x.chunks} chunk(s), team {info_x.team})",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS},
-        "plan": plan}), flush=True)
+        "kv_tokens_per_s": cfg.context_tokens() / (med * 1e-3),
+        "plan": plan,
+        "cpu_baseline": base}), flush=True)
 
 
 def main():
@@ -371,7 +508,8 @@ def main():
         # milliseconds, longer than a few sub-millisecond launches take
         measure_workload(args.workload, reps=max(args.steps, 5), warmup=max(args.warmup, 30),
                          group_scales=args.int8_scales == "group", n_pairs=args.outlier_pairs,
-                         q_heads=args.q_heads)
+                         q_heads=args.q_heads,
+                         cpu_seconds=0.0 if args.no_cpu_baseline else min(args.cpu_seconds, 10.0))
         return
     import numpy as np
     import torch
@@ -402,10 +540,15 @@ def main():
 
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
-    mbuf = {k: torch.empty((B, HQ), dtype=torch.float32, device=dev)
+    # every layer's output and per-(layer, request, query head) meter fields
+    # are kept for the step ([L, B, Hq] each), as the workload asks
+    out = torch.empty((L, B, HQ, D), dtype=torch.float32, device=dev)
+    mbuf = {k: torch.empty((L, B, HQ), dtype=torch.float32, device=dev)
             for k in ("tv", "bound_raw", "meter", "log_a")}
-    meter = kvq.MeterOut(**{k: v.data_ptr() for k, v in mbuf.items()})
+    meters = [kvq.MeterOut(**{k: v[layer].data_ptr() for k, v in mbuf.items()}) for layer in range(L)]
+    meter = meters[0]
+    # the calls report a team wait that ran out here (KVQ_DEVSTATUS_*)
+    status = torch.zeros(4, dtype=torch.int32, device=dev)
     # prebuilt C arguments per layer
     qargs, aargs = [], []
     for layer, Ld in enumerate(layers):
@@ -416,8 +559,9 @@ def main():
             k_out=st.k.data_ptr(), v_out=st.v.data_ptr(), k_scale_out=st.k_scale.data_ptr(),
             v_scale_out=st.v_scale.data_ptr(), witness_out=st.witness.data_ptr(), layer=layer))
         aargs.append(kvq.AttnArgs(batch=B, num_q_heads=HQ, num_kv_heads=HKV, head_dim=D,
-                                  sm_scale=sm_scale, split_tokens=0, q=Ld["q"].data_ptr(),
-                                  prefix=kvq.Region(), suffix=Ld["view"].to_c(), out=out.data_ptr()))
+                                  sm_scale=sm_scale, split_tokens=0, plan_flags=0,
+                                  status=status.data_ptr(), q=Ld["q"].data_ptr(),
+                                  prefix=kvq.Region(), suffix=Ld["view"].to_c(), out=out[layer].data_ptr()))
     info = kvq.PlanInfo()
     assert lib.kvq_decode_plan(ctypes.byref(aargs[0]), ctypes.byref(meter), 0, ctypes.byref(info)) == 0
     kernel_name = (f"decode_mfma_team_kernel<FP8, FP8, dense, full> (team {info.team}, "
@@ -435,7 +579,7 @@ def main():
                 raise RuntimeError(f"kvq_quantize status {rc}")
             if ev is not None:
                 ev[layer][0].record(stream)
-            rc = lib.kvq_decode_attn(ctypes.byref(aargs[layer]), ctypes.byref(meter), ws.data_ptr(),
+            rc = lib.kvq_decode_attn(ctypes.byref(aargs[layer]), ctypes.byref(meters[layer]), ws.data_ptr(),
                                      ws_bytes, sp)
             if ev is not None:
                 ev[layer][1].record(stream)
@@ -470,6 +614,11 @@ def main():
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall_ms / args.steps:.3f} ms/step)")
+    # the last timed step's results: every layer's outputs finite, TV <= bound
+    # on every (layer, request, query head), no team wait ran out, and sampled
+    # cells against the oracle
+    check = validate_step(cfg, L, layers, out, mbuf, status)
+    log(f"last step checked: {check}")
 
     # per-launch duration of the decode kernel, events on the launch stream
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -499,6 +648,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_detail": "fp32 logits (q split exactly into bf16 pieces against FP8 codes widened "
+                        "exactly to bf16), fp32 softmax and meter; P.V as fp16 weights x fp16 values "
+                        "(FP8 codes exact in fp16) with fp32 accumulation; storage FP8 E4M3",
         "data": "synthetic",
         "config": {"workload": f"qwen3-8b-shape decode step: {L} layers x batch {B} x {S} tokens, "
                                f"{HQ} q / {HKV} KV heads, d=128, K8/V8 FP8 E4M3 per-token scales, "
@@ -510,6 +662,7 @@ def main():
                      "kernel": kernel_name + ", one launch per layer",
                      "avg_launch_ms": dec_avg_ms, "bytes_per_launch": bytes_launch},
         "cpu_baseline": None,
+        "step_check": check,
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on host cores")

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 10
+#define KVQ_ABI_VERSION 11
 #define KVQ_HEAD_DIM 128
 #define KVQ_N_BANDS 16
 #define KVQ_INT8_BLOCK 256
@@ -74,7 +74,9 @@ typedef enum kvq_status {
  *                       scales [.., L, 4] laid out like the codes' rows (WitCert
  *                       Sec. 6.2.3, Table 4: token x G_c-channel groups, G_c = 32,
  *                       paging-safe).  Keys and values of a region use it together
- *                       (or keys alone for kvq_meter); decoded on the vector ALUs. */
+ *                       (or keys alone for kvq_meter).  Decoded on the matrix cores
+ *                       (one contraction per 32-channel group, scaled per token
+ *                       after it), or on the vector ALUs where those do not apply. */
 typedef enum kvq_format {
   KVQ_FMT_BF16 = 0,
   KVQ_FMT_FP8_E4M3 = 1,
@@ -98,8 +100,9 @@ typedef enum kvq_format {
  * Logical token order is prefix tokens 0..P-1, then suffix tokens 0..n_b-1; the
  * dither stream of a token uses its index inside its own region. */
 typedef struct kvq_region {
-  int32_t k_format;         /* KVQ_FMT_BF16 | KVQ_FMT_FP8_E4M3 | KVQ_FMT_INT8_DITHER */
-  int32_t v_format;         /* same set */
+  int32_t k_format;         /* KVQ_FMT_BF16 | KVQ_FMT_FP8_E4M3 | KVQ_FMT_INT8_DITHER |
+                               KVQ_FMT_INT8_G32 */
+  int32_t v_format;         /* same set; INT8_G32 keys and values go together */
   const void *k;            /* stored key codes */
   const void *v;            /* stored value codes (may be NULL for kvq_meter) */
   const void *k_scale;      /* float (FP8) or fp16 bits (INT8); NULL for BF16 */
@@ -132,6 +135,32 @@ typedef struct kvq_region {
   int32_t n_outlier_pairs;      /* m in [0, 16]; 0: no bypass */
 } kvq_region;
 
+/* Plan flags (kvq_attn_args.plan_flags).  0 is the library's choice; a flag
+ * only narrows that choice, never enables a plan the arguments do not allow.
+ * Unknown bits return KVQ_ERR_UNSUPPORTED.  Results of every plan meet the
+ * same accuracy; they are bitwise equal only within one plan. */
+#define KVQ_PLAN_NO_TEAM           0x01u /* never the team launch (the TV pairs go
+                                            through the workspace instead of LDS) */
+#define KVQ_PLAN_VECTOR_ALU        0x02u /* the vector-ALU kernel for every region
+                                            (no matrix cores, no team, one launch
+                                            per region) */
+#define KVQ_PLAN_GROUP8_SEPARATE   0x04u /* a group of 8 on the team plan: two
+                                            launches of 4 query heads, each
+                                            reading the cache, not one paired launch */
+#define KVQ_PLAN_FINALIZE_IN_PLACE 0x08u /* per-chunk plan: the TV and the block
+                                            report in the decode launch's last
+                                            work-group, no finish launch */
+#define KVQ_PLAN_LAUNCH_PER_REGION 0x10u /* per-chunk plan: one launch per region,
+                                            not one over cartridge and suffix */
+#define KVQ_PLAN_ALL_FLAGS         0x1Fu
+
+/* Bits a decode or meter call ORs into its status word (kvq_attn_args.status). */
+#define KVQ_DEVSTATUS_TEAM_WAIT    0x1u  /* a team launch's bounded wait ran out (the
+                                            device was shared with other work longer
+                                            than the wait budget, about 10 ms): the
+                                            results of the affected (request, KV
+                                            head) pairs are NaN, none is stale */
+
 /* Decode-step attention over prefix ++ suffix for every (request, query head).
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).  sm_scale is the
  * logit scale (1/sqrt(128) for the workloads here). */
@@ -140,9 +169,14 @@ typedef struct kvq_attn_args {
   int32_t num_q_heads;
   int32_t num_kv_heads;     /* num_q_heads / num_kv_heads must be 1, 2, 4 or 8 */
   int32_t head_dim;         /* must be 128 */
-  float sm_scale;
+  float sm_scale;           /* in (0, 1e6] */
   int32_t split_tokens;     /* tokens per work chunk; 0 = library choice; else a multiple of 64 */
-  const float *q;           /* device fp32 [batch, num_q_heads, 128], post-RoPE */
+  uint32_t plan_flags;      /* KVQ_PLAN_* bits, 0 = library choice */
+  uint32_t *status;         /* device uint32 the call ORs KVQ_DEVSTATUS_* bits into, in
+                               stream order (the caller clears it), or NULL.  The team
+                               plan is taken only with a status word: it is the one plan
+                               whose waits can run out.  16-byte aligned. */
+  const float *q;           /* device fp32 [batch, num_q_heads, 128], post-RoPE, finite */
   kvq_region prefix;        /* prefix.length == 0: no shared prefix */
   kvq_region suffix;
   float *out;               /* device fp32 [batch, num_q_heads, 128] = sum_t p~_t v^_t */
@@ -154,6 +188,13 @@ typedef struct kvq_attn_args {
  *   log_a     = log E_p~[e^{c_t}],  c_t = sm_scale * sum_b ||q_b|| w_{t,b}
  *   bound_raw = 1/2 (A^2 - 1), +inf when beyond the float range
  *   meter     = min(1, bound_raw)
+ * A is evaluated in the log domain and c is never truncated: when a term of
+ * the log-domain sum overflows the float range, log_a and bound_raw are +inf
+ * and meter is 1, the trivial bound (WitCert Sec. 3 numerics, Sec. 6.2.4).
+ * c_t is rounded upward: sm_scale ||q_b|| is formed in float64, raised by
+ * 2^-20 relative and split into fp16 pieces whose sum is not below it, so
+ * the fp32 sum over the 16 bands (at most 16 roundings to nearest of
+ * non-negative terms) is not below c_t of the stored witness.
  * Tier B (WitCert Sec. 4.2, Lemma 2; Sec. 6.2.3): the sub-Gaussian certificate
  * of subtractively dithered INT8 keys, from the stored scales and the query
  * alone (no witness).  Requesting any of its outputs needs delta_b in (0, 1)
@@ -296,7 +337,9 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  *    where its kernels allow, each reading the cache.  Members wait only
  *    for members of their own team, with a bounded wait: a wait that runs
  *    out (another kernel holding the device for longer) leaves NaN in that
- *    (request, KV head)'s results, never a hang.
+ *    (request, KV head)'s results, never a hang, and sets
+ *    KVQ_DEVSTATUS_TEAM_WAIT in the call's status word.  Taken only when
+ *    args->status is non-NULL and plan_flags allow it.
  *  - team == 0: `chunks` chunks of each (request, KV head) over both regions,
  *    one work-group each, in one launch (cartridge page: one kernel spans the
  *    shared cartridge and the live suffix) when both regions have keys of one
@@ -306,7 +349,7 @@ size_t kvq_workspace_bytes(const kvq_attn_args *args, const kvq_meter_out *meter
  * from an epoch kept in the workspace, which the launch's last work-group
  * moves past every tag it used, so each replay waits for fresh tags.
  * workspace_bytes is what this plan needs; kvq_workspace_bytes may return
- * more (it covers the per-chunk plan of the same arguments too). */
+ * more (it covers the other plan of the same arguments too). */
 typedef struct kvq_plan_info {
   int32_t team;             /* work-groups per (request, KV head); 0: no team launch */
   int32_t n_teams;          /* teams; a group of 8 runs two raw teams (4 query heads each) per team */
@@ -327,19 +370,27 @@ kvq_status kvq_decode_plan(const kvq_attn_args *args, const kvq_meter_out *meter
                            kvq_plan_info *info);
 
 /* Prepare a workspace for first use: clears all of it (one fill kernel on
- * `stream`).  The team epoch restarts from 0 after about 2^32 / (rounds + 1)
- * team launches on one workspace (some 4 * 10^8 for the batch-64 step); a
- * caller that runs that many should clear the workspace again before then, so
- * that no word of a launch that long ago can carry a tag being waited for.  A workspace stays ready after every successful kvq_decode_attn /
- * kvq_meter call: the per-chunk plan's arrival counters (after the first 256
- * bytes) are reset by the last work-group of each (request, KV head); team
- * launches tag their exchange words with an epoch kept in the first 256
- * bytes, which each launch advances past its tags on the device, instead of
- * clearing them.  Calls of other shapes may share the workspace; clearing it
- * again when the shape changes also removes the small chance (2^-32 per
- * word) that a word left by the other plan's partial results carries the
- * tag a team launch waits for.  Calls that share a workspace must not
- * overlap in time. */
+ * `stream`).  A workspace stays ready after every successful kvq_decode_attn /
+ * kvq_meter call, of any shape and either plan, so calls of different shapes
+ * may share one workspace (not at the same time: calls that share a
+ * workspace must not overlap).  Layout, from the start:
+ *  - 256 bytes of control words: the team epoch and the count of finished
+ *    team work-groups (0 at rest);
+ *  - 1 MiB of per-chunk arrival counters, one per (request, KV head), each
+ *    reset to 0 by the group's last work-group;
+ *  - the team plan's exchange slots, when a team plan exists for the
+ *    arguments;
+ *  - the per-chunk plan's partial states and TV spill.
+ * So the two plans of the same arguments never share a word.  Team words are
+ * 64-bit (tag, value) pairs.  A tag is a signalling-NaN bit pattern that no
+ * kernel stores as data (arithmetic never produces one, and no input is
+ * copied into the workspace), so no partial state or spill word of any call
+ * can pass for a team word.  A launch waits only for tags above every tag
+ * used on the workspace since the epoch last restarted.  The epoch restarts
+ * after 2^22 - 2^18 tags (about 430,000 launches of the batch-64 step); the
+ * launch that restarts it clears every word any team launch on the workspace
+ * can read (at most 2 x resident work-groups x 4,480 bytes, 4.6 MB here), so
+ * no word from before the restart carries a tag being waited for. */
 kvq_status kvq_workspace_init(void *workspace, size_t workspace_bytes, kvq_stream stream);
 
 /* Decode attention with the fused meter (WitCert Sec. 6 meter loop, read path;

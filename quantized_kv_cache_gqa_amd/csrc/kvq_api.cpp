@@ -4,7 +4,6 @@
 
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -17,13 +16,28 @@ using namespace kvq;
 
 constexpr size_t kAlign = 256;
 // Workspace layout: the team launch's control words (epoch, finished count)
-// in the first 256 bytes, which no plan uses otherwise; then the per-chunk
-// plan's arrival counters (one per (request, KV head), at most 2^18, zero at
-// rest); the team plan's slots start after the counters' MiB, so neither
-// plan's words land on the other's counters or on the control words when
-// calls of different shapes share a workspace.
+// in the first 256 bytes, which no plan uses otherwise; the per-chunk plan's
+// arrival counters (one per (request, KV head), at most 2^18, zero at rest)
+// in the next MiB; then the team plan's exchange slots when a team plan
+// exists for the arguments (whatever the plan flags and the status word),
+// and after them the per-chunk plan's partials and spill.  So the two plans
+// of one set of arguments never share a word, and every team word of any
+// shape lies in the first 2 x (resident work-groups) slots after kTeamOff.
 constexpr size_t kCtlBytes = 256;
 constexpr size_t kCounterBytes = (size_t)1 << 20;
+constexpr size_t kTeamOff = kCtlBytes + kCounterBytes;
+
+// Bounded waits of the team exchange: polls per batch of words before a wait
+// gives up, and a member that never publishes (none).  Only a test build
+// (KVQ_TEST_HOOKS) can change them, through kvq_test_set_team_hooks, to force
+// a run-out from the host.
+#ifdef KVQ_TEST_HOOKS
+unsigned g_spin_limit = 1u << 18;
+int g_silent_member = -1;
+#else
+constexpr unsigned g_spin_limit = 1u << 18;
+constexpr int g_silent_member = -1;
+#endif
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -48,34 +62,23 @@ struct Plan {
   size_t off_fin = 0, off_tvp = 0, off_rkey = 0;
   int team = 0, n_teams = 0, grid = 0, rounds = 0;   // team launch (team > 0)
   int halves = 1;               // team launch of a group of 8: 2 = pairs of raw teams in one launch
+  unsigned flags = 0;           // KVQ_PLAN_* bits of the call
+  size_t team_res = 0;          // bytes of the team region (0: no team plan for these arguments)
   size_t off_counters = 0, off_partials = 0, off_spill = 0, off_rspill = 0, off_ublk = 0, bytes = 0;
 };
-
-// decimal value of an environment variable in [lo, 2^32), else dflt
-unsigned env_uint(const char *name, unsigned dflt, unsigned long lo) {
-  const char *v = getenv(name);
-  if (!v || !*v) return dflt;
-  char *end = nullptr;
-  const unsigned long x = strtoul(v, &end, 10);
-  return (end && *end == 0 && x >= lo && x <= 0xffffffffUL) ? (unsigned)x : dflt;
-}
-
-bool env_is(const char *name, char c) {
-  const char *v = getenv(name);
-  return v && v[0] == c;
-}
 
 // Team plan for a one-region launch with the TV on the matrix-core path:
 // T members per (request, KV head), chunks of <= TEAM_MAX_CHUNK tokens (whole
 // 16-token tiles), persistent teams over the groups.  Picks the T with the
 // least work per member over all rounds (a round's fixed cost is counted as
-// 256 tokens).  Returns false when no team launch applies.
-bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
-  if (env_is("KVQ_DECODE_TEAM", '0') || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
-  // A group of 8 runs as one launch of paired raw teams of 4 query heads each
-  // (KVQ_TEAM_HALVES=0: two launches, one per 4 heads, each reading the cache).
+// 256 tokens).  Returns false when the arguments admit no team launch (the
+// plan flags and the status word are the caller's business).  hv = 2: a group
+// of 8 as one launch of paired raw teams of 4 query heads each; hv = 1: one
+// launch per 4 heads, each reading the cache.
+bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p, int hv) {
+  // (the kernel-group test below uses the padded group of the matrix-core
+  // kernels: a group of 1 or 2 is a tile of 4)
   if (!p.tv || p.tier_b || p.report || a->split_tokens != 0 || (p.kgroup != 4 && p.group != 8)) return false;
-  if (p.group == 8 && env_is("KVQ_DECODE_KERNEL", 'g')) return false;
   if ((p.prefix_len > 0) == (p.suffix_cap > 0)) return false;   // exactly one region
   const kvq_region &r = p.prefix_len > 0 ? a->prefix : a->suffix;
   if (r.k_format != KVQ_FMT_BF16 && r.k_format != KVQ_FMT_FP8_E4M3) return false;
@@ -94,7 +97,7 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
                            team_capacity(r.k_format, vf_dec, paged, full, ext));
   (void)vf;
   if (cap <= 0) return false;
-  const int hv = (p.group == 8 && !env_is("KVQ_TEAM_HALVES", '0')) ? 2 : 1;
+  if (p.group != 8) hv = 1;
   const int capg = cap / hv;                       // resident work-groups per logical team slot
   if (capg <= 0) return false;
   const int64_t len = r.length;
@@ -128,7 +131,7 @@ bool plan_team(const kvq_attn_args *a, bool meter_only, int groups, Plan &p) {
   p.total_chunks = p.team;
   p.rounds = (groups + p.n_teams - 1) / p.n_teams;
   p.off_counters = kCtlBytes;
-  p.off_partials = kCtlBytes + kCounterBytes;
+  p.off_partials = kTeamOff;
   p.off_spill = p.off_partials + round_up((size_t)p.n_teams * hv * 2 * p.team * TEAM_SLOT_BYTES, kAlign);
   p.bytes = p.off_spill;
   return true;
@@ -183,8 +186,11 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   p.group = a->num_q_heads / a->num_kv_heads;
   if (p.group != 1 && p.group != 2 && p.group != 4 && p.group != 8) return KVQ_ERR_UNSUPPORTED;
   p.kgroup = p.group;
+  if (a->plan_flags & ~(uint32_t)KVQ_PLAN_ALL_FLAGS) return KVQ_ERR_UNSUPPORTED;
+  p.flags = a->plan_flags;
   if (!a->q) return KVQ_ERR_NULL;
   if (!aligned16(a->q)) return KVQ_ERR_ALIGN;
+  if (a->status && !aligned16(a->status)) return KVQ_ERR_ALIGN;
   if (!meter_only) {
     if (!a->out) return KVQ_ERR_NULL;
     if (!aligned16(a->out)) return KVQ_ERR_ALIGN;
@@ -198,7 +204,7 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   p.suffix_cap = a->suffix.length;
   // a group of 1 or 2 query heads runs on the matrix-core kernels as a tile of
   // 4 heads (the rest copies of the last, never written) where they apply
-  if ((p.group == 1 || p.group == 2) && !env_is("KVQ_DECODE_KERNEL", 'g')) {
+  if ((p.group == 1 || p.group == 2) && !(p.flags & KVQ_PLAN_VECTOR_ALU)) {
     bool ok = true;
     for (int pre = 0; pre < 2; ++pre) {
       const kvq_region &r = pre ? a->prefix : a->suffix;
@@ -297,10 +303,27 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
         return KVQ_ERR_UNSUPPORTED;
     }
   }
-  if (allow_team && plan_team(a, meter_only, groups, p)) return KVQ_OK;
+  // The team region these arguments would use (reserved whatever the flags
+  // and the status word, so that per-chunk words of these arguments never
+  // land on it); the team plan itself is taken only with a status word, to
+  // which a wait that runs out is reported, and when the flags allow it.
+  {
+    Plan t = p;
+    if (plan_team(a, meter_only, groups, t, 2)) p.team_res = t.bytes - kTeamOff;
+    Plan t1 = p;
+    if (p.group == 8 && plan_team(a, meter_only, groups, t1, 1))
+      p.team_res = std::max(p.team_res, t1.bytes - kTeamOff);
+    const bool want = allow_team && a->status && !(p.flags & (KVQ_PLAN_NO_TEAM | KVQ_PLAN_VECTOR_ALU));
+    Plan tp = p;
+    if (want && p.team_res > 0 &&
+        plan_team(a, meter_only, groups, tp, (p.flags & KVQ_PLAN_GROUP8_SEPARATE) ? 1 : 2)) {
+      p = tp;
+      return KVQ_OK;
+    }
+  }
   const int wg = std::max(p.group, p.kgroup);      // heads per group in the workspace
   p.off_counters = kCtlBytes;
-  p.off_partials = round_up(kCtlBytes + (size_t)groups * sizeof(uint32_t), kAlign);
+  p.off_partials = round_up(kTeamOff + p.team_res, kAlign);
   p.off_spill = p.off_partials +
                 round_up((size_t)groups * p.total_chunks * wg * PART_STRIDE * sizeof(float), kAlign);
   p.bytes = p.off_spill;
@@ -316,9 +339,9 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   }
   // Several chunks per group: the last work-group of a group would stream the
   // whole group's spill alone for the TV and the report; a finish launch
-  // spreads that over FIN_BLOCKS-block ranges instead (KVQ_DEFER_FINISH=0, a
-  // test hook, keeps it in the decode launch).
-  p.defer = p.total_chunks > 1 && (p.tv || p.report) && !env_is("KVQ_DEFER_FINISH", '0');
+  // spreads that over FIN_BLOCKS-block ranges instead (KVQ_PLAN_FINALIZE_IN_PLACE
+  // keeps it in the decode launch).
+  p.defer = p.total_chunks > 1 && (p.tv || p.report) && !(p.flags & KVQ_PLAN_FINALIZE_IN_PLACE);
   if (p.defer) {
     p.fin_blocks = (p.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK +
                    (p.suffix_cap + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
@@ -381,6 +404,8 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   d.sm_scale = a->sm_scale;
   d.q = a->q;
   d.out = meter_only ? nullptr : a->out;
+  d.plan_flags = p.flags;
+  d.status = a->status;
   d.chunk = p.chunk;
   d.total_chunks = p.total_chunks;
   d.prefix_len = p.prefix_len;
@@ -461,7 +486,7 @@ int chunk_launch_count(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch
 // launch sets of 4 query heads each (the group-4 kernels; each reads the
 // cache once), instead of the vector-ALU kernel.
 bool split_halves(const Plan &p, const DecodeLaunch &dp, const DecodeLaunch &ds) {
-  if (p.group != 8 || env_is("KVQ_DECODE_KERNEL", 'g')) return false;
+  if (p.group != 8 || (p.flags & KVQ_PLAN_VECTOR_ALU)) return false;
   DecodeLaunch hp = dp, hs = ds;
   hp.group = hs.group = 4;
   if (p.pre_chunks > 0 && !mfma_path_supports(hp)) return false;
@@ -512,12 +537,12 @@ kvq_status run_decode(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, 
     d.team = p.team;
     d.n_teams = p.n_teams;
     d.team_ctl = reinterpret_cast<uint32_t *>(ws);
-    // Bounded waits of the team exchange.  Two test hooks, read from the
-    // environment: KVQ_TEAM_SPIN_LIMIT (polls per batch of words, default
-    // 2^18) and KVQ_TEAM_SILENT_MEMBER (that member of every team never
-    // publishes, so the others' waits run out and the results turn to NaN).
-    d.spin_limit = env_uint("KVQ_TEAM_SPIN_LIMIT", 1u << 18, 1);
-    d.silent_member = (int)env_uint("KVQ_TEAM_SILENT_MEMBER", 0xffffffffu, 0);
+    d.spin_limit = g_spin_limit;
+    d.silent_member = g_silent_member;
+    // every word a team launch of any shape on this workspace can read: at
+    // most 2 slots per resident work-group, from the team region's start
+    const size_t reach = (size_t)2 * std::max(team_capacity_max(), p.grid) * TEAM_SLOT_BYTES;
+    d.team_clear_bytes = std::min(reach, ws_bytes - kTeamOff) & ~(size_t)15;
     if (p.group == 8 && p.halves == 2) {           // one launch, paired raw teams of 4 heads
       make_half(d, 0);
       d.halves = 2;
@@ -613,12 +638,12 @@ kvq_status kvq_quantize(const kvq_quant_args *a, kvq_stream stream) {
 }
 
 size_t kvq_workspace_bytes(const kvq_attn_args *a, const kvq_meter_out *m) {
-  // the size does not depend on out/v; it also covers the per-chunk plan of
-  // the same arguments, so one workspace serves both whichever is taken
+  // the size does not depend on out/v; the per-chunk plan's region lies after
+  // the team region of the same arguments, so its end covers both plans
   Plan p, q;
   if (make_plan(a, m, true, p) != KVQ_OK) return 0;
-  if (p.team && make_plan(a, m, true, q, false) == KVQ_OK) return std::max(p.bytes, q.bytes);
-  return p.bytes;
+  if (make_plan(a, m, true, q, false) != KVQ_OK) return 0;
+  return std::max(p.bytes, q.bytes);
 }
 
 kvq_status kvq_decode_plan(const kvq_attn_args *a, const kvq_meter_out *m, int meter_only,
@@ -668,5 +693,15 @@ kvq_status kvq_meter(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, s
                      kvq_stream stream) {
   return run_decode(a, m, ws, ws_bytes, (hipStream_t)stream, true);
 }
+
+#ifdef KVQ_TEST_HOOKS
+// Test builds only: a smaller wait budget and a member that never publishes,
+// so a GPU test can force a team wait to run out (the results turn to NaN
+// and the status word reports it).  spin_limit 0 restores the default.
+void kvq_test_set_team_hooks(unsigned spin_limit, int silent_member) {
+  g_spin_limit = spin_limit ? spin_limit : (1u << 18);
+  g_silent_member = silent_member;
+}
+#endif
 
 }  // extern "C"

@@ -27,7 +27,6 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
-#include <stdlib.h>
 
 #include "kvq_decode_common.h"
 
@@ -85,17 +84,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       qv[h][i + 3] = t.w * qs;
     }
     // band norms of bands 2j and 2j+1 (coordinates 4b..4b+3 and 64+4b..64+4b+3)
+    // (raised in float64 and rounded up to fp32: c formed from them with
+    // 5 roundings of non-negative terms stays at or above its exact value)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int bb = 2 * j + e;
-      float ss = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = qp[4 * bb + i], c = qp[64 + 4 * bb + i];
-        ss += a * a + c * c;
-      }
-      qn[h][e] = sqrtf(ss) * qs;
-    }
+    for (int e = 0; e < 2; ++e) qn[h][e] = f32_round_up(band_factor_up(qp, 2 * j + e, d.sm_scale));
   }
 
   // value side (WitCert Sec. 3 output bound): zv = sum p~ rho on the attention
@@ -681,10 +673,9 @@ static hipError_t launch_k(const DecodeLaunch &d, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeLaunch &d, hipStream_t s) {
-  // KVQ_DECODE_KERNEL=generic selects the vector-ALU kernel for every shape
-  // (used to test both kernels against the oracle on the same inputs)
-  const char *sel = getenv("KVQ_DECODE_KERNEL");
-  const bool generic = sel && sel[0] == 'g';
+  // KVQ_PLAN_VECTOR_ALU selects the vector-ALU kernel for every shape (the
+  // tests run both kernels against the oracle on the same inputs)
+  const bool generic = (d.plan_flags & KVQ_PLAN_VECTOR_ALU) != 0;
   if (!generic && mfma_path_supports(d)) return launch_decode_mfma(d, s);
   switch (d.group) {
     case 1: return launch_k<1>(d, s);

@@ -83,6 +83,44 @@ __device__ __forceinline__ float merge_factor(float m, float mnew) {
   return m == NEG_INF ? 0.0f : fast_exp2(m - mnew);
 }
 
+// Theorem 2's c_t = sm_scale sum_b ||q_b|| w_{t,b} (WitCert Sec. 4.1), in log2
+// units, must not fall below its exact value for the stored witness.  The
+// band factor sm_scale ||q_b|| log2(e) is formed in float64 from the fp32
+// query (band b: coordinates 4b..4b+3 and 64+4b..64+4b+3) and raised by
+// 2^-19 relative, which exceeds the relative error of the fp32 sums c is
+// formed with later (at most 17 roundings to nearest of non-negative terms,
+// 17 * 2^-24 < 2^-19).
+constexpr double C_RAISE = 1.0 + 0x1p-19;
+__device__ __forceinline__ double band_factor_up(const float *qp, int bb, float sm_scale) {
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const double a = qp[4 * bb + i], c = qp[64 + 4 * bb + i];
+    ss = fma(a, a, ss);
+    ss = fma(c, c, ss);
+  }
+  return sqrt(ss) * (double)sm_scale * 1.4426950408889634074 * C_RAISE;
+}
+
+// the smallest float >= x (x >= 0, finite or +inf)
+__device__ __forceinline__ float f32_round_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
+// log A (WitCert Thm. 1, in nats) from the attention state (Mq, Zq) and the
+// state (Mm, Zm) over l~ + c, both in log2 units.  A is evaluated in the log
+// domain; when a term of its sum overflowed (c or l~ + c reached +inf, which
+// leaves Mm = +inf or Zm not finite) the result is +inf, the trivial bound
+// (WitCert Sec. 3 numerics, Sec. 6.2.4), never a truncated c.
+__device__ __forceinline__ double meter_log_a(float Mq, float Zq, float Mm, float Zm) {
+  if (!(Zq > 0.0f)) return 0.0;                     // no token: empty sums
+  if (Mm == __builtin_huge_valf() || !(Zm <= 3.4028234663852886e38f)) return __builtin_huge_val();
+  if (!(Zm > 0.0f)) return 0.0;
+  return ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
+}
+
 // Dequantize the 16 values (dims 16j..16j+15) of one stored row.
 // FP8: returns the E4M3 values (the per-token scale is applied by the caller).
 // INT8: s_c (code - xi) with the block scales and the regenerated dither.
@@ -329,9 +367,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
       d.out[qh * D + 64 + lane] = o1 * inv;
     }
     if (lane == 0) {
-      double log_a = 0.0;
-      if (do_meter && Zq > 0.0f && Zm > 0.0f)
-        log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
+      const double log_a = do_meter ? meter_log_a(Mq, Zq, Mm, Zm) : 0.0;
       double bound = 0.5 * expm1(2.0 * log_a);
       const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
       if (d.log_a && hv) d.log_a[qh] = (float)log_a;

@@ -309,6 +309,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   //      head, whose results are not written)
   bf16x8_t bq[4];
   f16x4_t bw;
+  float c_unscale = 1.0f;                          // 2^-ce of this lane's head (see below)
   {
     const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
 #pragma unroll
@@ -323,19 +324,41 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
         bq[s][e] = (__bf16)piece;                   // exact: piece is a bf16 value
       }
     }
+    // witness dot: the raised band factors of head hh (bands 4 g .. 4 g + 3
+    // in this lane), scaled by a power of two 2^ce so that the head's largest
+    // lies in [2^14, 2^15) (no fp16 piece overflows or loses its bits), then
+    // split into three fp16 pieces h1 + h2 + h3 >= the scaled factor (h3
+    // rounded up; the remainders are exact in float64).  Column pp = 0, 1, 2
+    // carries piece pp; the collapsed sum is scaled back by 2^-ce (exact).
+    double fb[4], fhi = 0.0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int bb = 4 * g + e;
-      float ss = 0.0f;
+      fb[e] = band_factor_up(qp, 4 * g + e, d.sm_scale);
+      fhi = fhi > fb[e] ? fhi : fb[e];
+    }
+    fhi = fhi > __shfl_xor(fhi, 16) ? fhi : __shfl_xor(fhi, 16);
+    fhi = fhi > __shfl_xor(fhi, 32) ? fhi : __shfl_xor(fhi, 32);
+    int ce = 0;
+    if (fhi > 0.0 && fhi <= 1.7976931348623157e308) {
+      int ex;
+      frexp(fhi, &ex);                               // fhi in [2^(ex-1), 2^ex)
+      ce = min(max(15 - ex, -120), 120);
+    }
+    c_unscale = ldexpf(1.0f, -ce);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = qp[4 * bb + i], c = qp[64 + 4 * bb + i];
-        ss += a * a + c * c;
+    for (int e = 0; e < 4; ++e) {
+      const double x = ldexp(fb[e], ce);
+      const _Float16 h1 = (_Float16)x;
+      const double r1 = x - (double)h1;
+      const _Float16 h2 = (_Float16)r1;
+      const double r2 = r1 - (double)h2;
+      _Float16 h3 = (_Float16)r2;
+      if ((double)h3 < r2) {                         // next fp16 toward +inf
+        uint16_t u = __builtin_bit_cast(uint16_t, h3);
+        u = (u == 0x8000u || u == 0u) ? (uint16_t)1u : (uint16_t)((u & 0x8000u) ? u - 1u : u + 1u);
+        h3 = __builtin_bit_cast(_Float16, u);
       }
-      const float qn = sqrtf(ss) * qs;
-      const _Float16 h1 = (_Float16)qn;
-      const _Float16 h2 = (_Float16)(qn - (float)h1);
-      bw[e] = pp == 0 ? h1 : (pp == 1 ? h2 : (_Float16)0.0f);
+      bw[e] = pp == 0 ? h1 : (pp == 1 ? h2 : (pp == 2 ? h3 : (_Float16)0.0f));
     }
   }
 
@@ -570,7 +593,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const bool valid = tk < c1;
     float lq = collapse(dq, pp) * T.ks;
     float le = (do_tv && has_exact) ? collapse(de, pp) : lq;
-    const float cc = (do_meter && has_wit) ? collapse(dc, pp) : 0.0f;
+    const float cc = (do_meter && has_wit) ? collapse(dc, pp) * c_unscale : 0.0f;
     if (!valid) {
       lq = NEG_INF;
       le = NEG_INF;

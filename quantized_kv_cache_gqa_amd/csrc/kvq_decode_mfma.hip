@@ -3,6 +3,8 @@
 // one region, and the persistent team kernel of the single-region TV case.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvq_decode_mfma.h"
 
 namespace kvq {
@@ -115,18 +117,19 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
   // the exchange is the round's critical path: its waves issue ahead of the
   // co-resident work-group's streaming waves (wave priority only)
   __builtin_amdgcn_s_setprio(1);
-  const uint32_t tag = epoch + (uint32_t)round + 1u;
+  const uint32_t tag = team_tag(epoch + (uint32_t)round + 1u);   // round - 1's is tag - 1
   uint64_t *slots = reinterpret_cast<uint64_t *>(d.partials) + (size_t)(slot_team * 2 + (round & 1)) * T * SLOT_WORDS;
   uint64_t *mine = slots + (size_t)member * SLOT_WORDS;
   __shared__ float mq_s[G][64];
   __shared__ float unit_s[WAVES][64];
   __shared__ float fin_s[G][4];
   __shared__ float tvw_s[WAVES][G];
-  __shared__ int bad_s;
+  __shared__ int bad_s;    // this round's group: a wait ran out, its results are NaN
+  __shared__ int late_s;   // any wait of this epilogue ran out (reported in the status word)
   const float qnan = __builtin_nanf("");
 
   // 1. publish this member's merged states and accumulator
-  if (tid == 0) bad_s = 0;
+  if (tid == 0) bad_s = late_s = 0;
   __syncthreads();
   for (int idx = tid; idx < G * PART_STRIDE; idx += 256) {
     const int h = idx / PART_STRIDE, k = idx - h * PART_STRIDE;
@@ -190,7 +193,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     const float qnan_s = __builtin_nanf("");
     Mq = Zq = Mm = Zm = Me = Ze = qnan_s;
     Zv = Vm = Mn = Zn = Cm = qnan_s;
-    if (lane == 0) bad_s = 1;
+    if (lane == 0) bad_s = late_s = 1;
   }
   mq_s[h][lane] = Mq;
   for (int off = 1; off < T; off <<= 1) {           // lanes >= T hold empty states
@@ -316,7 +319,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
       const size_t qu = (size_t)b * d.h_q + (size_t)kvh * d.qg + qh0 + hu;
       if (split) {
         unit_s[h][lane] = o;
-        if (!oku) bad_s = 1;
+        if (!oku) bad_s = late_s = 1;
       } else {
         if (qh0 + hu < d.qg) d.out[qu * D + dim] = oku ? o * iZu : qnan;
         ok = ok && oku;
@@ -333,9 +336,7 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     }
   }
   if (member == h % T && lane == 0) {
-    double log_a = 0.0;
-    if (do_meter && Zq > 0.0f && Zm > 0.0f)
-      log_a = ((double)Mm - (double)Mq) * 0.69314718055994530942 + log((double)Zm) - log((double)Zq);
+    const double log_a = do_meter ? meter_log_a(Mq, Zq, Mm, Zm) : 0.0;
     const double bound = 0.5 * expm1(2.0 * log_a);
     const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
     if (d.log_a && hv) d.log_a[qh] = ok ? (float)log_a : qnan;
@@ -372,11 +373,12 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
     }
     sh = wave_sum_fixed(sh, T);
     okp = __all(okp);
+    if (!okp && lane == 0) late_s = 1;
     const int pg = team + (round - 1) * d.n_teams;
     const int pb = pg / d.h_kv, pk = pg - pb * d.h_kv;
     if (lane == 0 && hv) d.tv[(size_t)pb * d.h_q + (size_t)pk * d.qg + qh0 + h] = okp ? 0.5f * sh : qnan;
   }
-  if (!ok) bad_s = 1;
+  if (!ok) bad_s = late_s = 1;
   __syncthreads();
   if (tid < G) {
     const float share = ((tvw_s[0][tid] + tvw_s[1][tid]) + tvw_s[2][tid]) + tvw_s[3][tid];
@@ -394,10 +396,15 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
       sh = v[0];
     }
     sh = wave_sum_fixed(sh, T);
+    if (!__all(okp) && lane == 0) late_s = 1;
     okp = __all(okp) && bad_s == 0;
     if (lane == 0 && hv) d.tv[qh] = okp ? 0.5f * sh : qnan;
   }
   __syncthreads();                  // LDS buffers are reused by the next round
+  // a wait that ran out is reported to the caller, not only as NaN results
+  if (tid == 0 && late_s && d.status)
+    __hip_atomic_fetch_or(d.status, (uint32_t)KVQ_DEVSTATUS_TEAM_WAIT, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -436,19 +443,34 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_team_kernel(const DecodeLa
     team_epilogue<EXT>(d, epoch, part_s, spill_s, team, rt, qh0, member, round, grp + d.n_teams >= groups,
                        b, kvh, c0, c1);
   }
-  // Every work-group counts itself out after reading the epoch; the last one
-  // moves the epoch past all of this launch's tags and rearms the count, so
-  // the next launch on this workspace (a graph replay included) waits for
-  // tags no earlier launch wrote.
+  // Every work-group counts itself out after reading the epoch and after its
+  // own tagged stores have completed (so nothing of this launch lands after
+  // the count); the last one moves the epoch past all of this launch's tags
+  // and rearms the count, so the next launch on this workspace (a graph
+  // replay included) waits for tags no earlier launch wrote.  When the
+  // epoch restarts, that work-group first clears every word a team launch on
+  // this workspace can read, so no word from before the restart carries a
+  // tag that a later launch waits for.
+  __shared__ int last_s;
+  wait_own_stores();
+  __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t done = __hip_atomic_fetch_add(d.team_ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
-      const uint32_t rounds = (uint32_t)((groups + d.n_teams - 1) / d.n_teams);
-      uint32_t next = epoch + rounds + 1u;
-      if (next > 0xF0000000u) next = 0u;             // tags stay in [1, 2^32)
-      __hip_atomic_store(d.team_ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(d.team_ctl, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    last_s = done == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last_s) return;
+  const uint32_t rounds = (uint32_t)((groups + d.n_teams - 1) / d.n_teams);
+  uint32_t next = epoch + rounds + 1u;
+  if (next > TEAM_EPOCH_MAX) {                     // restart: the next launch may use up to 2^18 rounds
+    next = 0u;
+    uint4 *w = reinterpret_cast<uint4 *>(d.partials);
+    const size_t n = d.team_clear_bytes / sizeof(uint4);
+    for (size_t i = threadIdx.x; i < n; i += blockDim.x) w[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(d.team_ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(d.team_ctl, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -523,6 +545,18 @@ int team_capacity(int k_format, int v_format, bool paged, bool full, bool ext) {
     return 0;
   c = per_cu * cus;
   return c;
+}
+
+int team_capacity_max() {
+  int best = 0;
+  const int kfs[2] = {KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16};
+  const int vfs[3] = {KVQ_FMT_FP8_E4M3, KVQ_FMT_BF16, VF_NONE};
+  for (int kf : kfs)
+    for (int vf : vfs)
+      for (int paged = 0; paged < 2; ++paged)
+        for (int fe = 0; fe < 3; ++fe)                  // (full, ext): plain, full, full + extensions
+          best = std::max(best, team_capacity(kf, vf, paged != 0, fe >= 1, fe == 2));
+  return best;
 }
 
 hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream) {

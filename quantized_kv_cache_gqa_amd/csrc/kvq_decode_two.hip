@@ -6,7 +6,6 @@
 // launch of its own, so the results are bitwise the same.
 #include <hip/hip_runtime.h>
 
-#include <stdlib.h>
 
 #include "kvq_decode_mfma.h"
 
@@ -65,10 +64,7 @@ hipError_t launch_2p(const DecodeLaunch &d1, const DecodeLaunch &d2, hipStream_t
 // with BF16 keys any mix of BF16 and FP8 values, with FP8 keys the same value
 // format in both; the meter-only call (no values) either way.
 bool two_region_supported(const DecodeLaunch &d1, const DecodeLaunch &d2) {
-  const char *sel = getenv("KVQ_DECODE_TWO");   // "0": one launch per region (test hook)
-  if (sel && sel[0] == '0') return false;
-  const char *ker = getenv("KVQ_DECODE_KERNEL");  // "generic": vector-ALU kernels only
-  if (ker && ker[0] == 'g') return false;
+  if (d1.plan_flags & (KVQ_PLAN_LAUNCH_PER_REGION | KVQ_PLAN_VECTOR_ALU)) return false;
   if (!mfma_path_supports(d1) || !mfma_path_supports(d2) || d1.region.paged) return false;
   if (d1.k_format != d2.k_format) return false;
   const int v1 = d1.v_format, v2 = d2.v_format;

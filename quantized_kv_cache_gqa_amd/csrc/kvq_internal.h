@@ -104,11 +104,24 @@ struct DecodeLaunch {
   float *rkey;                  // [groups][G][n_blocks] page-in keys
   int fin_ranges;               // ranges per group
   int fin_blocks;               // 256-token blocks per group over both regions
-  uint32_t *team_ctl;           // team launch: [0] epoch (round r's tag is epoch + r + 1),
-                                // [1] work-groups finished (0 at rest)
+  uint32_t *team_ctl;           // team launch: [0] epoch (round r's tag is
+                                // team_tag(epoch + r + 1)), [1] work-groups finished (0 at rest)
   unsigned spin_limit;          // team launch: polls per batch of words before giving up
-  int silent_member;            // team launch: member that never publishes (test hook; -1: none)
+  int silent_member;            // team launch: member that never publishes (test builds; -1: none)
+  size_t team_clear_bytes;      // team launch: bytes from `partials` that every team launch on
+                                // this workspace may read; cleared when the epoch restarts
+  unsigned plan_flags;          // KVQ_PLAN_* bits of the call
+  uint32_t *status;             // the call's status word (KVQ_DEVSTATUS_* bits ORed in), or NULL
 };
+
+// Team exchange tags: signalling-NaN bit patterns 0x7F800000 | e with e in
+// [1, 2^22), which no kernel stores as data (arithmetic yields quiet NaNs).
+// A launch uses e = epoch + round + 1 for round < rounds <= 2^18 (groups are
+// at most 2^18), so the epoch stays at or below TEAM_EPOCH_MAX and restarts
+// from 0 once the next launch could pass 2^22 - 1.
+constexpr uint32_t TEAM_TAG_BASE = 0x7F800000u;
+constexpr uint32_t TEAM_EPOCH_MAX = (1u << 22) - (1u << 18) - 1u;
+__host__ __device__ inline uint32_t team_tag(uint32_t e) { return TEAM_TAG_BASE | e; }
 
 // m~, z~, m', z', m_e, z_e, z_b, z_v, acc[128], max ||v||, m-, z-, max c, 4 pad
 constexpr int PART_STRIDE = 144;
@@ -142,6 +155,9 @@ constexpr size_t TEAM_SLOT_BYTES = 560 * 8;
 // Resident work-groups of the team kernel on the current device (0: no team
 // launch possible).
 int team_capacity(int k_format, int v_format, bool paged, bool full, bool ext);
+// The largest team_capacity over every team kernel instance on the current
+// device (bounds the exchange slots any team launch can use).
+int team_capacity_max();
 hipError_t launch_decode_team(const DecodeLaunch &d, int grid, hipStream_t stream);
 
 }  // namespace kvq

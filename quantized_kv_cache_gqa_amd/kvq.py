@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_PKG, "libkvq.so")
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+# the same kernels with kvq_test_set_team_hooks (tests only)
+TEST_LIB_PATH = os.path.join(_PKG, "libkvq_test.so")
 
 FMT = {"bf16": 0, "fp8": 1, "int8": 2, "fp32": 3, "int8g32": 5}
 INT8_GROUP = 32                # channels per scale of "int8g32"
@@ -24,6 +26,13 @@ N_BANDS = 16
 INT8_BLOCK = 256
 STATUS = {0: "ok", 1: "null", 2: "shape", 3: "format", 4: "align", 5: "unsupported",
           6: "workspace", 7: "launch"}
+# plan flags (kvq_attn_args.plan_flags) and device status bits
+PLAN_NO_TEAM = 0x01
+PLAN_VECTOR_ALU = 0x02
+PLAN_GROUP8_SEPARATE = 0x04
+PLAN_FINALIZE_IN_PLACE = 0x08
+PLAN_LAUNCH_PER_REGION = 0x10
+DEVSTATUS_TEAM_WAIT = 0x1
 
 
 class KvqError(RuntimeError):
@@ -49,6 +58,7 @@ class Region(ctypes.Structure):
 class AttnArgs(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("num_q_heads", c_int32), ("num_kv_heads", c_int32),
                 ("head_dim", c_int32), ("sm_scale", ctypes.c_float), ("split_tokens", c_int32),
+                ("plan_flags", ctypes.c_uint32), ("status", c_void_p),
                 ("q", c_void_p), ("prefix", Region), ("suffix", Region), ("out", c_void_p)]
 
 
@@ -73,10 +83,11 @@ class QuantArgs(ctypes.Structure):
 
 
 _lib = None
+_test_lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 
 class PlanInfo(ctypes.Structure):
@@ -87,11 +98,13 @@ class PlanInfo(ctypes.Structure):
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load the library (after torch, so both share torch's HIP runtime)."""
-    global _lib
-    if _lib is not None:
+    global _lib, _test_lib
+    if path == LIB_PATH and _lib is not None:
         return _lib
+    if path == TEST_LIB_PATH and _test_lib is not None:
+        return _test_lib
     if not os.path.exists(path):
-        raise RuntimeError(f"libkvq.so not built at {path}; run quantized_kv_cache_gqa_amd.build")
+        raise RuntimeError(f"{os.path.basename(path)} not built at {path}; run quantized_kv_cache_gqa_amd.build")
     lib = ctypes.CDLL(path)
     lib.kvq_abi_version.restype = ctypes.c_int
     if lib.kvq_abi_version() != ABI_VERSION:
@@ -112,8 +125,18 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut), c_void_p,
                       ctypes.c_size_t, c_void_p]
-    _lib = lib
+    if path == TEST_LIB_PATH:
+        lib.kvq_test_set_team_hooks.restype = None
+        lib.kvq_test_set_team_hooks.argtypes = [ctypes.c_uint, ctypes.c_int]
+        _test_lib = lib
+    else:
+        _lib = lib
     return lib
+
+
+def load_test() -> ctypes.CDLL:
+    """The test build (same kernels, plus kvq_test_set_team_hooks)."""
+    return load(TEST_LIB_PATH)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -248,10 +271,11 @@ class RegionView:
 
 
 def _attn_args(q, prefix: Optional[RegionView], suffix: Optional[RegionView], out, sm_scale,
-               split_tokens, num_kv_heads, need_v=True) -> AttnArgs:
+               split_tokens, num_kv_heads, need_v=True, plan_flags: int = 0, status=None) -> AttnArgs:
     batch, hq, d = q.shape
     return AttnArgs(batch=batch, num_q_heads=hq, num_kv_heads=num_kv_heads, head_dim=d,
-                    sm_scale=sm_scale, split_tokens=split_tokens, q=_ptr(q),
+                    sm_scale=sm_scale, split_tokens=split_tokens, plan_flags=plan_flags,
+                    status=status if isinstance(status, int) else _ptr(status), q=_ptr(q),
                     prefix=prefix.to_c(need_v) if prefix else Region(),
                     suffix=suffix.to_c(need_v) if suffix else Region(), out=_ptr(out))
 
@@ -261,11 +285,17 @@ def workspace_bytes(args: AttnArgs, meter: MeterOut) -> int:
 
 
 class Workspace:
-    """Device scratch for kvq_decode_attn / kvq_meter (grown on demand)."""
+    """Device scratch for kvq_decode_attn / kvq_meter (grown on demand), with
+    the status word the calls that use it report to (int32 [4], word 0)."""
 
     def __init__(self, device):
         self.device = device
         self.buf: Optional[torch.Tensor] = None
+        self.status = torch.zeros(4, dtype=torch.int32, device=device)
+
+    def read_status(self) -> int:
+        """The status bits reported so far (synchronizes with the device)."""
+        return int(self.status[0].item())
 
     def get(self, nbytes: int, stream=None) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
@@ -302,14 +332,17 @@ def _meter_keys(meter, tier_b_delta, value_bound, two_sided, report):
 def plan(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
          suffix: Optional[RegionView], *, sm_scale: float, split_tokens: int = 0,
          meter: bool = True, meter_only: bool = False, tier_b_delta: Optional[float] = None,
-         value_bound: bool = False, two_sided: bool = False, report: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False, report: bool = False,
+         plan_flags: int = 0, with_status: bool = True) -> dict:
     """kvq_decode_plan for the arguments decode_attn would pass (host only;
-    the output and meter pointers only need to be non-NULL and aligned)."""
+    the output, meter and status pointers only need to be non-NULL and
+    aligned)."""
     dummy = _ptr(q) if meter else None
     keys = _meter_keys(meter, tier_b_delta, value_bound, two_sided, report)
     m = MeterOut(**{k: dummy for k in keys}, delta_b=tier_b_delta or 0.0)
     args = _attn_args(q, prefix, suffix, None if meter_only else q, sm_scale, split_tokens,
-                      num_kv_heads, need_v=not meter_only)
+                      num_kv_heads, need_v=not meter_only, plan_flags=plan_flags,
+                      status=_ptr(q) if with_status else None)
     info = PlanInfo()
     _check(load().kvq_decode_plan(ctypes.byref(args), ctypes.byref(m), int(meter_only), ctypes.byref(info)),
            "kvq_decode_plan")
@@ -321,13 +354,16 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
                 meter: bool = True, workspace: Optional[Workspace] = None, out=None,
                 meter_bufs=None, stream=None, meter_only: bool = False,
                 tier_b_delta: Optional[float] = None, value_bound: bool = False,
-                two_sided: bool = False, report: bool = False):
+                two_sided: bool = False, report: bool = False, plan_flags: int = 0,
+                status: Optional[torch.Tensor] = None, lib: Optional[ctypes.CDLL] = None):
     """kvq_decode_attn (or kvq_meter when meter_only).  Returns (out, dict of
     meter tensors); tier_b_delta adds the Tier B outputs with that failure
     probability, value_bound the value term and the joint output bound,
     two_sided the two-sided form of the meter, report the per-block risk
-    report ([batch, num_q_heads, n_blocks] arrays)."""
-    lib = load()
+    report ([batch, num_q_heads, n_blocks] arrays).  The call reports to
+    `status` (int32 device tensor), else to the workspace's status word.
+    plan_flags: KVQ_PLAN_* bits.  lib: another build of the library (tests)."""
+    lib = lib or load()
     batch, hq, d = q.shape
     if out is None and not meter_only:
         out = torch.empty((batch, hq, d), dtype=torch.float32, device=q.device)
@@ -341,12 +377,15 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
             else:
                 meter_bufs[k] = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
     m = MeterOut(**{k: _ptr(v) for k, v in meter_bufs.items()}, delta_b=tier_b_delta or 0.0)
+    workspace = workspace or Workspace(q.device)
+    if status is None:
+        status = workspace.status
     args = _attn_args(q, prefix, suffix, None if meter_only else out, sm_scale, split_tokens,
-                      num_kv_heads, need_v=not meter_only)
-    nbytes = workspace_bytes(args, m)
+                      num_kv_heads, need_v=not meter_only, plan_flags=plan_flags, status=status)
+    nbytes = int(lib.kvq_workspace_bytes(ctypes.byref(args), ctypes.byref(m)))
     if nbytes == 0:
         raise KvqError(2, "kvq_workspace_bytes (invalid arguments)")
-    ws = (workspace or Workspace(q.device)).get(nbytes, stream)
+    ws = workspace.get(nbytes, stream)
     fn = lib.kvq_meter if meter_only else lib.kvq_decode_attn
     _check(fn(ctypes.byref(args), ctypes.byref(m), ws.data_ptr(), ws.numel(), _stream(stream)),
            "kvq_meter" if meter_only else "kvq_decode_attn")

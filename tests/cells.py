@@ -20,6 +20,10 @@ from workloads import Config, gen_layer
 SM_SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
 PREFIX_STREAM = 1_000_000
 
+# kvq_attn_args.plan_flags of every call GpuCase.run and plan() make, unless
+# a call names its own (a test or fixture sets it with monkeypatch.setattr)
+PLAN_FLAGS = 0
+
 
 def dither_seed(cfg: Config) -> int:
     return (cfg.seed * 0x9E3779B97F4A7C15) % (1 << 64)
@@ -139,22 +143,30 @@ class GpuCase:
 
     def run(self, split_tokens: int = 0, meter: bool = True, meter_only: bool = False,
             workspace=None, tier_b_delta=None, value_bound: bool = False, two_sided: bool = False,
-            report: bool = False):
+            report: bool = False, plan_flags=None, expect_status: Optional[int] = 0, lib=None):
+        """One decode (or meter) call; the call's status word must read
+        expect_status afterwards (None: not checked)."""
+        status = torch.zeros(4, dtype=torch.int32, device=self.device)
         out, m = self.kvq.decode_attn(self.inp["q"], self.cfg.h_kv, self.prefix_view,
                                       self.suffix_view, sm_scale=SM_SCALE, split_tokens=split_tokens,
                                       meter=meter, meter_only=meter_only, workspace=workspace,
                                       tier_b_delta=tier_b_delta, value_bound=value_bound,
-                                      two_sided=two_sided, report=report)
+                                      two_sided=two_sided, report=report,
+                                      plan_flags=PLAN_FLAGS if plan_flags is None else plan_flags,
+                                      status=status, lib=lib)
         torch.cuda.synchronize()
+        if expect_status is not None:
+            assert int(status[0]) == expect_status, f"status word {int(status[0]):#x}"
         return out, m
 
 
 def plan(case: GpuCase, split_tokens: int = 0, meter_only: bool = False, tier_b_delta=None,
-         value_bound: bool = False, two_sided: bool = False, report: bool = False) -> dict:
+         value_bound: bool = False, two_sided: bool = False, report: bool = False,
+         plan_flags=None) -> dict:
     return case.kvq.plan(case.inp["q"], case.cfg.h_kv, case.prefix_view, case.suffix_view,
                          sm_scale=SM_SCALE, split_tokens=split_tokens, meter_only=meter_only,
                          tier_b_delta=tier_b_delta, value_bound=value_bound, two_sided=two_sided,
-                         report=report)
+                         report=report, plan_flags=PLAN_FLAGS if plan_flags is None else plan_flags)
 
 
 def oracle_cell(case: GpuCase, b: int, kvh: int, tier_b_delta=None):

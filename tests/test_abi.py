@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 10
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION == 11
     for s in range(8):
         assert lib.kvq_status_string(s).decode()
     assert lib.kvq_status_string(99) == b"unknown status"
@@ -83,9 +83,12 @@ def _region(length, kf="fp8", vf="fp8", exact=True, witness=True):
                       k_exact_format=0, length=length)
 
 
-def _args(batch=64, hq=32, hkv=8, prefix=0, suffix=12628, split=0, **kw):
+TEAM_OFF = 256 + (1 << 20)  # team region: after the control words and the counters' MiB
+
+
+def _args(batch=64, hq=32, hkv=8, prefix=0, suffix=12628, split=0, flags=0, status=FAKE, **kw):
     return kvq.AttnArgs(batch=batch, num_q_heads=hq, num_kv_heads=hkv, head_dim=128,
-                        sm_scale=128 ** -0.5, split_tokens=split, q=FAKE,
+                        sm_scale=128 ** -0.5, split_tokens=split, plan_flags=flags, status=status, q=FAKE,
                         prefix=_region(prefix, "bf16", "fp8", False, False) if prefix else kvq.Region(),
                         suffix=_region(suffix, **kw), out=FAKE)
 
@@ -96,39 +99,40 @@ def _plan(lib, a, m, meter_only=0):
     return info
 
 
-def test_workspace_plan_of_the_batch64_step(lib, monkeypatch):
-    """The per-chunk plan (team launches off, as on a host without a device):
-    one chunk per (request, KV head), partials and the TV's spill rows."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    a = _args()
+def test_workspace_plan_of_the_batch64_step(lib):
+    """The per-chunk plan: one chunk per (request, KV head), partials and the
+    TV's spill rows, after the control words, the counters' MiB and the team
+    region of the same arguments (none without a device)."""
+    a = _args(flags=kvq.PLAN_NO_TEAM)
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
     groups, chunks, G = 64 * 8, 1, 4        # 512 groups fill the GPU: one chunk each
-    counters = 256 + 2048                   # team control words, then one counter per group
+    team = _plan(lib, _args(), m)           # the team plan of the same arguments, if any
+    region = team.workspace_bytes if team.team else TEAM_OFF
     partials = groups * chunks * G * 144 * 4
     spill = groups * 12640 * G * 8                # 12628 tokens padded to 16-token tiles
-    assert n == counters + partials + spill
+    assert n == region + partials + spill
     info = _plan(lib, a, m)
     assert (info.team, info.chunk, info.chunks, info.workspace_bytes) == (0, 12672, 1, n)
-    # without TV: no spill
+    # without TV: no spill (and no team plan either)
     m2 = kvq.MeterOut(tv=None, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
-    assert lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m2)) == counters + partials
+    assert lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m2)) == TEAM_OFF + partials
 
 
-def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
+def test_plan_query_matches_workspace_bytes(lib):
     """kvq_decode_plan reports one size for the decode and the meter call;
     kvq_workspace_bytes covers it and the per-chunk plan of the same
-    arguments; without a device there is no team plan and the sizes agree."""
+    arguments, whose region lies after the team region; without a device
+    there is no team plan and the sizes agree."""
     a = _args()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     n = lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m))
     d, mo = _plan(lib, a, m, 0), _plan(lib, a, m, 1)
     assert d.workspace_bytes == mo.workspace_bytes <= n
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    assert _plan(lib, a, m, 0).workspace_bytes <= n
-    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    chunked = _plan(lib, _args(flags=kvq.PLAN_NO_TEAM), m, 0)
+    assert chunked.workspace_bytes == n and chunked.team == 0
     if d.team:
-        assert d.workspace_bytes >= 256 + (1 << 20)    # slots after the control words and counters
+        assert TEAM_OFF < d.workspace_bytes < n        # slots after the control words and counters
     else:
         assert d.workspace_bytes == n
     if not torch.cuda.is_available():
@@ -141,30 +145,26 @@ def test_plan_query_matches_workspace_bytes(lib, monkeypatch):
     ("bf16", "fp8", 1),
     ("fp8", "fp8", 2),       # key formats differ: one launch per region
 ])
-def test_two_region_calls_take_one_launch_where_formats_allow(lib, monkeypatch, suffix_k, suffix_v, launches):
+def test_two_region_calls_take_one_launch_where_formats_allow(lib, suffix_k, suffix_v, launches):
     """A shared BF16-key prefix and a suffix: one kernel over both regions
-    when the key formats agree, else one per region; KVQ_DECODE_TWO=0 (a test
-    hook) forces one per region; a one-region call is one launch."""
-    monkeypatch.delenv("KVQ_DECODE_TWO", raising=False)
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    when the key formats agree, else one per region; KVQ_PLAN_LAUNCH_PER_REGION
+    forces one per region; a one-region call is one launch."""
     a = _args(batch=16, prefix=632, suffix=1024, kf=suffix_k, vf=suffix_v, exact=False, witness=False)
     m = kvq.MeterOut()
     for meter_only in (0, 1):
         info = _plan(lib, a, m, meter_only)
         assert (info.team, info.launches, info.reserved) == (0, launches, 0)
         assert info.chunks >= 2
-    monkeypatch.setenv("KVQ_DECODE_TWO", "0")
+    a.plan_flags = kvq.PLAN_LAUNCH_PER_REGION
     assert _plan(lib, a, m).launches == 2
-    monkeypatch.delenv("KVQ_DECODE_TWO")
     one = _args(batch=16, suffix=1024, kf=suffix_k, vf=suffix_v, exact=False, witness=False)
     assert _plan(lib, one, m).launches == 1
 
 
-def test_tier_b_arguments_are_checked(lib, monkeypatch):
+def test_tier_b_arguments_are_checked(lib):
     """Tier B needs a failure probability in (0, 1) and keys whose residual is
     the dither's (INT8) or zero (BF16); FP8 keys are rejected, never metered
     with the wrong proxy.  A Tier B call never takes the team plan."""
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     good = _args(batch=8, suffix=32768, kf="int8", vf="int8")
     bad = _args(batch=8, suffix=32768, kf="fp8", vf="fp8")
     mk = lambda delta: kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE,
@@ -209,18 +209,17 @@ def test_value_side_and_tier_a_arguments_are_checked(lib):
                                ctypes.byref(info)) == 0
 
 
-def test_block_report_arguments_and_workspace(lib, monkeypatch):
+def test_block_report_arguments_and_workspace(lib):
     """The report adds the c spill and the per-block radii to the workspace,
     never takes the team plan, needs the Tier B request for Tier B's
     contributions, and ranks at most 512 blocks."""
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     a = _args(batch=64, suffix=12628)
     info = kvq.PlanInfo()
     base = kvq.MeterOut(tv=FAKE, meter=FAKE)
     rep = kvq.MeterOut(tv=FAKE, meter=FAKE, block_mass=FAKE, block_excess=FAKE, block_order=FAKE)
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    n0 = _plan(lib, a, base).workspace_bytes
-    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    n0 = _plan(lib, _args(batch=64, suffix=12628, flags=kvq.PLAN_NO_TEAM), base).workspace_bytes
+    team = _plan(lib, a, base)                            # its team region, if any, is not reserved
+    n0 -= (team.workspace_bytes - TEAM_OFF) if team.team else 0   # for the report (no team plan)
     p = _plan(lib, a, rep)
     groups, rows, nb = 64 * 8, 12640, 50
     assert p.team == 0
@@ -288,13 +287,12 @@ def test_quantize_argument_checks(lib):
     assert lib.kvq_quantize(None, None) == 1
 
 
-def test_int8_group_scale_format_arguments(lib, monkeypatch):
+def test_int8_group_scale_format_arguments(lib):
     """INT8 with per-(token, 32-channel group) scales: keys and values of a
     region share the layout (keys alone for the meter); pages are allowed
     since a token's scales sit in its own row; Tier B accepts the keys but
     not Tier B's per-block contributions (the radius is per token); the
     write path needs no block-aligned start."""
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     g = _args(batch=8, suffix=32768, kf="int8g32", vf="int8g32")
     tier_b = dict(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE, log_a_b=FAKE, bound_b_raw=FAKE,
                   meter_b=FAKE, delta_b=1e-6)
@@ -328,11 +326,10 @@ def test_int8_group_scale_format_arguments(lib, monkeypatch):
     assert lib.kvq_quantize(ctypes.byref(q), None) == 2            # dither tag range
 
 
-def test_outlier_pair_arguments(lib, monkeypatch):
+def test_outlier_pair_arguments(lib):
     """Fixed outlier pairs need group-scale keys, at most 16 pairs, both
     pointers, and (write path) bf16 input, since the stored values are the
     inputs themselves."""
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     info = kvq.PlanInfo()
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     for kf, n, pairs, vals, status in (("int8g32", 4, FAKE, FAKE, 0), ("int8g32", 16, FAKE, FAKE, 0),
@@ -371,71 +368,137 @@ def test_outlier_store_bytes_match_the_page(tmp_path):
         assert n == 10 * b, (m, n)
 
 
-def test_automatic_chunks_are_at_least_640_tokens(lib, monkeypatch):
+def test_automatic_chunks_are_at_least_640_tokens(lib):
     """The per-chunk plan fills about 512 work-groups, but no automatic chunk is
     shorter than 640 tokens (a multiple of 64): fewer, longer chunks won on
     small steps.  An explicit split_tokens is taken as given."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    nt = kvq.PLAN_NO_TEAM
     for batch, hkv, suffix, chunk in ((64, 8, 12628, 12672), (8, 8, 32768, 4096), (4, 8, 131072, 8192),
                                       (16, 8, 1024, 640), (1, 1, 64, 640), (1, 1, 100000, 640)):
-        info = _plan(lib, _args(batch=batch, hkv=hkv, hq=4 * hkv, suffix=suffix), m)
+        info = _plan(lib, _args(batch=batch, hkv=hkv, hq=4 * hkv, suffix=suffix, flags=nt), m)
         assert info.chunk == chunk, (batch, hkv, suffix, info.chunk)
         assert info.chunks == -(-suffix // chunk)
-    info = _plan(lib, _args(batch=16, suffix=1024, split=128), m)
+    info = _plan(lib, _args(batch=16, suffix=1024, split=128, flags=nt), m)
     assert (info.chunk, info.chunks) == (128, 8)
 
 
-def test_several_chunks_per_group_add_a_finish_launch(lib, monkeypatch):
+def test_several_chunks_per_group_add_a_finish_launch(lib):
     """With several chunks per (request, KV head) and a TV or block report,
     the per-chunk plan runs those passes in one more launch (its normalizers
-    and partial sums in the workspace); KVQ_DEFER_FINISH=0 (a test hook) keeps
-    them in the decode launch's last work-group."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+    and partial sums in the workspace); KVQ_PLAN_FINALIZE_IN_PLACE keeps them
+    in the decode launch's last work-group."""
+    nt = kvq.PLAN_NO_TEAM
     tv = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
-    one_chunk = _plan(lib, _args(), tv)                          # 512 groups: one chunk each
+    one_chunk = _plan(lib, _args(flags=nt), tv)                  # 512 groups: one chunk each
     assert (one_chunk.chunks, one_chunk.launches) == (1, 1)
-    a = _args(batch=4, suffix=131072)
+    a = _args(batch=4, suffix=131072, flags=nt)
     info = _plan(lib, a, tv)
     assert info.chunks > 1 and info.launches == 2
     assert _plan(lib, a, kvq.MeterOut(meter=FAKE)).launches == 1  # no TV, no report: nothing to finish
-    monkeypatch.setenv("KVQ_DEFER_FINISH", "0")
+    a.plan_flags = nt | kvq.PLAN_FINALIZE_IN_PLACE
     kept = _plan(lib, a, tv)
     assert kept.launches == 1 and kept.workspace_bytes < info.workspace_bytes
 
 
-def test_group_of_eight_takes_two_launch_sets_on_the_matrix_cores(lib, monkeypatch):
+def test_group_of_eight_takes_two_launch_sets_on_the_matrix_cores(lib):
     """8 query heads per KV head with formats the matrix-core kernels take:
     two launch sets of 4 heads (the planner reports twice the launches);
-    KVQ_DECODE_KERNEL=generic keeps one vector-ALU launch."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+    KVQ_PLAN_VECTOR_ALU keeps one vector-ALU launch."""
+    nt, va = kvq.PLAN_NO_TEAM, kvq.PLAN_VECTOR_ALU
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
-    g4 = _plan(lib, _args(batch=2, hq=16, hkv=4, suffix=4096), m)
-    g8 = _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096), m)
+    g4 = _plan(lib, _args(batch=2, hq=16, hkv=4, suffix=4096, flags=nt), m)
+    g8 = _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096, flags=nt), m)
     assert g8.launches == 2 * g4.launches
-    monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
-    assert _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096), m).launches == g4.launches
-    monkeypatch.delenv("KVQ_DECODE_KERNEL")
-    f32 = _args(batch=2, hq=32, hkv=4, suffix=4096)
+    assert _plan(lib, _args(batch=2, hq=32, hkv=4, suffix=4096, flags=va), m).launches == g4.launches
+    f32 = _args(batch=2, hq=32, hkv=4, suffix=4096, flags=nt)
     f32.suffix.k_exact_format = 3                                 # fp32 exact keys: vector ALUs
     assert _plan(lib, f32, m).launches == g4.launches
 
 
-def test_groups_of_one_and_two_plan_the_padded_tile(lib, monkeypatch):
+def test_groups_of_one_and_two_plan_the_padded_tile(lib):
     """1 or 2 query heads per KV head on matrix-core formats: the per-chunk
     workspace is sized for the 4-head tile (as for a group of 4 with the same
     KV heads); on the vector-ALU kernel it is sized for the group itself."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    nt, va = kvq.PLAN_NO_TEAM, kvq.PLAN_VECTOR_ALU
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
-    g4 = _plan(lib, _args(batch=4, hq=32, hkv=8, suffix=4096), m)
+    g4 = _plan(lib, _args(batch=4, hq=32, hkv=8, suffix=4096, flags=nt), m)
     for hq in (8, 16):
-        padded = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096), m)
+        padded = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096, flags=nt), m)
         assert (padded.workspace_bytes, padded.launches) == (g4.workspace_bytes, g4.launches), hq
-        monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
-        own = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096), m)
-        monkeypatch.delenv("KVQ_DECODE_KERNEL")
+        own = _plan(lib, _args(batch=4, hq=hq, hkv=8, suffix=4096, flags=va), m)
         assert own.workspace_bytes < padded.workspace_bytes, hq
+
+
+# every variable an earlier build of the library read
+OLD_ENV = {"KVQ_DECODE_TEAM": "0", "KVQ_DECODE_KERNEL": "generic", "KVQ_TEAM_HALVES": "0",
+           "KVQ_DEFER_FINISH": "0", "KVQ_DECODE_TWO": "0", "KVQ_TEAM_SPIN_LIMIT": "1",
+           "KVQ_TEAM_SILENT_MEMBER": "0"}
+
+
+def _plan_tuple(lib, a, m, meter_only=0):
+    i = _plan(lib, a, m, meter_only)
+    return (i.team, i.n_teams, i.rounds, i.grid, i.chunk, i.chunks, i.launches, i.workspace_bytes,
+            lib.kvq_workspace_bytes(ctypes.byref(a), ctypes.byref(m)))
+
+
+def test_environment_variables_change_nothing(lib, monkeypatch):
+    """The product library reads no environment: it imports no getenv, exports
+    no test hook, and every plan is the same with each variable that earlier
+    builds read set (plan choices are kvq_attn_args.plan_flags only)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    und = subprocess.run([nm, "-D", "--undefined-only", kvq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", und)
+    dfn = subprocess.run([nm, "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "kvq_test_set_team_hooks" not in dfn
+    tv = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    shapes = [_args(), _args(batch=4, suffix=131072), _args(batch=2, hq=64, hkv=8, suffix=4096),
+              _args(batch=2, hq=8, hkv=8, suffix=4096), _args(batch=16, prefix=632, suffix=1024, kf="bf16",
+                                                               vf="bf16", exact=False, witness=False)]
+    before = [_plan_tuple(lib, a, tv, mo) for a in shapes for mo in (0, 1)]
+    for k, v in OLD_ENV.items():
+        monkeypatch.setenv(k, v)
+    assert [_plan_tuple(lib, a, tv, mo) for a in shapes for mo in (0, 1)] == before
+
+
+def test_test_build_exports_the_team_hooks():
+    """libkvq_test.so is the same library plus kvq_test_set_team_hooks (its
+    host layer compiled with KVQ_TEST_HOOKS); only the tests load it."""
+    assert os.path.exists(kvq.TEST_LIB_PATH)
+    t = kvq.load_test()
+    assert t.kvq_abi_version() == kvq.ABI_VERSION
+    assert hasattr(t, "kvq_test_set_team_hooks")
+    for name in declared_functions():
+        assert hasattr(t, name), name
+
+
+def test_plan_flags_and_status_word_are_checked(lib):
+    """Unknown plan flags and a misaligned status word are rejected before
+    any launch; each flag narrows the plan as documented."""
+    m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
+    info = kvq.PlanInfo()
+    for flags in (0x20, 0x80000000, kvq.PLAN_NO_TEAM | 0x40):
+        a = _args(flags=flags)
+        assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, ctypes.byref(info)) == 5, flags
+        assert lib.kvq_decode_attn(ctypes.byref(a), ctypes.byref(m), FAKE, 1 << 40, None) == 5, flags
+    a = _args(status=FAKE + 4)
+    assert lib.kvq_decode_plan(ctypes.byref(a), ctypes.byref(m), 0, ctypes.byref(info)) == 4
+    # no team plan without a status word, nor with NO_TEAM or VECTOR_ALU
+    for a in (_args(status=None), _args(flags=kvq.PLAN_NO_TEAM), _args(flags=kvq.PLAN_VECTOR_ALU)):
+        assert _plan(lib, a, m).team == 0
+    # the same workspace size whatever the flags: the per-chunk region always
+    # lies after the team region of the arguments
+    sizes = {lib.kvq_workspace_bytes(ctypes.byref(_args(flags=f, status=s)), ctypes.byref(m))
+             for f in (0, kvq.PLAN_NO_TEAM, kvq.PLAN_GROUP8_SEPARATE) for s in (FAKE, None)}
+    assert len(sizes) == 1
+    # finalize in place: one launch where the finish launch would be added
+    long = _args(batch=4, suffix=131072, flags=kvq.PLAN_NO_TEAM)
+    assert _plan(lib, long, m).launches == 2
+    long.plan_flags |= kvq.PLAN_FINALIZE_IN_PLACE
+    assert _plan(lib, long, m).launches == 1

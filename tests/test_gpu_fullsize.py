@@ -103,9 +103,6 @@ def test_full_size_gqa_groups_sampled_cells(gpu_lib, monkeypatch, q_heads):
     teams in one launch.  Sampled cells against the oracle."""
     import dataclasses
     from cells import plan
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
-    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
     base = CONFIGS[3]
     cfg = dataclasses.replace(base, h_q=q_heads, name=base.name + f"-hq{q_heads}")
     layer = cfg.layers - 1

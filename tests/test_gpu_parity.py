@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import cells as cellmod
+from quantized_kv_cache_gqa_amd import kvq
 from cells import GpuCase, SM_SCALE, check_block_report, check_results, check_stored, oracle_cell, plan
 from oracle.numerics import e4m3_table
 from workloads import (CONFIGS, INT8_DITHER_B8_S32K, LONG_B4_S128K_SPLIT, QWEN3_B64_S12628_K8V8,
@@ -118,12 +120,10 @@ SMALL = {
 def kernel(request, monkeypatch):
     """Run a test with the library's kernel choice, with the vector-ALU kernel,
     and with team launches off (TV spill in the workspace)."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     if request.param == "generic":
-        monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
+        monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_VECTOR_ALU)
     elif request.param == "noteam":
-        monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+        monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM)
     return request.param
 
 
@@ -202,7 +202,6 @@ def test_bound_dominates_tv_every_cell(gpu_lib):
 def _team_plan(case, monkeypatch):
     """The plan the library reports with team launches allowed, checked against
     what a team launch must satisfy, and the spill plan it replaces."""
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     p = plan(case)
     cfg = case.cfg
     groups = cfg.batch * cfg.h_kv
@@ -212,9 +211,13 @@ def _team_plan(case, monkeypatch):
     assert p["n_teams"] * p["rounds"] >= groups > p["n_teams"] * (p["rounds"] - 1), p
     assert p["grid"] % 8 == 0 and p["grid"] >= p["team"] * p["n_teams"], p
     assert plan(case, meter_only=True) == p          # one workspace fits both calls
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM)
     assert plan(case)["team"] == 0
-    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", 0)
+    # no status word to report a run-out to: the per-chunk plan, which has no waits
+    nostat = kvq.plan(case.inp["q"], cfg.h_kv, case.prefix_view, case.suffix_view, sm_scale=SM_SCALE,
+                      with_status=False)
+    assert nostat["team"] == 0 and nostat["workspace_bytes"] > p["workspace_bytes"], nostat
     return p
 
 
@@ -223,13 +226,12 @@ def test_team_many_members_and_empty_chunks(gpu_lib, monkeypatch):
     tens of members of 64+ tokens each, those past the short request's end
     with empty chunks; parity on every cell and agreement with the
     spill-to-workspace path."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     cfg = small_variant(LONG_B4_S128K_SPLIT, batch=2, h_kv=2, suffix_len=5000, lens=(5000, 1500))
     case = GpuCase(cfg)
     p = _team_plan(case, monkeypatch)
     assert p["team"] >= 16 and p["chunk"] * (p["team"] - 1) >= 1500, p   # members with no tokens
     out_t, m_t, _ = _all_cells(case)
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM)
     out_s, m_s = case.run()
     # the two paths round the fp16 P.V weights against different running
     # maxima: compare per head as the oracle bar does (norm-relative)
@@ -243,7 +245,6 @@ def test_team_several_rounds_sampled_cells(gpu_lib, monkeypatch):
     """640 groups of ragged 3000-token requests: more groups than resident
     teams, so every team runs several rounds (tags of successive rounds, slot
     parity reuse); sampled cells against the oracle, bitwise repeatable."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
     lens = tuple(3000 - 37 * i for i in range(80))
     cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=80, h_kv=8, suffix_len=3000, lens=lens)
     case = GpuCase(cfg)
@@ -264,30 +265,34 @@ def test_team_wait_budget_runs_out_to_nan_not_a_hang(gpu_lib, monkeypatch, group
     result of the affected groups is NaN (never a stale or partial value),
     and the next call without the hooks is correct again.  A group of 8 runs
     its paired 4-head teams in one launch."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
     make = lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
     cfg = make() if group == 4 else _g8(make)()
     case = GpuCase(cfg, value_witness=True)
     p = _team_plan(case, monkeypatch)
     assert p["team"] >= 2, p
     assert plan(case, value_bound=True, two_sided=True)["team"] == p["team"]
-    monkeypatch.setenv("KVQ_TEAM_SPIN_LIMIT", "64")
-    monkeypatch.setenv("KVQ_TEAM_SILENT_MEMBER", "1")
-    t0 = time.time()
-    out, m = case.run()
-    assert time.time() - t0 < 30
-    assert torch.isnan(out).all()
-    for k in ("tv", "bound_raw", "meter", "log_a"):
-        assert torch.isnan(m[k]).all(), k
-    out, m = case.run(value_bound=True, two_sided=True)   # the team kernel with the extensions
-    assert torch.isnan(out).all()
-    for k in ("tv", "meter", "value_err", "out_bound", "v_norm_max", "log_a_minus", "meter_two_sided",
-              "bound_tanh"):
-        assert torch.isnan(m[k]).all(), k
-    monkeypatch.delenv("KVQ_TEAM_SPIN_LIMIT")
-    monkeypatch.delenv("KVQ_TEAM_SILENT_MEMBER")
+    # the test build of the library (same kernels) exposes the two hooks
+    tlib = kvq.load_test()
+    tlib.kvq_test_set_team_hooks(64, 1)
+    try:
+        t0 = time.time()
+        out, m = case.run(lib=tlib, expect_status=kvq.DEVSTATUS_TEAM_WAIT)   # reported, not silent
+        assert time.time() - t0 < 30
+        assert torch.isnan(out).all()
+        for k in ("tv", "bound_raw", "meter", "log_a"):
+            assert torch.isnan(m[k]).all(), k
+        out, m = case.run(value_bound=True, two_sided=True, lib=tlib,       # the team kernel with
+                          expect_status=kvq.DEVSTATUS_TEAM_WAIT)            # the extensions
+        assert torch.isnan(out).all()
+        for k in ("tv", "meter", "value_err", "out_bound", "v_norm_max", "log_a_minus", "meter_two_sided",
+                  "bound_tanh"):
+            assert torch.isnan(m[k]).all(), k
+    finally:
+        tlib.kvq_test_set_team_hooks(0, -1)
+    o_t, m_t = case.run(lib=tlib)                   # hooks off: status clear, results as the product's
     _all_cells(case)
+    o_p, m_p = case.run()
+    assert torch.equal(o_t, o_p) and all(torch.equal(m_t[k], m_p[k]) for k in m_p)
     _all_cells(case, value_bound=True, two_sided=True)
 
 
@@ -299,8 +304,6 @@ def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch, group):
     eager team calls on the same workspace between the replays; a
     per-chunk call on that workspace between them changes nothing either.
     A group of 8 captures its one launch of paired 4-head teams."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
     from quantized_kv_cache_gqa_amd import kvq
     make = lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
     cfg = make() if group == 4 else _g8(make)()
@@ -310,14 +313,15 @@ def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch, group):
         assert p["launches"] == 1 and p["grid"] >= 2 * p["team"] * p["n_teams"], p
     ws = kvq.Workspace(torch.device("cuda"))
 
-    def call(out=None, meter_bufs=None):
+    def call(out=None, meter_bufs=None, plan_flags=0):
         return kvq.decode_attn(case.inp["q"], cfg.h_kv, case.prefix_view, case.suffix_view,
-                               sm_scale=SM_SCALE, workspace=ws, out=out, meter_bufs=meter_bufs)
+                               sm_scale=SM_SCALE, workspace=ws, out=out, meter_bufs=meter_bufs,
+                               plan_flags=plan_flags)
 
     o_team, m_team = call()
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM)
     o_chunk, m_chunk = case.run()
-    monkeypatch.delenv("KVQ_DECODE_TEAM")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", 0)
     torch.cuda.synchronize()
     og = torch.empty_like(o_chunk)
     mg = {k: torch.empty_like(v) for k, v in m_chunk.items()}
@@ -342,13 +346,12 @@ def test_graph_capture_of_a_team_launch(gpu_lib, monkeypatch, group):
         for k in m_team:
             assert torch.equal(m2[k], m_team[k]), k
         if it == 1:                                 # the per-chunk plan on the same workspace
-            monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
-            o3, m3 = call()
-            monkeypatch.delenv("KVQ_DECODE_TEAM")
+            o3, m3 = call(plan_flags=kvq.PLAN_NO_TEAM)
             torch.cuda.synchronize()
             assert torch.equal(o3, o_chunk)
             for k in m_chunk:
                 assert torch.equal(m3[k], m_chunk[k]), k
+    assert ws.read_status() == 0
 
 
 def _two_region_fp8(paged):
@@ -374,18 +377,18 @@ def test_two_regions_in_one_launch(gpu_lib, monkeypatch, name):
     """Cartridge + suffix in one launch (every chunk of either region may be the
     last to arrive and merge): every cell against the oracle, and bitwise the
     results of one launch per region, for the decode and the meter-only call."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_DECODE_TWO", raising=False)
     cfg = TWO_REGION[name]()
     case = GpuCase(cfg, page_seed=5)
     split = 128
-    monkeypatch.setenv("KVQ_DEFER_FINISH", "0")      # decode launches only (the finish
-    p = plan(case, split_tokens=split)              # launch has its own test)
+    # decode launches only (the finish launch has its own test)
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM | kvq.PLAN_FINALIZE_IN_PLACE)
+    p = plan(case, split_tokens=split)
     assert (p["team"], p["launches"]) == (0, 1), p
     assert plan(case, split_tokens=split, meter_only=True)["launches"] == 1
     o1, m1, _ = _all_cells(case, split_tokens=split)
     _, q1 = case.run(split_tokens=split, meter_only=True)
-    monkeypatch.setenv("KVQ_DECODE_TWO", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS",
+                        kvq.PLAN_NO_TEAM | kvq.PLAN_FINALIZE_IN_PLACE | kvq.PLAN_LAUNCH_PER_REGION)
     assert plan(case, split_tokens=split)["launches"] == 2
     o2, m2 = case.run(split_tokens=split)
     _, q2 = case.run(split_tokens=split, meter_only=True)
@@ -536,7 +539,7 @@ def test_block_report_every_cell(gpu_lib, kernel, monkeypatch, name, with_b):
                 qh = kvh * cfg.group + h
                 a_1 = math.expm1(float(ref["log_a"][h]))
                 assert abs(float(m["block_excess"][b, qh].double().sum()) - a_1) <= 1e-4 * max(1.0, a_1)
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", cellmod.PLAN_FLAGS | kvq.PLAN_NO_TEAM)
     o2, m2 = case.run(tier_b_delta=delta)
     assert torch.equal(out, o2)
     for k in m2:
@@ -624,19 +627,17 @@ FINISH = {
 @pytest.mark.parametrize("name", list(FINISH))
 def test_finish_launch_matches_the_oracle_and_the_in_kernel_finalize(gpu_lib, monkeypatch, name):
     """Several chunks per group: the TV and the block report run in the finish
-    launch.  Both that and the decode launch's own finalize (KVQ_DEFER_FINISH=0)
+    launch.  Both that and the decode launch's own finalize (KVQ_PLAN_FINALIZE_IN_PLACE)
     match the oracle on every cell; the page-in order is the same, the TV
     differs by summation order only."""
-    monkeypatch.setenv("KVQ_DECODE_TEAM", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM)
     make, delta = FINISH[name]
     cfg = make()
     case = GpuCase(cfg, page_seed=12)
     res = {}
     for mode in ("finish", "kept"):
         if mode == "kept":
-            monkeypatch.setenv("KVQ_DEFER_FINISH", "0")
-        else:
-            monkeypatch.delenv("KVQ_DEFER_FINISH", raising=False)
+            monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_NO_TEAM | kvq.PLAN_FINALIZE_IN_PLACE)
         p = plan(case, split_tokens=512, report=True, tier_b_delta=delta)
         assert p["chunks"] > 1 and (p["launches"] >= 2) == (mode == "finish"), p
         out, m = case.run(split_tokens=512, report=True, tier_b_delta=delta)
@@ -700,23 +701,20 @@ def test_group_of_eight_team_pairs_against_two_launches(gpu_lib, monkeypatch):
     take query heads 0-3 and 4-7, on a shape with several rounds, ragged
     requests, the value side and the two-sided form; sampled cells against the
     oracle, bitwise repeatable, and within rounding of two launches of 4 heads
-    (KVQ_TEAM_HALVES=0, whose plan has its own team size and chunk)."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
-    monkeypatch.delenv("KVQ_TEAM_HALVES", raising=False)
+    (KVQ_PLAN_GROUP8_SEPARATE, whose plan has its own team size and chunk)."""
     lens = tuple(3000 - 61 * i for i in range(40))
     cfg = _g8(lambda: small_variant(QWEN3_B64_S12628_K8V8, batch=40, h_kv=8, suffix_len=3000, lens=lens))()
     case = GpuCase(cfg, value_witness=True)
     kw = dict(value_bound=True, two_sided=True)
     p = _team_plan(case, monkeypatch)
     assert p["rounds"] >= 3, p
-    monkeypatch.delenv("KVQ_DECODE_TEAM", raising=False)
     pe = plan(case, **kw)
     assert pe["team"] and pe["launches"] == 1, pe
     assert pe["grid"] >= 2 * pe["team"] * pe["n_teams"] and pe["grid"] % 8 == 0, pe
     o1, m1, _ = _all_cells(case, cells=[(0, 0), (13, 7), (39, 3), (39, 0)], **kw)
     o1b, m1b = case.run(**kw)
     assert torch.equal(o1, o1b)
-    monkeypatch.setenv("KVQ_TEAM_HALVES", "0")
+    monkeypatch.setattr(cellmod, "PLAN_FLAGS", kvq.PLAN_GROUP8_SEPARATE)
     q = plan(case, **kw)
     assert q["team"] and q["launches"] == 2, q
     o2, m2 = case.run(**kw)
@@ -732,15 +730,18 @@ def test_group_of_eight_team_pairs_against_two_launches(gpu_lib, monkeypatch):
 
 def test_team_epoch_restarts_below_its_limit(gpu_lib, monkeypatch):
     """The team epoch kept in the workspace's first word moves past each
-    launch's tags and restarts from 0 before the tags could wrap; results stay
-    exact across the restart (the control word is caller memory, set here
-    from the host)."""
-    monkeypatch.delenv("KVQ_DECODE_KERNEL", raising=False)
+    launch's tags and restarts from 0 before the tags could leave the
+    signalling-NaN range; the launch that restarts it clears the team region,
+    so words planted there with the tags the next launch waits for (the
+    control word and the region are caller memory, set here from the host)
+    are gone, and results stay exact across the restart."""
     from quantized_kv_cache_gqa_amd import kvq
     cfg = small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=3000, lens=(3000, 2500))
     case = GpuCase(cfg)
     p = _team_plan(case, monkeypatch)
     ws = kvq.Workspace(torch.device("cuda"))
+    team_off = 256 + (1 << 20)                     # after the control words and the counters
+    epoch_max = (1 << 22) - (1 << 18) - 1
 
     def call():
         return kvq.decode_attn(case.inp["q"], cfg.h_kv, case.prefix_view, case.suffix_view,
@@ -750,15 +751,23 @@ def test_team_epoch_restarts_below_its_limit(gpu_lib, monkeypatch):
     torch.cuda.synchronize()
     ctl = ws.buf[:8].view(torch.int32)
     assert int(ctl[0]) == p["rounds"] + 1 and int(ctl[1]) == 0
-    ctl[0] = int(0xF0000000 - p["rounds"]) - (1 << 32)          # the last epoch below the limit
+    region = ws.buf[team_off:p["workspace_bytes"]].view(torch.int64)
+    # every team word: tag of the first round after a restart, value 1e30
+    region.fill_((0x7F800001 << 32) | 0x7149F2CA)
+    ctl[0] = epoch_max - p["rounds"]                # this launch restarts the epoch at its end
     torch.cuda.synchronize()
-    for expect in (0, p["rounds"] + 1):
-        o, m = call()
-        torch.cuda.synchronize()
+    o, m = call()
+    torch.cuda.synchronize()
+    assert int(ctl[0]) == 0 and int(ctl[1]) == 0
+    assert int(region.count_nonzero()) == 0         # the restart cleared the region
+    for expect in (p["rounds"] + 1, 2 * (p["rounds"] + 1)):
         assert torch.equal(o, o_ref)
         for k in m_ref:
             assert torch.equal(m[k], m_ref[k]), k
+        o, m = call()
+        torch.cuda.synchronize()
         assert int(ctl[0]) == expect and int(ctl[1]) == 0
+    assert ws.read_status() == 0
 
 
 def _gq(make, g):
