@@ -336,8 +336,12 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       fb[e] = band_factor_up(qp, 4 * g + e, d.sm_scale);
       fhi = fhi > fb[e] ? fhi : fb[e];
     }
-    fhi = fhi > __shfl_xor(fhi, 16) ? fhi : __shfl_xor(fhi, 16);
-    fhi = fhi > __shfl_xor(fhi, 32) ? fhi : __shfl_xor(fhi, 32);
+    // (each shuffle once, by every lane: a shuffle under a divergent branch
+    // may read inactive lanes)
+    const double f16s = __shfl_xor(fhi, 16);
+    fhi = fhi > f16s ? fhi : f16s;
+    const double f32s = __shfl_xor(fhi, 32);
+    fhi = fhi > f32s ? fhi : f32s;
     int ce = 0;
     if (fhi > 0.0 && fhi <= 1.7976931348623157e308) {
       int ex;
