@@ -404,6 +404,26 @@ kvq_status kvq_decode_attn(const kvq_attn_args *args, const kvq_meter_out *meter
 kvq_status kvq_meter(const kvq_attn_args *args, const kvq_meter_out *meter,
                      void *workspace, size_t workspace_bytes, kvq_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * kvq_decode_attn with the library's own scratch instead of a caller
+ * workspace.  The scratch is one static device array of KVQ_SCRATCH_BYTES per
+ * device, held until the process ends; the call allocates nothing.  The
+ * caller still passes the inputs, outputs and (for the team plan) the status
+ * word.  The first call on a device looks the array up and enqueues one fill
+ * kernel on `stream` that clears it (make that first call outside graph
+ * capture if the capture must not contain it); later calls rely on the
+ * workspace protocol, which leaves the scratch ready after every call.
+ * Returns KVQ_ERR_WORKSPACE, before anything is enqueued, when the plan for
+ * these arguments needs more than KVQ_SCRATCH_BYTES (kvq_decode_plan's
+ * workspace_bytes); the per-chunk plan's TV spill is the large part (32
+ * bytes per cached token and KV head).  Every call on one device shares its
+ * array: calls that overlap in time on one device (other streams, other
+ * threads) race and must not be made. */
+#define KVQ_SCRATCH_BYTES ((size_t)96 << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_attn_args *args, const kvq_meter_out *meter,
+                                   kvq_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -363,6 +364,32 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
   return KVQ_OK;
 }
 
+// The scratch of kvq_decode_attn_noalloc: one array per device, brought in
+// by the code object (no allocation call).  Host code never uses the name as
+// an address: it looks up the device address once per device
+// (hipGetSymbolAddress, with that device current) and passes that pointer.
+__device__ __align__(256) unsigned char scratch[KVQ_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];       // device address of `scratch`, per device
+
+// The current device's scratch; the first call on a device looks it up and
+// enqueues one fill kernel on `stream` that clears it.
+kvq_status device_scratch(hipStream_t stream, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_LAUNCH;
+    if (launch_fill_zero(p, KVQ_SCRATCH_BYTES, stream) != hipSuccess) return KVQ_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
 RegionDev region_dev(const kvq_region &r, bool is_prefix) {
   RegionDev d;
   memset(&d, 0, sizeof(d));
@@ -692,6 +719,17 @@ kvq_status kvq_decode_attn(const kvq_attn_args *a, const kvq_meter_out *m, void 
 kvq_status kvq_meter(const kvq_attn_args *a, const kvq_meter_out *m, void *ws, size_t ws_bytes,
                      kvq_stream stream) {
   return run_decode(a, m, ws, ws_bytes, (hipStream_t)stream, true);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_attn_args *a, const kvq_meter_out *m, kvq_stream stream) {
+  Plan p;
+  const kvq_status s = make_plan(a, m, false, p);
+  if (s != KVQ_OK) return s;
+  if (p.bytes > KVQ_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;     // beyond the static scratch
+  void *ws = nullptr;
+  const kvq_status t = device_scratch((hipStream_t)stream, &ws);
+  if (t != KVQ_OK) return t;
+  return run_decode(a, m, ws, KVQ_SCRATCH_BYTES, (hipStream_t)stream, false);
 }
 
 #ifdef KVQ_TEST_HOOKS

@@ -86,7 +86,9 @@ _lib = None
 _test_lib = None
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
-           "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter"]
+           "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter",
+           "kvq_decode_attn_noalloc"]
+SCRATCH_BYTES = 96 << 20       # KVQ_SCRATCH_BYTES: the static scratch of kvq_decode_attn_noalloc
 ABI_VERSION = 11
 
 
@@ -125,6 +127,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut), c_void_p,
                       ctypes.c_size_t, c_void_p]
+    lib.kvq_decode_attn_noalloc.restype = ctypes.c_int
+    lib.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut), c_void_p]
     if path == TEST_LIB_PATH:
         lib.kvq_test_set_team_hooks.restype = None
         lib.kvq_test_set_team_hooks.argtypes = [ctypes.c_uint, ctypes.c_int]
@@ -390,3 +394,19 @@ def decode_attn(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView]
     _check(fn(ctypes.byref(args), ctypes.byref(m), ws.data_ptr(), ws.numel(), _stream(stream)),
            "kvq_meter" if meter_only else "kvq_decode_attn")
     return out, meter_bufs
+
+
+def decode_attn_noalloc(q: torch.Tensor, num_kv_heads: int, prefix: Optional[RegionView],
+                        suffix: Optional[RegionView], *, sm_scale: float, out: torch.Tensor,
+                        meter_bufs: dict, status: torch.Tensor, split_tokens: int = 0,
+                        plan_flags: int = 0, tier_b_delta: Optional[float] = None, stream=None) -> None:
+    """kvq_decode_attn_noalloc: the decode call on the library's static scratch.
+    The caller brings every output buffer and the status word (this function
+    allocates nothing either); raises KvqError(6) when the plan needs more than
+    SCRATCH_BYTES."""
+    lib = load()
+    m = MeterOut(**{k: _ptr(v) for k, v in meter_bufs.items()}, delta_b=tier_b_delta or 0.0)
+    args = _attn_args(q, prefix, suffix, out, sm_scale, split_tokens, num_kv_heads,
+                      plan_flags=plan_flags, status=status)
+    _check(lib.kvq_decode_attn_noalloc(ctypes.byref(args), ctypes.byref(m), _stream(stream)),
+           "kvq_decode_attn_noalloc")
