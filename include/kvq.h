@@ -189,12 +189,14 @@ typedef struct kvq_attn_args {
  *   bound_raw = 1/2 (A^2 - 1), +inf when beyond the float range
  *   meter     = min(1, bound_raw)
  * A is evaluated in the log domain and c is never truncated: when a term of
- * the log-domain sum overflows the float range, log_a and bound_raw are +inf
- * and meter is 1, the trivial bound (WitCert Sec. 3 numerics, Sec. 6.2.4).
- * c_t is rounded upward: sm_scale ||q_b|| is formed in float64, raised by
- * 2^-20 relative and split into fp16 pieces whose sum is not below it, so
- * the fp32 sum over the 16 bands (at most 16 roundings to nearest of
- * non-negative terms) is not below c_t of the stored witness.
+ * the log-domain sum overflows (or a band factor sm_scale ||q_b|| log2(e)
+ * reaches 2^15, beyond the fp16 operand of the matrix-core witness dot),
+ * log_a and bound_raw are +inf and meter is 1, the trivial bound (WitCert
+ * Sec. 3 numerics, Sec. 6.2.4); bound_tanh is then 1.  c_t is rounded
+ * upward: each band factor is raised by 2^-19 relative (a constant rounded
+ * up) and enters as fp16 pieces whose sum is not below it, which covers the
+ * fp32 roundings of the band norm and of the sum over the 16 bands, so the
+ * computed c_t is not below c_t of the stored witness.
  * Tier B (WitCert Sec. 4.2, Lemma 2; Sec. 6.2.3): the sub-Gaussian certificate
  * of subtractively dithered INT8 keys, from the stored scales and the query
  * alone (no witness).  Requesting any of its outputs needs delta_b in (0, 1)

@@ -429,6 +429,14 @@ void chunk_launches(const kvq_attn_args *a, const kvq_meter_out *m, const Plan &
   d.qg = p.group;
   d.qh0 = 0;
   d.sm_scale = a->sm_scale;
+  {
+    // the factor of the witness dot's band norms, raised by 2^-19 and rounded
+    // up to fp32 (its own rounding then only lifts it further)
+    const double cf = (double)a->sm_scale * 1.4426950408889634074 * (1.0 + 0x1p-19);
+    float f = (float)cf;
+    if ((double)f < cf) f = nextafterf(f, INFINITY);
+    d.c_factor = f;
+  }
   d.q = a->q;
   d.out = meter_only ? nullptr : a->out;
   d.plan_flags = p.flags;

@@ -84,10 +84,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
       qv[h][i + 3] = t.w * qs;
     }
     // band norms of bands 2j and 2j+1 (coordinates 4b..4b+3 and 64+4b..64+4b+3)
-    // (raised in float64 and rounded up to fp32: c formed from them with
-    // 5 roundings of non-negative terms stays at or above its exact value)
+    // (raised: c formed from them with 5 more roundings of non-negative
+    // terms stays at or above its exact value)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) qn[h][e] = f32_round_up(band_factor_up(qp, 2 * j + e, d.sm_scale));
+    for (int e = 0; e < 2; ++e) qn[h][e] = band_factor_up(qp, 2 * j + e, d.c_factor);
   }
 
   // value side (WitCert Sec. 3 output bound): zv = sum p~ rho on the attention
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         if (t < n) {
           const float pt = fast_exp2(lt[i] - Mt) * iZt;
           ms += pt;
-          ex += pt * expm1f(cr[i] * LN2);
+          if (pt > 0.0f) ex += pt * expm1f(c_or_inf(cr[i]) * LN2);
         }
       }
       for (int off = 1; off < 64; off <<= 1) {

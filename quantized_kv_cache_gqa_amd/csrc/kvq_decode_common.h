@@ -85,29 +85,33 @@ __device__ __forceinline__ float merge_factor(float m, float mnew) {
 
 // Theorem 2's c_t = sm_scale sum_b ||q_b|| w_{t,b} (WitCert Sec. 4.1), in log2
 // units, must not fall below its exact value for the stored witness.  The
-// band factor sm_scale ||q_b|| log2(e) is formed in float64 from the fp32
-// query (band b: coordinates 4b..4b+3 and 64+4b..64+4b+3) and raised by
-// 2^-19 relative, which exceeds the relative error of the fp32 sums c is
-// formed with later (at most 17 roundings to nearest of non-negative terms,
-// 17 * 2^-24 < 2^-19).
-constexpr double C_RAISE = 1.0 + 0x1p-19;
-__device__ __forceinline__ double band_factor_up(const float *qp, int bb, float sm_scale) {
-  double ss = 0.0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const double a = qp[4 * bb + i], c = qp[64 + 4 * bb + i];
-    ss = fma(a, a, ss);
-    ss = fma(c, c, ss);
-  }
-  return sqrt(ss) * (double)sm_scale * 1.4426950408889634074 * C_RAISE;
+// band factor ||q_b|| sm_scale log2(e) (band b: coordinates 4b..4b+3 and
+// 64+4b..64+4b+3 of the fp32 query) is formed in fp32 against c_factor =
+// sm_scale log2(e) (1 + 2^-19) rounded up: the sum of squares takes 8
+// roundings of non-negative terms, the square root one more (it halves the
+// sum's relative error), the product one: at most 6 units of 2^-24 below the
+// raised value.  The sums c is formed with later lose at most 17 more (17
+// roundings to nearest of non-negative terms); 23 < 32 = the raise, so c is
+// at or above its exact value.
+__device__ __forceinline__ float band_factor_up(float4 a, float4 c, float c_factor) {
+  float ss = a.x * a.x;
+  ss = fmaf(c.x, c.x, ss);
+  ss = fmaf(a.y, a.y, ss);
+  ss = fmaf(c.y, c.y, ss);
+  ss = fmaf(a.z, a.z, ss);
+  ss = fmaf(c.z, c.z, ss);
+  ss = fmaf(a.w, a.w, ss);
+  ss = fmaf(c.w, c.w, ss);
+  return sqrtf(ss) * c_factor;
+}
+__device__ __forceinline__ float band_factor_up(const float *qp, int bb, float c_factor) {
+  return band_factor_up(*reinterpret_cast<const float4 *>(qp + 4 * bb),
+                        *reinterpret_cast<const float4 *>(qp + 64 + 4 * bb), c_factor);
 }
 
-// the smallest float >= x (x >= 0, finite or +inf)
-__device__ __forceinline__ float f32_round_up(double x) {
-  float f = (float)x;
-  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
-  return f;
-}
+// A spilled c for the block report: NaN (an overflowed witness dot whose
+// band had witness 0) counts as +inf, the trivial contribution.
+__device__ __forceinline__ float c_or_inf(float c) { return c == c ? c : __builtin_huge_valf(); }
 
 // log A (WitCert Thm. 1, in nats) from the attention state (Mq, Zq) and the
 // state (Mm, Zm) over l~ + c, both in log2 units.  A is evaluated in the log
@@ -218,7 +222,7 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
         if (t < n) {
           const float pt = fast_exp2(rd(sp + 2 * (size_t)e) - Mt) * iZt;
           ms += pt;
-          ex += pt * expm1f(rd(rp + e) * LN2);
+          if (pt > 0.0f) ex += pt * expm1f(c_or_inf(rd(rp + e)) * LN2);
         }
       }
       for (int off = 1; off < 64; off <<= 1) {
@@ -384,7 +388,10 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         if (d.bound_two_sided && hv) d.bound_two_sided[qh] = tf;
         if (d.meter_two_sided && hv) d.meter_two_sided[qh] = fminf(fminf(1.0f, bf), tf);
         // tanh shape: tanh(max_t c_t), c in natural units
-        if (d.bound_tanh && hv) d.bound_tanh[qh] = (float)tanh((double)Cmax * 0.69314718055994530942);
+        // (a meter sum that overflowed, log A = +inf, had a c of +inf or NaN,
+        // which a maximum skips: the trivial bound then, as for log A)
+        if (d.bound_tanh && hv)
+          d.bound_tanh[qh] = log_a == __builtin_huge_val() ? 1.0f : (float)tanh((double)Cmax * 0.69314718055994530942);
       }
       if (d.has_value) {
         // value side and the joint output bound (WitCert Sec. 3): the meter

@@ -47,6 +47,9 @@ __device__ __forceinline__ float bf16_round(float x) {
   return __uint_as_float(f32_to_bf16_bits(x) << 16);
 }
 
+// the same rounding (to nearest, ties to even) by the conversion instruction
+__device__ __forceinline__ float bf16_hw_round(float x) { return (float)(__bf16)x; }
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // 8 E4M3 codes (two dwords) -> 8 bf16, exact.
@@ -309,7 +312,6 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   //      head, whose results are not written)
   bf16x8_t bq[4];
   f16x4_t bw;
-  float c_unscale = 1.0f;                          // 2^-ce of this lane's head (see below)
   {
     const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
 #pragma unroll
@@ -325,44 +327,26 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       }
     }
     // witness dot: the raised band factors of head hh (bands 4 g .. 4 g + 3
-    // in this lane), scaled by a power of two 2^ce so that the head's largest
-    // lies in [2^14, 2^15) (no fp16 piece overflows or loses its bits), then
-    // split into three fp16 pieces h1 + h2 + h3 >= the scaled factor (h3
-    // rounded up; the remainders are exact in float64).  Column pp = 0, 1, 2
-    // carries piece pp; the collapsed sum is scaled back by 2^-ce (exact).
-    double fb[4], fhi = 0.0;
+    // in this lane) as two fp16 pieces h1 + h2 >= the factor (h1 to nearest,
+    // h2 the fp32-exact remainder rounded up), in columns pp = 0 and 1.  A
+    // factor at or beyond 2^15, past what the fp16 operand holds, is an
+    // overflow: its piece is +inf, so every c of that head is +inf (or NaN
+    // where the band's witness is 0), which the finalize reports as the
+    // trivial bound (WitCert Sec. 3 numerics: +inf on overflow, c never
+    // truncated).  (Scaling the factors instead would keep a scale factor
+    // live through the tile loop, which measurably slows it.)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      fb[e] = band_factor_up(qp, 4 * g + e, d.sm_scale);
-      fhi = fhi > fb[e] ? fhi : fb[e];
-    }
-    // (each shuffle once, by every lane: a shuffle under a divergent branch
-    // may read inactive lanes)
-    const double f16s = __shfl_xor(fhi, 16);
-    fhi = fhi > f16s ? fhi : f16s;
-    const double f32s = __shfl_xor(fhi, 32);
-    fhi = fhi > f32s ? fhi : f32s;
-    int ce = 0;
-    if (fhi > 0.0 && fhi <= 1.7976931348623157e308) {
-      int ex;
-      frexp(fhi, &ex);                               // fhi in [2^(ex-1), 2^ex)
-      ce = min(max(15 - ex, -120), 120);
-    }
-    c_unscale = ldexpf(1.0f, -ce);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double x = ldexp(fb[e], ce);
-      const _Float16 h1 = (_Float16)x;
-      const double r1 = x - (double)h1;
-      const _Float16 h2 = (_Float16)r1;
-      const double r2 = r1 - (double)h2;
-      _Float16 h3 = (_Float16)r2;
-      if ((double)h3 < r2) {                         // next fp16 toward +inf
-        uint16_t u = __builtin_bit_cast(uint16_t, h3);
-        u = (u == 0x8000u || u == 0u) ? (uint16_t)1u : (uint16_t)((u & 0x8000u) ? u - 1u : u + 1u);
-        h3 = __builtin_bit_cast(_Float16, u);
-      }
-      bw[e] = pp == 0 ? h1 : (pp == 1 ? h2 : (pp == 2 ? h3 : (_Float16)0.0f));
+      const float f = band_factor_up(qp, 4 * g + e, d.c_factor);
+      const bool ok = f < 32768.0f;                  // (inputs are finite)
+      const _Float16 h1n = (_Float16)f;
+      const float r = f - (float)h1n;                 // exact
+      const _Float16 h2n = (_Float16)r;
+      const uint16_t u = __builtin_bit_cast(uint16_t, h2n);   // next fp16 toward +inf if below
+      const uint16_t up = (u & 0x7fffu) == 0u ? (uint16_t)1u : (uint16_t)((u & 0x8000u) ? u - 1u : u + 1u);
+      const _Float16 h1 = ok ? h1n : __builtin_bit_cast(_Float16, (uint16_t)0x7c00u);
+      const _Float16 h2 = ok ? __builtin_bit_cast(_Float16, (float)h2n < r ? up : u) : (_Float16)0.0f;
+      bw[e] = pp == 0 ? h1 : (pp == 1 ? h2 : (_Float16)0.0f);
     }
   }
 
@@ -597,7 +581,7 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const bool valid = tk < c1;
     float lq = collapse(dq, pp) * T.ks;
     float le = (do_tv && has_exact) ? collapse(de, pp) : lq;
-    const float cc = (do_meter && has_wit) ? collapse(dc, pp) * c_unscale : 0.0f;
+    const float cc = (do_meter && has_wit) ? collapse(dc, pp) : 0.0f;
     if (!valid) {
       lq = NEG_INF;
       le = NEG_INF;

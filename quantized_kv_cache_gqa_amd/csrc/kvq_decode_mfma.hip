@@ -352,7 +352,9 @@ __device__ __forceinline__ void team_epilogue(const DecodeLaunch &d, uint32_t ep
         if (d.log_a_minus && hv) d.log_a_minus[qh] = ok ? (float)log_am : qnan;
         if (d.bound_two_sided && hv) d.bound_two_sided[qh] = ok ? tf : qnan;
         if (d.meter_two_sided && hv) d.meter_two_sided[qh] = ok ? fminf(fminf(1.0f, bf), tf) : qnan;
-        if (d.bound_tanh && hv) d.bound_tanh[qh] = ok ? (float)tanh((double)Cm * 0.69314718055994530942) : qnan;
+        if (d.bound_tanh && hv)       // (log A = +inf: an overflowed c, which a maximum skips)
+          d.bound_tanh[qh] = ok ? (log_a == __builtin_huge_val() ? 1.0f : (float)tanh((double)Cm * 0.69314718055994530942))
+                                : qnan;
       }
       if (d.has_value) {
         const float verr = Zq > 0.0f ? Zv / Zq : 0.0f;

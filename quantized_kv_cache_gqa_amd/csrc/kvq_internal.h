@@ -60,6 +60,7 @@ struct DecodeLaunch {
   // launches of 4 heads each)
   int qg, qh0;
   float sm_scale;
+  float c_factor;               // sm_scale log2(e) (1 + 2^-19), rounded up to fp32 (see band_factor_up)
   const float *q;
   float *out;
   RegionDev region;
