@@ -251,6 +251,17 @@ def check_stored(case: GpuCase, b: int, kvh: int, encs) -> None:
 
 TOL_OUT = 2e-3
 TOL_METER = 1e-5
+# The kernels round c upward (its band factors are raised by 2^-19 so that
+# the fp32 roundings of the witness dot cannot take c below its exact value
+# for the stored witness, which keeps the bound sound): their log A may then
+# exceed the oracle's by up to this fraction of max_t c_t, never fall below.
+C_RAISE_REL = 2.0 ** -18
+
+
+def log_a_within(g: float, r: float, cmax: float) -> bool:
+    """log A within 1e-5 of the oracle's, plus the one-sided allowance of the
+    upward-rounded c."""
+    return r - TOL_METER <= g <= r + TOL_METER + C_RAISE_REL * cmax
 
 
 def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kvh: int, ref,
@@ -272,17 +283,28 @@ def check_results(case: GpuCase, out, meter: Dict[str, torch.Tensor], b: int, kv
             assert abs(tv - ref["tv"][h]) <= TOL_METER, (b, qh, tv, ref["tv"][h])
             worst["tv"] = max(worst["tv"], abs(tv - ref["tv"][h]))
         if "bound_raw" in meter:
+            # log A within its bar; bound_raw within 1e-5 (relative above 1), or,
+            # above 1, through log A (reading 14: "relative 1e-5 on bound_raw,
+            # or absolute 1e-5 on log A"); +inf matches +inf, except within
+            # 1e-3 of the overflow edge
+            cmax = float(np.max(ref["c"][h])) if np.size(ref["c"][h]) else 0.0
+            lg, lr = float(meter["log_a"][b, qh]), float(ref["log_a"][h])
+            assert log_a_within(lg, lr, cmax), (b, qh, "log_a", lg, lr, cmax)
+            worst["log_a"] = max(worst.get("log_a", 0.0), abs(lg - lr))
             bg = float(meter["bound_raw"][b, qh])
             br = float(ref["bound_raw"][h])
             if math.isinf(br) or math.isinf(bg):
                 edge = 0.5 * math.log(2 * float(np.finfo(np.float32).max) + 1)
-                assert math.isinf(br) == math.isinf(bg) or abs(float(ref["log_a"][h]) - edge) < 1e-3
+                assert math.isinf(br) == math.isinf(bg) or abs(lr - edge) < 1e-3 + C_RAISE_REL * cmax
             else:
+                # (the raise's share: d bound / d log A relative to max(1, bound)
+                # is at most 3 below bound 1 and at most 3 above it)
                 err = abs(bg - br) / max(1.0, br)
-                assert err <= TOL_METER, (b, qh, bg, br)
+                assert err <= TOL_METER + 3 * C_RAISE_REL * cmax or (br > 1.0 and log_a_within(lg, lr, cmax)), \
+                    (b, qh, bg, br)
                 worst["bound"] = max(worst["bound"], err)
             mg = float(meter["meter"][b, qh])
-            assert abs(mg - float(ref["meter"][h])) <= TOL_METER
+            assert abs(mg - float(ref["meter"][h])) <= TOL_METER + 3 * C_RAISE_REL * cmax, (b, qh, mg)
             worst["meter"] = max(worst["meter"], abs(mg - float(ref["meter"][h])))
         if "bound_b_raw" in meter:
             # Tier B: the same bar as Tier A (log A and bound within 1e-5,

@@ -1,6 +1,7 @@
-"""Parity at the workloads' full sizes, in the launch configuration the bench
-uses (library-chosen split, or the workload's own), on sampled cells that the
-oracle computes one by one."""
+"""Parity at the workloads' full sizes on sampled cells that the oracle
+computes one by one: the meter extensions, the group-scale INT8 format with
+outlier pairs, and GQA groups of 1 and 8 (every cell of the plain workloads
+is in test_gpu_fullsize_every_cell.py)."""
 import pytest
 import torch
 
@@ -10,33 +11,10 @@ from workloads import CONFIGS
 pytestmark = pytest.mark.gpu
 
 SAMPLES = {
-    2: None,                                      # every cell (16 x 8)
     3: [(0, 0), (63, 7), (17, 3), (40, 5)],
     4: [(0, 0), (7, 7), (3, 2)],
     5: [(0, 0), (3, 7), (2, 4)],
 }
-
-
-@pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_sampled_cells(gpu_lib, idx):
-    cfg = CONFIGS[idx]
-    layer = cfg.layers - 1                        # last layer: largest layer id in the dither tag
-    case = GpuCase(cfg, layer=layer, page_seed=1)
-    out, m = case.run(split_tokens=cfg.split_tokens)
-    cells = SAMPLES[idx] or [(b, h) for b in range(cfg.batch) for h in range(cfg.h_kv)]
-    worst = {}
-    for b, kvh in cells:
-        encs, ref = oracle_cell(case, b, kvh)
-        check_stored(case, b, kvh, encs)
-        w = check_results(case, out, m, b, kvh, ref)
-        for k, v in w.items():
-            worst[k] = max(worst.get(k, 0.0), v)
-    # properties over every cell of the layer
-    assert torch.all(m["tv"] <= m["bound_raw"] + 1e-6)
-    assert torch.all(torch.isfinite(out))
-    print(f"[{cfg.name} layer {layer}] sampled={len(cells)} worst={worst}", flush=True)
-    del case
-    torch.cuda.empty_cache()
 
 
 EXTENSIONS = {4: 1e-9, 5: None}                   # Tier B's delta (INT8 keys only)
