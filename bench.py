@@ -490,6 +490,20 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         "cpu_baseline": base}), flush=True)
 
 
+def copy_calibrate(nbytes: int):
+    """One plain device copy of `nbytes` bytes, so that HBM counters taken over
+    the same run can be scaled by what they read for a copy of known size."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy of {nbytes} bytes done")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -503,6 +517,8 @@ def main():
         h_kv = CONFIGS[args.workload].h_kv if args.workload else 0
         if not h_kv or args.q_heads % h_kv or args.q_heads // h_kv not in (1, 2, 4, 8):
             sys.exit("--q-heads needs --workload and 1, 2, 4 or 8 query heads per KV head")
+    if args.copy_calibrate:
+        copy_calibrate(args.copy_calibrate)
     if args.workload != 0:
         # at least 30 untimed launches first: the clocks settle over some
         # milliseconds, longer than a few sub-millisecond launches take
@@ -586,15 +602,6 @@ def main():
             if rc:
                 raise RuntimeError(f"kvq_decode_attn status {rc}")
 
-    if args.copy_calibrate:
-        n = args.copy_calibrate // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.copy_calibrate} bytes done")
-        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
   const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
   const int pre_nb = (d.prefix_len + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK;
   __shared__ float fin_s[G][4];
-  __shared__ float tvpart_s[256];
+  __shared__ float tvw_s[WAVES][G];
   __shared__ int last_s;
   if (tid < 4 * G) fin_s[tid >> 2][tid & 3] = d.fin[(size_t)grp * 4 * G + tid];
   __syncthreads();
@@ -525,14 +525,8 @@ __global__ __launch_bounds__(256) void finish_kernel(const DecodeLaunch d) {
         if (t + 1 < n) tvp_add(acc, x[i][k].z, x[i][k].w, Mt, iZt, Me, iZe);
       }
     }
-    tvpart_s[tid] = acc;
-    __syncthreads();
-    if (tid < G) {
-      float sum = 0.0f;
-      for (int t = 0; t < 256; ++t)                   // fixed order
-        if (((2 * t) % (4 * G)) / 4 == tid) sum += tvpart_s[t];
-      st_dev(d.tvp + ((size_t)grp * d.fin_ranges + r) * G + tid, sum);
-    }
+    const float sum = head_share_sum<G>(acc, tvw_s);
+    if (tid < G) st_dev(d.tvp + ((size_t)grp * d.fin_ranges + r) * G + tid, sum);
   }
 
   // ---- block report: wavefront w takes block r FIN_BLOCKS + w

@@ -94,6 +94,7 @@ __device__ __forceinline__ float merge_factor(float m, float mnew) {
 // roundings to nearest of non-negative terms); 23 < 32 = the raise, so c is
 // at or above its exact value.
 __device__ __forceinline__ float band_factor_up(float4 a, float4 c, float c_factor) {
+#pragma clang fp contract(off)                         // (the product is rounded by itself)
   float ss = a.x * a.x;
   ss = fmaf(c.x, c.x, ss);
   ss = fmaf(a.y, a.y, ss);
@@ -181,6 +182,28 @@ __device__ __forceinline__ void load_row16(const void *base, size_t row, int j, 
       }
     }
   }
+}
+
+// TV shares of a 256-thread work-group whose thread t holds a partial sum of
+// head (t % 2G) / 2: per head, a butterfly over the wavefront's lanes of that
+// head (lane bit 0 and the bits from log2(2G) up), then the four wavefronts'
+// sums in wavefront order.  Returns head tid's total in threads tid < G
+// (fixed order: bitwise reproducible).  Every thread of the work-group must
+// call it.
+template <int G>
+__device__ __forceinline__ float head_share_sum(float x, float (*tvw)[G]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  x += __shfl_xor(x, 1);
+#pragma unroll
+  for (int off = 2 * G; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  if (lane < 2 * G && (lane & 1) == 0) tvw[wv][lane >> 1] = x;
+  __syncthreads();
+  float s = 0.0f;
+  if (tid < G) {
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += tvw[w][tid];
+  }
+  return s;
 }
 
 // Block-decomposable risk report (WitCert Sec. 6.3.5), run by the finalizing
@@ -431,7 +454,7 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
     // (a group with several chunks runs this pass in the finish launch
     // instead, spread over many work-groups)
     constexpr int TV_U = 4;
-    __shared__ float tvpart_s[256];
+    __shared__ float tvw_s[WAVES][G];
     const int hmine = ((2 * tid) % (4 * G)) / 4;
     float acc_tv = 0.0f;
     if (do_tv) {
@@ -468,14 +491,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
         }
       }
     }
-    tvpart_s[tid] = acc_tv;
-    __syncthreads();
-    if (tid < G) {
-      float s = 0.0f;
-      for (int t = 0; t < 256; ++t)                   // fixed order: bitwise reproducible
-        if (((2 * t) % (4 * G)) / 4 == tid) s += tvpart_s[t];
-      if (d.qh0 + tid < d.qg) d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * s;
-    }
+    const float s = head_share_sum<G>(acc_tv, tvw_s);
+    if (tid < G && d.qh0 + tid < d.qg) d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.5f * s;
   }
   if (d.has_report) block_report_pass<G>(d, grp, b, kvh, single, suf_len, fin_s);
   if (tid == 0 && !single)                          // ready for the next call

@@ -50,6 +50,28 @@ __device__ __forceinline__ float bf16_round(float x) {
 // the same rounding (to nearest, ties to even) by the conversion instruction
 __device__ __forceinline__ float bf16_hw_round(float x) { return (float)(__bf16)x; }
 
+// x * y rounded to fp32 by itself (never fused into a following add)
+__device__ __forceinline__ float mul_rn(float x, float y) {
+#pragma clang fp contract(off)
+  return x * y;
+}
+
+// Piece p of the exact three-way bf16 split x = hi + mid + lo (p = 3: zero).
+// All three pieces are formed and one is picked with bit masks: a select
+// chain on the lane's p compiles to divergent branches, and a load feeding
+// the next element is then not issued before the branches close.
+// (No contraction: a product feeding x must not be fused into x - hi, or the
+// pieces would split the unrounded product and kernels would differ in the
+// last bit depending on how the compiler schedules them.)
+__device__ __forceinline__ float split3_piece(float x, int p) {
+#pragma clang fp contract(off)
+  const float hi = bf16_round(x);
+  const float mid = bf16_round(x - hi);
+  const float lo = bf16_round(x - hi - mid);
+  const uint32_t m0 = 0u - (uint32_t)(p == 0), m1 = 0u - (uint32_t)(p == 1), m2 = 0u - (uint32_t)(p == 2);
+  return __uint_as_float((__float_as_uint(hi) & m0) | (__float_as_uint(mid) & m1) | (__float_as_uint(lo) & m2));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // 8 E4M3 codes (two dwords) -> 8 bf16, exact.
@@ -131,11 +153,31 @@ struct TileRegs {
   uint4 ko;        // outlier values 8 g .. 8 g + 7 of token j16 (bf16, 0 past 2 m)
 };
 
-// Addressing of one (request, KV head) region range ending at c1, and the
-// loads of one 16-token tile.  Dense regions: one uniform base per tensor and
-// 32-bit per-lane row offsets (a request holds < 2^24 tokens); paged suffix:
-// per-token page lookup with 64-bit rows.  Rows are clamped to the last valid
-// token, so a tile past the end re-reads a valid row (its data is unused).
+// Tokens between a wavefront's consecutive tiles in the tile loop (the
+// work-group's four wavefronts take 16-token tiles in turn).
+constexpr int TILE_STEP = 16 * WAVES;
+
+// Page ids of one tile of a paged region: `lo` holds its tokens 0..7, `hi`
+// tokens 8..15 (the same page when pages hold 16 tokens).  Unused when dense.
+struct TilePages {
+  int lo = 0, hi = 0;
+};
+
+// Addressing of one (request, KV head) region range [c0, c1), and the loads
+// of one 16-token tile.  Dense regions: one uniform base per tensor and 32-bit
+// per-lane row offsets (a request holds < 2^24 tokens); paged suffix: 64-bit
+// rows from the tile's page ids.  Rows are clamped to the last valid token, so
+// a tile past the end re-reads a valid row (its data is unused).
+//
+// Page ids come from a per-wavefront window: one vector load fetches the
+// pages of the wavefront's next 64 tiles (lane i: tile kw + i; tiles are
+// TILE_STEP tokens apart from tb = c0 + 16 wv), and each tile reads its two
+// ids back with lane reads.  A page lookup per token instead puts a
+// dependent load in front of every tile's loads, and its wait drains the
+// in-order load counter, so a wavefront keeps about one tile in flight.
+// (Tiles start on multiples of 16 tokens: chunk starts are multiples of 64,
+// team chunks whole tiles, so a tile never spans more than two 8-token pages
+// or one 16-token page.)
 template <int KF, int VF, bool PAGED>
 struct TileSrc {
   using RowT = typename std::conditional<PAGED, size_t, uint32_t>::type;
@@ -147,9 +189,23 @@ struct TileSrc {
   int n_op;
   const int32_t *ptab;
   int pshift, page_size, h_kv, kvh, last;
+  // paged regions: the page window (empty for dense regions)
+  struct Window {
+    int tb;                    // first token of this wavefront's tiles
+    int kw;                    // first tile index held
+    int32_t lo, hi;
+  };
+  struct NoWindow {};
+  using WinT = typename std::conditional<PAGED, Window, NoWindow>::type;
+  mutable WinT win;
 
-  __device__ __forceinline__ TileSrc(const DecodeLaunch &d, int b, int kvh_, int c1) {
+  __device__ __forceinline__ TileSrc(const DecodeLaunch &d, int b, int kvh_, int c0, int c1) {
     const RegionDev &R = d.region;
+    if constexpr (PAGED) {
+      win.tb = c0 + 16 * (int)(threadIdx.x >> 6);
+      win.kw = -64;            // (the first tile refills)
+      win.lo = win.hi = 0;
+    }
     const size_t sh = R.is_prefix ? (size_t)kvh_ : (size_t)b * d.h_kv + kvh_;
     const size_t row0 = PAGED ? 0 : sh * (size_t)R.length;
     ptab = PAGED ? R.page_table + (size_t)b * R.max_pages : nullptr;
@@ -171,10 +227,36 @@ struct TileSrc {
     kob = R.kout + row0 * (size_t)(2 * R.n_op);
   }
 
-  __device__ __forceinline__ RowT row_of(int t) const {   // row index relative to row0
+  // the page ids of tile t0 (a tile of this wavefront, at or after every
+  // tile asked for before); refills the window every 64 tiles
+  __device__ __forceinline__ TilePages tile_pages(int t0) const {
+    TilePages P;
+    if constexpr (PAGED) {
+      const int k = __builtin_amdgcn_readfirstlane((t0 - win.tb) / TILE_STEP);
+      if (k - win.kw >= 64) {
+        // t0 <= last here (the loop loads only while a tile of the chunk
+        // remains), so every clamped index below is a valid token
+        const int t = win.tb + TILE_STEP * (k + (int)(threadIdx.x & 63));
+        win.lo = ptab[min(t, last) >> pshift];
+        if (page_size == 8) win.hi = ptab[min(t + 8, last) >> 3];
+        win.kw = k;
+      }
+      P.lo = __builtin_amdgcn_readlane(win.lo, k - win.kw);
+      P.hi = page_size == 8 ? __builtin_amdgcn_readlane(win.hi, k - win.kw) : P.lo;
+    }
+    return P;
+  }
+
+  // row index (relative to row0) of token t of the tile whose pages are P
+  __device__ __forceinline__ RowT row_of(int t, const TilePages &P) const {
     t = min(t, last);
     if constexpr (PAGED) {
-      const size_t pg = (size_t)ptab[t >> pshift];
+      // a token past the end clamps to the last one, whose page is lo or hi
+      // by its own position (or both, for a tile wholly past the end).  A
+      // mask select: a select of the two fields compiles to an indexed load
+      // from a stack copy of P, whose wait would drain the tile's loads.
+      const uint32_t m = 0u - ((uint32_t)t >> 3 & 1u);
+      const size_t pg = (size_t)(((uint32_t)P.lo & ~m) | ((uint32_t)P.hi & m));
       return (pg * h_kv + kvh) * page_size + (t & (page_size - 1));
     } else {
       return (RowT)t;
@@ -182,15 +264,16 @@ struct TileSrc {
   }
 
   __device__ __forceinline__ void load(TileRegs &T, int t0, bool exact, bool wit, bool vrec) const {
-    load_keys(T, t0, exact);
-    load_rest(T, t0, wit, vrec);
+    const TilePages P = tile_pages(t0);
+    load_keys(T, t0, exact, P);
+    load_rest(T, t0, wit, vrec, P);
   }
 
   // stored and exact keys with the key scale (what the logits need first)
-  __device__ __forceinline__ void load_keys(TileRegs &T, int t0, bool exact) const {
+  __device__ __forceinline__ void load_keys(TileRegs &T, int t0, bool exact, const TilePages &P) const {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
-    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
+    const RowT ra = row_of(t0 + j16, P), rk = row_of(t0 + 4 * g + pp, P);
     if constexpr (KF == KVQ_FMT_FP8_E4M3 || KF == KVQ_FMT_INT8_DITHER) {
       const uint4 *p = reinterpret_cast<const uint4 *>(kb + ra * D + 32 * g);
       T.k[0] = p[0];
@@ -205,7 +288,7 @@ struct TileSrc {
       T.k[0] = uint4{a0.x, a0.y, a1.x, a1.y};
       T.k[1] = uint4{a2.x, a2.y, a3.x, a3.y};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) T.kg[e] = *reinterpret_cast<const uint2 *>(ksg + row_of(t0 + 4 * g + e) * 4);
+      for (int e = 0; e < 4; ++e) T.kg[e] = *reinterpret_cast<const uint2 *>(ksg + row_of(t0 + 4 * g + e, P) * 4);
       T.ks = 1.0f;
       if (n_op > 0) {
         // values 8 g + 2 i, 8 g + 2 i + 1 (a pair's two channels) as one word;
@@ -231,22 +314,22 @@ struct TileSrc {
   }
 
   // witness, values and the value scale
-  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit, bool vrec) const {
+  __device__ __forceinline__ void load_rest(TileRegs &T, int t0, bool wit, bool vrec, const TilePages &P) const {
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4, j16 = lane & 15, pp = lane & 3;
-    const RowT ra = row_of(t0 + j16), rk = row_of(t0 + 4 * g + pp);
+    const RowT ra = row_of(t0 + j16, P), rk = row_of(t0 + 4 * g + pp, P);
     if (wit) T.wit = *reinterpret_cast<const uint2 *>(wb + ra * NB + 4 * g);
     if (vrec) T.vrec = *reinterpret_cast<const uint32_t *>(vwb + rk * 2);
     if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const RowT re = row_of(t0 + 4 * g + e);
+        const RowT re = row_of(t0 + 4 * g + e, P);
         T.v8[e] = *reinterpret_cast<const uint2 *>(vbb + re * D + 8 * j16);
         if constexpr (VF == KVQ_FMT_INT8_G32) T.vg[e] = vsg[re * 4 + (j16 >> 2)];
       }
       T.vs = VF == KVQ_FMT_FP8_E4M3 ? vsb[rk] : 1.0f;
     } else if constexpr (VF == KVQ_FMT_BF16) {
-      const RowT r0 = row_of(t0 + (lane >> 3)), r1 = row_of(t0 + 8 + (lane >> 3));
+      const RowT r0 = row_of(t0 + (lane >> 3), P), r1 = row_of(t0 + 8 + (lane >> 3), P);
       const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
       const uint4 *p1 = reinterpret_cast<const uint4 *>(vbb + r1 * (2 * D) + 32 * (lane & 7));
       T.vb[0] = p0[0]; T.vb[1] = p0[1];
@@ -307,23 +390,68 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     tb_l = logf(2.0f * (float)(d.prefix_len + sl)) + d.tier_b_log_inv_delta;
   }
 
+  // The wavefront's first tile is requested ahead of the query work below,
+  // so that its loads and q's travel together (with INT8 block scales the
+  // loop loads its first tile after the block's operands).
+  // (A short-lived source serves that load, so that the loop's own source,
+  // built below, is not live across the query work.)
+  constexpr bool BLOCK_LOOP = KF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_DITHER;
+  static_assert(!(PAGED && BLOCK_LOOP), "block-scale INT8 regions are never paged");
+  TileRegs ta, tb;
+  typename TileSrc<KF, VF, PAGED>::WinT win0{};    // (paged: the page window it fetched)
+  if constexpr (!BLOCK_LOOP && !SPILL_LDS) {
+    const TileSrc<KF, VF, PAGED> first(d, b, kvh, c0, c1);
+    if (c0 + 16 * wv < c1) first.load(ta, c0 + 16 * wv, do_tv && has_exact, do_meter && has_wit, do_v);
+    win0 = first.win;
+  }
+
   // ---- B operands of the logit contractions, column j16 = 4 hh + pp (a
   //      group of 1 or 2 query heads pads the tile with copies of its last
   //      head, whose results are not written)
   bf16x8_t bq[4];
   f16x4_t bw;
+  const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
+  // Every q value of this lane: dims 32 g .. 32 g + 31 (the split) and the
+  // dims of bands 4 g .. 4 g + 3 (the witness factors: 4 k .. 4 k + 3 and
+  // 64 + 4 k .. 64 + 4 k + 3 for band k).  A chunk's launch requests them
+  // all before any is used (with its first tile, above), so the prologue
+  // costs one round trip.
+  //
+  // The team launch (SPILL_LDS) keeps each q element's load next to its
+  // split, where the select of the split's piece makes the loads run one
+  // after another, and loads its first tile in the loop: its round prologue
+  // then lasts as long as the memory system takes to answer, which keeps
+  // the two work-groups of a CU taking turns at streaming (about one
+  // streaming work-group per CU, HBM steady near 5.9 TB/s).  Measured on the
+  // batch-64 x 12,628-token layer, issuing the loads together lets the
+  // teams' rounds fall into step instead: all work-groups stream at once and
+  // then all exchange at once, and the launch is 2.5% slower (0.657 against
+  // 0.641 ms); a fixed pause in its place is slower still.
+  float4 qa[8], qband[8];
+  if constexpr (!SPILL_LDS) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[i] = reinterpret_cast<const float4 *>(qp + 32 * g)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qband[2 * e] = *reinterpret_cast<const float4 *>(qp + 4 * (4 * g + e));
+      qband[2 * e + 1] = *reinterpret_cast<const float4 *>(qp + 64 + 4 * (4 * g + e));
+    }
+  }
   {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
+    const float *qf = reinterpret_cast<const float *>(qa);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = qp[32 * g + 8 * s + e] * qs;
-        const float hi = bf16_round(x);
-        const float mid = bf16_round(x - hi);
-        const float lo = bf16_round(x - hi - mid);
-        const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
-        bq[s][e] = (__bf16)piece;                   // exact: piece is a bf16 value
+      for (int e = 0; e < 8; ++e) {                 // exact: each piece is a bf16 value
+        if constexpr (SPILL_LDS) {
+          const float x = mul_rn(qp[32 * g + 8 * s + e], qs);
+          const float hi = bf16_round(x);
+          const float mid = bf16_round(x - hi);
+          const float lo = bf16_round(x - hi - mid);
+          bq[s][e] = (__bf16)(pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f)));
+        } else {
+          bq[s][e] = (__bf16)split3_piece(mul_rn(qf[8 * s + e], qs), pp);
+        }
       }
     }
     // witness dot: the raised band factors of head hh (bands 4 g .. 4 g + 3
@@ -337,7 +465,9 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     // live through the tile loop, which measurably slows it.)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float f = band_factor_up(qp, 4 * g + e, d.c_factor);
+#pragma clang fp contract(off)                         // (f rounded: r below is exact)
+      const float f = SPILL_LDS ? band_factor_up(qp, 4 * g + e, d.c_factor)
+                                : band_factor_up(qband[2 * e], qband[2 * e + 1], d.c_factor);
       const bool ok = f < 32768.0f;                  // (inputs are finite)
       const _Float16 h1n = (_Float16)f;
       const float r = f - (float)h1n;                 // exact
@@ -377,21 +507,23 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
     if constexpr (I8K) {
       const uint16_t *ks = (const uint16_t *)R.k_scale + srow;
-      const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
+      // the block's scales and q (dims 32 g .. 32 g + 31), all loads first
+      uint4 sc[4];
+      float4 qv[8];
+#pragma unroll
+      for (int s8 = 0; s8 < 4; ++s8) sc[s8] = *reinterpret_cast<const uint4 *>(ks + 32 * g + 8 * s8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = reinterpret_cast<const float4 *>(qp + 32 * g)[i];
+      const float *qf = reinterpret_cast<const float *>(qv);
       float ss = 0.0f;                             // sum of (q_c s_c)^2 in log2 units
 #pragma unroll
       for (int s8 = 0; s8 < 4; ++s8) {
-        const uint4 sc = *reinterpret_cast<const uint4 *>(ks + 32 * g + 8 * s8);
-        const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+        const uint32_t sw[4] = {sc[s8].x, sc[s8].y, sc[s8].z, sc[s8].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = qp[32 * g + 8 * s8 + e] * qs * fp16_bits_to_f32((sw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          const float x = mul_rn(mul_rn(qf[8 * s8 + e], qs), fp16_bits_to_f32((sw[e >> 1] >> (16 * (e & 1))) & 0xffffu));
           ss = fmaf(x, x, ss);
-          const float hi = bf16_round(x);
-          const float mid = bf16_round(x - hi);
-          const float lo = bf16_round(x - hi - mid);
-          const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
-          bqs[s8][e] = (__bf16)piece;
+          bqs[s8][e] = (__bf16)split3_piece(x, pp);
         }
       }
       if (do_b) {
@@ -426,7 +558,6 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   bf16x8_t bqo;
   const int n_op = R.n_op;
   if constexpr (GK) {
-    const float *qp = d.q + ((size_t)b * d.h_q + (size_t)kvh * d.qg + min(qh0 + hh, d.qg - 1)) * D;
     uint32_t bm0 = 0, bm1 = 0;                       // bypassed pairs 0..31, 32..63
     if (n_op > 0) {
       const int32_t *opp = R.opairs + (size_t)kvh * n_op;
@@ -443,14 +574,19 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
           const int P = opp[slot];
           bool act = P >= 0 && P < 64;
           for (int i = 0; i < slot; ++i) act = act && opp[i] != P;
-          if (act) x = qp[P + 64 * (k & 1)] * qs;
+          if (act) x = mul_rn(qp[P + 64 * (k & 1)], qs);
         }
-        const float hi = bf16_round(x);
-        const float mid = bf16_round(x - hi);
-        const float lo = bf16_round(x - hi - mid);
-        bqo[e] = (__bf16)(pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f)));
+        bqo[e] = (__bf16)split3_piece(x, pp);
       }
     }
+    // q at channels 32 s8 + 8 g .. + 7, all loads first
+    float4 qv[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 4; ++s8) {
+      qv[2 * s8] = *reinterpret_cast<const float4 *>(qp + 32 * s8 + 8 * g);
+      qv[2 * s8 + 1] = *reinterpret_cast<const float4 *>(qp + 32 * s8 + 8 * g + 4);
+    }
+    const float *qf = reinterpret_cast<const float *>(qv);
 #pragma unroll
     for (int s8 = 0; s8 < 4; ++s8) {
       // channels 32 s8 + 8 g + e: pair (32 s8 + 8 g + e) mod 64
@@ -458,23 +594,20 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool byp = (bw_ >> (8 * g + e)) & 1u;
-        const float x = byp ? 0.0f : qp[32 * s8 + 8 * g + e] * qs;
+        const float x = byp ? 0.0f : mul_rn(qf[8 * s8 + e], qs);
         qg2[s8] = fmaf(x, x, qg2[s8]);
-        const float hi = bf16_round(x);
-        const float mid = bf16_round(x - hi);
-        const float lo = bf16_round(x - hi - mid);
-        const float piece = pp == 0 ? hi : (pp == 1 ? mid : (pp == 2 ? lo : 0.0f));
-        bqs[s8][e] = (__bf16)piece;
+        bqs[s8][e] = (__bf16)split3_piece(x, pp);
       }
       qg2[s8] += __shfl_xor(qg2[s8], 16);
       qg2[s8] += __shfl_xor(qg2[s8], 32);
     }
   }
 
-  const TileSrc<KF, VF, PAGED> src(d, b, kvh, c1);
+  const TileSrc<KF, VF, PAGED> src(d, b, kvh, c0, c1);
+  if constexpr (!BLOCK_LOOP && !SPILL_LDS) src.win = win0;
+  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit, do_v); };
   float *spill_g = ((do_tv || do_r) && !SPILL_LDS) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
   float *rspill_g = do_r ? rspill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
-  auto load_tile = [&](TileRegs &T, int t0) { src.load(T, t0, do_tv && has_exact, do_meter && has_wit, do_v); };
 
   // per-lane accumulator states (lane = one (token slot, head) pair)
   float mq = NEG_INF, zq = 0.0f;     // attention softmax, maximum uniform per head
@@ -740,11 +873,11 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     }
   };
 
-  // two register sets, no copies: the loads of one tile overlap the other's
-  // math.  The next tile is always loaded (rows clamp to the last valid
-  // token, so past the end this re-reads a valid row and the data is unused).
-  TileRegs ta, tb;
-  if constexpr (I8K || I8V) {
+  // two register sets (ta, tb), no copies: the loads of one tile overlap the
+  // other's math.  The next tile is always loaded (rows clamp to the last
+  // valid token, so past the end this re-reads a valid row and the data is
+  // unused).
+  if constexpr (BLOCK_LOOP) {
     // INT8: wavefront wv takes whole 256-token blocks wv, wv + 4, ... of the
     // chunk, so the block operands change once per 16 tiles
     const int blk0 = c0 / KVQ_INT8_BLOCK;
@@ -764,9 +897,11 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       }
     }
   } else {
-    constexpr int STEP = 16 * WAVES;
-    int t0 = c0 + 16 * wv;
-    if (t0 < c1) load_tile(ta, t0);
+    constexpr int STEP = TILE_STEP;
+    int t0 = c0 + 16 * wv;                      // (a chunk's first tile is loaded above)
+    if constexpr (SPILL_LDS) {
+      if (t0 < c1) load_tile(ta, t0);
+    }
     while (t0 < c1) {
       load_tile(tb, t0 + STEP);
       process(ta, t0);

@@ -82,8 +82,7 @@ class QuantArgs(ctypes.Structure):
                 ("outlier_pairs", c_void_p), ("k_outliers_out", c_void_p), ("n_outlier_pairs", c_int32)]
 
 
-_lib = None
-_test_lib = None
+_libs = {}                      # loaded libraries by absolute path
 
 SYMBOLS = ["kvq_abi_version", "kvq_status_string", "kvq_quantize", "kvq_workspace_bytes",
            "kvq_decode_plan", "kvq_workspace_init", "kvq_decode_attn", "kvq_meter",
@@ -100,11 +99,9 @@ class PlanInfo(ctypes.Structure):
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load the library (after torch, so both share torch's HIP runtime)."""
-    global _lib, _test_lib
-    if path == LIB_PATH and _lib is not None:
-        return _lib
-    if path == TEST_LIB_PATH and _test_lib is not None:
-        return _test_lib
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
     if not os.path.exists(path):
         raise RuntimeError(f"{os.path.basename(path)} not built at {path}; run quantized_kv_cache_gqa_amd.build")
     lib = ctypes.CDLL(path)
@@ -129,12 +126,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                       ctypes.c_size_t, c_void_p]
     lib.kvq_decode_attn_noalloc.restype = ctypes.c_int
     lib.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(MeterOut), c_void_p]
-    if path == TEST_LIB_PATH:
+    if hasattr(lib, "kvq_test_set_team_hooks"):
         lib.kvq_test_set_team_hooks.restype = None
         lib.kvq_test_set_team_hooks.argtypes = [ctypes.c_uint, ctypes.c_int]
-        _test_lib = lib
-    else:
-        _lib = lib
+    _libs[path] = lib
     return lib
 
 

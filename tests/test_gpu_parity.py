@@ -398,6 +398,28 @@ def test_two_regions_in_one_launch(gpu_lib, monkeypatch, name):
         assert torch.equal(q1[k], q2[k]), k
 
 
+PAGED_LONG = {
+    "fp8": lambda ps: small_variant(QWEN3_B64_S12628_K8V8, batch=2, h_kv=2, suffix_len=9216, lens=(9216, 8200),
+                                    suffix_paged=True, suffix_page_size=ps),
+    "cartridge-bf16": lambda ps: small_variant(QWEN3_SHARED_CARTRIDGE_PAGED, batch=2, h_kv=2, suffix_len=9216,
+                                               lens=(9216, 5000), suffix_page_size=ps),
+}
+
+
+@pytest.mark.parametrize("page_size", [8, 16])
+@pytest.mark.parametrize("name", list(PAGED_LONG))
+def test_paged_chunks_longer_than_the_page_window(gpu_lib, name, page_size):
+    """Paged suffixes in 8,192-token chunks: each wavefront walks 128 tiles,
+    so the page ids of its tiles are fetched in three windows of 64 (the last
+    past the chunk's end), with 8- and 16-token pages, a full and a ragged
+    request, every cell against the oracle."""
+    cfg = PAGED_LONG[name](page_size)
+    case = GpuCase(cfg, page_seed=11)
+    p = plan(case, split_tokens=8192)
+    assert p["team"] == 0 and p["chunk"] == 8192, p
+    _all_cells(case, split_tokens=8192)
+
+
 def _tier_b_two_region():
     """A BF16 shared prefix (radius 0) before a dithered INT8 suffix: two
     launches, one per key format, both accumulating E_p~[e^u]."""
