@@ -217,7 +217,7 @@ __device__ __forceinline__ float head_share_sum(float x, float (*tvw)[G]) {
 // block's entries l + 64 i, all of head (l % 4G) / 4, and the sums reduce
 // over the other lane bits in a fixed order (bitwise reproducible).
 template <int G>
-__device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh, bool single, int suf_len,
+__device__ __forceinline__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh, bool single, int suf_len,
                                   const float (*fin)[6]) {
   constexpr float LN2 = 0.69314718055994530942f;
   const int tid = threadIdx.x;
@@ -294,7 +294,7 @@ __device__ void block_report_pass(const DecodeLaunch &d, int grp, int b, int kvh
 // (in chunk order) into out, log A, bound, meter, then the TV over the spilled
 // logit pairs.  Called by all 256 threads.
 template <int G>
-__device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_STRIDE], int grp,
+__device__ __forceinline__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_STRIDE], int grp,
                                int chunk_idx, int b, int kvh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
@@ -334,6 +334,8 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
     else
       st_dev(&part_g[idx], r);
   }
+  // (requested before the arrival count, whose round trip hides it)
+  const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
   if (single) {
     // spill rows and merged_s were written by this work-group only
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -355,36 +357,99 @@ __device__ void chunk_epilogue(const DecodeLaunch &d, float (*part_s)[G][PART_ST
   // ================= finalize: this work-group arrived last for (b, kvh)
   __shared__ float fin_s[G][6];   // M~, 1/Z~, M_e, 1/Z_e (log2 units)
   const float *pg = single ? &merged_s[0][0] : d.partials + (size_t)grp * total_chunks * G * PART_STRIDE;
-  const int suf_len = d.suffix_lengths ? min(max(d.suffix_lengths[b], 0), d.suffix_cap) : d.suffix_cap;
-  const int S = d.prefix_len + suf_len;
+  // Wavefront h merges head h.  Lane c holds the states of chunk cb + c of a
+  // batch of 64, all requested at once, together with the first 8 chunks'
+  // output words; maxima reduce over the lanes (exact), sums run over the
+  // chunks in order through lane reads (the same arithmetic as a loop over
+  // the chunks).  A finalize of up to 8 chunks takes one round trip.
+  const bool two = d.has_two_sided != 0, val = d.has_value != 0, tb = d.has_tier_b != 0;
+  const int nc = total_chunks;
+  auto lane_f = [](float x, int i) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i)); };
   for (int h = wv; h < G; h += WAVES) {
-    float Mq = NEG_INF, Mm = NEG_INF, Me = NEG_INF, Mn = NEG_INF;
-    for (int c = 0; c < total_chunks; ++c) {
-      const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
-      Mq = fmaxf(Mq, rd(pc + 0));
-      Mm = fmaxf(Mm, rd(pc + 2));
-      Me = fmaxf(Me, rd(pc + 4));
-      if (d.has_two_sided) Mn = fmaxf(Mn, rd(pc + PART_MN));
+    struct St {
+      float m0, z1, m2, z3, m4, z5, zb, zv, vmax, mn, zn, cmax;
+    };
+    auto load_st = [&](int c) {                     // chunk c's states (NEG_INF / 0: no chunk)
+      St x{NEG_INF, 0.0f, NEG_INF, 0.0f, NEG_INF, 0.0f, 0.0f, 0.0f, 0.0f, NEG_INF, 0.0f, 0.0f};
+      if (c < nc) {
+        const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
+        x.m0 = rd(pc + 0); x.z1 = rd(pc + 1); x.m2 = rd(pc + 2); x.z3 = rd(pc + 3);
+        x.m4 = rd(pc + 4); x.z5 = rd(pc + 5);
+        if (tb) x.zb = rd(pc + 6);
+        if (val) { x.zv = rd(pc + 7); x.vmax = rd(pc + PART_VMAX); }
+        if (two) { x.mn = rd(pc + PART_MN); x.zn = rd(pc + PART_ZN); x.cmax = rd(pc + PART_CMAX); }
+      }
+      return x;
+    };
+    const St st0 = load_st(lane);
+    float a0[8], a1[8];                             // output words of chunks 0..7
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a0[j] = a1[j] = 0.0f;
+      if (j < nc) {
+        const float *pc = pg + ((size_t)j * G + h) * PART_STRIDE;
+        a0[j] = rd(pc + 8 + lane);
+        a1[j] = rd(pc + 8 + 64 + lane);
+      }
+    }
+    float Mq = st0.m0, Mm = st0.m2, Me = st0.m4, Mn = st0.mn;
+    for (int cb = 64; cb < nc; cb += 64) {          // more than 64 chunks
+      const St x = load_st(cb + lane);
+      Mq = fmaxf(Mq, x.m0); Mm = fmaxf(Mm, x.m2); Me = fmaxf(Me, x.m4); Mn = fmaxf(Mn, x.mn);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      Mq = fmaxf(Mq, __shfl_xor(Mq, off));
+      Mm = fmaxf(Mm, __shfl_xor(Mm, off));
+      Me = fmaxf(Me, __shfl_xor(Me, off));
+      if (two) Mn = fmaxf(Mn, __shfl_xor(Mn, off));
     }
     float Zn = 0.0f, Cmax = 0.0f;
     float Zq = 0.0f, Zm = 0.0f, Ze = 0.0f, Zb = 0.0f, Zv = 0.0f, Vmax = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int c = 0; c < total_chunks; ++c) {
-      const float *pc = pg + ((size_t)c * G + h) * PART_STRIDE;
-      const float fq = merge_factor(rd(pc + 0), Mq);
-      Zq += rd(pc + 1) * fq;
-      if (d.has_tier_b) Zb += rd(pc + 6) * fq;
-      if (d.has_value) {
-        Zv += rd(pc + 7) * fq;
-        Vmax = fmaxf(Vmax, rd(pc + PART_VMAX));
+    for (int cb = 0; cb < nc; cb += 64) {
+      const St x = cb == 0 ? st0 : load_st(cb + lane);
+      // this lane's chunk: its merge factors on the group's maxima; the sums
+      // take each chunk's term as one fused multiply-add, in chunk order
+      const float fq = merge_factor(x.m0, Mq), fm = merge_factor(x.m2, Mm), fe = merge_factor(x.m4, Me);
+      const float fn = merge_factor(x.mn, Mn);
+      const int n = min(64, nc - cb);
+      for (int i = 0; i < n; ++i) {
+        const float f = lane_f(fq, i);
+        Zq = fmaf(lane_f(x.z1, i), f, Zq);
+        if (tb) Zb = fmaf(lane_f(x.zb, i), f, Zb);
+        if (val) {
+          Zv = fmaf(lane_f(x.zv, i), f, Zv);
+          Vmax = fmaxf(Vmax, lane_f(x.vmax, i));
+        }
+        if (two) {
+          Zn = fmaf(lane_f(x.zn, i), lane_f(fn, i), Zn);
+          Cmax = fmaxf(Cmax, lane_f(x.cmax, i));
+        }
+        Zm = fmaf(lane_f(x.z3, i), lane_f(fm, i), Zm);
+        Ze = fmaf(lane_f(x.z5, i), lane_f(fe, i), Ze);
       }
-      if (d.has_two_sided) {
-        Zn += rd(pc + PART_ZN) * merge_factor(rd(pc + PART_MN), Mn);
-        Cmax = fmaxf(Cmax, rd(pc + PART_CMAX));
+      // outputs: 8 chunks' words in flight at a time (the first 8 are loaded)
+      for (int i0 = 0; i0 < n; i0 += 8) {
+        if (cb + i0 >= 8) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            a0[j] = a1[j] = 0.0f;
+            if (i0 + j < n) {
+              const float *pc = pg + ((size_t)(cb + i0 + j) * G + h) * PART_STRIDE;
+              a0[j] = rd(pc + 8 + lane);
+              a1[j] = rd(pc + 8 + 64 + lane);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (i0 + j < n) {
+            const float f = lane_f(fq, i0 + j);
+            o0 = fmaf(a0[j], f, o0);
+            o1 = fmaf(a1[j], f, o1);
+          }
+        }
       }
-      Zm += rd(pc + 3) * merge_factor(rd(pc + 2), Mm);
-      Ze += rd(pc + 5) * merge_factor(rd(pc + 4), Me);
-      o0 += rd(pc + 8 + lane) * fq;
-      o1 += rd(pc + 8 + 64 + lane) * fq;
     }
     const size_t qh = (size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + h;
     const bool hv = d.qh0 + h < d.qg;               // a query head (not a padding head)
