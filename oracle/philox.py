@@ -14,13 +14,15 @@ and between rounds the key is advanced by the Weyl constants 0x9E3779B9 and
 
 Dither stream (WitCert, Sec. 6.2.1: the dither is regenerated at read time
 from a counter built from (request, layer, KV head, token, channel), and
-Sec. 6.3.1: one generator call serves four channels).  The pages fix neither
-the word layout nor the mapping to [-1/2, 1/2); our reading:
-    counter = (token, channel >> 2, (kv << 31) | (layer << 16) | kv_head, stream)
+Sec. 6.3.1: Philox4x32-10 on that five-tuple, one generator call serving four
+channels).  The five-tuple has no key/value component, so a token's keys and
+values share their dither.  The pages fix neither the word layout nor the
+mapping to [-1/2, 1/2); our reading:
+    counter = (token, channel >> 2, (layer << 16) | kv_head, stream)
     key     = (seed & 0xFFFFFFFF, seed >> 32)
     u       = output word (channel & 3)
     xi      = (u >> 8) * 2^-24 - 1/2          (exact in float32)
-with kv = 0 for keys and 1 for values, layer < 2^15, kv_head < 2^16.
+with layer < 2^15 and kv_head < 2^16.
 """
 from __future__ import annotations
 
@@ -54,27 +56,28 @@ def philox4x32_10(ctr: np.ndarray, key) -> np.ndarray:
     return c.astype(np.uint32)
 
 
-def dither_counters(tokens, channels, kv: int, layer: int, kv_head: int, stream: int):
+def dither_counters(tokens, channels, layer: int, kv_head: int, stream: int):
     """Counter words for every (token, channel) pair (broadcast shapes)."""
     t = np.asarray(tokens, dtype=np.uint64)
     ch = np.asarray(channels, dtype=np.uint64)
     t, ch = np.broadcast_arrays(t, ch)
-    w2 = (int(kv) << 31) | (int(layer) << 16) | int(kv_head)
+    w2 = (int(layer) << 16) | int(kv_head)
     ctr = np.stack([t & MASK32, ch >> np.uint64(2),
                     np.full(t.shape, w2, np.uint64),
                     np.full(t.shape, int(stream) & MASK32, np.uint64)], axis=-1)
     return ctr
 
 
-def dither(seed: int, layer: int, kv: int, kv_head: int, stream: int,
+def dither(seed: int, layer: int, kv_head: int, stream: int,
            tokens: np.ndarray, n_channels: int = 128) -> np.ndarray:
-    """Dither xi in [-1/2, 1/2) as float32, shape (len(tokens), n_channels)."""
-    if not (0 <= layer < 1 << 15 and 0 <= kv_head < 1 << 16 and kv in (0, 1)):
-        raise ValueError("dither: layer/kv_head/kv out of range")
+    """Dither xi in [-1/2, 1/2) as float32, shape (len(tokens), n_channels);
+    the same for a token's keys and values."""
+    if not (0 <= layer < 1 << 15 and 0 <= kv_head < 1 << 16):
+        raise ValueError("dither: layer/kv_head out of range")
     tokens = np.asarray(tokens, dtype=np.int64)
     t = np.repeat(tokens, n_channels // 4)
     cg = np.tile(np.arange(0, n_channels, 4), len(tokens))
-    ctr = dither_counters(t, cg, kv, layer, kv_head, stream).reshape(-1, 4)
+    ctr = dither_counters(t, cg, layer, kv_head, stream).reshape(-1, 4)
     out = philox4x32_10(ctr, (seed & MASK32, (seed >> 32) & MASK32))
     u = out.reshape(len(tokens), n_channels)      # word (c & 3) of group c >> 2
     xi = (u >> np.uint32(8)).astype(np.float64) * 2.0 ** -24 - 0.5

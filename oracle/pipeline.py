@@ -61,7 +61,7 @@ def _encode_one(x, fmt, spec: RegionSpec, kv: int, kv_head: int, pairs=None):
         codes, s = quant.fp8_token_quantize(x)
         return codes, s, quant.fp8_token_dequant(codes, s), 0
     if fmt in ("int8", "int8g32"):
-        xi = dither(spec.seed, spec.layer, kv, kv_head, spec.stream,
+        xi = dither(spec.seed, spec.layer, kv_head, spec.stream,
                     np.arange(x.shape[0]), x.shape[1])
         if fmt == "int8g32":
             if pairs is not None and len(pairs) > 0:

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecodeLaunch d) {
   const int32_t *ptab = R.paged ? R.page_table + (size_t)b * R.max_pages : nullptr;
   const uint32_t stream = (uint32_t)(R.is_prefix ? R.stream_id
                                                  : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
-  const uint32_t ktag = dither_tag(0, R.layer, kvh), vtag = dither_tag(1, R.layer, kvh);
+  const uint32_t ktag = dither_tag(R.layer, kvh), vtag = ktag;     // (shared by keys and values)
   const int nblk_cap = (R.length + BLK - 1) / BLK;
   float *spill_g = (do_tv || do_r) ? spill_region<G>(d, grp, R.is_prefix != 0) : nullptr;
   float *rspill_g = do_r ? rspill_region<G>(d, grp, R.is_prefix != 0) : nullptr;

@@ -124,13 +124,15 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int byte0) {
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
-// The dither of 8 channels (two generator calls), split into two exact-sum
-// bf16 pieces of -xi: -xi = hi + lo + r with |r| <= 2^-18 |xi|.
-__device__ __forceinline__ void neg_dither8_bf16(uint32_t token, uint32_t g0, uint32_t tag, uint32_t stream,
-                                                 uint32_t k0, uint32_t k1, bf16x8_t &hi, bf16x8_t &lo) {
-  float xi[8];
+// The dither of 8 channels: channel groups g0 and g0 + 1 (two generator calls).
+__device__ __forceinline__ void dither8(uint32_t token, uint32_t g0, uint32_t tag, uint32_t stream, uint32_t k0,
+                                        uint32_t k1, float (&xi)[8]) {
   dither4(token, g0, tag, stream, k0, k1, xi);
   dither4(token, g0 + 1, tag, stream, k0, k1, xi + 4);
+}
+
+// -xi split into two exact-sum bf16 pieces: -xi = hi + lo + r, |r| <= 2^-18 |xi|.
+__device__ __forceinline__ void neg_split8_bf16(const float (&xi)[8], bf16x8_t &hi, bf16x8_t &lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = -xi[e];
@@ -139,6 +141,10 @@ __device__ __forceinline__ void neg_dither8_bf16(uint32_t token, uint32_t g0, ui
     lo[e] = (__bf16)(x - h);
   }
 }
+
+// Row length (floats) of a wavefront's LDS tile of dithers: 16 tokens x 128
+// channels, each row padded by 4 so that the 16 rows start in different banks.
+constexpr int XI_ROW = D + 4;
 
 struct TileRegs {
   uint4 k[4];      // FP8: k[0..1] = 32 codes; BF16: k[0..3] = 32 values
@@ -494,14 +500,25 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   constexpr bool GV = VF == KVQ_FMT_INT8_G32;
   bf16x8_t bqs[4];
   float sv8[8];                                    // value scales of dims 8 j16 + n
-  uint32_t i8_stream = 0, i8_ktag = 0, i8_vtag = 0;
+  uint32_t i8_stream = 0, i8_tag = 0;
   size_t i8_scale_row0 = 0;
   if constexpr (I8K || I8V || GK || GV) {
     const size_t sh = R.is_prefix ? (size_t)kvh : (size_t)b * d.h_kv + kvh;
     i8_scale_row0 = sh * (size_t)((R.length + KVQ_INT8_BLOCK - 1) / KVQ_INT8_BLOCK);
     i8_stream = (uint32_t)(R.is_prefix ? R.stream_id : (R.stream_ids ? R.stream_ids[b] : R.stream_id + b));
-    i8_ktag = dither_tag(0, R.layer, kvh);
-    i8_vtag = dither_tag(1, R.layer, kvh);
+    i8_tag = dither_tag(R.layer, kvh);             // (keys and values share a token's dither)
+  }
+  // Dithered INT8 keys and values: the key phase of a tile computes each
+  // generator call once and leaves the tile's 16 x 128 dithers in this
+  // wavefront's LDS tile, where the value phase reads its own (token,
+  // channel) set (the two phases hold transposed sets per lane).  The per-tile
+  // wavefront barriers order the writes before the reads and the reads before
+  // the next tile's writes.
+  constexpr bool SHARE_XI = I8K && I8V;
+  float (*xi_s)[XI_ROW] = nullptr;
+  if constexpr (SHARE_XI) {
+    __shared__ __attribute__((aligned(16))) float xi_tile[WAVES][16][XI_ROW];
+    xi_s = xi_tile[wv];
   }
   auto set_block = [&](int blk) {
     const size_t srow = (i8_scale_row0 + (size_t)blk) * D;
@@ -646,9 +663,15 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       for (int s = 0; s < 4; ++s) {
         const uint4 cw = {i8x2_to_bf16x2(w[2 * s], 0), i8x2_to_bf16x2(w[2 * s], 2),
                           i8x2_to_bf16x2(w[2 * s + 1], 0), i8x2_to_bf16x2(w[2 * s + 1], 2)};
+        float xi[8];
+        dither8((uint32_t)(t0 + j16), (uint32_t)(8 * g + 2 * s), i8_tag, i8_stream, R.seed_lo, R.seed_hi, xi);
+        if constexpr (SHARE_XI) {
+          float4 *dst = reinterpret_cast<float4 *>(&xi_s[j16][32 * g + 8 * s]);
+          dst[0] = make_float4(xi[0], xi[1], xi[2], xi[3]);
+          dst[1] = make_float4(xi[4], xi[5], xi[6], xi[7]);
+        }
         bf16x8_t xh, xl;
-        neg_dither8_bf16((uint32_t)(t0 + j16), (uint32_t)(8 * g + 2 * s), i8_ktag, i8_stream, R.seed_lo,
-                         R.seed_hi, xh, xl);
+        neg_split8_bf16(xi, xh, xl);
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], dq, 0, 0, 0);
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], dq, 0, 0, 0);
         dq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bqs[s], dq, 0, 0, 0);
@@ -662,9 +685,10 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       for (int s = 0; s < 4; ++s) {
         const uint4 cw = {i8x2_to_bf16x2(w[2 * s], 0), i8x2_to_bf16x2(w[2 * s], 2),
                           i8x2_to_bf16x2(w[2 * s + 1], 0), i8x2_to_bf16x2(w[2 * s + 1], 2)};
+        float xi[8];
+        dither8((uint32_t)(t0 + j16), (uint32_t)(8 * s + 2 * g), i8_tag, i8_stream, R.seed_lo, R.seed_hi, xi);
         bf16x8_t xh, xl;
-        neg_dither8_bf16((uint32_t)(t0 + j16), (uint32_t)(8 * s + 2 * g), i8_ktag, i8_stream, R.seed_lo,
-                         R.seed_hi, xh, xl);
+        neg_split8_bf16(xi, xh, xl);
         ds[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw), bqs[s], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
                                                       0, 0, 0);
         ds[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bqs[s], ds[s], 0, 0, 0);
@@ -832,9 +856,14 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float xi[8];
-        const uint32_t tok = (uint32_t)(t0 + 4 * g + e);
-        dither4(tok, (uint32_t)(2 * j16), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi);
-        dither4(tok, (uint32_t)(2 * j16 + 1), i8_vtag, i8_stream, R.seed_lo, R.seed_hi, xi + 4);
+        if constexpr (SHARE_XI) {                  // left by this tile's key phase
+          const float4 *src = reinterpret_cast<const float4 *>(&xi_s[4 * g + e][8 * j16]);
+          const float4 a = src[0], c = src[1];
+          xi[0] = a.x; xi[1] = a.y; xi[2] = a.z; xi[3] = a.w;
+          xi[4] = c.x; xi[5] = c.y; xi[6] = c.z; xi[7] = c.w;
+        } else {
+          dither8((uint32_t)(t0 + 4 * g + e), (uint32_t)(2 * j16), i8_tag, i8_stream, R.seed_lo, R.seed_hi, xi);
+        }
         const uint32_t cw[2] = {T.v8[e].x, T.v8[e].y};
 #pragma unroll
         for (int n = 0; n < 8; ++n) {

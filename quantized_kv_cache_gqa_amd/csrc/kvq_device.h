@@ -113,7 +113,10 @@ __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
 }
 
 // Dither for channels 4g..4g+3 of one token: counter (token, g, tag, stream),
-// tag = (kv << 31) | (layer << 16) | kv_head; xi = (u >> 8) 2^-24 - 1/2.
+// tag = (layer << 16) | kv_head; xi = (u >> 8) 2^-24 - 1/2.  The counter is
+// the pages' five-tuple (request stream, layer, KV head, token, channel),
+// which has no key/value component: a token's keys and values share their
+// dither (WitCert Sec. 6.3.1, the write kernel's counter).
 __device__ __forceinline__ void dither4(uint32_t token, uint32_t g, uint32_t tag, uint32_t stream,
                                         uint32_t k0, uint32_t k1, float* xi) {
   u4 o = philox4x32_10(u4{token, g, tag, stream}, k0, k1);
@@ -123,8 +126,8 @@ __device__ __forceinline__ void dither4(uint32_t token, uint32_t g, uint32_t tag
   xi[3] = (float)(o.w >> 8) * 5.9604644775390625e-08f - 0.5f;
 }
 
-__device__ __forceinline__ uint32_t dither_tag(int kv, int layer, int kv_head) {
-  return ((uint32_t)kv << 31) | ((uint32_t)layer << 16) | (uint32_t)kv_head;
+__device__ __forceinline__ uint32_t dither_tag(int layer, int kv_head) {
+  return ((uint32_t)layer << 16) | (uint32_t)kv_head;
 }
 
 // ---------------------------------------------------------------- lane exchange

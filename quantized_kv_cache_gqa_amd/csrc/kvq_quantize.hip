@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t full_norm_up(const double *x) {
 __global__ __launch_bounds__(256) void quant_token_kernel(
     const void *__restrict__ in, int in_fmt, int target, int n_seq, int h_kv, int capacity,
     int tok_begin, int tok_end, uint8_t *__restrict__ out, void *__restrict__ scale_out,
-    uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out, int kv, uint32_t k0, uint32_t k1,
+    uint16_t *__restrict__ wit_out, uint16_t *__restrict__ vrec_out, uint32_t k0, uint32_t k1,
     int layer, int stream_id, const int32_t *__restrict__ stream_ids, const int32_t *__restrict__ opairs,
     int n_op, uint16_t *__restrict__ kout) {
 #pragma clang fp contract(off)
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
       sc[lane >> 5] = (uint16_t)s0b;
       sc[2 + (lane >> 5)] = (uint16_t)s1b;
     }
-    const uint32_t tag = dither_tag(kv, layer, kvh);
+    const uint32_t tag = dither_tag(layer, kvh);
     const uint32_t stream = (uint32_t)(stream_ids ? stream_ids[seq] : stream_id + seq);
     float xa[4], xb[4];
     dither4((uint32_t)t, (uint32_t)(lane >> 2), tag, stream, k0, k1, xa);
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void quant_token_kernel(
 
 // One work-group per (sequence, KV head, 256-token block): dithered INT8.
 __global__ __launch_bounds__(256) void quant_int8_block_kernel(
-    const void *__restrict__ in, int in_fmt, int kv, int n_seq, int h_kv, int capacity,
+    const void *__restrict__ in, int in_fmt, int n_seq, int h_kv, int capacity,
     int blk_begin, int n_blk, int tok_end, int8_t *__restrict__ out,
     uint16_t *__restrict__ scale_out, uint16_t *__restrict__ wit_out, uint32_t k0, uint32_t k1,
     int layer, int stream_id, const int32_t *__restrict__ stream_ids, uint16_t *__restrict__ vrec_out) {
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void quant_int8_block_kernel(
   }
   __syncthreads();
 
-  const uint32_t tag = dither_tag(kv, layer, kvh);
+  const uint32_t tag = dither_tag(layer, kvh);
   const uint32_t stream = (uint32_t)(stream_ids ? stream_ids[seq] : stream_id + seq);
   const int g = tid & 31;                                // channel group: channels 4g..4g+3
   const int ti = tid >> 5;                               // token within a group of 8
@@ -288,7 +288,7 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
     const int n_blk = (q.tok_end - 1) / BLK - blk_begin + 1;
     const long grid = (long)q.n_seq * q.h_kv * n_blk;
     hipLaunchKernelGGL(quant_int8_block_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
-                       q.in_format, which, q.n_seq, q.h_kv, q.capacity, blk_begin, n_blk, q.tok_end,
+                       q.in_format, q.n_seq, q.h_kv, q.capacity, blk_begin, n_blk, q.tok_end,
                        (int8_t *)out, (uint16_t *)sc, wit, (uint32_t)q.seed,
                        (uint32_t)(q.seed >> 32), q.layer, q.stream_id, q.stream_ids, vrec);
   } else {
@@ -296,7 +296,7 @@ static hipError_t launch_one(const QuantLaunch &q, int which, hipStream_t stream
     const long grid = (total + 3) / 4;
     hipLaunchKernelGGL(quant_token_kernel, dim3((unsigned)grid), dim3(256), 0, stream, in,
                        q.in_format, fmt, q.n_seq, q.h_kv, q.capacity, q.tok_begin, q.tok_end,
-                       (uint8_t *)out, sc, wit, vrec, which, (uint32_t)q.seed, (uint32_t)(q.seed >> 32),
+                       (uint8_t *)out, sc, wit, vrec, (uint32_t)q.seed, (uint32_t)(q.seed >> 32),
                        q.layer, q.stream_id, q.stream_ids, which == 0 ? q.opairs : nullptr,
                        which == 0 ? q.n_op : 0, which == 0 ? q.k_outliers_out : nullptr);
   }

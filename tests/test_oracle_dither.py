@@ -51,20 +51,36 @@ def test_philox_counter_words_all_matter():
 
 
 def test_dither_stream_unique_over_five_tuple():
+    """Distinct (stream, layer, KV head, token, channel group) give distinct
+    counters (WitCert Sec. 6.3.1's five-tuple)."""
     seen = set()
     for stream in range(3):
         for layer in (0, 1, 35):
-            for kv in (0, 1):
-                for kvh in (0, 7):
-                    ctr = dither_counters(np.arange(300)[:, None], np.arange(0, 128, 4)[None, :],
-                                          kv, layer, kvh, stream).reshape(-1, 4)
-                    for row in map(tuple, ctr.tolist()):
-                        assert row not in seen
-                        seen.add(row)
+            for kvh in (0, 7):
+                ctr = dither_counters(np.arange(300)[:, None], np.arange(0, 128, 4)[None, :],
+                                      layer, kvh, stream).reshape(-1, 4)
+                for row in map(tuple, ctr.tolist()):
+                    assert row not in seen
+                    seen.add(row)
+
+
+def test_keys_and_values_share_the_dither():
+    """The five-tuple has no key/value component: a token's keys and values are
+    quantized with the same dither, so equal inputs give equal codes, and a
+    changed input on one side leaves the other's codes alone."""
+    from oracle.pipeline import RegionSpec, encode_region
+    rng = np.random.default_rng(3)
+    x = _bf16(rng.standard_normal((2, 300, 128)))
+    spec = RegionSpec(k_fmt="int8", v_fmt="int8", seed=77, layer=4, stream=1)
+    enc = encode_region(x[0], x[0], spec, kv_head=2)
+    np.testing.assert_array_equal(enc.k_codes, enc.v_codes)
+    enc2 = encode_region(x[0], x[1], spec, kv_head=2)
+    np.testing.assert_array_equal(enc2.k_codes, enc.k_codes)
+    assert not np.array_equal(enc2.v_codes, enc.v_codes)
 
 
 def test_dither_range_and_uniformity():
-    xi = dither(20260004, 3, 0, 5, 2, np.arange(4096), 128).ravel().astype(np.float64)
+    xi = dither(20260004, 3, 5, 2, np.arange(4096), 128).ravel().astype(np.float64)
     assert xi.min() >= -0.5 and xi.max() < 0.5
     # exact on the 2^-24 grid
     assert np.all((xi + 0.5) * 2 ** 24 == np.round((xi + 0.5) * 2 ** 24))
@@ -87,7 +103,7 @@ def test_int8_dither_error_bound_no_clipping_and_moments():
     x = rng.standard_normal((T, 128))
     x[:, [5, 9, 60, 101]] *= 8
     x = _bf16(x)
-    xi = dither(99, 2, 0, 1, 0, np.arange(T), 128)
+    xi = dither(99, 2, 1, 0, np.arange(T), 128)
     codes, s16, clipped = int8_dither_quantize(x, xi)
     assert clipped == 0 and s16.shape == (4, 128) and s16.dtype == np.float16
     assert np.max(np.abs(codes.astype(int))) <= 127

@@ -29,7 +29,7 @@ def _x(rng, T):
 def test_each_token_encodes_on_its_own():
     rng = np.random.default_rng(1)
     x = _x(rng, 300)
-    xi = dither(7, 3, 0, 1, 2, np.arange(300), 128)
+    xi = dither(7, 3, 1, 2, np.arange(300), 128)
     codes, s, clipped = int8_dither_g32_quantize(x, xi)
     assert clipped == 0 and s.shape == (300, 4)
     for t in (0, 17, 299):

@@ -60,7 +60,7 @@ def test_key_store_bytes_match_table6():
 def test_no_active_slot_is_the_plain_format():
     rng = np.random.default_rng(1)
     x = _keys(rng, 50, pairs=(5,))
-    xi = dither(3, 1, 0, 0, 0, np.arange(50), 128)
+    xi = dither(3, 1, 0, 0, np.arange(50), 128)
     c0, s0, _ = int8_dither_g32_quantize(x, xi)
     for pairs in ([], [64, -1, 200], ):
         mask, active = outlier_mask(pairs)
@@ -82,7 +82,7 @@ def test_bypassed_channels_are_exact_and_leave_the_group_maximum():
     rng = np.random.default_rng(2)
     P = 9                                                        # channels 9 (group 0) and 73 (group 2)
     x = _keys(rng, 200, pairs=(P,), scale=500.0)
-    xi = dither(11, 2, 0, 3, 1, np.arange(200), 128)
+    xi = dither(11, 2, 3, 1, np.arange(200), 128)
     mask, _ = outlier_mask([P])
     codes, s, clipped = int8_dither_g32_quantize(x, xi, bypass=mask)
     assert clipped == 0
@@ -110,7 +110,7 @@ def test_table5_direction_bypass_needs_the_amax_exclusion():
     pairs = [3, 20, 41, 58]
     T = 512
     x = _keys(rng, T, pairs=pairs, scale=60.0)
-    xi = dither(5, 0, 0, 0, 0, np.arange(T), 128)
+    xi = dither(5, 0, 0, 0, np.arange(T), 128)
     q = rng.standard_normal((8, 128))
     mask, _ = outlier_mask(pairs)
     radii = {}
