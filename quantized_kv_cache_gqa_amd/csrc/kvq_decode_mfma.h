@@ -131,12 +131,14 @@ __device__ __forceinline__ void dither8(uint32_t token, uint32_t g0, uint32_t ta
   dither4(token, g0 + 1, tag, stream, k0, k1, xi + 4);
 }
 
-// -xi split into two exact-sum bf16 pieces: -xi = hi + lo + r, |r| <= 2^-18 |xi|.
+// -xi split into two exact-sum bf16 pieces: -xi = hi + lo + r, |r| <= 2^-18 |xi|
+// (the conversion instruction rounds to nearest even, as bf16_round does for
+// finite values, in one instruction per pair).
 __device__ __forceinline__ void neg_split8_bf16(const float (&xi)[8], bf16x8_t &hi, bf16x8_t &lo) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = -xi[e];
-    const float h = bf16_round(x);
+    const float h = bf16_hw_round(x);
     hi[e] = (__bf16)h;
     lo[e] = (__bf16)(x - h);
   }

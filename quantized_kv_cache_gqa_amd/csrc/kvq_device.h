@@ -91,9 +91,14 @@ __device__ __forceinline__ void e4m3x4(uint32_t w, float* f) {
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3"
 // (SC 2011): two 32x32->64 products per round, key advanced by the Weyl
-// constants between rounds, ten rounds.
+// constants between rounds, ten rounds.  Each round's two three-input XORs
+// are one instruction each (v_bitop3_b32 with truth table 0x96 = a ^ b ^ c).
 
 struct u4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 
 __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -101,9 +106,9 @@ __device__ __forceinline__ u4 philox4x32_10(u4 c, uint32_t k0, uint32_t k1) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
     u4 n;
-    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.x = xor3((uint32_t)(p1 >> 32), c.y, k0);
     n.y = (uint32_t)p1;
-    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.z = xor3((uint32_t)(p0 >> 32), c.w, k1);
     n.w = (uint32_t)p0;
     c = n;
     k0 += 0x9E3779B9u;
