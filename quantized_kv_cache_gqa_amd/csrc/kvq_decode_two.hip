@@ -19,7 +19,12 @@ __global__ __launch_bounds__(256, 2) void decode_two_kernel(const DecodeLaunch d
   if (L >= (unsigned)d1.batch * d1.h_kv * nc) return;
   __shared__ __attribute__((aligned(16))) float w_s[WAVES][64];
   __shared__ float part_s[WAVES][4][PART_STRIDE];
-  const int grp = (int)(L / nc), ci = (int)(L % nc);
+  // Groups in KV-head-major order: consecutive logical indices, which stay
+  // on one XCD, take one KV head across requests, so each XCD's L2 serves
+  // its heads' slice of the shared cartridge to every request, and the
+  // cartridge is fetched from HBM about once instead of once per XCD.
+  const int gi = (int)(L / nc), ci = (int)(L % nc);
+  const int grp = (gi % d1.batch) * d1.h_kv + gi / d1.batch;
   if (ci < d1.n_chunks)
     chunk_work<KF, VF1, false, FULL, EXT>(d1, grp, ci, w_s, part_s);
   else
