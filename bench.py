@@ -457,6 +457,29 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
             e1.record(stream)
         torch.cuda.synchronize()
         tier_b_ms = sorted(e0.elapsed_time(e1) for e0, e1 in b_evs)[reps // 2]
+    # the workload's own split-K size, where it names one (the timed launch
+    # above takes the library's automatic plan)
+    split_ms, split_plan = None, None
+    if cfg.split_tokens:
+        a_s = kvq._attn_args(inp["q"], prefix, suffix, out, sm, cfg.split_tokens, HKV, status=status)
+        info_s = kvq.PlanInfo()
+        assert lib.kvq_decode_plan(ctypes.byref(a_s), ctypes.byref(meter), 0, ctypes.byref(info_s)) == 0
+        ws_s = ws if info_s.workspace_bytes <= ws.numel() else torch.empty(info_s.workspace_bytes,
+                                                                            dtype=torch.uint8, device=dev)
+        if ws_s is not ws:
+            assert lib.kvq_workspace_init(ws_s.data_ptr(), ws_s.numel(), sp) == 0
+        for _ in range(5):
+            assert lib.kvq_decode_attn(ctypes.byref(a_s), ctypes.byref(meter), ws_s.data_ptr(), ws_s.numel(), sp) == 0
+        s_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in s_evs:
+            e0.record(stream)
+            assert lib.kvq_decode_attn(ctypes.byref(a_s), ctypes.byref(meter), ws_s.data_ptr(), ws_s.numel(), sp) == 0
+            e1.record(stream)
+        torch.cuda.synchronize()
+        split_ms = sorted(e0.elapsed_time(e1) for e0, e1 in s_evs)[reps // 2]
+        split_plan = f"{info_s.chunks} chunk(s) of {info_s.chunk} tokens" + (
+            f" and a finish launch ({info_s.launches} launches)" if info_s.launches > 1 else "")
+        del ws_s
     plan = (f"team {info.team}, {info.n_teams} teams x {info.rounds} rounds, chunk {info.chunk}"
             if info.team else f"{info.chunks} chunk(s) of {info.chunk} tokens per (request, KV head)")
     torch.cuda.synchronize()
@@ -486,7 +509,9 @@ def measure_workload(idx: int, reps: int, warmup: int, group_scales: bool = Fals
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS},
         "kv_tokens_per_s": cfg.context_tokens() / (med * 1e-3),
-        "plan": plan,
+        "plan": plan + " (the library's automatic plan)",
+        "with_configured_split_launch_ms": split_ms,
+        "configured_split_plan": (f"split_tokens {cfg.split_tokens}: {split_plan}" if split_plan else None),
         "cpu_baseline": base}), flush=True)
 
 
