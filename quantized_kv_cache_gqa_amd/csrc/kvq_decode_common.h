@@ -460,7 +460,7 @@ __device__ __forceinline__ void chunk_epilogue(const DecodeLaunch &d, float (*pa
     }
     if (lane == 0) {
       const double log_a = do_meter ? meter_log_a(Mq, Zq, Mm, Zm) : 0.0;
-      double bound = 0.5 * expm1(2.0 * log_a);
+      const double bound = log_a == 0.0 ? 0.0 : 0.5 * expm1(2.0 * log_a);   // (no witness: 0)
       const float bf = bound > 3.4028234663852886e38 ? __builtin_huge_valf() : (float)bound;
       if (d.log_a && hv) d.log_a[qh] = (float)log_a;
       if (d.bound_raw && hv) d.bound_raw[qh] = bf;
@@ -513,7 +513,10 @@ __device__ __forceinline__ void chunk_epilogue(const DecodeLaunch &d, float (*pa
     if (tid == 0) __hip_atomic_store(d.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  if (d.tv) {
+  if (d.tv && !do_tv) {
+    // no region holds exact keys: the stored keys are exact, TV = 0
+    if (tid < G && d.qh0 + tid < d.qg) d.tv[(size_t)b * d.h_q + (size_t)kvh * d.qg + d.qh0 + tid] = 0.0f;
+  } else if (d.tv) {
     // Thread tid reads entries 2 tid + 512 k (a float4: two entries of one
     // head); 512 is a multiple of 4G, so the head of its entries never changes.
     // (a group with several chunks runs this pass in the finish launch
