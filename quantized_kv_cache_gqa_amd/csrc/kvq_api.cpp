@@ -233,11 +233,19 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     // tokens: below that the partials' merge and the short work-groups cost
     // more than the parallelism gives (measured: a 1,656-token cartridge +
     // suffix step 46.6 us with 640-token chunks, 57.9 us with 448)
+    //
+    // A step that would then have fewer work-groups than CUs takes chunks of
+    // at least 256 tokens instead: a CU streams at most about 24 GB/s however
+    // many wavefronts it runs (measured: one 8-wavefront work-group per
+    // (request, KV head) on the 1,656-token step took 30.6 us against 27.9 us
+    // for 3 chunks of 4 wavefronts), so idle CUs are idle bandwidth (the
+    // single-request 696-token step: 15.6 us as 4 chunks, 17.6 us as 2).
     const int64_t target = 512;
     const int64_t per_group = groups >= target ? 1 : (target + groups - 1) / groups;
     int64_t c = (smax + per_group - 1) / per_group;
     c = (c + 63) / 64 * 64;
-    chunk = (int)(c < 640 ? 640 : c);
+    const int64_t min_chunk = (int64_t)groups * ((smax + 639) / 640) < 256 ? 256 : 640;
+    chunk = (int)(c < min_chunk ? min_chunk : c);
   }
   p.chunk = chunk;
   p.pre_chunks = (p.prefix_len + chunk - 1) / chunk;

@@ -371,14 +371,20 @@ def test_outlier_store_bytes_match_the_page(tmp_path):
 def test_automatic_chunks_are_at_least_640_tokens(lib):
     """The per-chunk plan fills about 512 work-groups, but no automatic chunk is
     shorter than 640 tokens (a multiple of 64): fewer, longer chunks won on
-    small steps.  An explicit split_tokens is taken as given."""
+    small steps.  A step that would then have fewer work-groups than CUs (256)
+    takes chunks of at least 256 tokens instead.  An explicit split_tokens is
+    taken as given."""
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     nt = kvq.PLAN_NO_TEAM
     for batch, hkv, suffix, chunk in ((64, 8, 12628, 12672), (8, 8, 32768, 4096), (4, 8, 131072, 8192),
-                                      (16, 8, 1024, 640), (1, 1, 64, 640), (1, 1, 100000, 640)):
+                                      (16, 8, 1024, 640), (1, 1, 64, 256), (1, 1, 100000, 256),
+                                      (1, 8, 12628, 256), (1, 8, 4096, 256), (2, 8, 12628, 640)):
         info = _plan(lib, _args(batch=batch, hkv=hkv, hq=4 * hkv, suffix=suffix, flags=nt), m)
         assert info.chunk == chunk, (batch, hkv, suffix, info.chunk)
         assert info.chunks == -(-suffix // chunk)
+    two = _plan(lib, _args(batch=1, hkv=1, hq=4, prefix=632, suffix=64, kf="bf16", vf="fp8", exact=False,
+                           witness=False), kvq.MeterOut())
+    assert (two.chunk, two.chunks, two.launches) == (256, 4, 1)
     info = _plan(lib, _args(batch=16, suffix=1024, split=128, flags=nt), m)
     assert (info.chunk, info.chunks) == (128, 8)
 
