@@ -94,6 +94,10 @@ typedef enum kvq_format {
  *                  [n_pages, Hk, P, 16], exact keys [n_pages, Hk, P, D]; token i of
  *                  request b sits in page page_table[b * max_pages + i / P], row i % P.
  *                  Paged INT8 is rejected (its 256-token blocks would span pages).
+ * Values in device memory are the caller's to keep in range, since the host
+ * checks cannot read them without a synchronization: page ids in [0, n_pages)
+ * for the pages a request's tokens use, suffix lengths (clamped to [0, length]
+ * by the kernels) and finite inputs.
  * Semantics:
  *   witness NULL  -> the stored keys are claimed exact for the meter (c_t = 0).
  *   k_exact NULL  -> the stored keys are claimed exact for the TV (l_t = l~_t).

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kvq_decode_mfma.h"
 
@@ -531,22 +532,25 @@ static const void *team_kernel(int k_format, int v_format, bool paged, bool full
 
 int team_capacity(int k_format, int v_format, bool paged, bool full, bool ext) {
   // resident work-groups of the team kernel with the largest LDS chunk;
-  // cached per device and kernel instance, 0 when the device cannot tell
+  // cached per device and kernel instance (callers on several host threads
+  // may fill an entry at once: they store the same value), 0 when the device
+  // cannot tell
   if (ext && !full) return 0;
-  static int cache[16][2][3][2][2][2];
+  static std::atomic<int> cache[16][2][3][2][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
   const int ki = k_format == KVQ_FMT_FP8_E4M3 ? 1 : 0;
   const int vi = v_format == KVQ_FMT_FP8_E4M3 ? 1 : (v_format == KVQ_FMT_BF16 ? 2 : 0);
-  int &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0][ext ? 1 : 0];
-  if (c > 0) return c;
+  std::atomic<int> &c = cache[dev][ki][vi][paged ? 1 : 0][full ? 1 : 0][ext ? 1 : 0];
+  const int known = c.load(std::memory_order_relaxed);
+  if (known > 0) return known;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, team_kernel(k_format, v_format, paged, full, ext),
                                                    256, (size_t)TEAM_MAX_CHUNK * 4 * sizeof(float2)) != hipSuccess)
     return 0;
-  c = per_cu * cus;
-  return c;
+  c.store(per_cu * cus, std::memory_order_relaxed);
+  return per_cu * cus;
 }
 
 int team_capacity_max() {
