@@ -508,3 +508,30 @@ def test_plan_flags_and_status_word_are_checked(lib):
     assert _plan(lib, long, m).launches == 2
     long.plan_flags |= kvq.PLAN_FINALIZE_IN_PLACE
     assert _plan(lib, long, m).launches == 1
+
+
+def test_header_is_c99_and_a_c_client_links_and_plans(tmp_path):
+    """include/kvq.h compiles as strict C99 with warnings as errors, and a C
+    program linked against libkvq.so plans the batch-64 step (host-only
+    calls) with the same answers the Python binding gets."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    exe = tmp_path / "c_client"
+    src = os.path.join(os.path.dirname(__file__), "helpers", "c_client.c")
+    libdir = os.path.dirname(kvq.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I",
+                        os.path.dirname(HEADER), src, "-o", str(exe), "-L", libdir, "-lkvq",
+                        "-Wl,-rpath," + libdir], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    out = dict(line.split(" ", 1) for line in r.stdout.strip().splitlines())
+    assert out["abi"] == str(kvq.ABI_VERSION)
+    assert out["status"] == "0 ok"
+    assert out["plan"] == "chunk 12672 chunks 1 launches 1 team 0"
+    ws = [int(x) for x in out["workspace"].split()]
+    assert ws[0] == ws[1] > 0
+    assert out["bad"] == "head_dim 5"
