@@ -16,8 +16,9 @@ log A: within 1e-5 of the oracle below, and above by at most 1e-5 plus
 2^-18 max_t c_t, the upward rounding of c the kernels apply so that the
 bound stays sound (c not below its exact value for the stored witness);
 bound_raw, meter and the two-sided form are held to the interval that this
-log A interval maps to (1e-5 relative slack), with the survey's rule that
-+inf and a finite value are both accepted within 1e-3 of the overflow edge.
+log A interval maps to (1e-5 relative slack); within 1e-3 of the overflow
+edge both +inf and a finite value are accepted (the float overflow of
+1/2 expm1(2 log A) sits there).
 Tier B's radius is not rounded in either direction: 1e-5 plus 2^-18 max u on
 both sides."""
 import math
