@@ -244,7 +244,14 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     const int64_t per_group = groups >= target ? 1 : (target + groups - 1) / groups;
     int64_t c = (smax + per_group - 1) / per_group;
     c = (c + 63) / 64 * 64;
-    const int64_t min_chunk = (int64_t)groups * ((smax + 639) / 640) < 256 ? 256 : 640;
+    // (Not with block-scale INT8 regions: their wavefronts take whole
+    // 256-token blocks, so a 256-token chunk would keep one of four busy.)
+    // (the values count for the meter call too: both calls plan one chunk)
+    const bool blocks = (p.prefix_len > 0 && (a->prefix.k_format == KVQ_FMT_INT8_DITHER ||
+                                              a->prefix.v_format == KVQ_FMT_INT8_DITHER)) ||
+                        (p.suffix_cap > 0 && (a->suffix.k_format == KVQ_FMT_INT8_DITHER ||
+                                              a->suffix.v_format == KVQ_FMT_INT8_DITHER));
+    const int64_t min_chunk = (!blocks && (int64_t)groups * ((smax + 639) / 640) < 256) ? 256 : 640;
     chunk = (int)(c < min_chunk ? min_chunk : c);
   }
   p.chunk = chunk;

@@ -372,8 +372,8 @@ def test_automatic_chunks_are_at_least_640_tokens(lib):
     """The per-chunk plan fills about 512 work-groups, but no automatic chunk is
     shorter than 640 tokens (a multiple of 64): fewer, longer chunks won on
     small steps.  A step that would then have fewer work-groups than CUs (256)
-    takes chunks of at least 256 tokens instead.  An explicit split_tokens is
-    taken as given."""
+    takes chunks of at least 256 tokens instead, unless a region holds
+    block-scale INT8.  An explicit split_tokens is taken as given."""
     m = kvq.MeterOut(tv=FAKE, bound_raw=FAKE, meter=FAKE, log_a=FAKE)
     nt = kvq.PLAN_NO_TEAM
     for batch, hkv, suffix, chunk in ((64, 8, 12628, 12672), (8, 8, 32768, 4096), (4, 8, 131072, 8192),
@@ -385,6 +385,10 @@ def test_automatic_chunks_are_at_least_640_tokens(lib):
     two = _plan(lib, _args(batch=1, hkv=1, hq=4, prefix=632, suffix=64, kf="bf16", vf="fp8", exact=False,
                            witness=False), kvq.MeterOut())
     assert (two.chunk, two.chunks, two.launches) == (256, 4, 1)
+    # block-scale INT8 keeps 640: its wavefronts take whole 256-token blocks
+    for meter_only in (0, 1):
+        i8 = _plan(lib, _args(batch=1, hkv=8, hq=32, suffix=4096, kf="int8", vf="int8", flags=nt), m, meter_only)
+        assert (i8.chunk, i8.chunks) == (640, 7), (meter_only, i8.chunk)
     info = _plan(lib, _args(batch=16, suffix=1024, split=128, flags=nt), m)
     assert (info.chunk, info.chunks) == (128, 8)
 
