@@ -235,11 +235,10 @@ kvq_status make_plan(const kvq_attn_args *a, const kvq_meter_out *m, bool meter_
     // suffix step 46.6 us with 640-token chunks, 57.9 us with 448)
     //
     // A step that would then have fewer work-groups than CUs takes chunks of
-    // at least 256 tokens instead: a CU streams at most about 24 GB/s however
-    // many wavefronts it runs (measured: one 8-wavefront work-group per
-    // (request, KV head) on the 1,656-token step took 30.6 us against 27.9 us
-    // for 3 chunks of 4 wavefronts), so idle CUs are idle bandwidth (the
-    // single-request 696-token step: 15.6 us as 4 chunks, 17.6 us as 2).
+    // at least 256 tokens instead: with few work-groups each one's chain of
+    // tiles sets the step's time, and more, shorter chains finish sooner
+    // than the extra partials cost (measured: the single-request 696-token
+    // step 15.6 us as 4 chunks, 17.6 us as 2).
     const int64_t target = 512;
     const int64_t per_group = groups >= target ? 1 : (target + groups - 1) / groups;
     int64_t c = (smax + per_group - 1) / per_group;
