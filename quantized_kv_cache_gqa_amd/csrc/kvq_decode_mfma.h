@@ -26,7 +26,9 @@
 // 8j..8j+7 of four token rows (a contiguous 512-byte span per load across the
 // wavefront) and a byte transpose in registers (v_perm) forms, for each n, the
 // four tokens' bytes of dim 8j + n.  The 8 N-tiles accumulate the whole output
-// of the four heads (lanes 0..15 hold it).  BF16 values use vector-ALU FMAs.
+// of the four heads (lanes 0..15 hold it).  BF16 values take the same layout
+// at two bytes a value on v_mfma_f32_16x16x32_bf16, the weights split into
+// two bf16 pieces along the contraction (see the tile's P.V).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -153,7 +155,7 @@ struct TileRegs {
   uint4 ke[4];     // exact keys (bf16), 32 values
   uint2 wit;       // 4 witness bands (fp16)
   uint2 v8[4];     // FP8 values: 8 dims of 4 tokens (MFMA B layout)
-  uint4 vb[4];     // BF16 values: 16 dims of 2 tokens (vector-ALU layout)
+  uint4 vb[4];     // BF16 values: token 4 g + e, dims 8 j16 .. 8 j16 + 7
   float ks, vs;    // scales of this lane's compact (token, head) slot
   uint32_t vrec;   // value record of this lane's token: fp16 (rho, ||v||)
   uint2 kg[4];     // INT8 group scales: the 4 fp16 key scales of token 4 g + e
@@ -337,11 +339,12 @@ struct TileSrc {
       }
       T.vs = VF == KVQ_FMT_FP8_E4M3 ? vsb[rk] : 1.0f;
     } else if constexpr (VF == KVQ_FMT_BF16) {
-      const RowT r0 = row_of(t0 + (lane >> 3), P), r1 = row_of(t0 + 8 + (lane >> 3), P);
-      const uint4 *p0 = reinterpret_cast<const uint4 *>(vbb + r0 * (2 * D) + 32 * (lane & 7));
-      const uint4 *p1 = reinterpret_cast<const uint4 *>(vbb + r1 * (2 * D) + 32 * (lane & 7));
-      T.vb[0] = p0[0]; T.vb[1] = p0[1];
-      T.vb[2] = p1[0]; T.vb[3] = p1[1];
+      // the FP8 layout at two bytes a value: 16 lanes read one 256-byte row
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const RowT re = row_of(t0 + 4 * g + e, P);
+        T.vb[e] = *reinterpret_cast<const uint4 *>(vbb + re * (2 * D) + 16 * j16);
+      }
       T.vs = 1.0f;
     }
   }
@@ -636,17 +639,11 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
   float zv = 0.0f, vmax = 0.0f;      // value side: sum p~ rho, max ||v||
   float mn = NEG_INF, zn = 0.0f;     // l~ - c (Prop. 1's A-)
   float cmax = 0.0f;                 // max c (the tanh shape)
-  // FP8 values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
-  // register r = head r (lanes 0..15).  BF16 values: acc[h][i] per lane.
+  // Values: output in MFMA accumulators, N-tile n, lane j16 = dims 8 j16 + n,
+  // register r = head r (lanes 0..15).
   f32x4_t ov[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) ov[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int NACC = (VF == KVQ_FMT_BF16) ? G : 1;
-  float acc[NACC][16];
-#pragma unroll
-  for (int h = 0; h < NACC; ++h)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
 
   auto process = [&](const TileRegs &T, int t0) {
     // ---- logit contractions on the matrix cores
@@ -775,16 +772,11 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       float fh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) fh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 4 * h));
-      if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {   // MFMA accumulators
+      if constexpr (VF != VF_NONE) {               // MFMA accumulators
 #pragma unroll
         for (int n = 0; n < 8; ++n)
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[n][r] *= fh[r];
-      } else if constexpr (VF == KVQ_FMT_BF16) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[h][i] *= fh[h];
       }
       mq = mnew;
     }
@@ -879,25 +871,38 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
     } else if constexpr (VF == KVQ_FMT_BF16) {
-      w_s[wv][4 * (4 * g + pp) + hh] = p;
+      // weights as for FP8 values, split into two bf16 pieces hi + lo (exact
+      // to 2^-16 of p) along the contraction: K element i < 4 pairs piece hi
+      // of token 4 g + i with its value, i >= 4 piece lo with the same value,
+      // so one 16x16x32 product per N-tile adds (hi + lo) v; the bf16 values
+      // enter exactly and the products accumulate in fp32
+      w_s[wv][16 * hh + 4 * g + pp] = p;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const float4 w0 = *reinterpret_cast<const float4 *>(&w_s[wv][4 * (lane >> 3)]);
-      const float4 w1 = *reinterpret_cast<const float4 *>(&w_s[wv][4 * ((lane >> 3) + 8)]);
-      const float wa[G] = {w0.x, w0.y, w0.z, w0.w};
-      const float wb[G] = {w1.x, w1.y, w1.z, w1.w};
-      const uint32_t a[8] = {T.vb[0].x, T.vb[0].y, T.vb[0].z, T.vb[0].w,
-                             T.vb[1].x, T.vb[1].y, T.vb[1].z, T.vb[1].w};
-      const uint32_t c[8] = {T.vb[2].x, T.vb[2].y, T.vb[2].z, T.vb[2].w,
-                             T.vb[3].x, T.vb[3].y, T.vb[3].z, T.vb[3].w};
+      const float4 wa = *reinterpret_cast<const float4 *>(&w_s[wv][16 * (j16 & 3) + 4 * g]);
+      const bool arow = j16 < 4;
+      const float w4[4] = {arow ? wa.x : 0.0f, arow ? wa.y : 0.0f, arow ? wa.z : 0.0f, arow ? wa.w : 0.0f};
+      bf16x8_t aw;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        const float hi = bf16_hw_round(w4[i]);
+        aw[i] = (__bf16)hi;
+        aw[4 + i] = (__bf16)(w4[i] - hi);              // (w - hi exact in fp32)
+      }
+      const uint32_t rw[4][4] = {{T.vb[0].x, T.vb[0].y, T.vb[0].z, T.vb[0].w},
+                                 {T.vb[1].x, T.vb[1].y, T.vb[1].z, T.vb[1].w},
+                                 {T.vb[2].x, T.vb[2].y, T.vb[2].z, T.vb[2].w},
+                                 {T.vb[3].x, T.vb[3].y, T.vb[3].z, T.vb[3].w}};
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][2 * i] = fmaf(wa[h], bf16_lo(a[i]), fmaf(wb[h], bf16_lo(c[i]), acc[h][2 * i]));
-          acc[h][2 * i + 1] = fmaf(wa[h], bf16_hi(a[i]), fmaf(wb[h], bf16_hi(c[i]), acc[h][2 * i + 1]));
-        }
+      for (int n = 0; n < 8; ++n) {
+        // dim 8 j16 + n of tokens 4 g .. 4 g + 3: half n & 1 of word n >> 1
+        const int k = n >> 1;
+        const uint32_t v01 = (n & 1) ? ((rw[0][k] >> 16) | (rw[1][k] & 0xffff0000u))
+                                     : ((rw[0][k] & 0xffffu) | (rw[1][k] << 16));
+        const uint32_t v23 = (n & 1) ? ((rw[2][k] >> 16) | (rw[3][k] & 0xffff0000u))
+                                     : ((rw[2][k] & 0xffffu) | (rw[3][k] << 16));
+        ov[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, as_bf16x8(uint4{v01, v23, v01, v23}), ov[n], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -974,15 +979,6 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
       cmax = fmaxf(cmax, __shfl_xor(cmax, off));
     }
   }
-  if constexpr (VF == KVQ_FMT_BF16) {
-#pragma unroll
-    for (int off = 8; off < 64; off <<= 1)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
-  }
-
   if (lane < 16 && pp == 0) {                      // lane 4h holds head h
     part_s[wv][hh][0] = mq; part_s[wv][hh][1] = zq;
     part_s[wv][hh][2] = mm; part_s[wv][hh][3] = zm;
@@ -994,19 +990,12 @@ __device__ __forceinline__ void mfma_chunk(const DecodeLaunch &d, int b, int kvh
     part_s[wv][hh][PART_ZN] = zn;
     part_s[wv][hh][PART_CMAX] = cmax;
   }
-  if constexpr (VF == KVQ_FMT_FP8_E4M3 || VF == KVQ_FMT_INT8_DITHER || VF == KVQ_FMT_INT8_G32) {   // MFMA accumulators
+  if constexpr (VF != VF_NONE) {                  // MFMA accumulators
     if (lane < 16) {
 #pragma unroll
       for (int n = 0; n < 8; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) part_s[wv][r][8 + 8 * lane + n] = ov[n][r];
-    }
-  } else if constexpr (VF == KVQ_FMT_BF16) {
-    if (lane < 8) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part_s[wv][h][8 + 16 * lane + i] = acc[h][i];
     }
   } else {
     if (lane < 16) {
