@@ -58,6 +58,57 @@ def test_fp8_hardware_decode_matches_e4m3_table(gpu_lib):
     np.testing.assert_array_equal(out.cpu().numpy().reshape(-1), ref.astype(np.float32))
 
 
+@pytest.mark.parametrize("scale", [1e-30, 1.0, 1e30])
+@pytest.mark.parametrize("paged", [False, True])
+def test_bf16_values_keep_their_range(gpu_lib, scale, paged):
+    """BF16 values enter the matrix product exactly (no fp16 conversion), so
+    values far outside fp16's range, huge or tiny, come out to the output bar
+    against the oracle (exact attention: BF16 keys, no witness); 700 ragged
+    tokens over several tiles, both the dense and the paged suffix."""
+    from oracle.attention import decode_step
+    kvq = gpu_lib
+    dev = "cuda"
+    rng = np.random.default_rng(23)
+    B, H, S, G = 2, 2, 704, 4
+    lens = [700, 333]
+    k = torch.from_numpy(rng.standard_normal((B, H, S, 128)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy((rng.standard_normal((B, H, S, 128)) * scale).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((B, H * G, 128)).astype(np.float32))
+    st = kvq.alloc_stored(B, H, S, "bf16", "bf16", False, dev)
+    st.k.copy_(k.to(dev))
+    st.v.copy_(v.to(dev))
+    ln = torch.tensor(lens, dtype=torch.int32, device=dev)
+    if paged:
+        # 16-token pages in shuffled order: page table [B, S / 16]
+        ps, mp = 16, S // 16
+        table = torch.from_numpy(rng.permutation(B * mp).astype(np.int32)).view(B, mp).to(dev)
+
+        def scatter(t):
+            src = t.view(B, H, mp, ps, 128).permute(0, 2, 1, 3, 4).reshape(B * mp, H, ps, 128)
+            out = torch.empty_like(src)
+            out[table.view(-1).long()] = src
+            return out.contiguous()
+
+        pst = kvq.Stored("bf16", "bf16", scatter(st.k), scatter(st.v), None, None, None, None, None, None)
+        view = kvq.RegionView(pst, S, lengths=ln, page_table=table, page_size=ps, use_witness=False)
+    else:
+        view = kvq.RegionView(st, S, lengths=ln, use_witness=False)
+    out, _ = kvq.decode_attn(q.to(dev), H, None, view, sm_scale=SM_SCALE, meter=False)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    for b in range(B):
+        for h in range(H):
+            n = lens[b]
+            kk = k[b, h, :n].double().numpy()
+            vv = v[b, h, :n].double().numpy()
+            ref = decode_step(q[b, h * G:(h + 1) * G].double().numpy(), kk, kk, vv, None, SM_SCALE)
+            og = out[b, h * G:(h + 1) * G].double().cpu().numpy()
+            for g in range(G):
+                rel = np.linalg.norm(og[g] - ref["out"][g]) / np.linalg.norm(ref["out"][g])
+                assert rel <= 2e-3, (scale, paged, b, h, g, rel)
+                assert np.max(np.abs(og[g] - ref["out"][g])) <= 2e-3 * np.max(np.abs(ref["out"][g]))
+
+
 def test_write_path_edge_values_bit_exact(gpu_lib):
     """Zero rows, tiny and huge magnitudes, E4M3 midpoints: codes, scales and
     witness against the oracle encoders."""
